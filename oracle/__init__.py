@@ -1,0 +1,24 @@
+"""CPU oracle for MLA with decoupled RoPE, weight-absorbed form.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+its Python binding) may import, call or link anything here.  Only the test
+suite, the smoke check and the CPU-baseline leg of the benchmark use it.
+
+Everything here is plain, slow, float64 numpy written from the pages'
+equations:
+
+* ``rope``        -- the rotary position operator R_p (RoFormer Theta, pairs
+                     (2j, 2j+1)).
+* ``attention``   -- the materialised definition (K = [W_UK c ; R_t k^R],
+                     V = W_UV c, plain softmax attention), which is the
+                     spec; the absorbed twin (q~ = W_UK^T q^C, score against
+                     the latent), used only as a self-check; and a brute-force
+                     pure-Python version for tiny cases.
+* ``paging``      -- where a (sequence, position) lands in a paged cache.
+* ``accounting``  -- per-token cache sizes of the layouts the pages compare.
+
+No function here shares code with the GPU path, and none reads any value the
+GPU produced.
+"""
+
+from . import accounting, attention, paging, rope  # noqa: F401

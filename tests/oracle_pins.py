@@ -1,0 +1,287 @@
+"""Pins that tie the CPU oracle to what the pages and the mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+a closed form, an invariant, a special case that reduces to a library
+routine, brute force on a tiny input, or a figure the pages print.  The test
+modules call them directly, and the mutation tests plant plausible mistakes
+in the oracle and check that at least one pin fails.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+from oracle import accounting, attention, paging, rope
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.sqrt(np.mean(b * b)), 1e-300))
+
+
+def _small_problem(seed=0, n_heads=3, d_h=8, d_v=6, d_c=12, d_r=8, t=40, n=2):
+    rng = np.random.default_rng(seed)
+    return dict(
+        qc=rng.standard_normal((n, n_heads, d_h)),
+        qr=rng.standard_normal((n, n_heads, d_r)),
+        c=rng.standard_normal((t, d_c)),
+        kr=rng.standard_normal((t, d_r)),
+        w_uk=rng.standard_normal((n_heads, d_h, d_c)) / math.sqrt(d_c),
+        w_uv=rng.standard_normal((n_heads, d_v, d_c)) / math.sqrt(d_c),
+        scale=1.0 / math.sqrt(d_h + d_r),
+    )
+
+
+# ---------------------------------------------------------------- RoPE ----
+
+def pin_rope_identity_at_zero():
+    """R_0 = I exactly (every angle is 0)."""
+    for d in (2, 8, 64):
+        assert np.array_equal(rope.rotation_matrix(0, d), np.eye(d))
+        x = np.random.default_rng(d).standard_normal(d)
+        assert np.array_equal(rope.rotate(x, 0), x)
+
+
+def pin_rope_closed_form():
+    """theta_j = base^(-2j/d): theta_0 = 1 and, for d = 4, theta_1 = 10000^(-1/2) = 0.01.
+
+    With theta_0 = 1 the first plane turns by exactly p radians, counter-
+    clockwise: e_0 -> (cos p, sin p), e_1 -> (-sin p, cos p).  Pairs are
+    (2j, 2j+1): rotating e_2 in 8 dims moves only coordinates 2 and 3.
+    """
+    th = rope.thetas(4)
+    assert th[0] == 1.0 and abs(th[1] - 0.01) < 1e-17
+    th64 = rope.thetas(64)
+    assert abs(th64[16] - 0.01) < 1e-17 and abs(th64[31] - 10000.0 ** (-62 / 64)) < 1e-18
+    for p in (1, 3, 255):
+        got = rope.rotate(np.array([1.0, 0.0]), p)
+        assert np.allclose(got, [math.cos(p), math.sin(p)], rtol=0, atol=1e-15)
+        got = rope.rotate(np.array([0.0, 1.0]), p)
+        assert np.allclose(got, [-math.sin(p), math.cos(p)], rtol=0, atol=1e-15)
+    e2 = np.zeros(8)
+    e2[2] = 1.0
+    got = rope.rotate(e2, 7)
+    a = 7 * 10000.0 ** (-2 / 8)
+    want = np.zeros(8)
+    want[2], want[3] = math.cos(a), math.sin(a)
+    assert np.allclose(got, want, rtol=0, atol=1e-15)
+    # the vectorised rotation and the explicit matrix agree
+    x = np.random.default_rng(1).standard_normal(32)
+    for p in (0, 5, 1000, 131071):
+        assert np.allclose(rope.rotation_matrix(p, 32) @ x, rope.rotate(x, p), rtol=0, atol=1e-12)
+
+
+def pin_rope_orthogonal():
+    for p in (1, 17, 4095, 131071):
+        r = rope.rotation_matrix(p, 64)
+        assert np.max(np.abs(r.T @ r - np.eye(64))) < 1e-13
+
+
+def pin_rope_relative():
+    """R_t^T R_m = R_{m-t} (the RoPE relative property)."""
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        t, m = (int(v) for v in rng.integers(0, 1024, size=2))
+        lhs = rope.rotation_matrix(t, 64).T @ rope.rotation_matrix(m, 64)
+        assert np.max(np.abs(lhs - rope.rotation_matrix(m - t, 64))) < 1e-12
+    p_max = 1 << 17
+    bound = 16 * 2.0 ** -52 * p_max
+    for _ in range(10):
+        t, m = (int(v) for v in rng.integers(0, p_max, size=2))
+        lhs = rope.rotation_matrix(t, 64).T @ rope.rotation_matrix(m, 64)
+        assert np.max(np.abs(lhs - rope.rotation_matrix(m - t, 64))) < bound
+
+
+def pin_shift_invariance():
+    """Shifting every position by a constant leaves scores, and so outputs, unchanged."""
+    pb = _small_problem(seed=3, t=30, n=3)
+    q_pos = np.array([29, 10, 20])
+    base = attention.materialised(pb["qc"], pb["qr"], q_pos, pb["c"], pb["kr"], pb["w_uk"],
+                                  pb["w_uv"], pb["scale"], causal=True)
+    for delta in (1, 1000, 1 << 17):
+        sh = attention.materialised(pb["qc"], pb["qr"], q_pos + delta, pb["c"], pb["kr"], pb["w_uk"],
+                                    pb["w_uv"], pb["scale"], causal=True, key_offset=delta)
+        for k in ("o", "obar", "lse"):
+            assert _rel(sh[k], base[k]) < 1e-9, (k, delta)
+    # and a shift of the query alone does change them (the test can see a mistake)
+    moved = attention.materialised(pb["qc"], pb["qr"], q_pos, pb["c"], pb["kr"], pb["w_uk"],
+                                   pb["w_uv"], pb["scale"], causal=True, key_offset=1)
+    assert _rel(moved["lse"][0], base["lse"][0]) > 1e-6
+
+
+# ----------------------------------------------------------- attention ----
+
+def pin_absorbed_equals_materialised():
+    """Absorption is exact: q~ = W_UK^T q^C and W_UV sum(alpha c) reproduce the definition."""
+    for causal in (False, True):
+        pb = _small_problem(seed=11, n_heads=4, d_h=16, d_v=16, d_c=32, d_r=8, t=200, n=5)
+        q_pos = np.array([199, 150, 3, 0, 120]) if causal else np.full(5, 199)
+        m = attention.materialised(pb["qc"], pb["qr"], q_pos, pb["c"], pb["kr"], pb["w_uk"],
+                                   pb["w_uv"], pb["scale"], causal=causal, key_chunk=64)
+        a = attention.absorbed(pb["qc"], pb["qr"], q_pos, pb["c"], pb["kr"], pb["w_uk"],
+                               pb["w_uv"], pb["scale"], causal=causal)
+        for k in ("o", "obar", "lse"):
+            assert _rel(a[k], m[k]) <= 1e-12, (k, causal, _rel(a[k], m[k]))
+
+
+def pin_key_rank():
+    """The materialised content-key matrix [T x H d_h] has rank exactly d_c (T > d_c)."""
+    rng = np.random.default_rng(5)
+    t, h, d_h, d_c, d_r = 96, 4, 16, 24, 8
+    c = rng.standard_normal((t, d_c))
+    kr = rng.standard_normal((t, d_r))
+    w_uk = rng.standard_normal((h, d_h, d_c))
+    k = attention.materialise_keys(c, kr, w_uk, np.arange(t))
+    content = k[:, :, :d_h].reshape(t, h * d_h)
+    sv = np.linalg.svd(content, compute_uv=False)
+    assert sv[d_c - 1] / sv[0] > 1e-8 and sv[d_c] / sv[0] < 1e-13
+    # with the shared position key appended once, the rank is d_c + d_r
+    full = np.concatenate([content, k[:, 0, d_h:]], axis=1)
+    sv = np.linalg.svd(full, compute_uv=False)
+    assert sv[d_c + d_r - 1] / sv[0] > 1e-8 and sv[d_c + d_r] / sv[0] < 1e-13
+    # each head's key carries the same rotated k^R
+    assert np.array_equal(k[:, 0, d_h:], k[:, h - 1, d_h:])
+
+
+def pin_brute_force():
+    """2 heads x 4 tokens: scalar loops agree with the vectorised definition."""
+    rng = np.random.default_rng(13)
+    args = dict(qc=rng.standard_normal((2, 2, 2)), qr=rng.standard_normal((2, 2, 2)),
+                c=rng.standard_normal((4, 3)), kr=rng.standard_normal((4, 2)),
+                w_uk=rng.standard_normal((2, 2, 3)), w_uv=rng.standard_normal((2, 2, 3)), scale=0.7)
+    for causal, q_pos in ((False, np.array([3, 3])), (True, np.array([3, 1]))):
+        bf = attention.brute_force(args["qc"], args["qr"], q_pos, args["c"], args["kr"], args["w_uk"],
+                                   args["w_uv"], args["scale"], causal=causal)
+        m = attention.materialised(args["qc"], args["qr"], q_pos, args["c"], args["kr"], args["w_uk"],
+                                   args["w_uv"], args["scale"], causal=causal)
+        for k in ("o", "obar", "lse"):
+            assert _rel(m[k], bf[k]) <= 1e-14, (k, causal)
+
+
+def pin_special_cases():
+    """T = 1 gives obar = c_0 exactly; zero queries give uniform weights; no keys gives 0 / -inf."""
+    pb = _small_problem(seed=17, t=1, n=1)
+    m = attention.materialised(pb["qc"], pb["qr"], [0], pb["c"], pb["kr"], pb["w_uk"], pb["w_uv"],
+                               pb["scale"])
+    assert np.array_equal(m["obar"][0, 0], pb["c"][0])
+    pb = _small_problem(seed=19, t=33, n=1)
+    zq = np.zeros_like(pb["qc"])
+    zr = np.zeros_like(pb["qr"])
+    m = attention.materialised(zq, zr, [32], pb["c"], pb["kr"], pb["w_uk"], pb["w_uv"], pb["scale"])
+    assert _rel(m["obar"][0, 1], pb["c"].mean(axis=0)) < 1e-14
+    assert abs(m["lse"][0, 0] - math.log(33)) < 1e-14
+    e = attention.materialised(pb["qc"], pb["qr"], [0], pb["c"][:0], pb["kr"][:0], pb["w_uk"],
+                               pb["w_uv"], pb["scale"])
+    assert np.all(e["obar"] == 0) and np.all(e["o"] == 0) and np.all(np.isneginf(e["lse"]))
+
+
+def pin_sdpa():
+    """Against torch's scaled_dot_product_attention on the CPU in float64.
+
+    No-RoPE control (q^R = 0): textbook MHA with K = W_UK c, V = W_UV c.
+    General case: K = [W_UK c ; R_t k^R], Q = [q^C ; R_m q^R], causal mask.
+    """
+    import torch
+    import torch.nn.functional as F
+
+    pb = _small_problem(seed=23, n_heads=4, d_h=16, d_v=12, d_c=20, d_r=8, t=50, n=6)
+    q_pos = np.array([49, 40, 7, 0, 25, 49])
+    w_uk, w_uv, c = pb["w_uk"], pb["w_uv"], pb["c"]
+    k_content = np.stack([c @ w_uk[i].T for i in range(4)])  # [H, T, d_h], written out per head
+    v = np.stack([c @ w_uv[i].T for i in range(4)])         # [H, T, d_v]
+    # no-RoPE control
+    q = np.transpose(pb["qc"], (1, 0, 2))
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k_content),
+                                         torch.from_numpy(v), scale=pb["scale"]).numpy()
+    m = attention.materialised(pb["qc"], np.zeros_like(pb["qr"]), np.full(6, 49), c, pb["kr"] * 0,
+                               w_uk, w_uv, pb["scale"])
+    assert _rel(m["o"], np.transpose(ref, (1, 0, 2))) < 1e-13
+    # general, causal
+    qf = np.concatenate([pb["qc"], rope.rotate(pb["qr"], q_pos[:, None])], axis=-1).transpose(1, 0, 2)
+    kro = rope.rotate(pb["kr"], np.arange(50))
+    kf = np.concatenate([k_content, np.broadcast_to(kro, (4, 50, 8))], axis=-1)
+    mask = torch.from_numpy(np.arange(50)[None, :] <= q_pos[:, None])
+    ref = F.scaled_dot_product_attention(torch.from_numpy(np.ascontiguousarray(qf)),
+                                         torch.from_numpy(np.ascontiguousarray(kf)),
+                                         torch.from_numpy(v), attn_mask=mask, scale=pb["scale"]).numpy()
+    m = attention.materialised(pb["qc"], pb["qr"], q_pos, c, pb["kr"], w_uk, w_uv, pb["scale"], causal=True)
+    assert _rel(m["o"], np.transpose(ref, (1, 0, 2))) < 1e-13
+
+
+def pin_prefill_is_decode_of_prefix():
+    """A causal query at position m equals a decode over keys 0 .. m."""
+    pb = _small_problem(seed=29, t=64, n=4)
+    q_pos = np.array([0, 17, 40, 63])
+    pre = attention.materialised(pb["qc"], pb["qr"], q_pos, pb["c"], pb["kr"], pb["w_uk"], pb["w_uv"],
+                                 pb["scale"], causal=True)
+    for i, m in enumerate(q_pos):
+        dec = attention.materialised(pb["qc"][i:i + 1], pb["qr"][i:i + 1], [m], pb["c"][:m + 1],
+                                     pb["kr"][:m + 1], pb["w_uk"], pb["w_uv"], pb["scale"])
+        for k in ("o", "obar", "lse"):
+            assert _rel(pre[k][i], dec[k][0]) < 1e-13, (k, int(m))
+
+
+# ------------------------------------------------------ paging, figures ----
+
+def pin_paging():
+    """Hand-worked example: page size 4, sequence 1 owns physical pages [5, 2]."""
+    table = np.array([[0, 3, -1], [5, 2, -1]], dtype=np.int32)
+    assert paging.slot(table, 1, 0, 4) == 20
+    assert paging.slot(table, 1, 3, 4) == 23
+    assert paging.slot(table, 1, 4, 4) == 8
+    assert paging.slot(table, 1, 6, 4) == 10
+    assert paging.slot(table, 0, 5, 4) == 13
+    try:
+        paging.slot(table, 0, 9, 4)
+    except IndexError:
+        pass
+    else:
+        raise AssertionError("unallocated page must raise")
+
+
+def pin_page_figures():
+    g = json.load(open(GOLDEN))
+    f = g["toy_mha_numbers_per_token"]
+    assert accounting.mha(f["shape"]["n_heads"], f["shape"]["d_k"], f["shape"]["d_v"]) == f["value"]
+    f = g["toy_mla_numbers_per_token_per_head_rope"]
+    toy = accounting.mla_per_head_rope(f["shape"]["d_latent"], f["shape"]["n_heads"], f["shape"]["d_rope"])
+    assert toy == f["value"]
+    assert abs(accounting.reduction(toy, 4096) - g["toy_reduction_about"]["value"]) <= g["toy_reduction_about"]["abs_tol"]
+    f = g["dsv2_mha_dims_per_token"]
+    mha = accounting.mha(f["shape"]["n_heads"], f["shape"]["d_h"], f["shape"]["d_h"])
+    assert mha == f["value"]
+    lat = g["dsv2_latent_dims_per_token"]["value"]
+    assert abs(mha / lat - g["dsv2_latent_factor_about"]["value"]) <= 1.0
+    f = g["dsv2_decoupled_dims_per_token"]
+    dec = accounting.mla_shared_rope(f["shape"]["d_latent"], f["shape"]["d_rope"])
+    assert dec == f["value"]
+    assert abs(mha / dec - g["dsv2_decoupled_fraction_about"]["value"]) <= g["dsv2_decoupled_fraction_about"]["abs_tol"]
+
+
+ALL_PINS = [
+    pin_rope_identity_at_zero, pin_rope_closed_form, pin_rope_orthogonal, pin_rope_relative,
+    pin_shift_invariance, pin_absorbed_equals_materialised, pin_key_rank, pin_brute_force,
+    pin_special_cases, pin_sdpa, pin_prefill_is_decode_of_prefix, pin_paging, pin_page_figures,
+]
+
+
+def failing_pins():
+    """Names of the pins that fail (exceptions other than AssertionError count as failures)."""
+    bad = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception:  # noqa: BLE001 - a mutation may break a pin in any way
+            bad.append(pin.__name__)
+    return bad
+
+
+__all__ = ["ALL_PINS", "failing_pins", "oracle"]

@@ -1,0 +1,102 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+from oracle import attention, paging, rope
+
+_orig_rotate = rope.rotate
+_orig_thetas = rope.thetas
+_orig_matrix = rope.rotation_matrix
+_orig_materialised = attention.materialised
+_orig_values = attention.materialise_values
+_orig_keys = attention.materialise_keys
+_orig_visible = attention._visible
+_orig_slot = paging.slot
+
+
+def _clockwise_rotate(x, positions, base=10000.0):
+    return _orig_rotate(x, -np.asarray(positions), base)
+
+
+def _clockwise_matrix(p, d, base=10000.0):
+    return _orig_matrix(-p, d, base)
+
+
+def _half_split_rotate(x, positions, base=10000.0):
+    # "rotate-half" pairing (j, j + d/2) instead of (2j, 2j+1)
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    perm = np.empty(d, dtype=int)
+    perm[0::2] = np.arange(d // 2)
+    perm[1::2] = np.arange(d // 2) + d // 2
+    y = _orig_rotate(x[..., perm], positions, base)
+    out = np.empty_like(y)
+    out[..., perm] = y
+    return out
+
+
+def _wrong_thetas(d, base=10000.0):
+    return np.power(np.float64(base), -np.arange(d // 2, dtype=np.float64) / d)
+
+
+def _keys_without_rope(c, kr, w_uk, key_pos, base=10000.0):
+    k = _orig_keys(c, kr, w_uk, key_pos, base)
+    k[..., w_uk.shape[1]:] = 0.0
+    return k
+
+
+def _keys_unrotated(c, kr, w_uk, key_pos, base=10000.0):
+    return _orig_keys(c, kr, w_uk, np.zeros_like(np.asarray(key_pos)), base)
+
+
+def _values_from_uk(c, w_uv):
+    return _orig_values(c, w_uv[:, ::-1, :])  # wrong row order of W_UV (a transposed-index slip)
+
+
+def _strict_causal(q_pos, key_pos, causal):
+    if causal:
+        return key_pos[None, :] < np.asarray(q_pos)[:, None]
+    return _orig_visible(q_pos, key_pos, causal)
+
+
+def _materialised_no_scale(*a, **k):
+    if len(a) > 7:
+        a = a[:7] + (1.0,) + a[8:]
+    else:
+        k["scale"] = 1.0
+    return _orig_materialised(*a, **k)
+
+
+def _materialised_query_unrotated(qc, qr, q_pos, *a, **k):
+    return _orig_materialised(qc, qr, np.zeros_like(np.asarray(q_pos)), *a, **k)
+
+
+def _bad_slot(table, seq, pos, ps):
+    return int(table[seq, pos // ps]) * ps + pos // ps
+
+
+MUTATIONS = {
+    "rope_clockwise": [(rope, "rotate", _clockwise_rotate), (rope, "rotation_matrix", _clockwise_matrix)],
+    "rope_half_split_pairs": [(rope, "rotate", _half_split_rotate)],
+    "rope_theta_exponent": [(rope, "thetas", _wrong_thetas)],
+    "keys_drop_rope_term": [(attention, "materialise_keys", _keys_without_rope)],
+    "keys_not_rotated": [(attention, "materialise_keys", _keys_unrotated)],
+    "values_wrong_rows": [(attention, "materialise_values", _values_from_uk)],
+    "causal_excludes_diagonal": [(attention, "_visible", _strict_causal)],
+    "score_scale_dropped": [(attention, "materialised", _materialised_no_scale)],
+    "query_not_rotated": [(attention, "materialised", _materialised_query_unrotated)],
+    "paging_offset_slip": [(paging, "slot", _bad_slot)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    assert pins.failing_pins() == [], "pins must pass on the unmutated oracle"
+    for mod, attr, fn in MUTATIONS[name]:
+        monkeypatch.setattr(mod, attr, fn)
+    failed = pins.failing_pins()
+    assert failed, f"mutation {name} slipped past every pin"
