@@ -1,0 +1,177 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) library for Multi-head Latent
+ * Attention with decoupled RoPE in its weight-absorbed form.
+ *
+ * What is computed (per head i, query at position m, cached token t):
+ *
+ *   q~_i      = W_UK,i^T q^C_i                       (query absorption)
+ *   s_t       = scale * ( q~_i . c_t + R_m q^R_i . R_t k^R_t )
+ *   alpha     = softmax_t(s)            over the visible tokens
+ *   obar_i    = sum_t alpha_t c_t                    (latent output)
+ *   o_i       = W_UV,i obar_i                        (output absorption)
+ *
+ * Sources: "AI decoupled RoPE MLA" (operatorworld.com) -- recap section for
+ * the two absorbed forms (q~ = W^UK^T q, Attn = W^UV sum alpha c), and the
+ * decoupled-RoPE section for the score as the sum of a content term and a
+ * rotated position term with a d_r-wide position key; "Latent Attention Meets
+ * RoPE" (sahipadhai.cc), "Two small, telling details": the position key is
+ * one vector per token shared by every head, and the cache holds only the
+ * latent and that key; "Multi-Head Latent Attention" (talalahmed.dev), "Why
+ * this matters on a GPU": decode still runs the softmax and the weighted sum.
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Every pointer to tensor data is DEVICE memory unless its name ends in
+ *   _host.  Tensors are dense and row-major in the shapes given.  The caller
+ *   owns every buffer; the library allocates nothing and keeps no pointer
+ *   after a call returns.
+ * - dtype: all floating-point tensors that cross the ABI share dims->dtype
+ *   (MLA_F32 or MLA_BF16); lse is always float32; indices are int32.
+ *   Accumulation is float32 in every kernel.
+ * - Work is enqueued on `stream` (a hipStream_t, NULL = default stream) and
+ *   is asynchronous: no call synchronises.  Keep buffers alive until the
+ *   stream has passed the work.
+ * - Errors: arguments the host can see are checked before anything is
+ *   launched; a failed check returns a status code and launches nothing.
+ *   mla_last_error() then returns a thread-local description.  Device data
+ *   (positions, page ids, lengths) is not validated on the host: an
+ *   out-of-range page id or sequence index makes the kernels skip (for
+ *   writes) or clamp (for reads) that access, so memory stays safe but the
+ *   affected outputs are unspecified.
+ * - Page size must be 64 tokens.  Supported (n_heads, d_latent, d_rope)
+ *   for MLA_BF16 attention: (16, 256, 32) and (128, 512, 64); MLA_F32
+ *   accepts any n_heads <= 1024, d_latent <= 1024, d_rope <= 128.
+ * - Outputs never alias inputs, except that mla_rope_apply and mla_absorb_q
+ *   write disjoint column ranges of the same q_lat buffer.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, negative size, odd d_rope, ... */
+  MLA_ERR_UNSUPPORTED = 2, /* a shape / dtype combination with no kernel  */
+  MLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than needed    */
+  MLA_ERR_HIP = 4          /* a HIP runtime call or launch failed         */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef struct {
+  int32_t n_heads;     /* H: query heads                                  */
+  int32_t d_head;      /* d_h: content query / key width per head        */
+  int32_t d_v;         /* value width per head                           */
+  int32_t d_latent;    /* d_c: width of the cached latent c_t            */
+  int32_t d_rope;      /* d_r: width of the decoupled RoPE channel, even */
+  int32_t page_size;   /* tokens per cache page (must be 64)             */
+  int32_t dtype;       /* mla_dtype                                      */
+  float softmax_scale; /* one scale on the summed score                  */
+  double rope_base;    /* theta_j = rope_base^(-2j/d_r)                  */
+} mla_dims;
+
+/* A paged latent cache.  Row (page, slot) holds [ c_t | R_t k^R_t ]: the
+ * latent (d_latent) followed by the position key already rotated to its own
+ * position t (d_rope).  Sequence b's position p is in physical page
+ * block_table[b * max_pages_per_seq + p / page_size], row p % page_size. */
+typedef struct {
+  void* data;                 /* [num_pages, page_size, d_latent + d_rope]  */
+  int64_t num_pages;
+  const int32_t* block_table; /* [num_seqs, max_pages_per_seq], -1 = none   */
+  int32_t num_seqs;
+  int32_t max_pages_per_seq;
+} mla_paged_cache;
+
+/* mla_rope_apply -- the decoupled RoPE channel ("AI decoupled RoPE MLA",
+ * decoupled-RoPE section: RoPE is applied to the d_r-wide q^R and k^R only;
+ * "Detailed Illustration of the Problem", Step 1: rotation by R_{Theta,p}).
+ *
+ * Query part: for n < n_q and every head h,
+ *   q_lat[n, h, d_latent : d_latent + d_rope] = R_{q_pos[n]} q_rope[n, h, :]
+ *   q_rope [n_q, H, d_rope], q_pos [n_q], q_lat [n_q, H, d_latent + d_rope].
+ * Cache part: for m < n_kv, the row of (kv_seq[m], kv_pos[m]) becomes
+ *   [ kv_latent[m, :] | R_{kv_pos[m]} k_rope[m, :] ]
+ *   kv_latent [n_kv, d_latent], k_rope [n_kv, d_rope].
+ * Angles p * theta_j and their sine / cosine are formed in float64.  Either
+ * part may be empty (n = 0; its pointers may then be NULL).  Rows whose
+ * sequence, position or page id is out of range are skipped. */
+mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache,
+                          const void* q_rope, const int32_t* q_pos, int64_t n_q, void* q_lat,
+                          const void* kv_latent, const void* k_rope, const int32_t* kv_seq,
+                          const int32_t* kv_pos, int64_t n_kv, void* stream);
+
+/* mla_absorb_q -- query absorption ("AI decoupled RoPE MLA", recap section:
+ * q~_m = W^UK^T q_m, merged ahead of time and independent of the cache).
+ *   q_lat[n, h, 0 : d_latent] = W_UK[h]^T q_nope[n, h, :]
+ *   q_nope [n_q, H, d_head]; w_uk [H, d_head, d_latent] (stored [out, in],
+ *   so k^C = W_UK[h] c); q_lat [n_q, H, d_latent + d_rope]. */
+mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int64_t n_q,
+                        void* q_lat, void* stream);
+
+/* Bytes of workspace mla_decode needs for this batch (0 when no sequence is
+ * split).  seq_lens_host [batch] must hold the same lengths later passed to
+ * mla_decode. */
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host);
+
+/* mla_decode -- absorbed decode attention over the latent cache, split over
+ * the cache ("Multi-Head Latent Attention", "Why this matters on a GPU":
+ * decode reads the whole cache and still runs softmax and the weighted sum;
+ * "AI decoupled RoPE MLA", decoupled-RoPE score equation).
+ *   query b sits at position seq_lens[b] - 1 and sees cached positions
+ *   0 .. seq_lens[b] - 1;  q_lat [batch, H, d_latent + d_rope] (from
+ *   mla_rope_apply + mla_absorb_q);  out_latent [batch, H, d_latent] gets
+ *   obar = sum_t alpha_t c_t;  lse [batch, H] (float32, may be NULL) gets
+ *   log sum_t exp(s_t).  A sequence of length 0 yields obar = 0, lse = -inf.
+ * seq_lens is the device copy, seq_lens_host the same values on the host
+ * (used to plan the split).  workspace: device memory of at least
+ * mla_decode_workspace_size() bytes (may be NULL when that is 0).
+ * The result is bitwise reproducible and independent of which physical
+ * pages hold which positions.  Environment MLA_DECODE_SPLIT_PAGES=k forces
+ * splits of k pages (tests); it must be set identically for the size query. */
+mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                      const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch,
+                      void* out_latent, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* mla_prefill -- causal chunked prefill in the same absorbed form.
+ *   Sequence b contributes queries cu_q[b] .. cu_q[b+1]-1; its j-th query
+ *   sits at position q_start_pos[b] + j and sees cached positions t <= that
+ *   position (the chunk's own rows must already be in the cache, written by
+ *   mla_rope_apply).  q_lat [cu_q[batch], H, d_latent + d_rope];
+ *   out_latent [cu_q[batch], H, d_latent]; lse [cu_q[batch], H] or NULL.
+ * cu_q_host / q_start_pos_host are host copies of cu_q / q_start_pos. */
+mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                       const int32_t* cu_q, const int32_t* q_start_pos, const int32_t* cu_q_host,
+                       const int32_t* q_start_pos_host, int32_t batch, void* out_latent, float* lse,
+                       void* stream);
+
+/* mla_out_proj -- output absorption ("AI decoupled RoPE MLA", recap section:
+ * Attn_m = W^UV sum_t alpha_mt c_t).
+ *   out[n, h, :] = W_UV[h] out_latent[n, h, :]
+ *   out_latent [n, H, d_latent]; w_uv [H, d_v, d_latent]; out [n, H, d_v]. */
+mla_status mla_out_proj(const mla_dims* dims, const void* out_latent, const void* w_uv, int64_t n,
+                        void* out, void* stream);
+
+/* Static text for a status code. */
+const char* mla_status_string(mla_status status);
+
+/* Thread-local description of the last failed call on this thread ("" if
+ * none).  Valid until the next call on the same thread. */
+const char* mla_last_error(void);
+
+/* Split plan mla_decode would use: pages per split and the number of work
+ * items (sequence, split) it launches.  For tests and benchmarks. */
+mla_status mla_decode_plan(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host,
+                           int32_t* split_pages, int64_t* n_items);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,13 @@
+"""MI355X-native Multi-head Latent Attention with decoupled RoPE (weight-absorbed form).
+
+The computation lives in libmla.so (hand-written HIP kernels for gfx950 behind
+the C ABI of include/mla.h).  This package is its Python binding plus the
+device-side state that strings the five calls into decode and prefill steps.
+Importing it without the built library raises ImportError.
+"""
+
+from .binding import (  # noqa: F401
+    LIB, LIB_PATH, MLADims, MLAError, absorb_q, decode, decode_plan, decode_workspace,
+    decode_workspace_size, out_proj, prefill, rope_apply,
+)
+from .pipeline import DecodeStep, LatentCache, PrefillStep  # noqa: F401

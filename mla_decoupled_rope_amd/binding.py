@@ -1,0 +1,251 @@
+"""Thin ctypes binding over libmla.so (the C ABI in include/mla.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current HIP
+stream.  If the library is missing, importing this module raises: there is no
+fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_F32, MLA_BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_double),
+    ]
+
+
+class PagedCache(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p), ("num_pages", ctypes.c_int64), ("block_table", ctypes.c_void_p),
+        ("num_seqs", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mla_decoupled_rope_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    pd, pc = ctypes.POINTER(Dims), ctypes.POINTER(PagedCache)
+    sig = {
+        "mla_rope_apply": [pd, pc, vp, vp, i64, vp, vp, vp, vp, vp, i64, vp],
+        "mla_absorb_q": [pd, vp, vp, i64, vp, vp],
+        "mla_decode": [pd, pc, vp, vp, vp, i32, vp, vp, vp, sz, vp],
+        "mla_prefill": [pd, pc, vp, vp, vp, vp, vp, i32, vp, vp, vp],
+        "mla_out_proj": [pd, vp, vp, i64, vp, vp],
+        "mla_decode_plan": [pd, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(i64)],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.mla_decode_workspace_size.argtypes = [pd, i32, vp]
+    lib.mla_decode_workspace_size.restype = sz
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+EXPORTS = ("mla_rope_apply", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode", "mla_prefill",
+           "mla_out_proj", "mla_status_string", "mla_last_error", "mla_decode_plan")
+
+
+def _check(status: int):
+    if status != 0:
+        raise MLAError(status, LIB.mla_last_error().decode())
+
+
+@dataclass(frozen=True)
+class MLADims:
+    """Python mirror of mla_dims."""
+
+    n_heads: int
+    d_head: int
+    d_v: int
+    d_latent: int
+    d_rope: int
+    dtype: torch.dtype = torch.bfloat16
+    softmax_scale: float | None = None
+    rope_base: float = 10000.0
+    page_size: int = 64
+
+    @property
+    def row(self) -> int:
+        return self.d_latent + self.d_rope
+
+    def c(self) -> Dims:
+        scale = self.softmax_scale if self.softmax_scale is not None else 1.0 / math.sqrt(self.d_head + self.d_rope)
+        code = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}[self.dtype]
+        return Dims(self.n_heads, self.d_head, self.d_v, self.d_latent, self.d_rope, self.page_size, code,
+                    scale, self.rope_base)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _host_i32(t: torch.Tensor, name: str):
+    if t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous host int32 tensor")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _cache(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor) -> PagedCache:
+    _dev(cache, "cache", dims.dtype)
+    if cache.dim() != 3 or cache.shape[1] != dims.page_size or cache.shape[2] != dims.row:
+        raise ValueError(f"cache must be [num_pages, {dims.page_size}, {dims.row}]")
+    _dev(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs, max_pages_per_seq]")
+    return PagedCache(cache.data_ptr(), cache.shape[0], block_table.data_ptr(), block_table.shape[0],
+                      block_table.shape[1])
+
+
+def rope_apply(dims: MLADims, cache: torch.Tensor | None, block_table: torch.Tensor | None,
+               q_rope: torch.Tensor | None = None, q_pos: torch.Tensor | None = None,
+               q_lat: torch.Tensor | None = None, kv_latent: torch.Tensor | None = None,
+               k_rope: torch.Tensor | None = None, kv_seq: torch.Tensor | None = None,
+               kv_pos: torch.Tensor | None = None) -> None:
+    """mla_rope_apply: rotate q^R into q_lat[..., d_c:] and write [c | R k^R] rows into the cache."""
+    n_q = 0 if q_rope is None else q_rope.shape[0]
+    n_kv = 0 if kv_latent is None else kv_latent.shape[0]
+    if n_q:
+        _dev(q_rope, "q_rope", dims.dtype, (n_q, dims.n_heads, dims.d_rope))
+        _dev(q_pos, "q_pos", torch.int32, (n_q,))
+        _dev(q_lat, "q_lat", dims.dtype, (n_q, dims.n_heads, dims.row))
+    cstruct = None
+    if n_kv:
+        cstruct = _cache(dims, cache, block_table)
+        _dev(kv_latent, "kv_latent", dims.dtype, (n_kv, dims.d_latent))
+        _dev(k_rope, "k_rope", dims.dtype, (n_kv, dims.d_rope))
+        _dev(kv_seq, "kv_seq", torch.int32, (n_kv,))
+        _dev(kv_pos, "kv_pos", torch.int32, (n_kv,))
+    d = dims.c()
+    _check(LIB.mla_rope_apply(ctypes.byref(d), ctypes.byref(cstruct) if cstruct else None,
+                              _ptr(q_rope) if n_q else None, _ptr(q_pos) if n_q else None, n_q,
+                              _ptr(q_lat) if n_q else None, _ptr(kv_latent) if n_kv else None,
+                              _ptr(k_rope) if n_kv else None, _ptr(kv_seq) if n_kv else None,
+                              _ptr(kv_pos) if n_kv else None, n_kv, _stream()))
+
+
+def absorb_q(dims: MLADims, q_nope: torch.Tensor, w_uk: torch.Tensor, q_lat: torch.Tensor) -> None:
+    """mla_absorb_q: q_lat[n, h, :d_c] = W_UK[h]^T q_nope[n, h]."""
+    n = q_nope.shape[0]
+    _dev(q_nope, "q_nope", dims.dtype, (n, dims.n_heads, dims.d_head))
+    _dev(w_uk, "w_uk", dims.dtype, (dims.n_heads, dims.d_head, dims.d_latent))
+    _dev(q_lat, "q_lat", dims.dtype, (n, dims.n_heads, dims.row))
+    d = dims.c()
+    _check(LIB.mla_absorb_q(ctypes.byref(d), q_nope.data_ptr(), w_uk.data_ptr(), n, q_lat.data_ptr(), _stream()))
+
+
+def decode_plan(dims: MLADims, seq_lens_host: torch.Tensor):
+    _host_i32(seq_lens_host, "seq_lens_host")
+    d = dims.c()
+    sp, ni = ctypes.c_int32(), ctypes.c_int64()
+    _check(LIB.mla_decode_plan(ctypes.byref(d), seq_lens_host.numel(), seq_lens_host.data_ptr(),
+                               ctypes.byref(sp), ctypes.byref(ni)))
+    return sp.value, ni.value
+
+
+def decode_workspace_size(dims: MLADims, seq_lens_host: torch.Tensor) -> int:
+    _host_i32(seq_lens_host, "seq_lens_host")
+    d = dims.c()
+    return int(LIB.mla_decode_workspace_size(ctypes.byref(d), seq_lens_host.numel(), seq_lens_host.data_ptr()))
+
+
+def decode_workspace(dims: MLADims, seq_lens_host: torch.Tensor, device="cuda") -> torch.Tensor | None:
+    n = decode_workspace_size(dims, seq_lens_host)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def decode(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat: torch.Tensor,
+           seq_lens: torch.Tensor, seq_lens_host: torch.Tensor, out_latent: torch.Tensor,
+           lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> None:
+    """mla_decode: out_latent[b] = sum_t softmax(s)_t c_t over positions 0 .. seq_lens[b]-1."""
+    batch = seq_lens_host.numel()
+    cstruct = _cache(dims, cache, block_table)
+    _dev(q_lat, "q_lat", dims.dtype, (batch, dims.n_heads, dims.row))
+    _dev(seq_lens, "seq_lens", torch.int32, (batch,))
+    _host_i32(seq_lens_host, "seq_lens_host")
+    _dev(out_latent, "out_latent", dims.dtype, (batch, dims.n_heads, dims.d_latent))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (batch, dims.n_heads))
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+    d = dims.c()
+    _check(LIB.mla_decode(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), seq_lens.data_ptr(),
+                          seq_lens_host.data_ptr(), batch, out_latent.data_ptr(), _ptr(lse), _ptr(workspace),
+                          0 if workspace is None else workspace.numel(), _stream()))
+
+
+def prefill(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat: torch.Tensor,
+            cu_q: torch.Tensor, q_start: torch.Tensor, cu_q_host: torch.Tensor, q_start_host: torch.Tensor,
+            out_latent: torch.Tensor, lse: torch.Tensor | None = None) -> None:
+    """mla_prefill: causal absorbed attention for new query chunks over the cache."""
+    batch = q_start_host.numel()
+    cstruct = _cache(dims, cache, block_table)
+    _host_i32(cu_q_host, "cu_q_host")
+    _host_i32(q_start_host, "q_start_host")
+    if cu_q_host.numel() != batch + 1:
+        raise ValueError("cu_q must have batch + 1 entries")
+    n = int(cu_q_host[-1])
+    _dev(q_lat, "q_lat", dims.dtype, (n, dims.n_heads, dims.row))
+    _dev(cu_q, "cu_q", torch.int32, (batch + 1,))
+    _dev(q_start, "q_start", torch.int32, (batch,))
+    _dev(out_latent, "out_latent", dims.dtype, (n, dims.n_heads, dims.d_latent))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (n, dims.n_heads))
+    d = dims.c()
+    _check(LIB.mla_prefill(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), cu_q.data_ptr(),
+                           q_start.data_ptr(), cu_q_host.data_ptr(), q_start_host.data_ptr(), batch,
+                           out_latent.data_ptr(), _ptr(lse), _stream()))
+
+
+def out_proj(dims: MLADims, out_latent: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor) -> None:
+    """mla_out_proj: out[n, h] = W_UV[h] out_latent[n, h]."""
+    n = out_latent.shape[0]
+    _dev(out_latent, "out_latent", dims.dtype, (n, dims.n_heads, dims.d_latent))
+    _dev(w_uv, "w_uv", dims.dtype, (dims.n_heads, dims.d_v, dims.d_latent))
+    _dev(out, "out", dims.dtype, (n, dims.n_heads, dims.d_v))
+    d = dims.c()
+    _check(LIB.mla_out_proj(ctypes.byref(d), out_latent.data_ptr(), w_uv.data_ptr(), n, out.data_ptr(), _stream()))

@@ -1,0 +1,381 @@
+// C-ABI host layer of libmla: argument checks, the decode split plan, and
+// the kernel launches.  Nothing here allocates device memory or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <functional>
+#include <queue>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+#include "mla.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+mla_status fail(mla_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+mla_status hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MLA_TRY(expr)                   \
+  do {                                  \
+    const mla_status st_ = (expr);      \
+    if (st_ != MLA_OK) return st_;      \
+  } while (0)
+
+// Cache lines and CUs: the plan is a pure function of the lengths and these
+// constants, so the same batch always splits the same way on any device.
+constexpr int kPlanCUs = 256;
+constexpr size_t kWsAlign = 256;
+
+mla_status check_dims(const mla_dims* d) {
+  if (d == nullptr) return fail(MLA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->n_heads <= 0 || d->d_head <= 0 || d->d_v <= 0 || d->d_latent <= 0 || d->d_rope <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "every dimension must be positive (n_heads=%d d_head=%d d_v=%d d_latent=%d d_rope=%d)",
+                d->n_heads, d->d_head, d->d_v, d->d_latent, d->d_rope);
+  if (d->d_rope % 2 != 0) return fail(MLA_ERR_INVALID_ARG, "d_rope must be even (got %d)", d->d_rope);
+  if (d->d_rope > 128) return fail(MLA_ERR_UNSUPPORTED, "d_rope > 128 is not supported (got %d)", d->d_rope);
+  if (d->page_size != mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size must be 64 (got %d)", d->page_size);
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
+  if (!(std::isfinite(d->rope_base) && d->rope_base > 0.0))
+    return fail(MLA_ERR_INVALID_ARG, "rope_base must be finite and positive");
+  return MLA_OK;
+}
+
+mla_status check_attn_shape(const mla_dims* d) {
+  if (d->dtype == MLA_BF16) {
+    const bool dsv2 = d->n_heads == 128 && d->d_latent == 512 && d->d_rope == 64;
+    const bool tiny = d->n_heads == 16 && d->d_latent == 256 && d->d_rope == 32;
+    if (!dsv2 && !tiny)
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "bf16 attention supports (n_heads, d_latent, d_rope) = (128, 512, 64) or (16, 256, 32); got (%d, %d, %d)",
+                  d->n_heads, d->d_latent, d->d_rope);
+  } else {
+    if (d->n_heads > 1024 || d->d_latent > 1024 || d->d_latent + d->d_rope > 1152)
+      return fail(MLA_ERR_UNSUPPORTED, "float32 attention needs n_heads <= 1024, d_latent <= 1024, d_latent + d_rope <= 1152");
+  }
+  return MLA_OK;
+}
+
+mla_status check_cache(const mla_paged_cache* c) {
+  if (c == nullptr) return fail(MLA_ERR_INVALID_ARG, "cache is NULL");
+  if (c->num_pages < 0 || c->num_seqs < 0 || c->max_pages_per_seq <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "cache sizes must be non-negative (num_pages=%lld num_seqs=%d max_pages_per_seq=%d)",
+                static_cast<long long>(c->num_pages), c->num_seqs, c->max_pages_per_seq);
+  if (c->num_pages > 0 && c->data == nullptr) return fail(MLA_ERR_INVALID_ARG, "cache->data is NULL");
+  if (c->num_seqs > 0 && c->block_table == nullptr) return fail(MLA_ERR_INVALID_ARG, "cache->block_table is NULL");
+  if (c->num_pages > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "more than 2^31 - 1 pages");
+  return MLA_OK;
+}
+
+struct Plan {
+  int split_pages = 1;
+  int n_full = 0;
+  int64_t n_items = 0;  // (sequence, split) pairs = partial slots
+  bool needs_merge = false;
+};
+
+int env_split_pages() {
+  const char* e = std::getenv("MLA_DECODE_SPLIT_PAGES");
+  if (e == nullptr || *e == '\0') return 0;
+  const long v = std::strtol(e, nullptr, 10);
+  return v > 0 && v < (1 << 30) ? static_cast<int>(v) : 0;
+}
+
+// Makespan of the item list (full splits first, then remainders) under
+// greedy list scheduling on `workers` identical workers.
+double simulate(const std::vector<int>& pages, int L, int workers, double item_cost, double partial_cost) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int w = 0; w < workers; ++w) free_at.push(0.0);
+  double makespan = 0.0;
+  auto run = [&](double cost) {
+    const double t = free_at.top() + cost;
+    free_at.pop();
+    free_at.push(t);
+    makespan = std::max(makespan, t);
+  };
+  for (int pg : pages) {
+    const bool split = pg > L;
+    for (int k = 0; k < pg / L; ++k) run(L + item_cost + (split ? partial_cost : 0.0));
+  }
+  for (int pg : pages)
+    if (pg % L) run(pg % L + item_cost + (pg > L ? partial_cost : 0.0));
+  return makespan;
+}
+
+Plan make_plan(const mla_dims* d, int batch, const int32_t* lens) {
+  Plan p;
+  std::vector<int> pages(batch);
+  int64_t total = 0;
+  int max_pages = 1;
+  for (int b = 0; b < batch; ++b) {
+    const int t = lens[b] > 0 ? lens[b] : 0;
+    pages[b] = (t + mla::kPage - 1) / mla::kPage;
+    total += pages[b];
+    max_pages = std::max(max_pages, pages[b]);
+  }
+  int L = env_split_pages();
+  if (L == 0) {
+    const int row = d->d_latent + d->d_rope;
+    const int wg_per_cu = row > 288 ? 1 : 2;
+    const int workers = kPlanCUs * wg_per_cu;
+    const double page_bytes = 64.0 * row * 2.0;
+    const double partial_cost = 2.0 * d->n_heads * (d->d_latent + 1) * 4.0 / page_bytes;  // write + merge read
+    const double item_cost = 1.0;
+    double best = -1.0;
+    L = max_pages;
+    std::vector<int> cands = {max_pages};
+    for (int k = 1; k <= 16; ++k) {
+      const int64_t c = (total + static_cast<int64_t>(workers) * k - 1) / (static_cast<int64_t>(workers) * k);
+      cands.push_back(static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(c, max_pages))));
+    }
+    for (int c : cands) {
+      const double m = simulate(pages, c, workers, item_cost, partial_cost);
+      if (best < 0 || m < best - 1e-9 || (std::fabs(m - best) <= 1e-9 && c > L)) {
+        best = m;
+        L = c;
+      }
+    }
+  }
+  p.split_pages = L;
+  int64_t n_full = 0, n_rem = 0;
+  for (int b = 0; b < batch; ++b) {
+    n_full += pages[b] / L;
+    n_rem += (pages[b] % L) != 0;
+    const int ns = pages[b] / L + ((pages[b] % L) != 0);
+    if (ns != 1) p.needs_merge = true;
+  }
+  p.n_full = static_cast<int>(n_full);
+  p.n_items = n_full + n_rem;
+  return p;
+}
+
+size_t workspace_bytes(const mla_dims* d, const Plan& p) {
+  if (d->dtype != MLA_BF16 || !p.needs_merge || p.n_items == 0) return 0;
+  const size_t o = static_cast<size_t>(p.n_items) * d->n_heads * d->d_latent * sizeof(float);
+  const size_t o_al = (o + kWsAlign - 1) / kWsAlign * kWsAlign;
+  return o_al + static_cast<size_t>(p.n_items) * d->n_heads * sizeof(float);
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* mla_last_error(void) { return g_err.c_str(); }
+
+mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache, const void* q_rope,
+                          const int32_t* q_pos, int64_t n_q, void* q_lat, const void* kv_latent,
+                          const void* k_rope, const int32_t* kv_seq, const int32_t* kv_pos, int64_t n_kv,
+                          void* stream) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  if (n_q < 0 || n_kv < 0) return fail(MLA_ERR_INVALID_ARG, "n_q and n_kv must be >= 0");
+  if (n_q > 0 && (q_rope == nullptr || q_pos == nullptr || q_lat == nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "q_rope, q_pos and q_lat are required when n_q > 0");
+  if (n_kv > 0) {
+    MLA_TRY(check_cache(cache));
+    if (kv_latent == nullptr || k_rope == nullptr || kv_seq == nullptr || kv_pos == nullptr)
+      return fail(MLA_ERR_INVALID_ARG, "kv_latent, k_rope, kv_seq and kv_pos are required when n_kv > 0");
+  }
+  if (n_q * dims->n_heads + n_kv > (static_cast<int64_t>(UINT32_MAX) - 3) * 4)
+    return fail(MLA_ERR_UNSUPPORTED, "too many rows for one launch");
+  mla::RopeParams p{};
+  p.n_heads = dims->n_heads;
+  p.d_latent = dims->d_latent;
+  p.d_rope = dims->d_rope;
+  p.dtype = dims->dtype;
+  p.q_rope = q_rope; p.q_pos = q_pos; p.n_q = n_q; p.q_lat = q_lat;
+  p.kv_latent = kv_latent; p.k_rope = k_rope; p.kv_seq = kv_seq; p.kv_pos = kv_pos; p.n_kv = n_kv;
+  if (n_kv > 0) {
+    p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
+    p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
+  }
+  for (int j = 0; j < dims->d_rope / 2; ++j) p.theta[j] = std::pow(dims->rope_base, -2.0 * j / dims->d_rope);
+  const hipError_t e = mla::launch_rope(p, as_stream(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "rope launch");
+}
+
+mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int64_t n_q, void* q_lat,
+                        void* stream) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  if (n_q < 0) return fail(MLA_ERR_INVALID_ARG, "n_q must be >= 0");
+  if (n_q == 0) return MLA_OK;
+  if (q_nope == nullptr || w_uk == nullptr || q_lat == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "q_nope, w_uk and q_lat must be non-NULL");
+  if (dims->dtype == MLA_BF16 && (dims->d_head != 128 || dims->d_latent % 128 != 0))
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 absorption needs d_head = 128 and d_latent a multiple of 128");
+  if (n_q > 65535LL * 512 || n_q * dims->n_heads * dims->d_latent > (1LL << 40))
+    return fail(MLA_ERR_UNSUPPORTED, "n_q too large for one launch");
+  mla::GemmParams p{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
+                    q_nope, w_uk, q_lat, n_q};
+  const hipError_t e = mla::launch_absorb(p, as_stream(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "absorb launch");
+}
+
+mla_status mla_out_proj(const mla_dims* dims, const void* out_latent, const void* w_uv, int64_t n, void* out,
+                        void* stream) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  if (n < 0) return fail(MLA_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return MLA_OK;
+  if (out_latent == nullptr || w_uv == nullptr || out == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "out_latent, w_uv and out must be non-NULL");
+  if (dims->dtype == MLA_BF16 && (dims->d_latent % 32 != 0 || dims->d_v % 32 != 0))
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 output projection needs d_latent and d_v multiples of 32");
+  if (n > 65535LL * 32) return fail(MLA_ERR_UNSUPPORTED, "n too large for one launch");
+  mla::GemmParams p{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
+                    out_latent, w_uv, out, n};
+  const hipError_t e = mla::launch_out_proj(p, as_stream(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "out_proj launch");
+}
+
+mla_status mla_decode_plan(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host, int32_t* split_pages,
+                           int64_t* n_items) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch > 0 && seq_lens_host == nullptr) return fail(MLA_ERR_INVALID_ARG, "seq_lens_host is NULL");
+  const Plan p = make_plan(dims, batch, seq_lens_host);
+  if (split_pages) *split_pages = p.split_pages;
+  if (n_items) *n_items = p.n_items;
+  return MLA_OK;
+}
+
+size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host) {
+  if (check_dims(dims) != MLA_OK || batch <= 0 || seq_lens_host == nullptr) return 0;
+  return workspace_bytes(dims, make_plan(dims, batch, seq_lens_host));
+}
+
+mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat, const int32_t* seq_lens,
+                      const int32_t* seq_lens_host, int32_t batch, void* out_latent, float* lse, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  MLA_TRY(check_attn_shape(dims));
+  MLA_TRY(check_cache(cache));
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch == 0) return MLA_OK;
+  if (batch > cache->num_seqs)
+    return fail(MLA_ERR_INVALID_ARG, "batch (%d) exceeds the block table's rows (%d)", batch, cache->num_seqs);
+  if (q_lat == nullptr || seq_lens == nullptr || seq_lens_host == nullptr || out_latent == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "q_lat, seq_lens, seq_lens_host and out_latent must be non-NULL");
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens_host[b] < 0 ||
+        static_cast<int64_t>(seq_lens_host[b]) > static_cast<int64_t>(cache->max_pages_per_seq) * mla::kPage)
+      return fail(MLA_ERR_INVALID_ARG, "seq_lens_host[%d] = %d is negative or beyond the block table", b,
+                  seq_lens_host[b]);
+    if (seq_lens_host[b] > 0 && cache->num_pages == 0)
+      return fail(MLA_ERR_INVALID_ARG, "sequence %d has tokens but the cache has no pages", b);
+  }
+  mla::AttnParams p{};
+  p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
+  p.scale = dims->softmax_scale;
+  p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);
+  p.q_lat = q_lat; p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
+  p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
+  p.seq_lens = seq_lens; p.batch = batch; p.out_latent = out_latent; p.lse = lse;
+  hipStream_t s = as_stream(stream);
+  if (dims->dtype == MLA_F32) {
+    const hipError_t e = mla::launch_decode_f32(p, s);
+    return e == hipSuccess ? MLA_OK : hip_fail(e, "decode launch");
+  }
+  const Plan plan = make_plan(dims, batch, seq_lens_host);
+  const size_t need = workspace_bytes(dims, plan);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "decode needs %zu bytes of workspace, got %zu", need, workspace ? ws_bytes : 0);
+  if (plan.n_items > (1LL << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
+  p.split_pages = plan.split_pages;
+  p.n_full = plan.n_full;
+  p.n_items = plan.n_items;
+  p.n_head_chunks = 1;
+  if (need > 0) {
+    const size_t o = static_cast<size_t>(plan.n_items) * dims->n_heads * dims->d_latent * sizeof(float);
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (o + kWsAlign - 1) / kWsAlign * kWsAlign);
+  }
+  hipError_t e = mla::launch_decode_bf16(p, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (plan.needs_merge) {
+    e = mla::launch_merge(p, dims->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return MLA_OK;
+}
+
+mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat, const int32_t* cu_q,
+                       const int32_t* q_start_pos, const int32_t* cu_q_host, const int32_t* q_start_pos_host,
+                       int32_t batch, void* out_latent, float* lse, void* stream) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  MLA_TRY(check_attn_shape(dims));
+  MLA_TRY(check_cache(cache));
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch == 0) return MLA_OK;
+  if (batch > cache->num_seqs)
+    return fail(MLA_ERR_INVALID_ARG, "batch (%d) exceeds the block table's rows (%d)", batch, cache->num_seqs);
+  if (q_lat == nullptr || cu_q == nullptr || q_start_pos == nullptr || cu_q_host == nullptr ||
+      q_start_pos_host == nullptr || out_latent == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "q_lat, cu_q, q_start_pos, their host copies and out_latent must be non-NULL");
+  if (cu_q_host[0] != 0) return fail(MLA_ERR_INVALID_ARG, "cu_q[0] must be 0");
+  const int rows = 128;  // (query, head) rows per bf16 workgroup
+  int64_t n_blocks = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int nq = cu_q_host[b + 1] - cu_q_host[b];
+    if (nq < 0) return fail(MLA_ERR_INVALID_ARG, "cu_q must be non-decreasing (at %d)", b);
+    if (q_start_pos_host[b] < 0) return fail(MLA_ERR_INVALID_ARG, "q_start_pos[%d] is negative", b);
+    const int64_t last = static_cast<int64_t>(q_start_pos_host[b]) + nq;
+    if (last > 0 && cache->num_pages == 0)
+      return fail(MLA_ERR_INVALID_ARG, "sequence %d has tokens but the cache has no pages", b);
+    if (last > static_cast<int64_t>(cache->max_pages_per_seq) * mla::kPage)
+      return fail(MLA_ERR_INVALID_ARG, "sequence %d reaches position %lld beyond its block table", b,
+                  static_cast<long long>(last - 1));
+    if (nq > 0 && static_cast<int64_t>(nq) * dims->n_heads > (1LL << 31) - 1)
+      return fail(MLA_ERR_UNSUPPORTED, "too many query rows in sequence %d", b);
+    n_blocks += dims->dtype == MLA_BF16 ? (static_cast<int64_t>(nq) * dims->n_heads + rows - 1) / rows
+                                        : static_cast<int64_t>(nq) * dims->n_heads;
+  }
+  if (n_blocks == 0) return MLA_OK;
+  if (n_blocks > (1LL << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, "too many workgroups");
+  mla::AttnParams p{};
+  p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
+  p.scale = dims->softmax_scale;
+  p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);
+  p.q_lat = q_lat; p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
+  p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
+  p.batch = batch; p.cu_q = cu_q; p.q_start = q_start_pos; p.n_blocks = n_blocks;
+  p.out_latent = out_latent; p.lse = lse;
+  const hipError_t e = dims->dtype == MLA_BF16 ? mla::launch_prefill_bf16(p, as_stream(stream))
+                                               : mla::launch_prefill_f32(p, as_stream(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,584 @@
+// K3 / K5: absorbed MLA attention over the paged bf16 latent cache (decode
+// split over the cache, and causal chunked prefill), and K4: the merge of
+// decode splits.
+//
+// What one row computes ("AI decoupled RoPE MLA", decoupled-RoPE score
+// equation, with one scale on the summed score; "Multi-Head Latent
+// Attention", "Why this matters on a GPU": softmax and the weighted sum stay):
+//   s_t  = scale * Q_lat[row] . cache[t]           (576 = 512 + 64 wide:
+//          q~ . c_t  +  R_m q^R . R_t k^R_t, both halves in one dot product)
+//   obar = sum_t softmax(s)_t * cache[t][0 : d_c]  (V = first d_c columns)
+//
+// Every head of a query reads the same cache row ("Latent Attention Meets
+// RoPE": one latent and one shared position key per token), so a workgroup
+// takes 32*HG rows (heads, or (query, head) pairs in prefill) against one
+// stream of 64-token pages, and both products are dense MFMA contractions:
+//   S^T[token, row]  = K[token, 0:D]  . Q^T[0:D, row]    (v_mfma 16x16x32 bf16)
+//   O^T[c, row]     += V^T[c, token] . P^T[token, row]
+// Layout per workgroup:
+//   * Q for the wave's 32 rows stays in VGPRs for the whole split (D/4 regs);
+//   * O (32 rows x d_c, float32) stays in accumulators (d_c/2 regs);
+//   * each page (64 x D bf16, 72 KB at D = 576) is copied HBM -> LDS once by
+//     16-byte global_load_lds DMA, double buffered, and read by every wave;
+//     16-byte chunks are XOR-swizzled within groups of 8 so that the K reads
+//     (8 rows, same chunk) and the V transpose reads (4 rows x 2 chunks) hit
+//     distinct banks;
+//   * V^T fragments come from the same page with ds_read_tr16_b64, which
+//     turns four 8-byte row pieces into one token-contiguous column piece;
+//   * softmax in base 2 without rescaling O inside the loop: each row's
+//     reference max is fixed at its first visible key and P = 2^(s - m_ref)
+//     may grow to 2^64 (bf16 and float32 hold it); if a row's scores climb
+//     further the workgroup redoes the split exactly in two passes (true max,
+//     then accumulate).  The same data always takes the same path, so the
+//     result is deterministic.  (A VALU rescale of the 256 accumulator
+//     registers would force them out of AGPRs and spill.)
+// Tokens past the end of a sequence are masked; their LDS rows are filled
+// from the last valid row of the page, so garbage or NaN in unused page
+// slots never reaches the accumulators.
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace mla {
+
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kOverflowLog2 = 64.0f;  // P may reach 2^64 before a split is redone
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Physical 16-byte chunk slot of logical chunk j in LDS row r.  Full groups
+// of 8 chunks are XOR-swizzled with swz(r); a trailing group of 4 (when the
+// row is not a multiple of 8 chunks) with swz(r) & 3.  An involution: the
+// same function maps physical slots back to logical chunks.
+template <int D>
+__device__ __forceinline__ int phys_chunk(int r, int j) {
+  constexpr int CHF = (D / 8 / 8) * 8;
+  return j < CHF ? (j ^ swz(r)) : (j ^ (swz(r) & 3));
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+struct DecodeItem {
+  int b, s, n_s, slot;
+  bool ok;
+};
+
+// Map a work-item index to (sequence, split).  Items [0, n_full) are the
+// full splits of split_pages pages in sequence order, then one remainder
+// split per sequence whose page count is not a multiple of split_pages; the
+// long items go first.  slot = index of (b, s) in sequence-major order.
+__device__ DecodeItem find_decode_item(const AttnParams& p, int64_t item) {
+  const int lane = threadIdx.x & 63;
+  const int L = p.split_pages;
+  const bool want_full = item < p.n_full;
+  const int target = static_cast<int>(want_full ? item : item - p.n_full);
+  int base_cnt = 0, base_ns = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    const int b = b0 + lane;
+    int t = b < p.batch ? p.seq_lens[b] : 0;
+    t = t < 0 ? 0 : t;
+    const int pages = (t + kPage - 1) / kPage;
+    const int nf = pages / L;
+    const int rem = (pages % L) != 0 ? 1 : 0;
+    const int ns = nf + rem;
+    const int cnt = want_full ? nf : rem;
+    const int c_incl = wave_incl_scan(cnt);
+    const int ns_incl = wave_incl_scan(ns);
+    const int lo = base_cnt + c_incl - cnt;
+    const bool hit = cnt > 0 && target >= lo && target < lo + cnt;
+    const unsigned long long mask = __ballot(hit);
+    if (mask) {
+      const int src = __ffsll(static_cast<long long>(mask)) - 1;
+      DecodeItem it;
+      it.b = b0 + src;
+      const int lo_s = __shfl(lo, src, 64);
+      const int nf_s = __shfl(nf, src, 64);
+      it.n_s = __shfl(ns, src, 64);
+      it.s = want_full ? target - lo_s : nf_s;
+      it.slot = base_ns + __shfl(ns_incl, src, 64) - it.n_s + it.s;
+      it.ok = true;
+      return it;
+    }
+    base_cnt += __shfl(c_incl, 63, 64);
+    base_ns += __shfl(ns_incl, 63, 64);
+  }
+  DecodeItem none{0, 0, 0, 0, false};
+  return none;
+}
+
+struct PrefillBlock {
+  int b, rb;
+  bool ok;
+};
+
+// Prefill row blocks: sequence b has ceil(n_q(b) * H / rows) blocks of
+// `rows` consecutive (query, head) rows; blocks are issued last-first so
+// the long causal rows start first.
+__device__ PrefillBlock find_prefill_block(const AttnParams& p, int64_t blk, int rows) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    const int b = b0 + lane;
+    int nb = 0;
+    if (b < p.batch) {
+      const int nq = p.cu_q[b + 1] - p.cu_q[b];
+      nb = nq > 0 ? (nq * p.n_heads + rows - 1) / rows : 0;
+    }
+    const int incl = wave_incl_scan(nb);
+    const int lo = base + incl - nb;
+    const bool hit = nb > 0 && blk >= lo && blk < lo + nb;
+    const unsigned long long mask = __ballot(hit);
+    if (mask) {
+      const int src = __ffsll(static_cast<long long>(mask)) - 1;
+      PrefillBlock r{b0 + src, static_cast<int>(blk) - __shfl(lo, src, 64), true};
+      return r;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  PrefillBlock none{0, 0, false};
+  return none;
+}
+
+// Copy one page (64 rows x D bf16) into an LDS buffer with 16-byte DMA.
+// LDS chunk slot sl of row r holds global chunk sl ^ swz(r) (within the full
+// groups of 8 chunks).  Rows >= valid_rows are filled from row valid_rows-1.
+template <int D, int NT>
+__device__ __forceinline__ void dma_page(char* lds_buf, const char* page_base, int valid_rows, int tid,
+                                         int wave) {
+  constexpr int CH = D / 8;
+  constexpr int ROWB = D * 2;
+  constexpr int NDMA = kPage * CH / NT;
+  static_assert(kPage * CH % NT == 0, "page must split evenly over the workgroup");
+#pragma unroll
+  for (int k = 0; k < NDMA; ++k) {
+    const int slot = k * NT + tid;
+    const int r = slot / CH;
+    const int sl = slot - r * CH;
+    const int j = phys_chunk<D>(r, sl);
+    const int rs = r < valid_rows ? r : valid_rows - 1;
+    const char* src = page_base + rs * ROWB + j * 16;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                     (lds_void_t*)(lds_buf + (k * NT + wave * 64) * 16), 16, 0, 0);
+  }
+}
+
+
+template <int DC, int DR, int HG, int TW, bool PREFILL>
+__global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p) {
+  constexpr int D = DC + DR;
+  constexpr int NT = 64 * HG * TW;
+  constexpr int ROWS = 32 * HG;
+  constexpr int KS = D / 32;
+  constexpr int CB = DC / 16;
+  constexpr int TILE = kPage * D * 2;
+  static_assert(D % 32 == 0 && DC % 16 == 0, "dims");
+  static_assert(TW == 1 || HG <= 2, "two token lanes need half the waves' registers");
+  __shared__ __attribute__((aligned(16))) char smem[2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave % HG;
+  const int tw = wave / HG;
+  const int q16 = lane >> 4, r16 = lane & 15;
+  const int H = p.n_heads;
+
+  // ---- which rows and which keys
+  int b, page_begin, page_end, key_end;
+  int64_t row_g[2];
+  int limit[2];
+  bool row_ok[2];
+  bool final_out = true;
+  int slot = 0;
+  if constexpr (PREFILL) {
+    const PrefillBlock pb = find_prefill_block(p, p.n_blocks - 1 - static_cast<int64_t>(blockIdx.x), ROWS);
+    if (!pb.ok) return;
+    b = pb.b;
+    const int nq = p.cu_q[b + 1] - p.cu_q[b];
+    const int q0 = p.q_start[b];
+    const int r0 = pb.rb * ROWS;
+    const int last_q = min(nq - 1, (r0 + ROWS - 1) / H);
+    key_end = q0 + last_q + 1;
+    page_begin = 0;
+    page_end = (key_end + kPage - 1) / kPage;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int sr = r0 + hg * 32 + rb * 16 + r16;
+      row_ok[rb] = sr < nq * H;
+      row_g[rb] = static_cast<int64_t>(p.cu_q[b]) * H + sr;
+      limit[rb] = row_ok[rb] ? q0 + sr / H + 1 : 0;
+    }
+  } else {
+    const int64_t item = static_cast<int64_t>(blockIdx.x) / p.n_head_chunks;
+    const int hc = static_cast<int>(static_cast<int64_t>(blockIdx.x) % p.n_head_chunks);
+    const DecodeItem it = find_decode_item(p, item);
+    if (!it.ok || it.slot >= p.n_items) return;
+    b = it.b;
+    key_end = p.seq_lens[b];
+    const int pages = (key_end + kPage - 1) / kPage;
+    page_begin = it.s * p.split_pages;
+    page_end = min(pages, page_begin + p.split_pages);
+    final_out = it.n_s == 1;
+    slot = it.slot;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int head = hc * ROWS + hg * 32 + rb * 16 + r16;
+      row_ok[rb] = head < H;
+      row_g[rb] = static_cast<int64_t>(b) * H + head;
+      limit[rb] = key_end;
+    }
+  }
+  if (b >= p.num_seqs) return;
+  // wave-uniform bound on the visible keys of this wave's rows
+  int lim_max = max(limit[0], limit[1]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) lim_max = max(lim_max, __shfl_xor(lim_max, m, 64));
+
+  // ---- Q fragments (MFMA B operand: row = r16, d = ks*32 + 8*q16 .. +7)
+  const bf16_t* qlat = static_cast<const bf16_t*>(p.q_lat);
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[rb][ks] = row_ok[rb] ? *reinterpret_cast<const bf16x8*>(qlat + row_g[rb] * D + ks * 32 + q16 * 8)
+                              : bf16x8{};
+
+  f32x4 oacc[CB][2];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    oacc[cb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    oacc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.f, 0.f};
+
+  const char* cache = static_cast<const char*>(p.cache);
+  const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
+  auto page_ptr = [&](int pg) -> const char* {
+    int id = pg < p.max_pages ? bt[pg] : -1;
+    id = (id < 0 || id >= p.num_pages) ? 0 : id;
+    return cache + static_cast<int64_t>(id) * TILE;
+  };
+
+  // Per-lane LDS byte offsets inside a tile (sub-block 0); the chunk group
+  // and the sub-block enter as immediates.
+  constexpr int CHF8 = (D / 8 / 8) * 8;  // chunks in full swizzle groups
+  int k_off[2][2], k_tail[2], v_off[2][4];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int krow = tb * 16 + r16;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) k_off[tb][kb] = krow * (D * 2) + phys_chunk<D>(krow, kb * 4 + q16) * 16;
+    k_tail[tb] = krow * (D * 2) + (phys_chunk<D>(krow, CHF8 + q16) - CHF8) * 16;
+    const int vrow = tb * 16 + q16 * 4 + (r16 >> 2);
+#pragma unroll
+    for (int cl = 0; cl < 4; ++cl)
+      v_off[tb][cl] = vrow * (D * 2) + phys_chunk<D>(vrow, cl * 2 + ((r16 & 3) >> 1)) * 16 + (r16 & 1) * 8;
+  }
+
+  const int ntile = page_end - page_begin;
+
+  // One pass over the split's pages.  MODE 0: the reference max of a row is
+  // fixed at its first visible key and P = 2^(s - m_ref) may grow up to
+  // 2^kOverflowLog2 (bf16 and float32 hold that easily); a row whose scores
+  // climb further sets `overflow`.  MODE 1: running max only (no PV).
+  // MODE 2: P = 2^(s - m) with the true max m from a MODE 1 pass.
+  // O is never rescaled inside the loop.
+  auto run_pass = [&](auto mode_tag) -> bool {
+    constexpr int MODE = decltype(mode_tag)::value;
+    bool overflow = false;
+    if (ntile > 0) dma_page<D, NT>(smem, page_ptr(page_begin), min(kPage, key_end - page_begin * kPage), tid, wave);
+    for (int it = 0; it < ntile; ++it) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (it + 1 < ntile) {
+        const int pg = page_begin + it + 1;
+        dma_page<D, NT>(smem + ((it + 1) & 1) * TILE, page_ptr(pg), min(kPage, key_end - pg * kPage), tid, wave);
+      }
+      const char* buf = smem + (it & 1) * TILE;
+      const int tile_t0 = (page_begin + it) * kPage;
+#pragma unroll
+      for (int sbi = 0; sbi < 2 / TW; ++sbi) {
+        const int sb = TW == 1 ? sbi : tw;
+        const int t0 = tile_t0 + sb * 32;
+        // skip sub-blocks no row of this wave can see (wave-uniform)
+        if (t0 >= lim_max) continue;
+        // ---- S^T = K . Q^T over D
+        f32x4 sacc[2][2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          sacc[tb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+          sacc[tb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8 ka[2];
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            // chunk ks*4 + q16 of row krow: group ks/2 (immediate), in-group slot from k_off
+            const char* a = (ks / 2) * 128 < CHF8 * 16 ? buf + k_off[tb][ks & 1] + (ks / 2) * 128
+                                                       : buf + k_tail[tb] + (ks / 2) * 128;
+            ka[tb] = *reinterpret_cast<const bf16x8*>(a + sb * 32 * (D * 2));
+          }
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              sacc[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tb], qf[rb][ks], sacc[tb][rb], 0, 0, 0);
+        }
+        // ---- scores in base 2, masked; row max over the sub-block
+        float mx[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float m = -INFINITY;
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int t = t0 + tb * 16 + q16 * 4 + e;
+              const float v = t < limit[rb] ? sacc[tb][rb][e] * p.scale_log2 : -INFINITY;
+              sacc[tb][rb][e] = v;
+              m = fmaxf(m, v);
+            }
+          m = fmaxf(m, shfl_xor_f(m, 16));
+          mx[rb] = fmaxf(m, shfl_xor_f(m, 32));
+        }
+        if constexpr (MODE == 1) {
+          m_run[0] = fmaxf(m_run[0], mx[0]);
+          m_run[1] = fmaxf(m_run[1], mx[1]);
+          continue;
+        }
+        if constexpr (MODE == 0) {
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            if (m_run[rb] == -INFINITY) m_run[rb] = mx[rb];  // O and l are still zero: exact
+            overflow |= mx[rb] > m_run[rb] + kOverflowLog2;
+          }
+        }
+        // ---- P = 2^(s - m) in bf16; l sums the rounded values
+        bf16x8 pb[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+          bf16_t pv[8];
+          float lsum = 0.f;
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bf16_t q = f32_to_bf16_finite(__builtin_amdgcn_exp2f(sacc[tb][rb][e] - m_use));
+              pv[tb * 4 + e] = q;
+              lsum += bf16_to_f32(q);
+            }
+          l_part[rb] += lsum;
+          __builtin_memcpy(&pb[rb], pv, 16);
+        }
+        // ---- O^T += V^T . P^T ; V^T fragment from two transpose reads
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          i16x4 v[2];
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            // columns cb*16 + 4*(r16&3): chunk cb*2 + ((r16&3)>>1) = group cb/4, slot from v_off
+            const char* a = buf + v_off[tb][cb & 3] + (cb / 4) * 128 + sb * 32 * (D * 2);
+            v[tb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
+          }
+          bf16x8 va;
+          __builtin_memcpy(&va, &v[0], 8);
+          __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &v[1], 8);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            oacc[cb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb], oacc[cb][rb], 0, 0, 0);
+        }
+      }
+    }
+    return overflow;
+  };
+
+  const bool overflow = run_pass(std::integral_constant<int, 0>{});
+  if (__syncthreads_or(overflow ? 1 : 0)) {
+    // Rare: some row's scores rose by more than 2^kOverflowLog2 over its first
+    // visible key.  Redo the split exactly: true max first, then accumulate.
+    __syncthreads();
+    m_run[0] = m_run[1] = -INFINITY;
+    run_pass(std::integral_constant<int, 1>{});
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      oacc[cb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      oacc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    l_part[0] = l_part[1] = 0.f;
+    run_pass(std::integral_constant<int, 2>{});
+  }
+
+  // ---- combine the two token lanes of a head group (TW == 2)
+  if constexpr (TW == 2) {
+    __syncthreads();
+    float* xo = reinterpret_cast<float*>(smem);  // [hg][cb][rb][lane][4]
+    float* xs = xo + HG * CB * 2 * 64 * 4;       // [hg][rb][lane][m, l]
+    if (tw == 1) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          *reinterpret_cast<f32x4*>(&xo[(((hg * CB + cb) * 2 + rb) * 64 + lane) * 4]) = oacc[cb][rb];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        xs[((hg * 2 + rb) * 64 + lane) * 2 + 0] = m_run[rb];
+        xs[((hg * 2 + rb) * 64 + lane) * 2 + 1] = l_part[rb];
+      }
+    }
+    __syncthreads();
+    if (tw == 1) return;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float m1 = xs[((hg * 2 + rb) * 64 + lane) * 2 + 0];
+      const float l1 = xs[((hg * 2 + rb) * 64 + lane) * 2 + 1];
+      const float m = fmaxf(m_run[rb], m1);
+      const float mu = m == -INFINITY ? 0.f : m;
+      const float f0 = __builtin_amdgcn_exp2f(m_run[rb] - mu);
+      const float f1 = __builtin_amdgcn_exp2f(m1 - mu);
+      l_part[rb] = l_part[rb] * f0 + l1 * f1;
+      m_run[rb] = m;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[(((hg * CB + cb) * 2 + rb) * 64 + lane) * 4]);
+        oacc[cb][rb] = oacc[cb][rb] * f0 + o1 * f1;
+      }
+    }
+  }
+
+  // ---- normalise and store.  O^T lane layout: row r16, c = cb*16 + 4*q16 + e
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float l = l_part[rb];
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+    if (!row_ok[rb]) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float lse_v = l > 0.f ? (m_run[rb] + log2f(l)) * kLn2 : -INFINITY;
+    if (final_out) {
+      bf16_t* out = static_cast<bf16_t*>(p.out_latent) + row_g[rb] * DC;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int c = cb * 16 + 4 * q16;
+        uint2 pk;
+        pk.x = f32_to_bf16(oacc[cb][rb][0] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][rb][1] * inv)) << 16);
+        pk.y = f32_to_bf16(oacc[cb][rb][2] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][rb][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(out + c) = pk;
+      }
+      if (p.lse != nullptr && q16 == 0) p.lse[row_g[rb]] = lse_v;
+    } else {
+      const int64_t srow = static_cast<int64_t>(slot) * H + (row_g[rb] - static_cast<int64_t>(b) * H);
+      float* out = p.ws_o + srow * DC;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int c = cb * 16 + 4 * q16;
+        *reinterpret_cast<f32x4*>(out + c) = oacc[cb][rb] * inv;
+      }
+      if (q16 == 0) p.ws_lse[srow] = lse_v;
+    }
+  }
+}
+
+// K4: merge the splits of each sequence:  lse = log sum_s e^{lse_s},
+// obar = sum_s e^{lse_s - lse} obar_s, in split order (deterministic).
+// One workgroup per (sequence, 4 heads); 64 lanes per head.
+template <int DC>
+__global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
+  constexpr int PER = DC / 64;
+  const int b = blockIdx.x;
+  const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int H = p.n_heads;
+  const int L = p.split_pages;
+  // prefix of split counts over sequences before b, and b's own count
+  int base = 0, ns_b = 0;
+  for (int b0 = 0; b0 <= b; b0 += 64) {
+    const int bb = b0 + lane;
+    int t = bb < p.batch ? p.seq_lens[bb] : 0;
+    t = t < 0 ? 0 : t;
+    const int pages = (t + kPage - 1) / kPage;
+    const int ns = bb <= b ? pages / L + ((pages % L) != 0 ? 1 : 0) : 0;
+    const int incl = wave_incl_scan(ns);
+    if (b - b0 < 64) {
+      ns_b = __shfl(ns, b - b0, 64);
+      base += __shfl(incl, b - b0, 64) - ns_b;
+    } else {
+      base += __shfl(incl, 63, 64);
+    }
+  }
+  if (head >= H || ns_b == 1 || base + ns_b > p.n_items) return;
+  const int64_t row = static_cast<int64_t>(b) * H + head;
+  bf16_t* out = static_cast<bf16_t*>(p.out_latent) + row * DC;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  float m = -INFINITY;
+  for (int s = 0; s < ns_b; ++s) m = fmaxf(m, p.ws_lse[static_cast<int64_t>(base + s) * H + head]);
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < ns_b; ++s) {
+      const int64_t srow = static_cast<int64_t>(base + s) * H + head;
+      const float w = __expf(p.ws_lse[srow] - m);
+      wsum += w;
+      const float* src = p.ws_o + srow * DC + lane * PER;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, src[i], acc[i]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) out[lane * PER + i] = f32_to_bf16(acc[i] * inv);
+  if (p.lse != nullptr && lane == 0) p.lse[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
+template <int DC, int DR, int HG, int TW, bool PREFILL>
+hipError_t launch_attn(const AttnParams& p, int64_t n_wg, hipStream_t s) {
+  if (n_wg == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_bf16_kernel<DC, DR, HG, TW, PREFILL>), dim3(static_cast<unsigned>(n_wg)),
+                     dim3(64 * HG * TW), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s) {
+  const int64_t n_wg = p.n_items * p.n_head_chunks;
+  if (p.d_latent == 512 && p.d_rope == 64) return launch_attn<512, 64, 4, 1, false>(p, n_wg, s);
+  if (p.d_latent == 256 && p.d_rope == 32) return launch_attn<256, 32, 1, 2, false>(p, n_wg, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t s) {
+  if (p.d_latent == 512 && p.d_rope == 64) return launch_attn<512, 64, 4, 1, true>(p, p.n_blocks, s);
+  if (p.d_latent == 256 && p.d_rope == 32) return launch_attn<256, 32, 4, 1, true>(p, p.n_blocks, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge(const AttnParams& p, int dtype, hipStream_t s) {
+  (void)dtype;
+  if (p.batch == 0) return hipSuccess;
+  const dim3 grid(p.batch, (p.n_heads + 3) / 4);
+  if (p.d_latent == 512)
+    hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(256), 0, s, p);
+  else if (p.d_latent == 256)
+    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,84 @@
+// Shared device helpers and the internal launcher interface of libmla.
+// gfx950 (CDNA4) only: 64-wide waves, bf16 MFMA, LDS transpose reads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kPage = 64;  // tokens per cache page (one attention tile)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short bf16_t;  // storage type of a bf16 value
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Round-to-nearest-even float -> bf16 for values known to be finite.
+__device__ __forceinline__ bf16_t f32_to_bf16_finite(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// ---------------------------------------------------------------- params --
+
+struct RopeParams {
+  int n_heads, d_latent, d_rope, dtype;
+  const void* q_rope; const int32_t* q_pos; int64_t n_q; void* q_lat;
+  const void* kv_latent; const void* k_rope; const int32_t* kv_seq; const int32_t* kv_pos; int64_t n_kv;
+  void* cache; int64_t num_pages; const int32_t* block_table; int32_t num_seqs; int32_t max_pages;
+  double theta[64];  // theta_j, j < d_rope / 2 (float64, from the host)
+};
+
+struct GemmParams {
+  int n_heads, d_head, d_v, d_latent, d_rope, dtype;
+  const void* a; const void* w; void* out; int64_t n;
+};
+
+// Decode / prefill attention over the paged latent cache.
+struct AttnParams {
+  // shape
+  int n_heads, d_latent, d_rope;
+  float scale;       // softmax_scale
+  float scale_log2;  // softmax_scale * log2(e)
+  // inputs
+  const void* q_lat; const void* cache; int64_t num_pages;
+  const int32_t* block_table; int32_t num_seqs; int32_t max_pages;
+  // decode
+  const int32_t* seq_lens; int32_t batch; int32_t split_pages; int32_t n_full; int64_t n_items;
+  int32_t n_head_chunks;
+  // prefill
+  const int32_t* cu_q; const int32_t* q_start; int64_t n_blocks;
+  // outputs
+  void* out_latent; float* lse;
+  float* ws_o; float* ws_lse;  // split partials [slot, H, d_latent] / [slot, H]
+};
+
+// Launchers (each returns hipGetLastError() after the launch).
+hipError_t launch_rope(const RopeParams& p, hipStream_t s);
+hipError_t launch_absorb(const GemmParams& p, hipStream_t s);
+hipError_t launch_out_proj(const GemmParams& p, hipStream_t s);
+hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s);
+hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t s);
+hipError_t launch_merge(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_decode_f32(const AttnParams& p, hipStream_t s);
+hipError_t launch_prefill_f32(const AttnParams& p, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,211 @@
+// K2 (query absorption) and K6 (output absorption): per-head batched GEMMs.
+//
+// "AI decoupled RoPE MLA" (operatorworld.com), recap section: the two
+// up-projections move to the two sides of attention -- W^UK^T onto the query
+// (q~ = W^UK^T q, computed ahead of and independent of the cache) and W^UV
+// after the weighted sum (Attn = W^UV sum_t alpha_t c_t).
+//
+// bf16 path: v_mfma_f32_16x16x32_bf16 with float32 accumulation.  Both GEMMs
+// compute the transposed product (rows = output features, columns = tokens)
+// so that each lane stores four consecutive output features of one token.
+//  * absorb:   q~^T[j, n] = sum_i W_UK[h][i][j] q^C[n, h, i].  W_UK is stored
+//    [d_h, d_c], so the MFMA A operand (8 consecutive i for one j) is a
+//    column read: the W tile is staged in LDS and read with ds_read_tr16_b64.
+//  * out_proj: o^T[v, n] = sum_j W_UV[h][v][j] obar[n, h, j].  Both operands
+//    are already contiguous along j and come straight from global memory.
+// float32 path: one thread per output element, float32 accumulation.
+#include "common.hpp"
+
+namespace mla {
+
+namespace {
+
+constexpr int kAbsorbJTile = 128;  // output features per workgroup
+constexpr int kAbsorbLdsStride = kAbsorbJTile + 16;  // padded row (elements): 288 B
+constexpr int kAbsorbNChunk = 512;  // tokens per workgroup (looped in 64s)
+
+__device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// W_UK tile [d_head rows (i), 128 cols (j)] in LDS; each wave owns 32 j x 64 n.
+template <int DH>
+__global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) bf16_t w_lds[DH * kAbsorbLdsStride];
+  const int h = blockIdx.y;
+  const int j0 = blockIdx.x * kAbsorbJTile;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int H = p.n_heads;
+  const int DC = p.d_latent;
+  const int D = p.d_latent + p.d_rope;
+  const bf16_t* w = static_cast<const bf16_t*>(p.w) + static_cast<int64_t>(h) * DH * DC;
+  // stage W_UK[h][:, j0 : j0 + 128]
+  for (int c = tid; c < DH * (kAbsorbJTile / 8); c += 256) {
+    const int row = c / (kAbsorbJTile / 8), cc = c % (kAbsorbJTile / 8);
+    *reinterpret_cast<bf16x8*>(&w_lds[row * kAbsorbLdsStride + cc * 8]) =
+        load8(w + static_cast<int64_t>(row) * DC + j0 + cc * 8);
+  }
+  __syncthreads();
+  const bf16_t* q = static_cast<const bf16_t*>(p.a);
+  bf16_t* out = static_cast<bf16_t*>(p.out);
+  const int64_t n_begin = static_cast<int64_t>(blockIdx.z) * kAbsorbNChunk;
+  const int64_t n_end = min(p.n, n_begin + kAbsorbNChunk);
+  const int q16 = lane >> 4, r16 = lane & 15;
+  const int jw = wave * 32;  // this wave's j offset inside the tile
+  for (int64_t nb0 = n_begin; nb0 < n_end; nb0 += 64) {
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) {
+      bf16x8 bq[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int64_t n = nb0 + nb * 16 + r16;
+        if (n < n_end)
+          bq[nb] = load8(q + (n * H + h) * DH + ks * 32 + q16 * 8);
+        else
+          bq[nb] = bf16x8{};
+      }
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        // A = W^T[j, i]: group q16 takes rows i0 .. i0+7 of column block jcol
+        const int i0 = ks * 32 + q16 * 8;
+        const int jcol = jw + jb * 16 + 4 * (r16 & 3);
+        const int rr = r16 >> 2;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(&w_lds[(i0 + rr) * kAbsorbLdsStride + jcol]));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(&w_lds[(i0 + 4 + rr) * kAbsorbLdsStride + jcol]));
+        bf16x8 a;
+        __builtin_memcpy(&a, &lo, 8);
+        __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[jb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[nb], acc[jb][nb], 0, 0, 0);
+      }
+    }
+    // D^T[j][n]: lane holds n = nb*16 + r16, j = jb*16 + 4*q16 + e
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int64_t n = nb0 + nb * 16 + r16;
+      if (n >= n_end) continue;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const int j = j0 + jw + jb * 16 + 4 * q16;
+        uint2 packed;
+        packed.x = f32_to_bf16(acc[jb][nb][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[jb][nb][1])) << 16);
+        packed.y = f32_to_bf16(acc[jb][nb][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[jb][nb][3])) << 16);
+        *reinterpret_cast<uint2*>(out + (n * H + h) * D + j) = packed;
+      }
+    }
+  }
+}
+
+// o^T[v, n] = W_UV[h][v, :] . obar[n, h, :]; wave tile 32 v x 32 n, 4 waves over 128 v.
+__global__ void __launch_bounds__(256) out_proj_bf16_kernel(GemmParams p) {
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int v0 = blockIdx.x * 128 + wave * 32;
+  if (v0 >= p.d_v) return;
+  const int H = p.n_heads, DC = p.d_latent, DV = p.d_v;
+  const int q16 = lane >> 4, r16 = lane & 15;
+  const bf16_t* w = static_cast<const bf16_t*>(p.w) + static_cast<int64_t>(h) * DV * DC;
+  const bf16_t* ob = static_cast<const bf16_t*>(p.a);
+  bf16_t* out = static_cast<bf16_t*>(p.out);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.z) * 32;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool nv0 = n0 + r16 < p.n, nv1 = n0 + 16 + r16 < p.n;
+  const bf16_t* b0p = ob + ((n0 + r16) * H + h) * DC + q16 * 8;
+  const bf16_t* b1p = ob + ((n0 + 16 + r16) * H + h) * DC + q16 * 8;
+  const bf16_t* a0p = w + static_cast<int64_t>(v0 + r16) * DC + q16 * 8;
+  const bf16_t* a1p = w + static_cast<int64_t>(v0 + 16 + r16) * DC + q16 * 8;
+  for (int k = 0; k < DC; k += 32) {
+    const bf16x8 a0 = load8(a0p + k), a1 = load8(a1p + k);
+    const bf16x8 b0 = nv0 ? load8(b0p + k) : bf16x8{};
+    const bf16x8 b1 = nv1 ? load8(b1p + k) : bf16x8{};
+    acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[1][1], 0, 0, 0);
+  }
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int64_t n = n0 + nb * 16 + r16;
+    if (n >= p.n) continue;
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb) {
+      const int v = v0 + vb * 16 + 4 * q16;
+      uint2 packed;
+      packed.x = f32_to_bf16(acc[vb][nb][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[vb][nb][1])) << 16);
+      packed.y = f32_to_bf16(acc[vb][nb][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[vb][nb][3])) << 16);
+      *reinterpret_cast<uint2*>(out + (n * H + h) * DV + v) = packed;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) absorb_f32_kernel(GemmParams p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int DC = p.d_latent, DH = p.d_head, H = p.n_heads;
+  if (idx >= p.n * H * DC) return;
+  const int j = idx % DC;
+  const int64_t nh = idx / DC;
+  const int h = nh % H;
+  const float* q = static_cast<const float*>(p.a) + nh * DH;
+  const float* w = static_cast<const float*>(p.w) + static_cast<int64_t>(h) * DH * DC + j;
+  float acc = 0.f;
+  for (int i = 0; i < DH; ++i) acc = fmaf(q[i], w[static_cast<int64_t>(i) * DC], acc);
+  static_cast<float*>(p.out)[nh * (DC + p.d_rope) + j] = acc;
+}
+
+__global__ void __launch_bounds__(256) out_proj_f32_kernel(GemmParams p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int DC = p.d_latent, DV = p.d_v, H = p.n_heads;
+  if (idx >= p.n * H * DV) return;
+  const int v = idx % DV;
+  const int64_t nh = idx / DV;
+  const int h = nh % H;
+  const float* ob = static_cast<const float*>(p.a) + nh * DC;
+  const float* w = static_cast<const float*>(p.w) + (static_cast<int64_t>(h) * DV + v) * DC;
+  float acc = 0.f;
+  for (int j = 0; j < DC; ++j) acc = fmaf(w[j], ob[j], acc);
+  static_cast<float*>(p.out)[idx] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_absorb(const GemmParams& p, hipStream_t s) {
+  if (p.n == 0) return hipSuccess;
+  if (p.dtype == 0) {
+    const int64_t total = p.n * p.n_heads * p.d_latent;
+    hipLaunchKernelGGL(absorb_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, p);
+  } else {
+    const dim3 grid(p.d_latent / kAbsorbJTile, p.n_heads,
+                    static_cast<unsigned>((p.n + kAbsorbNChunk - 1) / kAbsorbNChunk));
+    hipLaunchKernelGGL(absorb_bf16_kernel<128>, grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_out_proj(const GemmParams& p, hipStream_t s) {
+  if (p.n == 0) return hipSuccess;
+  if (p.dtype == 0) {
+    const int64_t total = p.n * p.n_heads * p.d_v;
+    hipLaunchKernelGGL(out_proj_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, p);
+  } else {
+    const dim3 grid((p.d_v + 127) / 128, p.n_heads, static_cast<unsigned>((p.n + 31) / 32));
+    hipLaunchKernelGGL(out_proj_bf16_kernel, grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,79 @@
+// K1: the decoupled RoPE channel and the paged latent-cache write.
+//
+// "AI decoupled RoPE MLA" (operatorworld.com), decoupled-RoPE section: only
+// the d_r-wide q^R and k^R are rotated; "Latent Attention Meets RoPE", "Two
+// small, telling details": the cache keeps the latent and one shared
+// position key per token.  The key is stored already rotated to its own
+// position, so decode needs no positions at all (R_m^T R_t depends only on
+// t - m, "Detailed Illustration of the Problem", Step 3).
+//
+// One 64-lane wave per row: a query row (n, h) rotates q^R into the tail of
+// q_lat; a cache row copies c_t and writes R_t k^R_t into its page slot.
+// Angles p * theta_j and sin / cos are float64 (positions reach 2^17, where a
+// float32 angle would be off by ~1e-2 rad).
+#include "common.hpp"
+
+namespace mla {
+
+template <typename T> __device__ __forceinline__ double ld(const T* p, int64_t i);
+template <> __device__ __forceinline__ double ld<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ double ld<bf16_t>(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+template <typename T> __device__ __forceinline__ void st(T* p, int64_t i, double v);
+template <> __device__ __forceinline__ void st<float>(float* p, int64_t i, double v) { p[i] = static_cast<float>(v); }
+template <> __device__ __forceinline__ void st<bf16_t>(bf16_t* p, int64_t i, double v) {
+  p[i] = f32_to_bf16(static_cast<float>(v));
+}
+
+template <typename T>
+__device__ __forceinline__ void rotate_pairs(const RopeParams& p, const T* src, T* dst, int pos, int lane) {
+  const int half = p.d_rope / 2;
+  for (int j = lane; j < half; j += 64) {
+    double s, c;
+    sincos(static_cast<double>(pos) * p.theta[j], &s, &c);
+    const double x0 = ld(src, 2 * j), x1 = ld(src, 2 * j + 1);
+    st(dst, 2 * j, x0 * c - x1 * s);
+    st(dst, 2 * j + 1, x0 * s + x1 * c);
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) rope_kernel(RopeParams p) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  const int64_t nq_rows = p.n_q * p.n_heads;
+  const int64_t width = p.d_latent + p.d_rope;
+  if (row < nq_rows) {
+    const int pos = p.q_pos[row / p.n_heads];
+    const T* src = static_cast<const T*>(p.q_rope) + row * p.d_rope;
+    T* dst = static_cast<T*>(p.q_lat) + row * width + p.d_latent;
+    rotate_pairs<T>(p, src, dst, pos, lane);
+    return;
+  }
+  const int64_t m = row - nq_rows;
+  if (m >= p.n_kv) return;
+  const int b = p.kv_seq[m];
+  const int pos = p.kv_pos[m];
+  if (b < 0 || b >= p.num_seqs || pos < 0) return;
+  const int lp = pos / kPage;
+  if (lp >= p.max_pages) return;
+  const int page = p.block_table[static_cast<int64_t>(b) * p.max_pages + lp];
+  if (page < 0 || page >= p.num_pages) return;
+  T* dst = static_cast<T*>(p.cache) + (static_cast<int64_t>(page) * kPage + pos % kPage) * width;
+  const T* lat = static_cast<const T*>(p.kv_latent) + m * p.d_latent;
+  for (int c = lane; c < p.d_latent; c += 64) dst[c] = lat[c];
+  rotate_pairs<T>(p, static_cast<const T*>(p.k_rope) + m * p.d_rope, dst + p.d_latent, pos, lane);
+}
+
+hipError_t launch_rope(const RopeParams& p, hipStream_t s) {
+  const int64_t rows = p.n_q * p.n_heads + p.n_kv;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  if (p.dtype == 0)
+    hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(rope_kernel<bf16_t>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

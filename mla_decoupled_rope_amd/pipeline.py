@@ -1,0 +1,104 @@
+"""Device-side state and the two hot-path pipelines built from the five C-ABI calls.
+
+* ``LatentCache``  -- the paged [c | R k^R] cache and its block table.
+* ``DecodeStep``   -- rope_apply (new token + q^R) -> absorb_q -> decode
+                      (split + merge) -> out_proj, with every buffer
+                      preallocated so a step launches kernels only.
+* ``PrefillStep``  -- rope_apply (chunk rows + q^R) -> absorb_q -> prefill ->
+                      out_proj.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class LatentCache:
+    """Paged latent cache: data [num_pages, 64, d_c + d_r] and block table [num_seqs, max_pages]."""
+
+    def __init__(self, dims: B.MLADims, block_table, num_pages: int, device="cuda", fill: float | None = None):
+        self.dims = dims
+        bt = torch.as_tensor(block_table, dtype=torch.int32)
+        self.block_table_host = bt.contiguous()
+        self.block_table = bt.to(device).contiguous()
+        self.num_pages = int(num_pages)
+        if fill is None:
+            self.data = torch.empty((self.num_pages, dims.page_size, dims.row), dtype=dims.dtype, device=device)
+        else:
+            self.data = torch.full((self.num_pages, dims.page_size, dims.row), fill, dtype=dims.dtype, device=device)
+
+    def write(self, kv_latent: torch.Tensor, k_rope: torch.Tensor, kv_seq: torch.Tensor, kv_pos: torch.Tensor):
+        """Write rows [c | R_pos k^R] for (seq, pos) pairs (k^R un-rotated on input)."""
+        B.rope_apply(self.dims, self.data, self.block_table, kv_latent=kv_latent, k_rope=k_rope,
+                     kv_seq=kv_seq, kv_pos=kv_pos)
+
+
+class DecodeStep:
+    """One decode step for a fixed batch: buffers are allocated once here."""
+
+    def __init__(self, dims: B.MLADims, cache: LatentCache, seq_lens_host: torch.Tensor, device="cuda"):
+        self.dims, self.cache = dims, cache
+        self.seq_lens_host = seq_lens_host.to(torch.int32).contiguous()
+        self.seq_lens = self.seq_lens_host.to(device)
+        n = self.seq_lens_host.numel()
+        self.q_pos = (self.seq_lens - 1).clamp_min(0).to(torch.int32)
+        self.q_lat = torch.empty((n, dims.n_heads, dims.row), dtype=dims.dtype, device=device)
+        self.out_latent = torch.empty((n, dims.n_heads, dims.d_latent), dtype=dims.dtype, device=device)
+        self.lse = torch.empty((n, dims.n_heads), dtype=torch.float32, device=device)
+        self.out = torch.empty((n, dims.n_heads, dims.d_v), dtype=dims.dtype, device=device)
+        self.workspace = B.decode_workspace(dims, self.seq_lens_host, device)
+        self.kv_seq = torch.arange(n, dtype=torch.int32, device=device)
+
+    def run(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
+        """q_nope [B,H,d_h], q_rope [B,H,d_r] (un-rotated); optional new token rows at position T_b - 1."""
+        d = self.dims
+        if new_latent is not None:
+            B.rope_apply(d, self.cache.data, self.cache.block_table, q_rope=q_rope, q_pos=self.q_pos,
+                         q_lat=self.q_lat, kv_latent=new_latent, k_rope=new_k_rope, kv_seq=self.kv_seq,
+                         kv_pos=self.q_pos)
+        else:
+            B.rope_apply(d, None, None, q_rope=q_rope, q_pos=self.q_pos, q_lat=self.q_lat)
+        B.absorb_q(d, q_nope, w_uk, self.q_lat)
+        B.decode(d, self.cache.data, self.cache.block_table, self.q_lat, self.seq_lens, self.seq_lens_host,
+                 self.out_latent, self.lse, self.workspace)
+        B.out_proj(d, self.out_latent, w_uv, self.out)
+        return self.out
+
+
+class PrefillStep:
+    """Causal chunked prefill for fixed chunk sizes: buffers are allocated once here."""
+
+    def __init__(self, dims: B.MLADims, cache: LatentCache, cu_q_host: torch.Tensor, q_start_host: torch.Tensor,
+                 device="cuda"):
+        self.dims, self.cache = dims, cache
+        self.cu_q_host = cu_q_host.to(torch.int32).contiguous()
+        self.q_start_host = q_start_host.to(torch.int32).contiguous()
+        self.cu_q = self.cu_q_host.to(device)
+        self.q_start = self.q_start_host.to(device)
+        n = int(self.cu_q_host[-1])
+        counts = (self.cu_q_host[1:] - self.cu_q_host[:-1]).to(torch.int64)
+        seq = torch.repeat_interleave(torch.arange(len(counts), dtype=torch.int32), counts)
+        local = torch.arange(n, dtype=torch.int32) - self.cu_q_host[:-1].repeat_interleave(counts)
+        self.q_pos = (self.q_start_host.repeat_interleave(counts) + local).to(torch.int32).to(device)
+        self.kv_seq = seq.to(device)
+        self.q_lat = torch.empty((n, dims.n_heads, dims.row), dtype=dims.dtype, device=device)
+        self.out_latent = torch.empty((n, dims.n_heads, dims.d_latent), dtype=dims.dtype, device=device)
+        self.lse = torch.empty((n, dims.n_heads), dtype=torch.float32, device=device)
+        self.out = torch.empty((n, dims.n_heads, dims.d_v), dtype=dims.dtype, device=device)
+
+    def run(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
+        """Queries of the chunk at positions q_start[b] + j; optional chunk rows written to the cache first."""
+        d = self.dims
+        if new_latent is not None:
+            B.rope_apply(d, self.cache.data, self.cache.block_table, q_rope=q_rope, q_pos=self.q_pos,
+                         q_lat=self.q_lat, kv_latent=new_latent, k_rope=new_k_rope, kv_seq=self.kv_seq,
+                         kv_pos=self.q_pos)
+        else:
+            B.rope_apply(d, None, None, q_rope=q_rope, q_pos=self.q_pos, q_lat=self.q_lat)
+        B.absorb_q(d, q_nope, w_uk, self.q_lat)
+        B.prefill(d, self.cache.data, self.cache.block_table, self.q_lat, self.cu_q, self.q_start, self.cu_q_host,
+                  self.q_start_host, self.out_latent, self.lse)
+        B.out_proj(d, self.out_latent, w_uv, self.out)
+        return self.out

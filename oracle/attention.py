@@ -127,6 +127,20 @@ def materialised(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=F
     return {"o": o, "obar": obar, "lse": lse}
 
 
+def query_absorption(w_uk, qc):
+    """q~_{n,i} = W_UK,i^T q^C_{n,i} ("AI decoupled RoPE MLA", recap: merged ahead of the cache).
+
+    w_uk [H, d_h, d_c], qc [N, H, d_h] -> [N, H, d_c]."""
+    return np.einsum("hdc,nhd->nhc", np.asarray(w_uk, np.float64), np.asarray(qc, np.float64))
+
+
+def output_absorption(w_uv, obar):
+    """o_{n,i} = W_UV,i obar_{n,i} ("AI decoupled RoPE MLA", recap: W^UV applied after the sum).
+
+    w_uv [H, d_v, d_c], obar [N, H, d_c] -> [N, H, d_v]."""
+    return np.einsum("hvc,nhc->nhv", np.asarray(w_uv, np.float64), np.asarray(obar, np.float64))
+
+
 def absorbed(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False, key_offset=0):
     """The weight-absorbed evaluation order (self-check of ``materialised`` only).
 
@@ -139,13 +153,13 @@ def absorbed(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False
     w_uv = np.asarray(w_uv, np.float64)
     q_pos = np.asarray(q_pos)
     key_pos = key_offset + np.arange(c.shape[0])
-    q_tilde = np.einsum("hdc,nhd->nhc", w_uk, qc)  # W_UK^T q^C
+    q_tilde = query_absorption(w_uk, qc)  # W_UK^T q^C
     q_rot = rope.rotate(qr, q_pos[:, None], base)
     k_rot = rope.rotate(kr, key_pos, base)
     s = scale * (q_tilde @ c.T + q_rot @ k_rot.T)
     alpha, lse = _softmax(s, _visible(q_pos, key_pos, causal))
     obar = alpha @ c
-    o = np.einsum("hvc,nhc->nhv", w_uv, obar)
+    o = output_absorption(w_uv, obar)
     return {"o": o, "obar": obar, "lse": lse, "q_tilde": q_tilde, "q_rot": q_rot}
 
 

@@ -1,0 +1,101 @@
+"""Helpers for the GPU tests: move a synth.Case onto the device through the C ABI,
+run decode / prefill steps, and compare with the oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mla_decoupled_rope_amd as mla
+
+
+def tdtype(case) -> torch.dtype:
+    return torch.float32 if case.dtype == "f32" else torch.bfloat16
+
+
+def dims_of(case) -> mla.MLADims:
+    s = case.shape
+    return mla.MLADims(s.n_heads, s.d_head, s.d_v, s.d_latent, s.d_rope, dtype=tdtype(case),
+                       softmax_scale=s.scale, rope_base=s.rope_base, page_size=s.page_size)
+
+
+def dev(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype).contiguous()
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def build_cache(case, block_table=None, fill=float("nan")) -> mla.LatentCache:
+    """Allocate the paged cache (poisoned with `fill`) and write every token row through mla_rope_apply."""
+    dims = dims_of(case)
+    table = case.block_table if block_table is None else block_table
+    cache = mla.LatentCache(dims, table, case.num_pages, fill=fill)
+    seqs, pos = case.kv_seq_pos()
+    n = len(seqs)
+    chunk = 1 << 20
+    dt = tdtype(case)
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        cache.write(dev(case.c_rows[r0:r1], dt), dev(case.kr_rows[r0:r1], dt),
+                    torch.from_numpy(seqs[r0:r1]).to("cuda"), torch.from_numpy(pos[r0:r1]).to("cuda"))
+    return cache
+
+
+def run_decode(case, cache=None, block_table=None):
+    """Full decode step (q^R rotation, absorption, decode, out_proj).  Returns float64 numpy dict."""
+    dims = dims_of(case)
+    cache = build_cache(case, block_table) if cache is None else cache
+    step = mla.DecodeStep(dims, cache, torch.from_numpy(case.seq_lens))
+    dt = tdtype(case)
+    w_uk, w_uv = dev(case.w_uk, dt), dev(case.w_uv, dt)
+    out = step.run(dev(case.qc, dt), dev(case.qr, dt), w_uk, w_uv)
+    torch.cuda.synchronize()
+    return {"o": to64(out), "obar": to64(step.out_latent), "lse": to64(step.lse), "q_lat": to64(step.q_lat)}
+
+
+def run_prefill(case, cache=None):
+    dims = dims_of(case)
+    cache = build_cache(case) if cache is None else cache
+    step = mla.PrefillStep(dims, cache, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
+    dt = tdtype(case)
+    out = step.run(dev(case.qc, dt), dev(case.qr, dt), dev(case.w_uk, dt), dev(case.w_uv, dt))
+    torch.cuda.synchronize()
+    return {"o": to64(out), "obar": to64(step.out_latent), "lse": to64(step.lse), "q_lat": to64(step.q_lat)}
+
+
+def rel_errors(got: np.ndarray, want: np.ndarray):
+    """(max |err| / rms(want), rms(err) / rms(want)) over finite reference entries."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    mask = np.isfinite(want)
+    if not mask.all():
+        assert np.array_equal(np.isfinite(got), mask), "non-finite pattern differs"
+        got, want = got[mask], want[mask]
+    rms = np.sqrt(np.mean(want * want)) if want.size else 1.0
+    err = got - want
+    return float(np.max(np.abs(err)) / rms) if err.size else 0.0, float(np.sqrt(np.mean(err * err)) / rms) if err.size else 0.0
+
+
+# Pass criteria: float32 workloads max-abs error <= 1e-4 of the output RMS;
+# bf16 workloads max-abs <= 2e-2 and RMS error <= 5e-3 of the output RMS.
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 5e-3)}
+
+
+def assert_close(got, want, dtype: str, what: str = ""):
+    mx, rms = rel_errors(got, want)
+    tmax, trms = TOL[dtype]
+    assert mx <= tmax and rms <= trms, f"{what}: rel_max {mx:.3e} (<= {tmax}), rel_rms {rms:.3e} (<= {trms})"
+    return mx, rms
+
+
+def assert_lse_close(got, want, dtype: str, what: str = "lse"):
+    """lse is float32 on every path; compare absolute error in nats."""
+    got = np.asarray(got)
+    want = np.asarray(want)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: -inf pattern differs"
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    err = np.max(np.abs(got[fin] - want[fin])) if fin.any() else 0.0
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol}"

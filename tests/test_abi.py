@@ -1,0 +1,138 @@
+"""CPU-side checks of the C ABI: the library loads, exports what include/mla.h
+declares, rejects bad arguments before launching anything, and plans decode
+splits deterministically.  No kernel runs here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import mla_decoupled_rope_amd as mla
+from mla_decoupled_rope_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("mla_rope_apply", "mla_absorb_q", "mla_decode", "mla_prefill", "mla_out_proj"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} is declared in mla.h but not exported"
+    assert set(declared_functions()) == set(B.EXPORTS)
+
+
+def _dims(**kw):
+    base = dict(n_heads=128, d_head=128, d_v=128, d_latent=512, d_rope=64, page_size=64, dtype=B.MLA_BF16,
+                softmax_scale=0.0722, rope_base=10000.0)
+    base.update(kw)
+    return B.Dims(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def status_of_decode(d, batch=1, lens=(10,), ws=None, ws_bytes=0, cache_kw=None):
+    ck = dict(data=FAKE.value, num_pages=4, block_table=FAKE.value, num_seqs=4, max_pages_per_seq=4)
+    ck.update(cache_kw or {})
+    cache = B.PagedCache(**ck)
+    lens_host = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    return B.LIB.mla_decode(ctypes.byref(d), ctypes.byref(cache), FAKE, FAKE, lens_host, batch, FAKE, None, ws,
+                            ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw, status", [
+    (dict(d_rope=63), 1), (dict(n_heads=0), 1), (dict(page_size=32), 2), (dict(dtype=7), 1),
+    (dict(softmax_scale=float("nan")), 1), (dict(rope_base=-1.0), 1), (dict(n_heads=64), 2),
+    (dict(d_rope=256), 2),
+])
+def test_decode_rejects_bad_dims(kw, status):
+    assert status_of_decode(_dims(**kw)) == status
+    assert B.LIB.mla_last_error().decode()
+
+
+def test_decode_rejects_bad_arguments():
+    d = _dims()
+    assert B.LIB.mla_decode(None, None, None, None, None, 1, None, None, None, 0, None) == 1
+    assert status_of_decode(d, batch=-1) == 1
+    assert status_of_decode(d, batch=5, lens=(1, 1, 1, 1, 1)) == 1          # more rows than the block table
+    assert status_of_decode(d, lens=(300,)) == 1                          # beyond 4 pages of 64
+    assert status_of_decode(d, lens=(-3,)) == 1
+    assert status_of_decode(d, lens=(5,), cache_kw=dict(num_pages=0)) == 1  # tokens but no pages
+    assert status_of_decode(d, batch=0) == 0                              # empty batch: nothing to do
+
+
+def test_decode_workspace_is_checked(monkeypatch):
+    monkeypatch.setenv("MLA_DECODE_SPLIT_PAGES", "1")
+    d = _dims()
+    lens = (200,)
+    need = B.LIB.mla_decode_workspace_size(ctypes.byref(d), 1, (ctypes.c_int32 * 1)(*lens))
+    assert need > 0
+    assert status_of_decode(d, lens=lens) == 3
+    assert status_of_decode(d, lens=lens, ws=FAKE, ws_bytes=need - 1) == 3
+    assert "workspace" in B.LIB.mla_last_error().decode()
+
+
+def test_other_calls_validate():
+    d = _dims()
+    assert B.LIB.mla_absorb_q(ctypes.byref(d), None, FAKE, 3, FAKE, None) == 1
+    assert B.LIB.mla_absorb_q(ctypes.byref(d), FAKE, FAKE, -1, FAKE, None) == 1
+    assert B.LIB.mla_absorb_q(ctypes.byref(_dims(d_head=64)), FAKE, FAKE, 3, FAKE, None) == 2
+    assert B.LIB.mla_absorb_q(ctypes.byref(d), None, None, 0, None, None) == 0
+    assert B.LIB.mla_out_proj(ctypes.byref(d), FAKE, None, 2, FAKE, None) == 1
+    assert B.LIB.mla_out_proj(ctypes.byref(_dims(d_v=100)), FAKE, FAKE, 2, FAKE, None) == 2
+    assert B.LIB.mla_rope_apply(ctypes.byref(d), None, None, None, 2, None, None, None, None, None, 0, None) == 1
+    assert B.LIB.mla_rope_apply(ctypes.byref(d), None, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == 1
+    cache = B.PagedCache(FAKE.value, 4, FAKE.value, 2, 4)
+    cu = (ctypes.c_int32 * 3)(1, 2, 3)
+    st = (ctypes.c_int32 * 2)(0, 0)
+    assert B.LIB.mla_prefill(ctypes.byref(d), ctypes.byref(cache), FAKE, FAKE, FAKE, cu, st, 2, FAKE, None,
+                             None) == 1  # cu_q[0] != 0
+    cu = (ctypes.c_int32 * 3)(0, 5, 2)
+    assert B.LIB.mla_prefill(ctypes.byref(d), ctypes.byref(cache), FAKE, FAKE, FAKE, cu, st, 2, FAKE, None,
+                             None) == 1  # decreasing
+    cu = (ctypes.c_int32 * 3)(0, 5, 400)
+    assert B.LIB.mla_prefill(ctypes.byref(d), ctypes.byref(cache), FAKE, FAKE, FAKE, cu, st, 2, FAKE, None,
+                             None) == 1  # beyond the block table
+    assert B.LIB.mla_status_string(3).decode().startswith("workspace")
+
+
+def _plan(lens, dims=None):
+    dims = dims or mla.MLADims(128, 128, 128, 512, 64)
+    return mla.decode_plan(dims, torch.tensor(lens, dtype=torch.int32))
+
+
+def test_plan_is_deterministic_and_covers_every_page():
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        lens = rng.integers(0, 40000, size=int(rng.integers(1, 200))).tolist()
+        sp, n = _plan(lens)
+        assert (sp, n) == _plan(lens)
+        pages = [(t + 63) // 64 for t in lens]
+        assert n == sum(p // sp + (p % sp != 0) for p in pages)
+        assert sp >= 1
+
+
+def test_plan_shapes_of_the_named_workloads():
+    assert _plan([4096] * 64) == (16, 256)       # 64 x 4096: one split of 16 pages per CU
+    assert _plan([131072] * 4) == (32, 256)      # 4 x 131072
+    sp, n = _plan([256], mla.MLADims(16, 128, 128, 256, 32, dtype=torch.float32))
+    assert n >= 1
+
+
+def test_plan_env_override(monkeypatch):
+    monkeypatch.setenv("MLA_DECODE_SPLIT_PAGES", "3")
+    assert _plan([64 * 7, 1, 0]) == (3, 3 + 1)

@@ -1,0 +1,109 @@
+"""Op-level GPU parity: each C-ABI call against the oracle's definition of that step."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as G
+import mla_decoupled_rope_amd as mla
+import synth
+from oracle import attention, paging, rope
+
+pytestmark = pytest.mark.gpu
+
+BF16_ULP = 2.0 ** -8  # relative spacing bound of bf16 (one rounding is at most half of it)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [synth.TINY, synth.DSV2], ids=["tiny", "dsv2"])
+def test_rope_query_rotation(dtype, shape):
+    """q_lat[..., d_c:] = R_p q^R for positions up to 2^17 - 1 (angles in float64)."""
+    rng = np.random.default_rng(11)
+    n = 9
+    q_r = synth.to_storage(rng.standard_normal((n, shape.n_heads, shape.d_rope)), dtype)
+    pos = np.array([0, 1, 2, 255, 4095, 16383, 65536, 131071, 77777], np.int32)
+    case_dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    dims = mla.MLADims(shape.n_heads, shape.d_head, shape.d_v, shape.d_latent, shape.d_rope, dtype=case_dt)
+    q_lat = torch.zeros((n, shape.n_heads, shape.row), dtype=case_dt, device="cuda")
+    mla.rope_apply(dims, None, None, q_rope=G.dev(q_r, case_dt), q_pos=torch.from_numpy(pos).cuda(), q_lat=q_lat)
+    got = G.to64(q_lat)[..., shape.d_latent:]
+    want = rope.rotate(q_r, pos[:, None])
+    tol = 1e-6 if dtype == "f32" else BF16_ULP
+    assert np.all(np.abs(got - want) <= tol * np.abs(want) + 1e-30), np.max(np.abs(got - want))
+    assert np.all(G.to64(q_lat)[..., :shape.d_latent] == 0), "content columns must be untouched"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope_cache_write_paged(dtype):
+    """Rows land in block_table[b][p // 64] * 64 + p % 64; the latent is copied bit for bit,
+    the position key is rotated to its own position; nothing else is written."""
+    shape = synth.DSV2
+    lens = [70, 1, 200]
+    case = synth.direct_decode(shape, dtype, lens, seed=5, shuffle=True)
+    cache = G.build_cache(case)
+    torch.cuda.synchronize()
+    data = G.to64(cache.data).reshape(-1, shape.row)
+    seqs, pos = case.kv_seq_pos()
+    slots = paging.slots(case.block_table, seqs, pos, shape.page_size)
+    written = np.zeros(len(data), bool)
+    written[slots] = True
+    assert np.array_equal(data[slots, :shape.d_latent], case.c_rows.astype(np.float64)), "latent copy is not exact"
+    want = rope.rotate(case.kr_rows, pos)
+    got = data[slots, shape.d_latent:]
+    tol = 1e-6 if dtype == "f32" else BF16_ULP
+    assert np.all(np.abs(got - want) <= tol * np.abs(want) + 1e-30)
+    assert np.all(np.isnan(data[~written])), "rows outside the written slots changed"
+
+
+def test_rope_cache_write_skips_invalid_rows():
+    """Out-of-range sequence, negative position and unallocated pages are skipped."""
+    shape = synth.TINY
+    dims = mla.MLADims(shape.n_heads, shape.d_head, shape.d_v, shape.d_latent, shape.d_rope)
+    table = np.array([[1, -1], [0, 5]], np.int32)  # page 5 does not exist (2 pages)
+    cache = mla.LatentCache(dims, table, 2, fill=float("nan"))
+    rng = np.random.default_rng(3)
+    c = torch.from_numpy(rng.standard_normal((5, shape.d_latent)).astype(np.float32)).cuda().bfloat16()
+    kr = torch.from_numpy(rng.standard_normal((5, shape.d_rope)).astype(np.float32)).cuda().bfloat16()
+    seq = torch.tensor([0, 0, 2, 1, 0], dtype=torch.int32).cuda()
+    posv = torch.tensor([3, 64, 0, 70, -1], dtype=torch.int32).cuda()
+    cache.write(c, kr, seq, posv)
+    torch.cuda.synchronize()
+    data = G.to64(cache.data).reshape(-1, shape.row)
+    ok = ~np.isnan(data).all(axis=1)
+    assert ok.sum() == 1 and ok[64 + 3], "only (seq 0, pos 3) -> page 1 row 3 is valid"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [1, 17, 64, 300])
+def test_absorb_q(dtype, n):
+    shape = synth.DSV2 if dtype == "bf16" else synth.TINY
+    case = synth.direct_decode(shape, dtype, [1] * n, seed=100 + n)
+    dt = G.tdtype(case)
+    dims = G.dims_of(case)
+    q_lat = torch.full((n, shape.n_heads, shape.row), 7.0, dtype=dt, device="cuda")
+    mla.absorb_q(dims, G.dev(case.qc, dt), G.dev(case.w_uk, dt), q_lat)
+    got = G.to64(q_lat)
+    want = attention.query_absorption(case.w_uk, case.qc)
+    G.assert_close(got[..., :shape.d_latent], want, "f32" if dtype == "f32" else "bf16", "q~")
+    if dtype == "bf16":  # one rounding of a float32 accumulation
+        assert G.rel_errors(got[..., :shape.d_latent], want)[1] <= 2e-3
+    assert np.all(got[..., shape.d_latent:] == 7.0), "rope columns must be untouched"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [1, 31, 64, 257])
+def test_out_proj(dtype, n):
+    shape = synth.DSV2 if dtype == "bf16" else synth.TINY
+    rng = np.random.default_rng(200 + n)
+    obar = synth.to_storage(rng.standard_normal((n, shape.n_heads, shape.d_latent)), dtype)
+    w_uv = synth.to_storage(rng.standard_normal((shape.n_heads, shape.d_v, shape.d_latent)) / math.sqrt(shape.d_latent),
+                            dtype)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    dims = mla.MLADims(shape.n_heads, shape.d_head, shape.d_v, shape.d_latent, shape.d_rope, dtype=dt)
+    out = torch.empty((n, shape.n_heads, shape.d_v), dtype=dt, device="cuda")
+    mla.out_proj(dims, G.dev(obar, dt), G.dev(w_uv, dt), out)
+    got = G.to64(out)
+    want = attention.output_absorption(w_uv, obar)
+    G.assert_close(got, want, dtype, "o")
