@@ -1,0 +1,222 @@
+"""Benchmark: absorbed MLA decode with decoupled RoPE on one MI355X.
+
+One step = one pass of the decode hot path over a batch: RoPE on the new
+query's q^R and the new token's cache row (mla_rope_apply), query absorption
+(mla_absorb_q), split attention over the paged latent cache plus the split
+merge (mla_decode), output absorption (mla_out_proj).  Default workload:
+64 sequences x 4096 cached tokens, n_h = 128, d_c = 512, d_r = 64, bf16, in
+64-token pages.  Three identical cache copies are used in rotation so that
+the 256 MB Infinity Cache cannot serve a step from the previous one.
+
+Prints one JSON line.  --config selects other workloads for inspection.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "absorbed MLA decode tokens/s + % HBM roofline (n_h=128,d_c=512,d_r=64)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "attn_bf16.hip")
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def decode_bytes(seq_lens, n_heads=128, d_latent=512, d_rope=64) -> int:
+    """Algorithmic HBM bytes of one decode call: cache rows read once, the query
+    read once, the latent output written once, the block table read once."""
+    row = (d_latent + d_rope) * 2
+    t = np.asarray(seq_lens, np.int64)
+    per_q = n_heads * (d_latent + d_rope) * 2 + n_heads * d_latent * 2
+    return int(np.sum(row * t + per_q + 4 * ((t + 63) // 64)))
+
+
+def prefill_flops(case) -> float:
+    """2 * n_h * (576 + 512) per visible (query, key) pair, causal."""
+    s = case.shape
+    pairs = 0
+    for b in range(case.batch):
+        n = int(case.cu_q[b + 1] - case.cu_q[b])
+        p0 = int(case.q_start[b])
+        pairs += n * p0 + n * (n + 1) // 2
+    return 2.0 * s.n_heads * (s.row + s.d_latent) * pairs
+
+
+def load_traffic(config_name: str):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE)).get(config_name)
+    if not rec or rec.get("kernel_sha") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float = 15.0):
+    """The float64 materialised oracle on the host cores, on a bounded sample of sequences."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    done, t0 = 0, time.perf_counter()
+    order = list(range(case.batch))
+    for b in order:
+        attention.decode_batch(case.seq_lens, case.c_rows, case.kr_rows, case.row_offsets, case.qc, case.qr,
+                               case.w_uk, case.w_uv, case.shape.scale, case.shape.rope_base, seqs=[b])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"materialised float64 decode of {done} of {case.batch} sequences "
+                      f"({int(case.seq_lens[0])} cached tokens each) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU sharding of this path is a design note, not a measured mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mla_decoupled_rope_amd as mla
+    import synth
+    from mla_decoupled_rope_amd import binding as B
+
+    torch.cuda.set_device(0)
+    maker = {"c1": synth.config1, "c2": synth.config2, "c3": synth.config3, "c4": synth.config4,
+             "c5a": synth.config5_decode, "c5b": synth.config5_prefill}[args.config]
+    case = maker()
+    s = case.shape
+    dt = torch.float32 if case.dtype == "f32" else torch.bfloat16
+    dims = mla.MLADims(s.n_heads, s.d_head, s.d_v, s.d_latent, s.d_rope, dtype=dt, softmax_scale=s.scale)
+
+    def dev(x, dtype=dt):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(dtype).contiguous()
+
+    seqs, pos = case.kv_seq_pos()
+    cache0 = mla.LatentCache(dims, case.block_table, case.num_pages)
+    chunk = 1 << 20
+    for r0 in range(0, len(seqs), chunk):
+        r1 = min(len(seqs), r0 + chunk)
+        cache0.write(dev(case.c_rows[r0:r1]), dev(case.kr_rows[r0:r1]), torch.from_numpy(seqs[r0:r1]).cuda(),
+                     torch.from_numpy(pos[r0:r1]).cuda())
+    caches = [cache0]
+    for _ in range(1, max(1, args.copies)):
+        c = mla.LatentCache(dims, case.block_table, case.num_pages)
+        c.data.copy_(cache0.data)
+        caches.append(c)
+    w_uk, w_uv = dev(case.w_uk), dev(case.w_uv)
+    q_nope, q_rope = dev(case.qc), dev(case.qr)
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    if case.kind == "decode":
+        steps = [mla.DecodeStep(dims, c, torch.from_numpy(case.seq_lens)) for c in caches]
+        last = case.row_offsets + np.maximum(case.seq_lens - 1, 0)
+        new_lat, new_kr = dev(case.c_rows[last]), dev(case.kr_rows[last])
+
+        def step(i, timed):
+            st = steps[i % len(steps)]
+            B.rope_apply(dims, st.cache.data, st.cache.block_table, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat,
+                         kv_latent=new_lat, k_rope=new_kr, kv_seq=st.kv_seq, kv_pos=st.q_pos)
+            B.absorb_q(dims, q_nope, w_uk, st.q_lat)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            B.decode(dims, st.cache.data, st.cache.block_table, st.q_lat, st.seq_lens, st.seq_lens_host,
+                     st.out_latent, st.lse, st.workspace)
+            if timed:
+                e1.record(stream)
+                ev.append((e0, e1))
+            B.out_proj(dims, st.out_latent, w_uv, st.out)
+        tokens_per_step = case.batch
+        kernel_name = "mla_decode (split attention + merge)"
+        algo = decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope)
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+    else:
+        steps = [mla.PrefillStep(dims, c, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
+                 for c in caches]
+
+        def step(i, timed):
+            st = steps[i % len(steps)]
+            B.rope_apply(dims, None, None, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat)
+            B.absorb_q(dims, q_nope, w_uk, st.q_lat)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            B.prefill(dims, st.cache.data, st.cache.block_table, st.q_lat, st.cu_q, st.q_start, st.cu_q_host,
+                      st.q_start_host, st.out_latent, st.lse)
+            if timed:
+                e1.record(stream)
+                ev.append((e0, e1))
+            B.out_proj(dims, st.out_latent, w_uv, st.out)
+        tokens_per_step = int(case.cu_q[-1])
+        kernel_name = "mla_prefill (causal attention)"
+        algo = prefill_flops(case)
+        bound, unit, peak = "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_per_step = el / args.steps * 1e3
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    achieved = algo / (kern_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+    traffic = load_traffic(args.config)
+    out = {
+        "metric": METRIC if case.kind == "decode" else "absorbed MLA causal prefill tokens/s + % MFMA roofline",
+        "value": tokens_per_step / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic (seeded N(0,1) latents, keys and queries; weights N(0,1)/sqrt(d_c))",
+        "config": {"workload": case.note.get("workload", args.config), "config": args.config,
+                   "batch": case.batch, "seq_len": int(np.max(case.seq_lens)), "total_kv_tokens": case.total_tokens,
+                   "n_heads": s.n_heads, "d_latent": s.d_latent, "d_rope": s.d_rope, "page_size": s.page_size,
+                   "cache_copies": len(caches), "step": "rope_apply + absorb_q + decode/prefill + out_proj"},
+        "roofline": {"kernel": kernel_name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic, "algorithmic_per_launch": algo,
+                     "avg_launch_ms": kern_ms},
+    }
+    if case.kind == "decode" and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,9 +25,10 @@
  *   _host.  Tensors are dense and row-major in the shapes given.  The caller
  *   owns every buffer; the library allocates nothing and keeps no pointer
  *   after a call returns.
- * - dtype: all floating-point tensors that cross the ABI share dims->dtype
- *   (MLA_F32 or MLA_BF16); lse is always float32; indices are int32.
- *   Accumulation is float32 in every kernel.
+ * - dtype: the cache, q_rope, q_nope, kv_latent, k_rope, the weights and
+ *   out_latent share dims->dtype (MLA_F32 or MLA_BF16).  q_lat has
+ *   dims->q_lat_dtype.  The layer output of mla_out_proj and lse are always
+ *   float32; indices are int32.  Accumulation is float32 in every kernel.
  * - Work is enqueued on `stream` (a hipStream_t, NULL = default stream) and
  *   is asynchronous: no call synchronises.  Keep buffers alive until the
  *   stream has passed the work.
@@ -71,7 +72,13 @@ typedef struct {
   int32_t d_latent;    /* d_c: width of the cached latent c_t            */
   int32_t d_rope;      /* d_r: width of the decoupled RoPE channel, even */
   int32_t page_size;   /* tokens per cache page (must be 64)             */
-  int32_t dtype;       /* mla_dtype                                      */
+  int32_t dtype;       /* mla_dtype of cache, inputs, weights, out_latent */
+  int32_t q_lat_dtype; /* mla_dtype of q_lat.  MLA_F32 with dtype MLA_BF16
+                        * keeps the absorbed query at float32 and scores it
+                        * as a two-term bf16 split (hi + lo): twice the QK
+                        * MFMA work, bf16 rounding of q~ removed.  Supported
+                        * for d_latent + d_rope <= 288.  With dtype MLA_F32
+                        * it must be MLA_F32.                             */
   float softmax_scale; /* one scale on the summed score                  */
   double rope_base;    /* theta_j = rope_base^(-2j/d_r)                  */
 } mla_dims;
@@ -154,7 +161,8 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const
 /* mla_out_proj -- output absorption ("AI decoupled RoPE MLA", recap section:
  * Attn_m = W^UV sum_t alpha_mt c_t).
  *   out[n, h, :] = W_UV[h] out_latent[n, h, :]
- *   out_latent [n, H, d_latent]; w_uv [H, d_v, d_latent]; out [n, H, d_v]. */
+ *   out_latent [n, H, d_latent]; w_uv [H, d_v, d_latent]; out [n, H, d_v]
+ *   in float32 (the float32 accumulator is kept, not rounded to dtype). */
 mla_status mla_out_proj(const mla_dims* dims, const void* out_latent, const void* w_uv, int64_t n,
                         void* out, void* stream);
 

@@ -50,6 +50,10 @@ mla_status check_dims(const mla_dims* d) {
   if (d->d_rope > 128) return fail(MLA_ERR_UNSUPPORTED, "d_rope > 128 is not supported (got %d)", d->d_rope);
   if (d->page_size != mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size must be 64 (got %d)", d->page_size);
   if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (d->q_lat_dtype != MLA_F32 && d->q_lat_dtype != MLA_BF16)
+    return fail(MLA_ERR_INVALID_ARG, "unknown q_lat_dtype %d", d->q_lat_dtype);
+  if (d->dtype == MLA_F32 && d->q_lat_dtype != MLA_F32)
+    return fail(MLA_ERR_INVALID_ARG, "float32 inputs need a float32 q_lat");
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f))
     return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
   if (!(std::isfinite(d->rope_base) && d->rope_base > 0.0))
@@ -61,6 +65,8 @@ mla_status check_attn_shape(const mla_dims* d) {
   if (d->dtype == MLA_BF16) {
     const bool dsv2 = d->n_heads == 128 && d->d_latent == 512 && d->d_rope == 64;
     const bool tiny = d->n_heads == 16 && d->d_latent == 256 && d->d_rope == 32;
+    if (d->q_lat_dtype == MLA_F32 && d->d_latent + d->d_rope > 288)
+      return fail(MLA_ERR_UNSUPPORTED, "a float32 q_lat (two-term scores) needs d_latent + d_rope <= 288");
     if (!dsv2 && !tiny)
       return fail(MLA_ERR_UNSUPPORTED,
                   "bf16 attention supports (n_heads, d_latent, d_rope) = (128, 512, 64) or (16, 256, 32); got (%d, %d, %d)",
@@ -212,6 +218,7 @@ mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache, co
   p.d_latent = dims->d_latent;
   p.d_rope = dims->d_rope;
   p.dtype = dims->dtype;
+  p.q_lat_dtype = dims->q_lat_dtype;
   p.q_rope = q_rope; p.q_pos = q_pos; p.n_q = n_q; p.q_lat = q_lat;
   p.kv_latent = kv_latent; p.k_rope = k_rope; p.kv_seq = kv_seq; p.kv_pos = kv_pos; p.n_kv = n_kv;
   if (n_kv > 0) {
@@ -236,7 +243,7 @@ mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_
   if (n_q > 65535LL * 512 || n_q * dims->n_heads * dims->d_latent > (1LL << 40))
     return fail(MLA_ERR_UNSUPPORTED, "n_q too large for one launch");
   mla::GemmParams p{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
-                    q_nope, w_uk, q_lat, n_q};
+                    dims->q_lat_dtype, q_nope, w_uk, q_lat, n_q};
   const hipError_t e = mla::launch_absorb(p, as_stream(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "absorb launch");
 }
@@ -253,7 +260,7 @@ mla_status mla_out_proj(const mla_dims* dims, const void* out_latent, const void
     return fail(MLA_ERR_UNSUPPORTED, "bf16 output projection needs d_latent and d_v multiples of 32");
   if (n > 65535LL * 32) return fail(MLA_ERR_UNSUPPORTED, "n too large for one launch");
   mla::GemmParams p{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
-                    out_latent, w_uv, out, n};
+                    dims->q_lat_dtype, out_latent, w_uv, out, n};
   const hipError_t e = mla::launch_out_proj(p, as_stream(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "out_proj launch");
 }
@@ -298,6 +305,7 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
   }
   mla::AttnParams p{};
   p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
+  p.q_f32 = dims->q_lat_dtype == MLA_F32;
   p.scale = dims->softmax_scale;
   p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);
   p.q_lat = q_lat; p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
@@ -367,6 +375,7 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const
   if (n_blocks > (1LL << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, "too many workgroups");
   mla::AttnParams p{};
   p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
+  p.q_f32 = dims->q_lat_dtype == MLA_F32;
   p.scale = dims->softmax_scale;
   p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);
   p.q_lat = q_lat; p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;

@@ -150,30 +150,57 @@ __device__ PrefillBlock find_prefill_block(const AttnParams& p, int64_t blk, int
 }
 
 // Copy one page (64 rows x D bf16) into an LDS buffer with 16-byte DMA.
-// LDS chunk slot sl of row r holds global chunk sl ^ swz(r) (within the full
-// groups of 8 chunks).  Rows >= valid_rows are filled from row valid_rows-1.
-template <int D, int NT>
-__device__ __forceinline__ void dma_page(char* lds_buf, const char* page_base, int valid_rows, int tid,
+// LDS chunk slot sl of row r holds logical chunk phys_chunk(r, sl) of row r.
+// Rows go in groups of RG rows = 576 chunks = 9 wave instructions, and each
+// wave takes whole groups, so a lane's (row-in-group, slot) pairs depend only
+// on the lane: nothing is divided per tile and the LDS destination of every
+// instruction is wave-uniform.  Rows >= valid_rows read row valid_rows - 1.
+template <int D, int NW>
+__device__ __forceinline__ void dma_page(char* lds_buf, const char* page_base, int valid_rows, int lane,
                                          int wave) {
   constexpr int CH = D / 8;
   constexpr int ROWB = D * 2;
-  constexpr int NDMA = kPage * CH / NT;
-  static_assert(kPage * CH % NT == 0, "page must split evenly over the workgroup");
+  constexpr int RG = 576 / CH;
+  constexpr int NG = kPage / RG;
+  constexpr int GPW = NG / NW;
+  static_assert(RG * CH == 576 && NG % NW == 0, "page must split into whole row groups per wave");
+  // An opaque copy of the lane id keeps the per-lane offsets from being
+  // hoisted out of the page loop (they are cheap; registers are not).
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
 #pragma unroll
-  for (int k = 0; k < NDMA; ++k) {
-    const int slot = k * NT + tid;
-    const int r = slot / CH;
-    const int sl = slot - r * CH;
-    const int j = phys_chunk<D>(r, sl);
-    const int rs = r < valid_rows ? r : valid_rows - 1;
-    const char* src = page_base + rs * ROWB + j * 16;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                     (lds_void_t*)(lds_buf + (k * NT + wave * 64) * 16), 16, 0, 0);
+  for (int gg = 0; gg < GPW; ++gg) {
+    const int g = wave * GPW + gg;
+#pragma unroll
+    for (int kk = 0; kk < 9; ++kk) {
+      const int c = kk * 64 + ln;
+      const int rig = c / CH;
+      const int r = g * RG + rig;
+      const int j = phys_chunk<D>(r, c - rig * CH);
+      const int rs = r < valid_rows ? r : valid_rows - 1;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(page_base + rs * ROWB + j * 16),
+                                       (lds_void_t*)(lds_buf + g * RG * ROWB + kk * 1024), 16, 0, 0);
+    }
   }
 }
 
+// S += K . Q^T on VGPR accumulators.  Written as inline asm so that the
+// 16 score accumulators live in VGPRs while the 256 output accumulators hold
+// the AGPRs (the compiler otherwise puts both in AGPRs and spills).  The
+// first step uses an inline zero for srcC, so no VALU write feeds an MFMA.
+__device__ __forceinline__ void mfma_qk_first(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last score MFMA and the VALU reads of its result
+// (the hazard recognizer does not see inside inline asm).
+__device__ __forceinline__ void mfma_qk_drain(f32x4 (&s)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
+}
 
-template <int DC, int DR, int HG, int TW, bool PREFILL>
+template <int DC, int DR, int HG, int TW, bool PREFILL, bool QF32>
 __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p) {
   constexpr int D = DC + DR;
   constexpr int NT = 64 * HG * TW;
@@ -183,7 +210,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   constexpr int TILE = kPage * D * 2;
   static_assert(D % 32 == 0 && DC % 16 == 0, "dims");
   static_assert(TW == 1 || HG <= 2, "two token lanes need half the waves' registers");
-  __shared__ __attribute__((aligned(16))) char smem[2 * TILE];
+  __shared__ __attribute__((aligned(16))) char lds0[TILE];
+  __shared__ __attribute__((aligned(16))) char lds1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -203,12 +231,12 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   if constexpr (PREFILL) {
     const PrefillBlock pb = find_prefill_block(p, p.n_blocks - 1 - static_cast<int64_t>(blockIdx.x), ROWS);
     if (!pb.ok) return;
-    b = pb.b;
-    const int nq = p.cu_q[b + 1] - p.cu_q[b];
-    const int q0 = p.q_start[b];
-    const int r0 = pb.rb * ROWS;
+    b = __builtin_amdgcn_readfirstlane(pb.b);
+    const int nq = __builtin_amdgcn_readfirstlane(p.cu_q[b + 1] - p.cu_q[b]);
+    const int q0 = __builtin_amdgcn_readfirstlane(p.q_start[b]);
+    const int r0 = __builtin_amdgcn_readfirstlane(pb.rb) * ROWS;
     const int last_q = min(nq - 1, (r0 + ROWS - 1) / H);
-    key_end = q0 + last_q + 1;
+    key_end = __builtin_amdgcn_readfirstlane(q0 + last_q + 1);
     page_begin = 0;
     page_end = (key_end + kPage - 1) / kPage;
 #pragma unroll
@@ -223,13 +251,14 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     const int hc = static_cast<int>(static_cast<int64_t>(blockIdx.x) % p.n_head_chunks);
     const DecodeItem it = find_decode_item(p, item);
     if (!it.ok || it.slot >= p.n_items) return;
-    b = it.b;
-    key_end = p.seq_lens[b];
+    // the item is wave-uniform: keep it in scalar registers
+    b = __builtin_amdgcn_readfirstlane(it.b);
+    key_end = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
     const int pages = (key_end + kPage - 1) / kPage;
-    page_begin = it.s * p.split_pages;
+    page_begin = __builtin_amdgcn_readfirstlane(it.s) * p.split_pages;
     page_end = min(pages, page_begin + p.split_pages);
-    final_out = it.n_s == 1;
-    slot = it.slot;
+    final_out = __builtin_amdgcn_readfirstlane(it.n_s) == 1;
+    slot = __builtin_amdgcn_readfirstlane(it.slot);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int head = hc * ROWS + hg * 32 + rb * 16 + r16;
@@ -243,16 +272,34 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   int lim_max = max(limit[0], limit[1]);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) lim_max = max(lim_max, __shfl_xor(lim_max, m, 64));
+  lim_max = __builtin_amdgcn_readfirstlane(lim_max);
 
-  // ---- Q fragments (MFMA B operand: row = r16, d = ks*32 + 8*q16 .. +7)
-  const bf16_t* qlat = static_cast<const bf16_t*>(p.q_lat);
+  // ---- Q fragments (MFMA B operand: row = r16, d = ks*32 + 8*q16 .. +7).
+  // A float32 q_lat is split into hi = bf16(q) and lo = bf16(q - hi); the
+  // score then takes both terms (K.hi + K.lo), so q~ enters at ~16 bits.
   bf16x8 qf[2][KS];
+  bf16x8 qlo[QF32 ? 2 : 1][QF32 ? KS : 1];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[rb][ks] = row_ok[rb] ? *reinterpret_cast<const bf16x8*>(qlat + row_g[rb] * D + ks * 32 + q16 * 8)
-                              : bf16x8{};
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (QF32) {
+        const float* qlat = static_cast<const float*>(p.q_lat);
+        bf16_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = row_ok[rb] ? qlat[row_g[rb] * D + ks * 32 + q16 * 8 + e] : 0.f;
+          hi[e] = f32_to_bf16_finite(x);
+          lo[e] = f32_to_bf16_finite(x - bf16_to_f32(hi[e]));
+        }
+        __builtin_memcpy(&qf[rb][ks], hi, 16);
+        __builtin_memcpy(&qlo[rb][ks], lo, 16);
+      } else {
+        const bf16_t* qlat = static_cast<const bf16_t*>(p.q_lat);
+        qf[rb][ks] = row_ok[rb] ? *reinterpret_cast<const bf16x8*>(qlat + row_g[rb] * D + ks * 32 + q16 * 8)
+                                : bf16x8{};
+      }
+    }
 
   f32x4 oacc[CB][2];
 #pragma unroll
@@ -265,27 +312,19 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 
   const char* cache = static_cast<const char*>(p.cache);
   const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
-  auto page_ptr = [&](int pg) -> const char* {
-    int id = pg < p.max_pages ? bt[pg] : -1;
-    id = (id < 0 || id >= p.num_pages) ? 0 : id;
+  // Page ids of the split, 64 at a time: lane j holds page (base + j); a
+  // tile reads its id with readlane, so the loop issues no other vector loads.
+  auto load_ids = [&](int first_pg) -> int {
+    const int pg = first_pg + lane;
+    int id = (pg < page_end && pg < p.max_pages) ? bt[pg] : 0;
+    return (id < 0 || id >= p.num_pages) ? 0 : id;
+  };
+  auto page_ptr = [&](int ids, int pg) -> const char* {
+    const int id = __builtin_amdgcn_readlane(ids, (pg - page_begin) & 63);
     return cache + static_cast<int64_t>(id) * TILE;
   };
 
-  // Per-lane LDS byte offsets inside a tile (sub-block 0); the chunk group
-  // and the sub-block enter as immediates.
   constexpr int CHF8 = (D / 8 / 8) * 8;  // chunks in full swizzle groups
-  int k_off[2][2], k_tail[2], v_off[2][4];
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int krow = tb * 16 + r16;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) k_off[tb][kb] = krow * (D * 2) + phys_chunk<D>(krow, kb * 4 + q16) * 16;
-    k_tail[tb] = krow * (D * 2) + (phys_chunk<D>(krow, CHF8 + q16) - CHF8) * 16;
-    const int vrow = tb * 16 + q16 * 4 + (r16 >> 2);
-#pragma unroll
-    for (int cl = 0; cl < 4; ++cl)
-      v_off[tb][cl] = vrow * (D * 2) + phys_chunk<D>(vrow, cl * 2 + ((r16 & 3) >> 1)) * 16 + (r16 & 1) * 8;
-  }
 
   const int ntile = page_end - page_begin;
 
@@ -298,15 +337,21 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   auto run_pass = [&](auto mode_tag) -> bool {
     constexpr int MODE = decltype(mode_tag)::value;
     bool overflow = false;
-    if (ntile > 0) dma_page<D, NT>(smem, page_ptr(page_begin), min(kPage, key_end - page_begin * kPage), tid, wave);
-    for (int it = 0; it < ntile; ++it) {
+    int ids = load_ids(page_begin);
+    if (ntile > 0)
+      dma_page<D, NT / 64>(lds0, page_ptr(ids, page_begin), min(kPage, key_end - page_begin * kPage), lane, wave);
+    // One page: wait for `cur`, start the DMA of the next page into `nxt`,
+    // compute on `cur`.  The two buffers are distinct LDS objects, so the
+    // compiler can see that the DMA in flight never aliases the reads.
+    auto tile = [&](int it, char* cur, char* nxt) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (it + 1 < ntile) {
         const int pg = page_begin + it + 1;
-        dma_page<D, NT>(smem + ((it + 1) & 1) * TILE, page_ptr(pg), min(kPage, key_end - pg * kPage), tid, wave);
+        if (((it + 1) & 63) == 0) ids = load_ids(pg);
+        dma_page<D, NT / 64>(nxt, page_ptr(ids, pg), min(kPage, key_end - pg * kPage), lane, wave);
       }
-      const char* buf = smem + (it & 1) * TILE;
+      const char* buf = cur;
       const int tile_t0 = (page_begin + it) * kPage;
 #pragma unroll
       for (int sbi = 0; sbi < 2 / TW; ++sbi) {
@@ -314,29 +359,56 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
         const int t0 = tile_t0 + sb * 32;
         // skip sub-blocks no row of this wave can see (wave-uniform)
         if (t0 >= lim_max) continue;
-        // ---- S^T = K . Q^T over D
-        f32x4 sacc[2][2];
+        // Per-lane LDS byte offsets inside the tile, recomputed here from an
+        // opaque lane id rather than held in registers across the loop; the
+        // chunk group and the sub-block enter as immediates.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int lq16 = ln >> 4, lr16 = ln & 15;
+        int k_off[2][2], k_tail[2], v_off[2][4];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-          sacc[tb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-          sacc[tb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+          const int krow = tb * 16 + lr16;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          bf16x8 ka[2];
+          for (int kb = 0; kb < 2; ++kb) k_off[tb][kb] = krow * (D * 2) + phys_chunk<D>(krow, kb * 4 + lq16) * 16;
+          k_tail[tb] = krow * (D * 2) + (phys_chunk<D>(krow, CHF8 + lq16) - CHF8) * 16;
+          const int vrow = tb * 16 + lq16 * 4 + (lr16 >> 2);
+#pragma unroll
+          for (int cl = 0; cl < 4; ++cl)
+            v_off[tb][cl] = vrow * (D * 2) + phys_chunk<D>(vrow, cl * 2 + ((lr16 & 3) >> 1)) * 16 + (lr16 & 1) * 8;
+        }
+        // ---- S^T = K . Q^T over D
+        f32x4 sacc[2][2];
+        // K fragments run KPF steps ahead of the MFMAs that consume them.
+        constexpr int KPF = 2;
+        bf16x8 ka[KS][2];
+        auto load_k = [&](int ks) {
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
             // chunk ks*4 + q16 of row krow: group ks/2 (immediate), in-group slot from k_off
             const char* a = (ks / 2) * 128 < CHF8 * 16 ? buf + k_off[tb][ks & 1] + (ks / 2) * 128
                                                        : buf + k_tail[tb] + (ks / 2) * 128;
-            ka[tb] = *reinterpret_cast<const bf16x8*>(a + sb * 32 * (D * 2));
+            ka[ks][tb] = *reinterpret_cast<const bf16x8*>(a + sb * 32 * (D * 2));
           }
+        };
+#pragma unroll
+        for (int ks = 0; ks < KPF; ++ks) load_k(ks);
+        asm volatile("s_nop 1" ::: "memory");
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + KPF < KS) load_k(ks + KPF);
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-              sacc[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tb], qf[rb][ks], sacc[tb][rb], 0, 0, 0);
+            for (int rb = 0; rb < 2; ++rb) {
+              if (ks == 0)
+                mfma_qk_first(sacc[tb][rb], ka[ks][tb], qf[rb][ks]);
+              else
+                mfma_qk(sacc[tb][rb], ka[ks][tb], qf[rb][ks]);
+              if constexpr (QF32) mfma_qk(sacc[tb][rb], ka[ks][tb], qlo[rb][ks]);
+            }
         }
+        mfma_qk_drain(sacc);
         // ---- scores in base 2, masked; row max over the sub-block
         float mx[2];
 #pragma unroll
@@ -346,7 +418,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int t = t0 + tb * 16 + q16 * 4 + e;
+              const int t = t0 + tb * 16 + lq16 * 4 + e;
               const float v = t < limit[rb] ? sacc[tb][rb][e] * p.scale_log2 : -INFINITY;
               sacc[tb][rb][e] = v;
               m = fmaxf(m, v);
@@ -385,23 +457,36 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
           __builtin_memcpy(&pb[rb], pv, 16);
         }
         // ---- O^T += V^T . P^T ; V^T fragment from two transpose reads
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          i16x4 v[2];
+        // V^T fragments run VPF column blocks ahead of their MFMAs.
+        constexpr int VPF = 4;
+        i16x4 vt[CB][2];
+        auto load_v = [&](int cb) {
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
             // columns cb*16 + 4*(r16&3): chunk cb*2 + ((r16&3)>>1) = group cb/4, slot from v_off
             const char* a = buf + v_off[tb][cb & 3] + (cb / 4) * 128 + sb * 32 * (D * 2);
-            v[tb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
+            vt[cb][tb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
           }
+        };
+#pragma unroll
+        for (int cb = 0; cb < VPF; ++cb) load_v(cb);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          if (cb + VPF < CB) load_v(cb + VPF);
           bf16x8 va;
-          __builtin_memcpy(&va, &v[0], 8);
-          __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &v[1], 8);
+          __builtin_memcpy(&va, &vt[cb][0], 8);
+          __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vt[cb][1], 8);
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
             oacc[cb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb], oacc[cb][rb], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two transpose reads of block cb + VPF
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // the two MFMAs of block cb
         }
       }
+    };
+    for (int it = 0; it < ntile; it += 2) {
+      tile(it, lds0, lds1);
+      if (it + 1 < ntile) tile(it + 1, lds1, lds0);
     }
     return overflow;
   };
@@ -426,7 +511,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   // ---- combine the two token lanes of a head group (TW == 2)
   if constexpr (TW == 2) {
     __syncthreads();
-    float* xo = reinterpret_cast<float*>(smem);  // [hg][cb][rb][lane][4]
+    static_assert((HG * CB * 2 * 64 * 4 + HG * 2 * 64 * 2) * 4 <= TILE, "exchange must fit one page buffer");
+    float* xo = reinterpret_cast<float*>(lds0);  // [hg][cb][rb][lane][4]
     float* xs = xo + HG * CB * 2 * 64 * 4;       // [hg][rb][lane][m, l]
     if (tw == 1) {
 #pragma unroll
@@ -545,10 +631,10 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
   if (p.lse != nullptr && lane == 0) p.lse[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 
-template <int DC, int DR, int HG, int TW, bool PREFILL>
+template <int DC, int DR, int HG, int TW, bool PREFILL, bool QF32>
 hipError_t launch_attn(const AttnParams& p, int64_t n_wg, hipStream_t s) {
   if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_bf16_kernel<DC, DR, HG, TW, PREFILL>), dim3(static_cast<unsigned>(n_wg)),
+  hipLaunchKernelGGL((attn_bf16_kernel<DC, DR, HG, TW, PREFILL, QF32>), dim3(static_cast<unsigned>(n_wg)),
                      dim3(64 * HG * TW), 0, s, p);
   return hipGetLastError();
 }
@@ -557,14 +643,20 @@ hipError_t launch_attn(const AttnParams& p, int64_t n_wg, hipStream_t s) {
 
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s) {
   const int64_t n_wg = p.n_items * p.n_head_chunks;
-  if (p.d_latent == 512 && p.d_rope == 64) return launch_attn<512, 64, 4, 1, false>(p, n_wg, s);
-  if (p.d_latent == 256 && p.d_rope == 32) return launch_attn<256, 32, 1, 2, false>(p, n_wg, s);
+  if (p.d_latent == 512 && p.d_rope == 64 && !p.q_f32) return launch_attn<512, 64, 4, 1, false, false>(p, n_wg, s);
+  if (p.d_latent == 256 && p.d_rope == 32) {
+    if (p.q_f32) return launch_attn<256, 32, 1, 2, false, true>(p, n_wg, s);
+    return launch_attn<256, 32, 1, 2, false, false>(p, n_wg, s);
+  }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t s) {
-  if (p.d_latent == 512 && p.d_rope == 64) return launch_attn<512, 64, 4, 1, true>(p, p.n_blocks, s);
-  if (p.d_latent == 256 && p.d_rope == 32) return launch_attn<256, 32, 4, 1, true>(p, p.n_blocks, s);
+  if (p.d_latent == 512 && p.d_rope == 64 && !p.q_f32) return launch_attn<512, 64, 4, 1, true, false>(p, p.n_blocks, s);
+  if (p.d_latent == 256 && p.d_rope == 32) {
+    if (p.q_f32) return launch_attn<256, 32, 4, 1, true, true>(p, p.n_blocks, s);
+    return launch_attn<256, 32, 4, 1, true, false>(p, p.n_blocks, s);
+  }
   return hipErrorInvalidValue;
 }
 

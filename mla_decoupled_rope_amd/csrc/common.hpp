@@ -40,7 +40,7 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_x
 // ---------------------------------------------------------------- params --
 
 struct RopeParams {
-  int n_heads, d_latent, d_rope, dtype;
+  int n_heads, d_latent, d_rope, dtype, q_lat_dtype;
   const void* q_rope; const int32_t* q_pos; int64_t n_q; void* q_lat;
   const void* kv_latent; const void* k_rope; const int32_t* kv_seq; const int32_t* kv_pos; int64_t n_kv;
   void* cache; int64_t num_pages; const int32_t* block_table; int32_t num_seqs; int32_t max_pages;
@@ -48,7 +48,7 @@ struct RopeParams {
 };
 
 struct GemmParams {
-  int n_heads, d_head, d_v, d_latent, d_rope, dtype;
+  int n_heads, d_head, d_v, d_latent, d_rope, dtype, q_lat_dtype;
   const void* a; const void* w; void* out; int64_t n;
 };
 
@@ -56,6 +56,7 @@ struct GemmParams {
 struct AttnParams {
   // shape
   int n_heads, d_latent, d_rope;
+  int q_f32;         // q_lat is float32 (two-term bf16 split in QK)
   float scale;       // softmax_scale
   float scale_log2;  // softmax_scale * log2(e)
   // inputs

@@ -12,7 +12,8 @@
 //    [d_h, d_c], so the MFMA A operand (8 consecutive i for one j) is a
 //    column read: the W tile is staged in LDS and read with ds_read_tr16_b64.
 //  * out_proj: o^T[v, n] = sum_j W_UV[h][v][j] obar[n, h, j].  Both operands
-//    are already contiguous along j and come straight from global memory.
+//    are already contiguous along j and come straight from global memory;
+//    the float32 accumulator is stored as is (the layer output is float32).
 // float32 path: one thread per output element, float32 accumulation.
 #include "common.hpp"
 
@@ -29,7 +30,7 @@ __device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
 }
 
 // W_UK tile [d_head rows (i), 128 cols (j)] in LDS; each wave owns 32 j x 64 n.
-template <int DH>
+template <int DH, typename TQ>
 __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t w_lds[DH * kAbsorbLdsStride];
   const int h = blockIdx.y;
@@ -49,7 +50,7 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
   }
   __syncthreads();
   const bf16_t* q = static_cast<const bf16_t*>(p.a);
-  bf16_t* out = static_cast<bf16_t*>(p.out);
+  TQ* out = static_cast<TQ*>(p.out);
   const int64_t n_begin = static_cast<int64_t>(blockIdx.z) * kAbsorbNChunk;
   const int64_t n_end = min(p.n, n_begin + kAbsorbNChunk);
   const int q16 = lane >> 4, r16 = lane & 15;
@@ -97,10 +98,14 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
         const int j = j0 + jw + jb * 16 + 4 * q16;
-        uint2 packed;
-        packed.x = f32_to_bf16(acc[jb][nb][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[jb][nb][1])) << 16);
-        packed.y = f32_to_bf16(acc[jb][nb][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[jb][nb][3])) << 16);
-        *reinterpret_cast<uint2*>(out + (n * H + h) * D + j) = packed;
+        if constexpr (sizeof(TQ) == 4) {
+          *reinterpret_cast<f32x4*>(out + (n * H + h) * D + j) = acc[jb][nb];
+        } else {
+          uint2 packed;
+          packed.x = f32_to_bf16(acc[jb][nb][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[jb][nb][1])) << 16);
+          packed.y = f32_to_bf16(acc[jb][nb][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[jb][nb][3])) << 16);
+          *reinterpret_cast<uint2*>(out + (n * H + h) * D + j) = packed;
+        }
       }
     }
   }
@@ -117,7 +122,7 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(GemmParams p) {
   const int q16 = lane >> 4, r16 = lane & 15;
   const bf16_t* w = static_cast<const bf16_t*>(p.w) + static_cast<int64_t>(h) * DV * DC;
   const bf16_t* ob = static_cast<const bf16_t*>(p.a);
-  bf16_t* out = static_cast<bf16_t*>(p.out);
+  float* out = static_cast<float*>(p.out);
   const int64_t n0 = static_cast<int64_t>(blockIdx.z) * 32;
   f32x4 acc[2][2];
 #pragma unroll
@@ -145,10 +150,7 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int vb = 0; vb < 2; ++vb) {
       const int v = v0 + vb * 16 + 4 * q16;
-      uint2 packed;
-      packed.x = f32_to_bf16(acc[vb][nb][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[vb][nb][1])) << 16);
-      packed.y = f32_to_bf16(acc[vb][nb][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[vb][nb][3])) << 16);
-      *reinterpret_cast<uint2*>(out + (n * H + h) * DV + v) = packed;
+      *reinterpret_cast<f32x4*>(out + (n * H + h) * DV + v) = acc[vb][nb];
     }
   }
 }
@@ -191,7 +193,10 @@ hipError_t launch_absorb(const GemmParams& p, hipStream_t s) {
   } else {
     const dim3 grid(p.d_latent / kAbsorbJTile, p.n_heads,
                     static_cast<unsigned>((p.n + kAbsorbNChunk - 1) / kAbsorbNChunk));
-    hipLaunchKernelGGL(absorb_bf16_kernel<128>, grid, dim3(256), 0, s, p);
+    if (p.q_lat_dtype == 0)
+      hipLaunchKernelGGL((absorb_bf16_kernel<128, float>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((absorb_bf16_kernel<128, bf16_t>), grid, dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -25,8 +25,8 @@ template <> __device__ __forceinline__ void st<bf16_t>(bf16_t* p, int64_t i, dou
   p[i] = f32_to_bf16(static_cast<float>(v));
 }
 
-template <typename T>
-__device__ __forceinline__ void rotate_pairs(const RopeParams& p, const T* src, T* dst, int pos, int lane) {
+template <typename T, typename TO>
+__device__ __forceinline__ void rotate_pairs(const RopeParams& p, const T* src, TO* dst, int pos, int lane) {
   const int half = p.d_rope / 2;
   for (int j = lane; j < half; j += 64) {
     double s, c;
@@ -37,7 +37,7 @@ __device__ __forceinline__ void rotate_pairs(const RopeParams& p, const T* src, 
   }
 }
 
-template <typename T>
+template <typename T, typename TQ>
 __global__ void __launch_bounds__(256) rope_kernel(RopeParams p) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
@@ -46,8 +46,8 @@ __global__ void __launch_bounds__(256) rope_kernel(RopeParams p) {
   if (row < nq_rows) {
     const int pos = p.q_pos[row / p.n_heads];
     const T* src = static_cast<const T*>(p.q_rope) + row * p.d_rope;
-    T* dst = static_cast<T*>(p.q_lat) + row * width + p.d_latent;
-    rotate_pairs<T>(p, src, dst, pos, lane);
+    TQ* dst = static_cast<TQ*>(p.q_lat) + row * width + p.d_latent;
+    rotate_pairs<T, TQ>(p, src, dst, pos, lane);
     return;
   }
   const int64_t m = row - nq_rows;
@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(256) rope_kernel(RopeParams p) {
   T* dst = static_cast<T*>(p.cache) + (static_cast<int64_t>(page) * kPage + pos % kPage) * width;
   const T* lat = static_cast<const T*>(p.kv_latent) + m * p.d_latent;
   for (int c = lane; c < p.d_latent; c += 64) dst[c] = lat[c];
-  rotate_pairs<T>(p, static_cast<const T*>(p.k_rope) + m * p.d_rope, dst + p.d_latent, pos, lane);
+  rotate_pairs<T, T>(p, static_cast<const T*>(p.k_rope) + m * p.d_rope, dst + p.d_latent, pos, lane);
 }
 
 hipError_t launch_rope(const RopeParams& p, hipStream_t s) {
@@ -70,9 +70,11 @@ hipError_t launch_rope(const RopeParams& p, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
   if (p.dtype == 0)
-    hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((rope_kernel<float, float>), grid, dim3(256), 0, s, p);
+  else if (p.q_lat_dtype == 0)
+    hipLaunchKernelGGL((rope_kernel<bf16_t, float>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(rope_kernel<bf16_t>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((rope_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

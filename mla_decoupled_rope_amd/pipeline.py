@@ -44,10 +44,10 @@ class DecodeStep:
         self.seq_lens = self.seq_lens_host.to(device)
         n = self.seq_lens_host.numel()
         self.q_pos = (self.seq_lens - 1).clamp_min(0).to(torch.int32)
-        self.q_lat = torch.empty((n, dims.n_heads, dims.row), dtype=dims.dtype, device=device)
+        self.q_lat = torch.empty((n, dims.n_heads, dims.row), dtype=dims.qdtype, device=device)
         self.out_latent = torch.empty((n, dims.n_heads, dims.d_latent), dtype=dims.dtype, device=device)
         self.lse = torch.empty((n, dims.n_heads), dtype=torch.float32, device=device)
-        self.out = torch.empty((n, dims.n_heads, dims.d_v), dtype=dims.dtype, device=device)
+        self.out = torch.empty((n, dims.n_heads, dims.d_v), dtype=torch.float32, device=device)
         self.workspace = B.decode_workspace(dims, self.seq_lens_host, device)
         self.kv_seq = torch.arange(n, dtype=torch.int32, device=device)
 
@@ -83,10 +83,10 @@ class PrefillStep:
         local = torch.arange(n, dtype=torch.int32) - self.cu_q_host[:-1].repeat_interleave(counts)
         self.q_pos = (self.q_start_host.repeat_interleave(counts) + local).to(torch.int32).to(device)
         self.kv_seq = seq.to(device)
-        self.q_lat = torch.empty((n, dims.n_heads, dims.row), dtype=dims.dtype, device=device)
+        self.q_lat = torch.empty((n, dims.n_heads, dims.row), dtype=dims.qdtype, device=device)
         self.out_latent = torch.empty((n, dims.n_heads, dims.d_latent), dtype=dims.dtype, device=device)
         self.lse = torch.empty((n, dims.n_heads), dtype=torch.float32, device=device)
-        self.out = torch.empty((n, dims.n_heads, dims.d_v), dtype=dims.dtype, device=device)
+        self.out = torch.empty((n, dims.n_heads, dims.d_v), dtype=torch.float32, device=device)
 
     def run(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
         """Queries of the chunk at positions q_start[b] + j; optional chunk rows written to the cache first."""

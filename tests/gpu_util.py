@@ -13,10 +13,16 @@ def tdtype(case) -> torch.dtype:
     return torch.float32 if case.dtype == "f32" else torch.bfloat16
 
 
-def dims_of(case) -> mla.MLADims:
+def dims_of(case, precise=None) -> mla.MLADims:
+    """Library dims for a case.  precise=True keeps q_lat in float32 (two-term
+    bf16 scores); by default the tiny shape takes it and the DeepSeek-V2 shape
+    keeps a bf16 q_lat."""
     s = case.shape
+    if precise is None:
+        precise = s.row <= 288
+    qdt = torch.float32 if (case.dtype == "f32" or precise) else torch.bfloat16
     return mla.MLADims(s.n_heads, s.d_head, s.d_v, s.d_latent, s.d_rope, dtype=tdtype(case),
-                       softmax_scale=s.scale, rope_base=s.rope_base, page_size=s.page_size)
+                       softmax_scale=s.scale, rope_base=s.rope_base, page_size=s.page_size, q_lat_dtype=qdt)
 
 
 def dev(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
@@ -43,9 +49,9 @@ def build_cache(case, block_table=None, fill=float("nan")) -> mla.LatentCache:
     return cache
 
 
-def run_decode(case, cache=None, block_table=None):
+def run_decode(case, cache=None, block_table=None, precise=None):
     """Full decode step (q^R rotation, absorption, decode, out_proj).  Returns float64 numpy dict."""
-    dims = dims_of(case)
+    dims = dims_of(case, precise)
     cache = build_cache(case, block_table) if cache is None else cache
     step = mla.DecodeStep(dims, cache, torch.from_numpy(case.seq_lens))
     dt = tdtype(case)
@@ -55,8 +61,8 @@ def run_decode(case, cache=None, block_table=None):
     return {"o": to64(out), "obar": to64(step.out_latent), "lse": to64(step.lse), "q_lat": to64(step.q_lat)}
 
 
-def run_prefill(case, cache=None):
-    dims = dims_of(case)
+def run_prefill(case, cache=None, precise=None):
+    dims = dims_of(case, precise)
     cache = build_cache(case) if cache is None else cache
     step = mla.PrefillStep(dims, cache, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
     dt = tdtype(case)
@@ -66,27 +72,34 @@ def run_prefill(case, cache=None):
 
 
 def rel_errors(got: np.ndarray, want: np.ndarray):
-    """(max |err| / rms(want), rms(err) / rms(want)) over finite reference entries."""
+    """(max over output rows of max|err| / rms(that row of want), rms(err) / rms(want)).
+
+    A row is one output vector (the last axis: one (query, head) pair).  Rows
+    whose reference is all zero (no visible key) must match exactly."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
-    mask = np.isfinite(want)
-    if not mask.all():
-        assert np.array_equal(np.isfinite(got), mask), "non-finite pattern differs"
-        got, want = got[mask], want[mask]
-    rms = np.sqrt(np.mean(want * want)) if want.size else 1.0
+    if want.size == 0:
+        return 0.0, 0.0
     err = got - want
-    return float(np.max(np.abs(err)) / rms) if err.size else 0.0, float(np.sqrt(np.mean(err * err)) / rms) if err.size else 0.0
+    row_rms = np.sqrt(np.mean(want * want, axis=-1, keepdims=True))
+    zero = row_rms[..., 0] == 0
+    assert np.all(err[zero] == 0), "rows with no visible key must be exactly zero"
+    row_max = np.max(np.abs(err[~zero]) / row_rms[~zero]) if (~zero).any() else 0.0
+    rms = np.sqrt(np.mean(want * want))
+    return float(row_max), float(np.sqrt(np.mean(err * err)) / rms)
 
 
-# Pass criteria: float32 workloads max-abs error <= 1e-4 of the output RMS;
-# bf16 workloads max-abs <= 2e-2 and RMS error <= 5e-3 of the output RMS.
+# Pass criteria: float32 workloads max |err| <= 1e-4 of the output RMS; bf16
+# workloads max |err| <= 2e-2 and RMS error <= 5e-3 of the output RMS.  The
+# max is taken per output row against that row's RMS (rows that average few
+# keys are an order of magnitude larger than rows that average thousands).
 TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 5e-3)}
 
 
-def assert_close(got, want, dtype: str, what: str = ""):
+def assert_close(got, want, dtype: str, what: str = "", tol=None):
     mx, rms = rel_errors(got, want)
-    tmax, trms = TOL[dtype]
-    assert mx <= tmax and rms <= trms, f"{what}: rel_max {mx:.3e} (<= {tmax}), rel_rms {rms:.3e} (<= {trms})"
+    tmax, trms = TOL[dtype] if tol is None else tol
+    assert mx <= tmax and rms <= trms, f"{what}: row rel_max {mx:.3e} (<= {tmax}), rel_rms {rms:.3e} (<= {trms})"
     return mx, rms
 
 
