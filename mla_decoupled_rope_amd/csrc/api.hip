@@ -1,9 +1,11 @@
 // C-ABI host layer of libmla: argument checks, the decode split plan, and
 // the kernel launches.  Nothing here allocates device memory or synchronises.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <functional>
 #include <queue>
 #include <string>
@@ -103,39 +105,57 @@ int env_split_pages() {
   return v > 0 && v < (1 << 30) ? static_cast<int>(v) : 0;
 }
 
-// Makespan of the item list (full splits first, then remainders) under
-// greedy list scheduling on `workers` identical workers.
+// Makespan of the item list under greedy list scheduling on `workers`
+// identical workers: first the full splits of split sequences, then the
+// single-item sequences of exactly L pages, then the remainders.  The first
+// group all cost the same, so greedy placement deals them out evenly: r
+// workers end at `hi`, the others at `lo`.  The other two groups hold at most
+// one item per sequence; a heap tracks only the workers they have touched,
+// while untouched ones are counted per level.
 double simulate(const std::vector<int>& pages, int L, int workers, double item_cost, double partial_cost) {
-  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
-  for (int w = 0; w < workers; ++w) free_at.push(0.0);
-  double makespan = 0.0;
+  int64_t n_split = 0;
+  for (int pg : pages)
+    if (pg > L) n_split += pg / L;
+  const int64_t q = n_split / workers, r = n_split % workers;
+  const double lo = static_cast<double>(q) * (L + item_cost + partial_cost);
+  const double hi = r > 0 ? lo + (L + item_cost + partial_cost) : lo;
+  int64_t n_lo = workers - r, n_hi = r;
+  double makespan = n_hi > 0 ? hi : lo;
+  std::priority_queue<double, std::vector<double>, std::greater<double>> touched;
   auto run = [&](double cost) {
-    const double t = free_at.top() + cost;
-    free_at.pop();
-    free_at.push(t);
+    // the least loaded worker: an untouched one at lo, else the lesser of hi and the heap's top
+    double t;
+    if (n_lo > 0) {
+      t = lo;
+      --n_lo;
+    } else if (n_hi > 0 && (touched.empty() || hi <= touched.top())) {
+      t = hi;
+      --n_hi;
+    } else {
+      t = touched.top();
+      touched.pop();
+    }
+    t += cost;
+    touched.push(t);
     makespan = std::max(makespan, t);
   };
-  for (int pg : pages) {
-    const bool split = pg > L;
-    for (int k = 0; k < pg / L; ++k) run(L + item_cost + (split ? partial_cost : 0.0));
-  }
+  for (int pg : pages)
+    if (pg == L) run(L + item_cost);
   for (int pg : pages)
     if (pg % L) run(pg % L + item_cost + (pg > L ? partial_cost : 0.0));
   return makespan;
 }
 
-Plan make_plan(const mla_dims* d, int batch, const int32_t* lens) {
+Plan compute_plan(const mla_dims* d, const std::vector<int>& pages, int env) {
   Plan p;
-  std::vector<int> pages(batch);
+  const int batch = static_cast<int>(pages.size());
   int64_t total = 0;
   int max_pages = 1;
-  for (int b = 0; b < batch; ++b) {
-    const int t = lens[b] > 0 ? lens[b] : 0;
-    pages[b] = (t + mla::kPage - 1) / mla::kPage;
-    total += pages[b];
-    max_pages = std::max(max_pages, pages[b]);
+  for (int pg : pages) {
+    total += pg;
+    max_pages = std::max(max_pages, pg);
   }
-  int L = env_split_pages();
+  int L = env;
   if (L == 0) {
     const int row = d->d_latent + d->d_rope;
     const int wg_per_cu = row > 288 ? 1 : 2;
@@ -150,6 +170,8 @@ Plan make_plan(const mla_dims* d, int batch, const int32_t* lens) {
       const int64_t c = (total + static_cast<int64_t>(workers) * k - 1) / (static_cast<int64_t>(workers) * k);
       cands.push_back(static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(c, max_pages))));
     }
+    std::sort(cands.begin(), cands.end());
+    cands.erase(std::unique(cands.begin(), cands.end()), cands.end());
     for (int c : cands) {
       const double m = simulate(pages, c, workers, item_cost, partial_cost);
       if (best < 0 || m < best - 1e-9 || (std::fabs(m - best) <= 1e-9 && c > L)) {
@@ -169,6 +191,29 @@ Plan make_plan(const mla_dims* d, int batch, const int32_t* lens) {
   p.n_full = static_cast<int>(n_full);
   p.n_items = n_full + n_rem;
   return p;
+}
+
+// A serving loop asks for the same plan twice per step (workspace size, then
+// decode), and the plan changes only when a sequence enters a new page: keep
+// the last plan of each host thread, keyed by everything compute_plan reads.
+Plan make_plan(const mla_dims* d, int batch, const int32_t* lens) {
+  struct Entry {
+    int n_heads = -1, d_latent = -1, d_rope = -1, env = -1;
+    std::vector<int> pages;
+    Plan plan;
+  };
+  thread_local Entry last;
+  thread_local std::vector<int> pages;
+  pages.resize(batch);
+  for (int b = 0; b < batch; ++b) pages[b] = (std::max(lens[b], 0) + mla::kPage - 1) / mla::kPage;
+  const int env = env_split_pages();
+  if (last.n_heads == d->n_heads && last.d_latent == d->d_latent && last.d_rope == d->d_rope && last.env == env &&
+      last.pages == pages)
+    return last.plan;
+  last.plan = compute_plan(d, pages, env);
+  last.n_heads = d->n_heads; last.d_latent = d->d_latent; last.d_rope = d->d_rope; last.env = env;
+  last.pages = pages;
+  return last.plan;
 }
 
 size_t workspace_bytes(const mla_dims* d, const Plan& p) {

@@ -20,9 +20,11 @@
 //   * O (32 rows x d_c, float32) stays in accumulators (d_c/2 regs);
 //   * each page (64 x D bf16, 72 KB at D = 576) is copied HBM -> LDS once by
 //     16-byte global_load_lds DMA, double buffered, and read by every wave;
-//     16-byte chunks are XOR-swizzled within groups of 8 so that the K reads
-//     (8 rows, same chunk) and the V transpose reads (4 rows x 2 chunks) hit
-//     distinct banks;
+//     16-byte chunks are XOR-swizzled within groups of 8 by bits 1-2 of the
+//     row.  With 64 four-byte banks and 1152-byte rows (odd rows start half
+//     way round the banks), that puts every phase of a K read (16 lanes: 16
+//     rows, one chunk each) and every half-wave of a V transpose read (8 rows
+//     x 2 chunks x 8 bytes) on distinct banks;
 //   * V^T fragments come from the same page with ds_read_tr16_b64, which
 //     turns four 8-byte row pieces into one token-contiguous column piece;
 //   * softmax in base 2 without rescaling O inside the loop: each row's
@@ -35,6 +37,7 @@
 // Tokens past the end of a sequence are masked; their LDS rows are filled
 // from the last valid row of the page, so garbage or NaN in unused page
 // slots never reaches the accumulators.
+#include <cfloat>
 #include <type_traits>
 
 #include "common.hpp"
@@ -45,8 +48,12 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kOverflowLog2 = 64.0f;  // P may reach 2^64 before a split is redone
+// Word 3 of a raw (untyped) buffer resource on gfx9-family parts: 32-bit data
+// format, no swizzle, no index/thread-id addressing.
+constexpr int kBufferWord3 = 0x00020000;
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Bits 1-2 of the row: a function of r mod 8 only.
+__device__ __forceinline__ int swz(int r) { return r & 6; }
 
 // Physical 16-byte chunk slot of logical chunk j in LDS row r.  Full groups
 // of 8 chunks are XOR-swizzled with swz(r); a trailing group of 4 (when the
@@ -149,28 +156,42 @@ __device__ PrefillBlock find_prefill_block(const AttnParams& p, int64_t blk, int
   return none;
 }
 
-// Copy one page (64 rows x D bf16) into an LDS buffer with 16-byte DMA.
-// LDS chunk slot sl of row r holds logical chunk phys_chunk(r, sl) of row r.
-// Rows go in groups of RG rows = 576 chunks = 9 wave instructions, and each
-// wave takes whole groups, so a lane's (row-in-group, slot) pairs depend only
-// on the lane: nothing is divided per tile and the LDS destination of every
-// instruction is wave-uniform.  Rows >= valid_rows read row valid_rows - 1.
-template <int D, int NW>
-__device__ __forceinline__ void dma_page(char* lds_buf, const char* page_base, int valid_rows, int lane,
-                                         int wave) {
+// Copy one tile (TROWS consecutive cache rows of D bf16, starting at `src`)
+// into an LDS buffer with 16-byte buffer-load DMA.  LDS chunk slot sl of
+// tile row r holds logical chunk phys_chunk(r, sl) of that row.  Rows go in
+// groups of RG rows = 576 chunks = 9 wave instructions; a wave takes whole
+// groups (when there are fewer groups than waves, the first NG waves take
+// one each), so a lane's (row-in-group, slot) pairs depend only on the lane
+// and the LDS destination of every instruction is wave-uniform.  Rows
+// >= valid_rows read row valid_rows - 1.  Returns nothing; each issuing wave
+// has dma_loads<D, NW, TROWS>() loads in flight afterwards.
+template <int D, int TROWS>
+constexpr int dma_groups() { return TROWS / (576 / (D / 8)); }
+template <int D, int NW, int TROWS>
+constexpr int dma_loads() { return 9 * (dma_groups<D, TROWS>() >= NW ? dma_groups<D, TROWS>() / NW : 1); }
+
+template <int D, int NW, int TROWS>
+__device__ __forceinline__ void dma_tile(char* lds_buf, const char* src, int valid_rows, int lane, int wave) {
   constexpr int CH = D / 8;
   constexpr int ROWB = D * 2;
   constexpr int RG = 576 / CH;
-  constexpr int NG = kPage / RG;
-  constexpr int GPW = NG / NW;
-  static_assert(RG * CH == 576 && NG % NW == 0, "page must split into whole row groups per wave");
+  constexpr int NG = dma_groups<D, TROWS>();
+  constexpr int GPW = NG >= NW ? NG / NW : 1;
+  static_assert(RG * CH == 576 && TROWS % RG == 0 && (NG < NW || NG % NW == 0), "tile must split into row groups");
+  if (NG < NW && wave >= NG) return;
   // An opaque copy of the lane id keeps the per-lane offsets from being
-  // hoisted out of the page loop (they are cheap; registers are not).
+  // hoisted out of the tile loop (they are cheap; registers are not).
   int ln = lane;
   asm volatile("" : "+v"(ln));
+  // A raw buffer resource over the tile: the DMA goes through the buffer
+  // path, whose completion the compiler tracks on the vector-memory counter
+  // alone, so LDS reads in flight keep exact wait counts.  Offsets past the
+  // tile would read zeros; none are formed.
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), 0, TROWS * ROWB, kBufferWord3);
 #pragma unroll
   for (int gg = 0; gg < GPW; ++gg) {
-    const int g = wave * GPW + gg;
+    const int g = NG >= NW ? wave * GPW + gg : wave;
 #pragma unroll
     for (int kk = 0; kk < 9; ++kk) {
       const int c = kk * 64 + ln;
@@ -178,11 +199,16 @@ __device__ __forceinline__ void dma_page(char* lds_buf, const char* page_base, i
       const int r = g * RG + rig;
       const int j = phys_chunk<D>(r, c - rig * CH);
       const int rs = r < valid_rows ? r : valid_rows - 1;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(page_base + rs * ROWB + j * 16),
-                                       (lds_void_t*)(lds_buf + g * RG * ROWB + kk * 1024), 16, 0, 0);
+      const uint32_t off = static_cast<uint32_t>(rs * ROWB + j * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_buf + g * RG * ROWB + kk * 1024), 16, off, 0,
+                                               0, 0);
     }
   }
 }
+
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding and does not wait on the other counters (gfx9 encoding).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // S += K . Q^T on VGPR accumulators.  Written as inline asm so that the
 // 16 score accumulators live in VGPRs while the 256 output accumulators hold
@@ -206,12 +232,25 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   constexpr int NT = 64 * HG * TW;
   constexpr int ROWS = 32 * HG;
   constexpr int KS = D / 32;
+  // Q k-steps kept in LDS: the position part, plus (at d_c = 512) four
+  // content k-steps, which keeps the page loop within the register file.
+  constexpr int KSL = DR / 32 + (DC >= 512 ? 4 : 0);
+  constexpr int KSQ = KS - KSL;     // Q k-steps kept in VGPRs
+  constexpr int QCH = KSL * 4;      // 16-byte chunks per row of the LDS part of Q
+  static_assert(DR % 32 == 0, "position width must be a multiple of 32");
   constexpr int CB = DC / 16;
-  constexpr int TILE = kPage * D * 2;
+  constexpr int PAGE_BYTES = kPage * D * 2;
+  // LDS tiles of TROWS cache rows (32 per wave token lane), in a ring of three:
+  // one being read, two in flight.
+  constexpr int TROWS = 32 * TW;
+  constexpr int TILE = TROWS * D * 2;
+  constexpr int G = dma_loads<D, 64 * HG * TW / 64, TROWS>();
   static_assert(D % 32 == 0 && DC % 16 == 0, "dims");
   static_assert(TW == 1 || HG <= 2, "two token lanes need half the waves' registers");
   __shared__ __attribute__((aligned(16))) char lds0[TILE];
   __shared__ __attribute__((aligned(16))) char lds1[TILE];
+  __shared__ __attribute__((aligned(16))) char lds2[TILE];
+  __shared__ bf16x8 ldsq[(QF32 ? 2 : 1) * ROWS * QCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -221,13 +260,17 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   const int q16 = lane >> 4, r16 = lane & 15;
   const int H = p.n_heads;
 
-  // ---- which rows and which keys
-  int b, page_begin, page_end, key_end;
-  int64_t row_g[2];
+  // ---- which rows and which keys.  Everything here is wave-uniform except
+  // the row a lane serves: local row lrow(rb) of the workgroup's ROWS rows,
+  // global row row_base + lrow(rb), valid when lrow(rb) < row_count.  Row
+  // addresses are recomputed where needed instead of being held across the
+  // page loop.
+  int b, page_begin, page_end, key_end, row_count;
+  int64_t row_base;
   int limit[2];
-  bool row_ok[2];
   bool final_out = true;
   int slot = 0;
+  auto lrow = [&](int rb) { return hg * 32 + rb * 16 + (lane & 15); };
   if constexpr (PREFILL) {
     const PrefillBlock pb = find_prefill_block(p, p.n_blocks - 1 - static_cast<int64_t>(blockIdx.x), ROWS);
     if (!pb.ok) return;
@@ -239,12 +282,12 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     key_end = __builtin_amdgcn_readfirstlane(q0 + last_q + 1);
     page_begin = 0;
     page_end = (key_end + kPage - 1) / kPage;
+    row_base = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(p.cu_q[b])) * H + r0;
+    row_count = nq * H - r0;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const int sr = r0 + hg * 32 + rb * 16 + r16;
-      row_ok[rb] = sr < nq * H;
-      row_g[rb] = static_cast<int64_t>(p.cu_q[b]) * H + sr;
-      limit[rb] = row_ok[rb] ? q0 + sr / H + 1 : 0;
+      const int lr = lrow(rb);
+      limit[rb] = lr < row_count ? q0 + (r0 + lr) / H + 1 : 0;
     }
   } else {
     const int64_t item = static_cast<int64_t>(blockIdx.x) / p.n_head_chunks;
@@ -259,13 +302,9 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     page_end = min(pages, page_begin + p.split_pages);
     final_out = __builtin_amdgcn_readfirstlane(it.n_s) == 1;
     slot = __builtin_amdgcn_readfirstlane(it.slot);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int head = hc * ROWS + hg * 32 + rb * 16 + r16;
-      row_ok[rb] = head < H;
-      row_g[rb] = static_cast<int64_t>(b) * H + head;
-      limit[rb] = key_end;
-    }
+    row_base = static_cast<int64_t>(b) * H + hc * ROWS;
+    row_count = H - hc * ROWS;
+    limit[0] = limit[1] = key_end;
   }
   if (b >= p.num_seqs) return;
   // wave-uniform bound on the visible keys of this wave's rows
@@ -273,31 +312,54 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) lim_max = max(lim_max, __shfl_xor(lim_max, m, 64));
   lim_max = __builtin_amdgcn_readfirstlane(lim_max);
+  // wave-uniform lower bound: sub-blocks entirely below it need no mask
+  int lim_min = min(lrow(0) < row_count ? limit[0] : INT32_MAX, lrow(1) < row_count ? limit[1] : INT32_MAX);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, m, 64));
+  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
   // ---- Q fragments (MFMA B operand: row = r16, d = ks*32 + 8*q16 .. +7).
   // A float32 q_lat is split into hi = bf16(q) and lo = bf16(q - hi); the
   // score then takes both terms (K.hi + K.lo), so q~ enters at ~16 bits.
-  bf16x8 qf[2][KS];
-  bf16x8 qlo[QF32 ? 2 : 1][QF32 ? KS : 1];
+  // The first KSQ k-steps stay in VGPRs; the last KSL go to LDS,
+  // where each lane keeps exactly the fragments it will read back (no
+  // sharing, so no barrier), XOR-swizzled so a read phase hits 8 banks.
+  bf16x8 qf[2][KSQ];
+  bf16x8 qlo[QF32 ? 2 : 1][QF32 ? KSQ : 1];
+  // this lane's LDS home of a position fragment; lr, lq are the lane's r16, q16
+  auto q_slot = [&](int term, int rb, int ks, int lr, int lq) -> bf16x8* {
+    const int row = hg * 32 + rb * 16 + lr;
+    const int ch = (ks - KSQ) * 4 + lq;
+    return &ldsq[(term * ROWS + row) * QCH + (ch ^ (row & (QCH >= 8 ? 7 : QCH - 1)))];
+  };
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 hi8, lo8;
       if constexpr (QF32) {
         const float* qlat = static_cast<const float*>(p.q_lat);
         bf16_t hi[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = row_ok[rb] ? qlat[row_g[rb] * D + ks * 32 + q16 * 8 + e] : 0.f;
+          const float x = lrow(rb) < row_count ? qlat[(row_base + lrow(rb)) * D + ks * 32 + q16 * 8 + e] : 0.f;
           hi[e] = f32_to_bf16_finite(x);
           lo[e] = f32_to_bf16_finite(x - bf16_to_f32(hi[e]));
         }
-        __builtin_memcpy(&qf[rb][ks], hi, 16);
-        __builtin_memcpy(&qlo[rb][ks], lo, 16);
+        __builtin_memcpy(&hi8, hi, 16);
+        __builtin_memcpy(&lo8, lo, 16);
       } else {
         const bf16_t* qlat = static_cast<const bf16_t*>(p.q_lat);
-        qf[rb][ks] = row_ok[rb] ? *reinterpret_cast<const bf16x8*>(qlat + row_g[rb] * D + ks * 32 + q16 * 8)
-                                : bf16x8{};
+        hi8 = lrow(rb) < row_count
+                  ? *reinterpret_cast<const bf16x8*>(qlat + (row_base + lrow(rb)) * D + ks * 32 + q16 * 8)
+                  : bf16x8{};
+      }
+      if (ks < KSQ) {
+        qf[rb][ks < KSQ ? ks : 0] = hi8;
+        if constexpr (QF32) qlo[rb][ks < KSQ ? ks : 0] = lo8;
+      } else {
+        *q_slot(0, rb, ks, r16, q16) = hi8;
+        if constexpr (QF32) *q_slot(1, rb, ks, r16, q16) = lo8;
       }
     }
 
@@ -321,12 +383,14 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   };
   auto page_ptr = [&](int ids, int pg) -> const char* {
     const int id = __builtin_amdgcn_readlane(ids, (pg - page_begin) & 63);
-    return cache + static_cast<int64_t>(id) * TILE;
+    return cache + static_cast<int64_t>(id) * PAGE_BYTES;
   };
 
   constexpr int CHF8 = (D / 8 / 8) * 8;  // chunks in full swizzle groups
 
-  const int ntile = page_end - page_begin;
+  // tiles covering the split's keys [page_begin * 64, min(page_end * 64, key_end))
+  const int key_hi = min(page_end * kPage, key_end);
+  const int ntile = key_hi > page_begin * kPage ? (key_hi - page_begin * kPage + TROWS - 1) / TROWS : 0;
 
   // One pass over the split's pages.  MODE 0: the reference max of a row is
   // fixed at its first visible key and P = 2^(s - m_ref) may grow up to
@@ -338,57 +402,75 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     constexpr int MODE = decltype(mode_tag)::value;
     bool overflow = false;
     int ids = load_ids(page_begin);
-    if (ntile > 0)
-      dma_page<D, NT / 64>(lds0, page_ptr(ids, page_begin), min(kPage, key_end - page_begin * kPage), lane, wave);
-    // One page: wait for `cur`, start the DMA of the next page into `nxt`,
-    // compute on `cur`.  The two buffers are distinct LDS objects, so the
-    // compiler can see that the DMA in flight never aliases the reads.
-    auto tile = [&](int it, char* cur, char* nxt) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (it + 1 < ntile) {
-        const int pg = page_begin + it + 1;
-        if (((it + 1) & 63) == 0) ids = load_ids(pg);
-        dma_page<D, NT / 64>(nxt, page_ptr(ids, pg), min(kPage, key_end - pg * kPage), lane, wave);
-      }
+    // source of tile h: page page_begin + h*TROWS/64, from row (h*TROWS) % 64
+    auto tile_dma = [&](int h, char* dst) {
+      const int rel = h * TROWS;
+      const int pg = page_begin + rel / kPage;
+      if (rel % kPage == 0 && ((pg - page_begin) & 63) == 0 && pg != page_begin) ids = load_ids(pg);
+      const int t0 = page_begin * kPage + rel;
+      dma_tile<D, NT / 64, TROWS>(dst, page_ptr(ids, pg) + (rel % kPage) * (D * 2), min(TROWS, key_end - t0), lane,
+                                  wave);
+    };
+    if (ntile > 0) tile_dma(0, lds0);
+    if (ntile > 1) tile_dma(1, lds1);
+    // One tile: wait for `cur` (the next tile's DMA stays in flight), make it
+    // visible to all waves, start the DMA two tiles ahead into `nx2` (the
+    // buffer every wave finished reading one step ago), compute on `cur`.
+    // The three buffers are distinct LDS objects, so the compiler can see
+    // that the DMAs in flight never alias the reads.
+    auto tile = [&](int it, char* cur, char* nx2) {
+      if (it + 1 < ntile)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(G));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      // A bare barrier: __syncthreads() would also drain the DMA still in
+      // flight.  Every LDS read of the previous tile has been consumed by an
+      // MFMA by now; the memory clobber keeps this tile's reads below it.
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (it + 2 < ntile) tile_dma(it + 2, nx2);
       const char* buf = cur;
-      const int tile_t0 = (page_begin + it) * kPage;
-#pragma unroll
-      for (int sbi = 0; sbi < 2 / TW; ++sbi) {
-        const int sb = TW == 1 ? sbi : tw;
-        const int t0 = tile_t0 + sb * 32;
+      const int sb = TW == 1 ? 0 : tw;  // this wave's 32-row sub-block of the tile
+      const int t0 = page_begin * kPage + it * TROWS + sb * 32;
+      [&] {
         // skip sub-blocks no row of this wave can see (wave-uniform)
-        if (t0 >= lim_max) continue;
+        if (t0 >= lim_max) return;
         // Per-lane LDS byte offsets inside the tile, recomputed here from an
         // opaque lane id rather than held in registers across the loop; the
         // chunk group and the sub-block enter as immediates.
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int lq16 = ln >> 4, lr16 = ln & 15;
-        int k_off[2][2], k_tail[2], v_off[2][4];
+        // Rows 16 apart share a swizzle (swz depends on r mod 8), so the
+        // second 16-token block is a constant offset away.
+        constexpr int TB_OFF = 16 * D * 2;
+        int k_off[2], k_tail, v_off[4];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const int krow = tb * 16 + lr16;
+        for (int kb = 0; kb < 2; ++kb) k_off[kb] = lr16 * (D * 2) + phys_chunk<D>(lr16, kb * 4 + lq16) * 16;
+        k_tail = lr16 * (D * 2) + (phys_chunk<D>(lr16, CHF8 + lq16) - CHF8) * 16;
+        const int vrow = lq16 * 4 + (lr16 >> 2);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) k_off[tb][kb] = krow * (D * 2) + phys_chunk<D>(krow, kb * 4 + lq16) * 16;
-          k_tail[tb] = krow * (D * 2) + (phys_chunk<D>(krow, CHF8 + lq16) - CHF8) * 16;
-          const int vrow = tb * 16 + lq16 * 4 + (lr16 >> 2);
-#pragma unroll
-          for (int cl = 0; cl < 4; ++cl)
-            v_off[tb][cl] = vrow * (D * 2) + phys_chunk<D>(vrow, cl * 2 + ((lr16 & 3) >> 1)) * 16 + (lr16 & 1) * 8;
-        }
+        for (int cl = 0; cl < 4; ++cl)
+          v_off[cl] = vrow * (D * 2) + phys_chunk<D>(vrow, cl * 2 + ((lr16 & 3) >> 1)) * 16 + (lr16 & 1) * 8;
         // ---- S^T = K . Q^T over D
         f32x4 sacc[2][2];
         // K fragments run KPF steps ahead of the MFMAs that consume them.
         constexpr int KPF = 2;
         bf16x8 ka[KS][2];
+        bf16x8 qr[KS][2], qrlo[QF32 ? KS : 1][2];
         auto load_k = [&](int ks) {
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
             // chunk ks*4 + q16 of row krow: group ks/2 (immediate), in-group slot from k_off
-            const char* a = (ks / 2) * 128 < CHF8 * 16 ? buf + k_off[tb][ks & 1] + (ks / 2) * 128
-                                                       : buf + k_tail[tb] + (ks / 2) * 128;
-            ka[ks][tb] = *reinterpret_cast<const bf16x8*>(a + sb * 32 * (D * 2));
+            const char* a = (ks / 2) * 128 < CHF8 * 16 ? buf + k_off[ks & 1] + (ks / 2) * 128
+                                                       : buf + k_tail + (ks / 2) * 128;
+            ka[ks][tb] = *reinterpret_cast<const bf16x8*>(a + sb * 32 * (D * 2) + tb * TB_OFF);
+          }
+          if (ks >= KSQ) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              qr[ks][rb] = *q_slot(0, rb, ks, lr16, lq16);
+              if constexpr (QF32) qrlo[ks][rb] = *q_slot(1, rb, ks, lr16, lq16);
+            }
           }
         };
 #pragma unroll
@@ -401,62 +483,85 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
+              const bf16x8& qb = ks < KSQ ? qf[rb][ks < KSQ ? ks : 0] : qr[ks][rb];
               if (ks == 0)
-                mfma_qk_first(sacc[tb][rb], ka[ks][tb], qf[rb][ks]);
+                mfma_qk_first(sacc[tb][rb], ka[ks][tb], qb);
               else
-                mfma_qk(sacc[tb][rb], ka[ks][tb], qf[rb][ks]);
-              if constexpr (QF32) mfma_qk(sacc[tb][rb], ka[ks][tb], qlo[rb][ks]);
+                mfma_qk(sacc[tb][rb], ka[ks][tb], qb);
+              if constexpr (QF32)
+                mfma_qk(sacc[tb][rb], ka[ks][tb], ks < KSQ ? qlo[rb][ks < KSQ ? ks : 0] : qrlo[QF32 ? ks : 0][rb]);
             }
+          __builtin_amdgcn_sched_barrier(0);  // likewise for the K reads of step ks + KPF
         }
         mfma_qk_drain(sacc);
-        // ---- scores in base 2, masked; row max over the sub-block
-        float mx[2];
+        // ---- reference max.  Raw scores stay unscaled; the scale (times log2 e)
+        // is folded into the exponent's FMA.  Only sub-blocks that cross a
+        // row's last visible key are masked.  The cross-lane row max (two
+        // shuffles) is needed only while a row has no reference yet (its first
+        // visible sub-block) and in the max-only pass; otherwise each lane just
+        // checks its own scores against the reference for overflow.
+        const bool partial = t0 + 32 > lim_min;
+        if (partial) {
+          float ninf = -INFINITY;  // materialised here, not held across the loop
+          asm volatile("" : "+v"(ninf));
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int t = t0 + tb * 16 + lq16 * 4 + e;
+                if (t >= (PREFILL ? limit[rb] : key_end)) sacc[tb][rb][e] = ninf;
+              }
+        }
+        float lmx[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           float m = -INFINITY;
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int t = t0 + tb * 16 + lq16 * 4 + e;
-              const float v = t < limit[rb] ? sacc[tb][rb][e] * p.scale_log2 : -INFINITY;
-              sacc[tb][rb][e] = v;
-              m = fmaxf(m, v);
-            }
-          m = fmaxf(m, shfl_xor_f(m, 16));
-          mx[rb] = fmaxf(m, shfl_xor_f(m, 32));
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, sacc[tb][rb][e]);
+          lmx[rb] = m * p.scale_log2;  // this lane's max (scale > 0 keeps the order)
         }
-        if constexpr (MODE == 1) {
-          m_run[0] = fmaxf(m_run[0], mx[0]);
-          m_run[1] = fmaxf(m_run[1], mx[1]);
-          continue;
-        }
-        if constexpr (MODE == 0) {
+        const bool need_ref = MODE == 1 || __ballot(m_run[0] == -INFINITY || m_run[1] == -INFINITY) != 0;
+        if (need_ref) {
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
-            if (m_run[rb] == -INFINITY) m_run[rb] = mx[rb];  // O and l are still zero: exact
-            overflow |= mx[rb] > m_run[rb] + kOverflowLog2;
+            const float m = pair32_max(pair16_max(lmx[rb]));
+            if constexpr (MODE == 1)
+              m_run[rb] = fmaxf(m_run[rb], m);
+            else if (m_run[rb] == -INFINITY)
+              m_run[rb] = m;  // O and l are still zero: exact
           }
         }
-        // ---- P = 2^(s - m) in bf16; l sums the rounded values
+        if constexpr (MODE == 1) return;
+        if constexpr (MODE == 0)
+          overflow |= __ballot(lmx[0] > m_run[0] + kOverflowLog2 || lmx[1] > m_run[1] + kOverflowLog2) != 0;
+        // ---- P = 2^(scale*log2e*s - m) rounded to bf16 (hardware RNE, two at a time)
         bf16x8 pb[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-          bf16_t pv[8];
-          float lsum = 0.f;
+          // a row still without a reference has only masked (-inf) scores here,
+          // which give 0 against any finite reference
+          const float m_use = __builtin_fmaxf(m_run[rb], -FLT_MAX);
+          float pf[8];
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bf16_t q = f32_to_bf16_finite(__builtin_amdgcn_exp2f(sacc[tb][rb][e] - m_use));
-              pv[tb * 4 + e] = q;
-              lsum += bf16_to_f32(q);
-            }
+            for (int e = 0; e < 4; ++e)
+              pf[tb * 4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][rb][e], p.scale_log2, -m_use));
+          float lsum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) lsum += pf[i];
           l_part[rb] += lsum;
-          __builtin_memcpy(&pb[rb], pv, 16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16x2 pair = __builtin_convertvector((f32x2){pf[2 * i], pf[2 * i + 1]}, bf16x2);
+            pb[rb][2 * i] = pair[0];
+            pb[rb][2 * i + 1] = pair[1];
+          }
         }
-        // ---- O^T += V^T . P^T ; V^T fragment from two transpose reads
         // V^T fragments run VPF column blocks ahead of their MFMAs.
         constexpr int VPF = 4;
         i16x4 vt[CB][2];
@@ -464,7 +569,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
             // columns cb*16 + 4*(r16&3): chunk cb*2 + ((r16&3)>>1) = group cb/4, slot from v_off
-            const char* a = buf + v_off[tb][cb & 3] + (cb / 4) * 128 + sb * 32 * (D * 2);
+            const char* a = buf + v_off[cb & 3] + (cb / 4) * 128 + sb * 32 * (D * 2) + tb * TB_OFF;
             vt[cb][tb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
           }
         };
@@ -479,20 +584,29 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
             oacc[cb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb], oacc[cb][rb], 0, 0, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two transpose reads of block cb + VPF
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // the two MFMAs of block cb
+          // Keep source order: the reads of block cb + VPF stay above the MFMAs
+          // of block cb (the scheduler would otherwise sink them to their use).
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
+      }();
     };
-    for (int it = 0; it < ntile; it += 2) {
-      tile(it, lds0, lds1);
+    for (int it = 0; it < ntile; it += 3) {
+      tile(it, lds0, lds2);
       if (it + 1 < ntile) tile(it + 1, lds1, lds0);
+      if (it + 2 < ntile) tile(it + 2, lds2, lds1);
     }
     return overflow;
   };
 
   const bool overflow = run_pass(std::integral_constant<int, 0>{});
-  if (__syncthreads_or(overflow ? 1 : 0)) {
+  // workgroup OR of the waves' overflow flags, through the idle page buffer
+  __syncthreads();
+  if (lane == 0) reinterpret_cast<int*>(lds0)[wave] = overflow ? 1 : 0;
+  __syncthreads();
+  int any_overflow = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) any_overflow |= reinterpret_cast<const int*>(lds0)[w];
+  if (any_overflow) {
     // Rare: some row's scores rose by more than 2^kOverflowLog2 over its first
     // visible key.  Redo the split exactly: true max first, then accumulate.
     __syncthreads();
@@ -550,13 +664,13 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     float l = l_part[rb];
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
-    if (!row_ok[rb]) continue;
+    l = pair32_sum(pair16_sum(l));
+    if (lrow(rb) >= row_count) continue;
+    const int64_t row_g = row_base + lrow(rb);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float lse_v = l > 0.f ? (m_run[rb] + log2f(l)) * kLn2 : -INFINITY;
     if (final_out) {
-      bf16_t* out = static_cast<bf16_t*>(p.out_latent) + row_g[rb] * DC;
+      bf16_t* out = static_cast<bf16_t*>(p.out_latent) + row_g * DC;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int c = cb * 16 + 4 * q16;
@@ -565,9 +679,9 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
         pk.y = f32_to_bf16(oacc[cb][rb][2] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][rb][3] * inv)) << 16);
         *reinterpret_cast<uint2*>(out + c) = pk;
       }
-      if (p.lse != nullptr && q16 == 0) p.lse[row_g[rb]] = lse_v;
+      if (p.lse != nullptr && q16 == 0) p.lse[row_g] = lse_v;
     } else {
-      const int64_t srow = static_cast<int64_t>(slot) * H + (row_g[rb] - static_cast<int64_t>(b) * H);
+      const int64_t srow = static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
       float* out = p.ws_o + srow * DC;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
