@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="run one plain 256 MiB copy kernel before timing (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -130,6 +132,13 @@ def main():
         c = mla.LatentCache(dims, case.block_table, case.num_pages)
         c.data.copy_(cache0.data)
         caches.append(c)
+    if args.calibrate:
+        # a plain streaming kernel of known size: reads 256 MiB, writes 256 MiB
+        cal_src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")
+        cal_dst = torch.empty_like(cal_src)
+        torch.neg(cal_src, out=cal_dst)
+        torch.cuda.synchronize()
+        del cal_src, cal_dst
     w_uk, w_uv = dev(case.w_uk), dev(case.w_uv)
     q_nope, q_rope = dev(case.qc), dev(case.qr)
     stream = torch.cuda.current_stream()
