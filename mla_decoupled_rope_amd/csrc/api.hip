@@ -218,7 +218,7 @@ Plan make_plan(const mla_dims* d, int batch, const int32_t* lens) {
 
 size_t workspace_bytes(const mla_dims* d, const Plan& p) {
   if (d->dtype != MLA_BF16 || !p.needs_merge || p.n_items == 0) return 0;
-  const size_t o = static_cast<size_t>(p.n_items) * d->n_heads * d->d_latent * sizeof(float);
+  const size_t o = static_cast<size_t>(p.n_items) * d->n_heads * d->d_latent * sizeof(uint16_t);
   const size_t o_al = (o + kWsAlign - 1) / kWsAlign * kWsAlign;
   return o_al + static_cast<size_t>(p.n_items) * d->n_heads * sizeof(float);
 }
@@ -371,8 +371,8 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
   p.n_items = plan.n_items;
   p.n_head_chunks = 1;
   if (need > 0) {
-    const size_t o = static_cast<size_t>(plan.n_items) * dims->n_heads * dims->d_latent * sizeof(float);
-    p.ws_o = static_cast<float*>(workspace);
+    const size_t o = static_cast<size_t>(plan.n_items) * dims->n_heads * dims->d_latent * sizeof(uint16_t);
+    p.ws_o = static_cast<mla::bf16_t*>(workspace);
     p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (o + kWsAlign - 1) / kWsAlign * kWsAlign);
   }
   hipError_t e = mla::launch_decode_bf16(p, s);

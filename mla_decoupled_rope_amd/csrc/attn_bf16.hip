@@ -156,55 +156,68 @@ __device__ PrefillBlock find_prefill_block(const AttnParams& p, int64_t blk, int
   return none;
 }
 
-// Copy one tile (TROWS consecutive cache rows of D bf16, starting at `src`)
-// into an LDS buffer with 16-byte buffer-load DMA.  LDS chunk slot sl of
+// Tile DMA: TROWS consecutive cache rows of D bf16 (starting at `src`) go
+// into an LDS buffer by 16-byte buffer-load DMA.  LDS chunk slot sl of
 // tile row r holds logical chunk phys_chunk(r, sl) of that row.  Rows go in
 // groups of RG rows = 576 chunks = 9 wave instructions; a wave takes whole
 // groups (when there are fewer groups than waves, the first NG waves take
 // one each), so a lane's (row-in-group, slot) pairs depend only on the lane
 // and the LDS destination of every instruction is wave-uniform.  Rows
-// >= valid_rows read row valid_rows - 1.  Returns nothing; each issuing wave
-// has dma_loads<D, NW, TROWS>() loads in flight afterwards.
+// >= valid_rows read row valid_rows - 1.  Each issuing wave has
+// dma_loads<D, NW, TROWS>() loads in flight per tile.
 template <int D, int TROWS>
 constexpr int dma_groups() { return TROWS / (576 / (D / 8)); }
 template <int D, int NW, int TROWS>
 constexpr int dma_loads() { return 9 * (dma_groups<D, TROWS>() >= NW ? dma_groups<D, TROWS>() / NW : 1); }
 
+// One tile's DMA, prepared once and issued one 1 KiB instruction at a time,
+// so the issue (tens of cycles per instruction) can be spread over the MFMA
+// work of the tile being computed instead of stalling the wave in one burst.
 template <int D, int NW, int TROWS>
-__device__ __forceinline__ void dma_tile(char* lds_buf, const char* src, int valid_rows, int lane, int wave) {
-  constexpr int CH = D / 8;
-  constexpr int ROWB = D * 2;
-  constexpr int RG = 576 / CH;
-  constexpr int NG = dma_groups<D, TROWS>();
-  constexpr int GPW = NG >= NW ? NG / NW : 1;
+struct TileDma {
+  static constexpr int CH = D / 8;
+  static constexpr int ROWB = D * 2;
+  static constexpr int RG = 576 / CH;
+  static constexpr int NG = dma_groups<D, TROWS>();
+  static constexpr int GPW = NG >= NW ? NG / NW : 1;
+  static constexpr int N = 9 * GPW;  // instructions per issuing wave
   static_assert(RG * CH == 576 && TROWS % RG == 0 && (NG < NW || NG % NW == 0), "tile must split into row groups");
-  if (NG < NW && wave >= NG) return;
-  // An opaque copy of the lane id keeps the per-lane offsets from being
-  // hoisted out of the tile loop (they are cheap; registers are not).
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
+  __amdgpu_buffer_rsrc_t rsrc;
+  char* lds_buf;
+  int valid_rows;
+  bool active;  // wave-uniform: this wave has instructions to issue for this tile
+
   // A raw buffer resource over the tile: the DMA goes through the buffer
   // path, whose completion the compiler tracks on the vector-memory counter
   // alone, so LDS reads in flight keep exact wait counts.  Offsets past the
   // tile would read zeros; none are formed.
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), 0, TROWS * ROWB, kBufferWord3);
-#pragma unroll
-  for (int gg = 0; gg < GPW; ++gg) {
+  __device__ __forceinline__ TileDma(char* dst, const char* src, int valid, bool on, int wave)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), 0, TROWS * ROWB, kBufferWord3)),
+        lds_buf(dst), valid_rows(valid), active(on && (NG >= NW || wave < NG)) {}
+
+  // Instruction i (0 <= i < N, a compile-time constant at every call site).
+  __device__ __forceinline__ void issue(int i, int lane, int wave) const {
+    if (!active) return;
+    const int gg = i / 9, kk = i % 9;
     const int g = NG >= NW ? wave * GPW + gg : wave;
-#pragma unroll
-    for (int kk = 0; kk < 9; ++kk) {
-      const int c = kk * 64 + ln;
-      const int rig = c / CH;
-      const int r = g * RG + rig;
-      const int j = phys_chunk<D>(r, c - rig * CH);
-      const int rs = r < valid_rows ? r : valid_rows - 1;
-      const uint32_t off = static_cast<uint32_t>(rs * ROWB + j * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_buf + g * RG * ROWB + kk * 1024), 16, off, 0,
-                                               0, 0);
-    }
+    // An opaque copy of the lane id keeps the per-lane offsets from being
+    // hoisted out of the tile loop (they are cheap; registers are not).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int c = kk * 64 + ln;
+    const int rig = c / CH;
+    const int r = g * RG + rig;
+    const int j = phys_chunk<D>(r, c - rig * CH);
+    const int rs = r < valid_rows ? r : valid_rows - 1;
+    const uint32_t off = static_cast<uint32_t>(rs * ROWB + j * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_buf + g * RG * ROWB + kk * 1024), 16, off, 0, 0,
+                                             0);
   }
-}
+  __device__ __forceinline__ void issue_all(int lane, int wave) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) issue(i, lane, wave);
+  }
+};
 
 // s_waitcnt immediate that waits until at most n vector-memory loads are
 // outstanding and does not wait on the other counters (gfx9 encoding).
@@ -403,19 +416,20 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     bool overflow = false;
     int ids = load_ids(page_begin);
     // source of tile h: page page_begin + h*TROWS/64, from row (h*TROWS) % 64
-    auto tile_dma = [&](int h, char* dst) {
+    using Dma = TileDma<D, NT / 64, TROWS>;
+    auto tile_dma = [&](int h, char* dst) -> Dma {
       const int rel = h * TROWS;
       const int pg = page_begin + rel / kPage;
       if (rel % kPage == 0 && ((pg - page_begin) & 63) == 0 && pg != page_begin) ids = load_ids(pg);
       const int t0 = page_begin * kPage + rel;
-      dma_tile<D, NT / 64, TROWS>(dst, page_ptr(ids, pg) + (rel % kPage) * (D * 2), min(TROWS, key_end - t0), lane,
-                                  wave);
+      return Dma(dst, page_ptr(ids, pg) + (rel % kPage) * (D * 2), min(TROWS, key_end - t0), true, wave);
     };
-    if (ntile > 0) tile_dma(0, lds0);
-    if (ntile > 1) tile_dma(1, lds1);
+    if (ntile > 0) tile_dma(0, lds0).issue_all(lane, wave);
+    if (ntile > 1) tile_dma(1, lds1).issue_all(lane, wave);
     // One tile: wait for `cur` (the next tile's DMA stays in flight), make it
-    // visible to all waves, start the DMA two tiles ahead into `nx2` (the
-    // buffer every wave finished reading one step ago), compute on `cur`.
+    // visible to all waves, then compute on `cur` while issuing the DMA two
+    // tiles ahead into `nx2` (the buffer every wave finished reading one step
+    // ago).
     // The three buffers are distinct LDS objects, so the compiler can see
     // that the DMAs in flight never alias the reads.
     auto tile = [&](int it, char* cur, char* nx2) {
@@ -427,13 +441,17 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       // flight.  Every LDS read of the previous tile has been consumed by an
       // MFMA by now; the memory clobber keeps this tile's reads below it.
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (it + 2 < ntile) tile_dma(it + 2, nx2);
+      // the DMA two tiles ahead; its instructions are spread over the K steps below
+      const Dma dma = it + 2 < ntile ? tile_dma(it + 2, nx2) : Dma(nx2, cache, 1, false, wave);
       const char* buf = cur;
       const int sb = TW == 1 ? 0 : tw;  // this wave's 32-row sub-block of the tile
       const int t0 = page_begin * kPage + it * TROWS + sb * 32;
       [&] {
         // skip sub-blocks no row of this wave can see (wave-uniform)
-        if (t0 >= lim_max) return;
+        if (t0 >= lim_max) {
+          dma.issue_all(lane, wave);
+          return;
+        }
         // Per-lane LDS byte offsets inside the tile, recomputed here from an
         // opaque lane id rather than held in registers across the loop; the
         // chunk group and the sub-block enter as immediates.
@@ -491,6 +509,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
               if constexpr (QF32)
                 mfma_qk(sacc[tb][rb], ka[ks][tb], ks < KSQ ? qlo[rb][ks < KSQ ? ks : 0] : qrlo[QF32 ? ks : 0][rb]);
             }
+#pragma unroll
+          for (int i = ks * Dma::N / KS; i < (ks + 1) * Dma::N / KS; ++i) dma.issue(i, lane, wave);
           __builtin_amdgcn_sched_barrier(0);  // likewise for the K reads of step ks + KPF
         }
         mfma_qk_drain(sacc);
@@ -620,6 +640,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     }
     l_part[0] = l_part[1] = 0.f;
     run_pass(std::integral_constant<int, 2>{});
+    __syncthreads();  // the epilogue stages through the tile buffers
   }
 
   // ---- combine the two token lanes of a head group (TW == 2)
@@ -660,35 +681,54 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     }
   }
 
-  // ---- normalise and store.  O^T lane layout: row r16, c = cb*16 + 4*q16 + e
+  // ---- normalise and store.  O^T lane layout: row r16, c = cb*16 + 4*q16 + e,
+  // so a lane holds 4 columns of one row per column block.  Each wave stages
+  // 16 rows at a time (bf16) in its own part of an idle tile buffer, then
+  // writes whole rows (2*d_c contiguous bytes) with 16-byte stores.  Partial
+  // results of a split are stored normalised in bf16, like the final ones.
+  constexpr int SROW = DC * 2 + 32;  // staging row stride in bytes (padding spreads the rows over the banks)
+  static_assert(2 * 16 * SROW <= TILE && HG <= 4, "staging must fit two waves per idle tile buffer");
+  char* stage = (hg < 2 ? lds1 : lds2) + (hg % 2) * 16 * SROW;
+  bf16_t* const out_base = final_out ? static_cast<bf16_t*>(p.out_latent) : p.ws_o;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     float l = l_part[rb];
     l = pair32_sum(pair16_sum(l));
-    if (lrow(rb) >= row_count) continue;
-    const int64_t row_g = row_base + lrow(rb);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float lse_v = l > 0.f ? (m_run[rb] + log2f(l)) * kLn2 : -INFINITY;
-    if (final_out) {
-      bf16_t* out = static_cast<bf16_t*>(p.out_latent) + row_g * DC;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int c = cb * 16 + 4 * q16;
-        uint2 pk;
-        pk.x = f32_to_bf16(oacc[cb][rb][0] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][rb][1] * inv)) << 16);
-        pk.y = f32_to_bf16(oacc[cb][rb][2] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][rb][3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(out + c) = pk;
+    for (int cb = 0; cb < CB; ++cb) {
+      uint2 pk;
+      pk.x = f32_to_bf16(oacc[cb][rb][0] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][rb][1] * inv)) << 16);
+      pk.y = f32_to_bf16(oacc[cb][rb][2] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][rb][3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(stage + r16 * SROW + (cb * 16 + 4 * q16) * 2) = pk;
+    }
+    if (lrow(rb) < row_count && q16 == 0) {
+      const int64_t row_g = row_base + lrow(rb);
+      if (final_out) {
+        if (p.lse != nullptr) p.lse[row_g] = lse_v;
+      } else {
+        p.ws_lse[static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H)] = lse_v;
       }
-      if (p.lse != nullptr && q16 == 0) p.lse[row_g] = lse_v;
-    } else {
-      const int64_t srow = static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
-      float* out = p.ws_o + srow * DC;
+    }
+    // rows hg*32 + rb*16 + i of the workgroup, one 16-byte piece per lane
+    constexpr int PIECES = DC * 2 / 16;  // 16-byte pieces per row
+    static_assert(64 % PIECES == 0 || PIECES % 64 == 0, "row pieces must tile a wave");
+    constexpr int RPI = PIECES >= 64 ? 1 : 64 / PIECES;  // rows per store instruction
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int c = cb * 16 + 4 * q16;
-        *reinterpret_cast<f32x4*>(out + c) = oacc[cb][rb] * inv;
+    for (int i0 = 0; i0 < 16; i0 += RPI) {
+#pragma unroll
+      for (int pc0 = 0; pc0 < (PIECES >= 64 ? PIECES : 64); pc0 += 64) {
+        const int i = i0 + (PIECES >= 64 ? 0 : lane / PIECES);
+        const int pc = pc0 + (PIECES >= 64 ? lane : lane % PIECES);
+        const int lr = hg * 32 + rb * 16 + i;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(stage + i * SROW + pc * 16);
+        if (lr < row_count) {
+          const int64_t row_g = row_base + lr;
+          const int64_t orow = final_out ? row_g : static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
+          *reinterpret_cast<i32x4*>(out_base + orow * DC + pc * 8) = v;
+        }
       }
-      if (q16 == 0) p.ws_lse[srow] = lse_v;
     }
   }
 }
@@ -734,9 +774,9 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
       const int64_t srow = static_cast<int64_t>(base + s) * H + head;
       const float w = __expf(p.ws_lse[srow] - m);
       wsum += w;
-      const float* src = p.ws_o + srow * DC + lane * PER;
+      const bf16_t* src = p.ws_o + srow * DC + lane * PER;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, src[i], acc[i]);
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, bf16_to_f32(src[i]), acc[i]);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

@@ -14,6 +14,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short bf16_t;  // storage type of a bf16 value
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -92,7 +93,7 @@ struct AttnParams {
   const int32_t* cu_q; const int32_t* q_start; int64_t n_blocks;
   // outputs
   void* out_latent; float* lse;
-  float* ws_o; float* ws_lse;  // split partials [slot, H, d_latent] / [slot, H]
+  bf16_t* ws_o; float* ws_lse;  // split partials: normalised obar (bf16) [slot, H, d_latent] / lse [slot, H]
 };
 
 // Launchers (each returns hipGetLastError() after the launch).
