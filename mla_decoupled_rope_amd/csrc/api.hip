@@ -301,9 +301,10 @@ mla_status mla_out_proj(const mla_dims* dims, const void* out_latent, const void
   if (n == 0) return MLA_OK;
   if (out_latent == nullptr || w_uv == nullptr || out == nullptr)
     return fail(MLA_ERR_INVALID_ARG, "out_latent, w_uv and out must be non-NULL");
-  if (dims->dtype == MLA_BF16 && (dims->d_latent % 32 != 0 || dims->d_v % 32 != 0))
-    return fail(MLA_ERR_UNSUPPORTED, "bf16 output projection needs d_latent and d_v multiples of 32");
-  if (n > 65535LL * 32) return fail(MLA_ERR_UNSUPPORTED, "n too large for one launch");
+  if (dims->dtype == MLA_BF16 && (dims->d_latent % 32 != 0 || dims->d_latent > 512 || dims->d_v % 64 != 0))
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 output projection needs d_latent a multiple of 32 up to 512 and d_v a "
+                                     "multiple of 64");
+  if (n > (1LL << 31) / dims->n_heads) return fail(MLA_ERR_UNSUPPORTED, "n too large for one launch");
   mla::GemmParams p{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
                     dims->q_lat_dtype, out_latent, w_uv, out, n};
   const hipError_t e = mla::launch_out_proj(p, as_stream(stream));

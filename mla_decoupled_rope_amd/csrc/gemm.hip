@@ -24,6 +24,7 @@ namespace {
 constexpr int kAbsorbJTile = 128;  // output features per workgroup
 constexpr int kAbsorbLdsStride = kAbsorbJTile + 16;  // padded row (elements): 288 B
 constexpr int kAbsorbNChunk = 512;  // tokens per workgroup (looped in 64s)
+static_assert((128 * (kAbsorbJTile / 8)) % 256 == 0, "W tile pieces must split evenly over the threads");
 
 __device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
@@ -42,20 +43,43 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
   const int DC = p.d_latent;
   const int D = p.d_latent + p.d_rope;
   const bf16_t* w = static_cast<const bf16_t*>(p.w) + static_cast<int64_t>(h) * DH * DC;
-  // stage W_UK[h][:, j0 : j0 + 128]
-  for (int c = tid; c < DH * (kAbsorbJTile / 8); c += 256) {
-    const int row = c / (kAbsorbJTile / 8), cc = c % (kAbsorbJTile / 8);
-    *reinterpret_cast<bf16x8*>(&w_lds[row * kAbsorbLdsStride + cc * 8]) =
-        load8(w + static_cast<int64_t>(row) * DC + j0 + cc * 8);
-  }
-  __syncthreads();
   const bf16_t* q = static_cast<const bf16_t*>(p.a);
   TQ* out = static_cast<TQ*>(p.out);
   const int64_t n_begin = static_cast<int64_t>(blockIdx.z) * kAbsorbNChunk;
   const int64_t n_end = min(p.n, n_begin + kAbsorbNChunk);
   const int q16 = lane >> 4, r16 = lane & 15;
   const int jw = wave * 32;  // this wave's j offset inside the tile
+  // The B fragments (64 tokens x DH) of a chunk, all in flight at once.
+  bf16x8 bq[DH / 32][4];
+  auto load_q = [&](int64_t nb0) {
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int64_t n = nb0 + nb * 16 + r16;
+        bq[ks][nb] = n < n_end ? load8(q + (n * H + h) * DH + ks * 32 + q16 * 8) : bf16x8{};
+      }
+  };
+  // The first chunk's queries load together with the W tile: one memory round trip.
+  load_q(n_begin);
+  // stage W_UK[h][:, j0 : j0 + 128]: all of this thread's loads, then all its LDS stores
+  constexpr int WPT = DH * (kAbsorbJTile / 8) / 256;  // 16-byte pieces per thread
+  bf16x8 wv[WPT];
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int c = tid + k * 256;
+    const int row = c / (kAbsorbJTile / 8), cc = c % (kAbsorbJTile / 8);
+    wv[k] = load8(w + static_cast<int64_t>(row) * DC + j0 + cc * 8);
+  }
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int c = tid + k * 256;
+    const int row = c / (kAbsorbJTile / 8), cc = c % (kAbsorbJTile / 8);
+    *reinterpret_cast<bf16x8*>(&w_lds[row * kAbsorbLdsStride + cc * 8]) = wv[k];
+  }
+  __syncthreads();
   for (int64_t nb0 = n_begin; nb0 < n_end; nb0 += 64) {
+    if (nb0 != n_begin) load_q(nb0);
     f32x4 acc[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -63,15 +87,6 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
       for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DH / 32; ++ks) {
-      bf16x8 bq[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int64_t n = nb0 + nb * 16 + r16;
-        if (n < n_end)
-          bq[nb] = load8(q + (n * H + h) * DH + ks * 32 + q16 * 8);
-        else
-          bq[nb] = bf16x8{};
-      }
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
         // A = W^T[j, i]: group q16 takes rows i0 .. i0+7 of column block jcol
@@ -87,7 +102,7 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
         __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[jb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[nb], acc[jb][nb], 0, 0, 0);
+          acc[jb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq[ks][nb], acc[jb][nb], 0, 0, 0);
       }
     }
     // D^T[j][n]: lane holds n = nb*16 + r16, j = jb*16 + 4*q16 + e
@@ -111,46 +126,72 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
   }
 }
 
-// o^T[v, n] = W_UV[h][v, :] . obar[n, h, :]; wave tile 32 v x 32 n, 4 waves over 128 v.
+// o^T[v, n] = W_UV[h][v, :] . obar[n, h, :].  A workgroup takes one head and
+// 64 rows v; each of its four waves keeps its 16 rows of W_UV[h] (all of d_c)
+// in registers, loaded once, while the tokens go by in chunks of 64: a chunk
+// of obar[:, h, :] is staged in LDS once and read by all four waves.  So
+// W_UV is read once per call and obar twice (once per 64-row half of d_v).
+constexpr int kOutRows = 64;     // v rows per workgroup
+constexpr int kOutChunk = 64;    // tokens per chunk
+constexpr int kOutMaxK = 512;    // largest d_c this kernel takes
+constexpr int kOutLdsStride = kOutMaxK + 8;  // bf16 elements per staged row (padding against bank conflicts)
 __global__ void __launch_bounds__(256) out_proj_bf16_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) bf16_t ob_lds[kOutChunk * kOutLdsStride];
   const int h = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int v0 = blockIdx.x * 128 + wave * 32;
-  if (v0 >= p.d_v) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int v0 = blockIdx.x * kOutRows + wave * 16;
   const int H = p.n_heads, DC = p.d_latent, DV = p.d_v;
   const int q16 = lane >> 4, r16 = lane & 15;
-  const bf16_t* w = static_cast<const bf16_t*>(p.w) + static_cast<int64_t>(h) * DV * DC;
+  const int ks_n = DC / 32;
+  const bf16_t* w = static_cast<const bf16_t*>(p.w) + (static_cast<int64_t>(h) * DV + v0 + r16) * DC + q16 * 8;
   const bf16_t* ob = static_cast<const bf16_t*>(p.a);
   float* out = static_cast<float*>(p.out);
-  const int64_t n0 = static_cast<int64_t>(blockIdx.z) * 32;
-  f32x4 acc[2][2];
+  // A fragments: W_UV[h][v0 + r16][k*32 + q16*8 .. +7] for every k step
+  bf16x8 wa[kOutMaxK / 32];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int k = 0; k < kOutMaxK / 32; ++k)
+    if (k < ks_n) wa[k] = load8(w + k * 32);
+  for (int64_t c0 = 0; c0 < p.n; c0 += kOutChunk) {
+    const int rows = static_cast<int>(min<int64_t>(kOutChunk, p.n - c0));
+    // stage obar[c0 .. c0 + rows, h, :] (zeros past the end)
+    __syncthreads();
+    // all of this thread's loads first, then its LDS stores: one round trip
+    const int pieces = DC / 8;  // 16-byte pieces per row
+    constexpr int PPT = kOutChunk * (kOutMaxK / 8) / 256;  // pieces per thread at the largest d_c
+    bf16x8 v[PPT];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool nv0 = n0 + r16 < p.n, nv1 = n0 + 16 + r16 < p.n;
-  const bf16_t* b0p = ob + ((n0 + r16) * H + h) * DC + q16 * 8;
-  const bf16_t* b1p = ob + ((n0 + 16 + r16) * H + h) * DC + q16 * 8;
-  const bf16_t* a0p = w + static_cast<int64_t>(v0 + r16) * DC + q16 * 8;
-  const bf16_t* a1p = w + static_cast<int64_t>(v0 + 16 + r16) * DC + q16 * 8;
-  for (int k = 0; k < DC; k += 32) {
-    const bf16x8 a0 = load8(a0p + k), a1 = load8(a1p + k);
-    const bf16x8 b0 = nv0 ? load8(b0p + k) : bf16x8{};
-    const bf16x8 b1 = nv1 ? load8(b1p + k) : bf16x8{};
-    acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[0][0], 0, 0, 0);
-    acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b1, acc[0][1], 0, 0, 0);
-    acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b0, acc[1][0], 0, 0, 0);
-    acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[1][1], 0, 0, 0);
-  }
+    for (int k = 0; k < PPT; ++k) {
+      const int c = tid + k * 256;
+      const int r = c / pieces, pc = c % pieces;
+      v[k] = (c < kOutChunk * pieces && r < rows) ? load8(ob + ((c0 + r) * H + h) * DC + pc * 8) : bf16x8{};
+    }
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int64_t n = n0 + nb * 16 + r16;
-    if (n >= p.n) continue;
+    for (int k = 0; k < PPT; ++k) {
+      const int c = tid + k * 256;
+      const int r = c / pieces, pc = c % pieces;
+      if (c < kOutChunk * pieces) *reinterpret_cast<bf16x8*>(&ob_lds[r * kOutLdsStride + pc * 8]) = v[k];
+    }
+    __syncthreads();
+    f32x4 acc[4];
 #pragma unroll
-    for (int vb = 0; vb < 2; ++vb) {
-      const int v = v0 + vb * 16 + 4 * q16;
-      *reinterpret_cast<f32x4*>(out + (n * H + h) * DV + v) = acc[vb][nb];
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kOutMaxK / 32; ++k) {
+      if (k < ks_n) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&ob_lds[(nb * 16 + r16) * kOutLdsStride + k * 32 + q16 * 8]);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[k], bv, acc[nb], 0, 0, 0);
+        }
+      }
+    }
+    // D^T[v][n]: lane holds n = nb*16 + r16, v = v0 + 4*q16 + e
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int r = nb * 16 + r16;
+      if (r < rows) *reinterpret_cast<f32x4*>(out + ((c0 + r) * H + h) * DV + v0 + 4 * q16) = acc[nb];
     }
   }
 }
@@ -207,7 +248,7 @@ hipError_t launch_out_proj(const GemmParams& p, hipStream_t s) {
     const int64_t total = p.n * p.n_heads * p.d_v;
     hipLaunchKernelGGL(out_proj_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, p);
   } else {
-    const dim3 grid((p.d_v + 127) / 128, p.n_heads, static_cast<unsigned>((p.n + 31) / 32));
+    const dim3 grid(p.d_v / kOutRows, p.n_heads);
     hipLaunchKernelGGL(out_proj_bf16_kernel, grid, dim3(256), 0, s, p);
   }
   return hipGetLastError();
