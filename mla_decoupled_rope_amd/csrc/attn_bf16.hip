@@ -52,8 +52,12 @@ constexpr float kOverflowLog2 = 64.0f;  // P may reach 2^64 before a split is re
 // format, no swizzle, no index/thread-id addressing.
 constexpr int kBufferWord3 = 0x00020000;
 
-// Bits 1-2 of the row: a function of r mod 8 only.
-__device__ __forceinline__ int swz(int r) { return r & 6; }
+// XOR swizzle of row r: bit 1 of the row to bit 2, bits 2-3 to bits 0-1 (a
+// function of r mod 16).  With 64 four-byte banks and 1152-byte rows (odd rows
+// start half way round the banks), it puts every 16-lane phase of a K read
+// (16 rows, one chunk each) and every half-wave of a V transpose read (4 rows
+// x 4 chunks x 8 bytes in two pieces) on distinct banks.
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 // Physical 16-byte chunk slot of logical chunk j in LDS row r.  Full groups
 // of 8 chunks are XOR-swizzled with swz(r); a trailing group of 4 (when the
@@ -62,6 +66,7 @@ __device__ __forceinline__ int swz(int r) { return r & 6; }
 template <int D>
 __device__ __forceinline__ int phys_chunk(int r, int j) {
   constexpr int CHF = (D / 8 / 8) * 8;
+  if constexpr (CHF == D / 8) return j ^ swz(r);  // every chunk is in a full group: no branch
   return j < CHF ? (j ^ swz(r)) : (j ^ (swz(r) & 3));
 }
 
@@ -223,42 +228,47 @@ struct TileDma {
 // outstanding and does not wait on the other counters (gfx9 encoding).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// S += K . Q^T on VGPR accumulators.  Written as inline asm so that the
-// 16 score accumulators live in VGPRs while the 256 output accumulators hold
-// the AGPRs (the compiler otherwise puts both in AGPRs and spills).  The
-// first step uses an inline zero for srcC, so no VALU write feeds an MFMA.
-__device__ __forceinline__ void mfma_qk_first(f32x4& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+// S += K . Q^T on VGPR accumulators (v_mfma_f32_32x32x16_bf16, 16 floats a
+// lane).  Written as inline asm so that the score accumulators live in VGPRs
+// while the output accumulators hold the AGPRs (the compiler otherwise puts
+// both in AGPRs and spills).  The first step of an accumulator uses an inline
+// zero for srcC, so no VALU write feeds an MFMA.
+__device__ __forceinline__ void mfma_qk_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_qk(f32x4& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
-// Wait states between the last score MFMA and the VALU reads of its result
-// (the hazard recognizer does not see inside inline asm).
-__device__ __forceinline__ void mfma_qk_drain(f32x4 (&s)[2][2]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
+// Wait states between the last score MFMAs and the VALU reads of their
+// results (the hazard recognizer does not see inside inline asm).
+__device__ __forceinline__ void mfma_qk_drain(f32x16& s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
 }
 
+// MFMA 32x32x16 lane layouts used below (lane l, r = l % 32, h = l / 32):
+//   A[i][k]: row i = r, k = 8h .. 8h+7;   B[k][j]: column j = r, k = 8h .. 8h+7;
+//   D[i][j]: column j = r, rows i = 8g + 4h + e in register 4g + e (g, e < 4).
 template <int DC, int DR, int HG, int TW, bool PREFILL, bool QF32>
 __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p) {
   constexpr int D = DC + DR;
+  constexpr int ROWB = D * 2;       // bytes per cache row
   constexpr int NT = 64 * HG * TW;
   constexpr int ROWS = 32 * HG;
-  constexpr int KS = D / 32;
-  // Q k-steps kept in LDS: the position part, plus (at d_c = 512) four
+  constexpr int KS = D / 16;        // 16-wide k steps of the score contraction
+  // Q k-steps kept in LDS: the position part, plus (at d_c = 512) eight
   // content k-steps, which keeps the page loop within the register file.
-  constexpr int KSL = DR / 32 + (DC >= 512 ? 4 : 0);
+  constexpr int KSL = DR / 16 + (DC >= 512 ? 8 : 0);
   constexpr int KSQ = KS - KSL;     // Q k-steps kept in VGPRs
-  constexpr int QCH = KSL * 4;      // 16-byte chunks per row of the LDS part of Q
-  static_assert(DR % 32 == 0, "position width must be a multiple of 32");
-  constexpr int CB = DC / 16;
+  constexpr int QCH = KSL * 2;      // 16-byte chunks per row of the LDS part of Q
+  static_assert(DR % 16 == 0 && (QCH % 8 == 0 || QCH == 4), "LDS part of Q must swizzle within its row");
+  constexpr int CB = DC / 32;       // 32-wide column blocks of O
   constexpr int PAGE_BYTES = kPage * D * 2;
   // LDS tiles of TROWS cache rows (32 per wave token lane), in a ring of three:
   // one being read, two in flight.
   constexpr int TROWS = 32 * TW;
   constexpr int TILE = TROWS * D * 2;
   constexpr int G = dma_loads<D, 64 * HG * TW / 64, TROWS>();
-  static_assert(D % 32 == 0 && DC % 16 == 0, "dims");
+  static_assert(D % 32 == 0 && DC % 32 == 0, "dims");
   static_assert(TW == 1 || HG <= 2, "two token lanes need half the waves' registers");
   __shared__ __attribute__((aligned(16))) char lds0[TILE];
   __shared__ __attribute__((aligned(16))) char lds1[TILE];
@@ -270,20 +280,20 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave % HG;
   const int tw = wave / HG;
-  const int q16 = lane >> 4, r16 = lane & 15;
+  const int r32 = lane & 31, h2 = lane >> 5;
   const int H = p.n_heads;
 
   // ---- which rows and which keys.  Everything here is wave-uniform except
-  // the row a lane serves: local row lrow(rb) of the workgroup's ROWS rows,
-  // global row row_base + lrow(rb), valid when lrow(rb) < row_count.  Row
-  // addresses are recomputed where needed instead of being held across the
-  // page loop.
+  // the row a lane serves: lanes l and l ^ 32 serve local row lrow of the
+  // workgroup's ROWS rows, global row row_base + lrow, valid when lrow <
+  // row_count.  Row addresses are recomputed where needed instead of being
+  // held across the page loop.
   int b, page_begin, page_end, key_end, row_count;
   int64_t row_base;
-  int limit[2];
+  int limit;
   bool final_out = true;
   int slot = 0;
-  auto lrow = [&](int rb) { return hg * 32 + rb * 16 + (lane & 15); };
+  const int lrow = hg * 32 + r32;
   if constexpr (PREFILL) {
     const PrefillBlock pb = find_prefill_block(p, p.n_blocks - 1 - static_cast<int64_t>(blockIdx.x), ROWS);
     if (!pb.ok) return;
@@ -297,11 +307,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     page_end = (key_end + kPage - 1) / kPage;
     row_base = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(p.cu_q[b])) * H + r0;
     row_count = nq * H - r0;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int lr = lrow(rb);
-      limit[rb] = lr < row_count ? q0 + (r0 + lr) / H + 1 : 0;
-    }
+    limit = lrow < row_count ? q0 + (r0 + lrow) / H + 1 : 0;
   } else {
     const int64_t item = static_cast<int64_t>(blockIdx.x) / p.n_head_chunks;
     const int hc = static_cast<int>(static_cast<int64_t>(blockIdx.x) % p.n_head_chunks);
@@ -317,73 +323,67 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     slot = __builtin_amdgcn_readfirstlane(it.slot);
     row_base = static_cast<int64_t>(b) * H + hc * ROWS;
     row_count = H - hc * ROWS;
-    limit[0] = limit[1] = key_end;
+    limit = key_end;
   }
   if (b >= p.num_seqs) return;
   // wave-uniform bound on the visible keys of this wave's rows
-  int lim_max = max(limit[0], limit[1]);
+  int lim_max = limit;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) lim_max = max(lim_max, __shfl_xor(lim_max, m, 64));
   lim_max = __builtin_amdgcn_readfirstlane(lim_max);
   // wave-uniform lower bound: sub-blocks entirely below it need no mask
-  int lim_min = min(lrow(0) < row_count ? limit[0] : INT32_MAX, lrow(1) < row_count ? limit[1] : INT32_MAX);
+  int lim_min = lrow < row_count ? limit : INT32_MAX;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, m, 64));
   lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
-  // ---- Q fragments (MFMA B operand: row = r16, d = ks*32 + 8*q16 .. +7).
+  // ---- Q fragments (MFMA B operand: row = r32, d = ks*16 + 8*h2 .. +7).
   // A float32 q_lat is split into hi = bf16(q) and lo = bf16(q - hi); the
   // score then takes both terms (K.hi + K.lo), so q~ enters at ~16 bits.
-  // The first KSQ k-steps stay in VGPRs; the last KSL go to LDS,
-  // where each lane keeps exactly the fragments it will read back (no
-  // sharing, so no barrier), XOR-swizzled so a read phase hits 8 banks.
-  bf16x8 qf[2][KSQ];
-  bf16x8 qlo[QF32 ? 2 : 1][QF32 ? KSQ : 1];
-  // this lane's LDS home of a position fragment; lr, lq are the lane's r16, q16
-  auto q_slot = [&](int term, int rb, int ks, int lr, int lq) -> bf16x8* {
-    const int row = hg * 32 + rb * 16 + lr;
-    const int ch = (ks - KSQ) * 4 + lq;
-    return &ldsq[(term * ROWS + row) * QCH + (ch ^ (row & (QCH >= 8 ? 7 : QCH - 1)))];
+  // The first KSQ k-steps stay in VGPRs; the last KSL go to LDS, where each
+  // lane keeps exactly the fragments it will read back (no sharing, so no
+  // barrier), XOR-swizzled like the cache tiles.
+  bf16x8 qf[KSQ];
+  bf16x8 qlo[QF32 ? KSQ : 1];
+  // this lane's LDS home of a fragment of k-step ks; lr, lh are the lane's r32, h2
+  auto q_slot = [&](int term, int ks, int lr, int lh) -> bf16x8* {
+    const int row = hg * 32 + lr;
+    const int ch = (ks - KSQ) * 2 + lh;
+    return &ldsq[(term * ROWS + row) * QCH + (ch ^ (swz(row) & (QCH >= 8 ? 7 : QCH - 1)))];
   };
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8 hi8, lo8;
+    if constexpr (QF32) {
+      const float* qlat = static_cast<const float*>(p.q_lat);
+      bf16_t hi[8], lo[8];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 hi8, lo8;
-      if constexpr (QF32) {
-        const float* qlat = static_cast<const float*>(p.q_lat);
-        bf16_t hi[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = lrow(rb) < row_count ? qlat[(row_base + lrow(rb)) * D + ks * 32 + q16 * 8 + e] : 0.f;
-          hi[e] = f32_to_bf16_finite(x);
-          lo[e] = f32_to_bf16_finite(x - bf16_to_f32(hi[e]));
-        }
-        __builtin_memcpy(&hi8, hi, 16);
-        __builtin_memcpy(&lo8, lo, 16);
-      } else {
-        const bf16_t* qlat = static_cast<const bf16_t*>(p.q_lat);
-        hi8 = lrow(rb) < row_count
-                  ? *reinterpret_cast<const bf16x8*>(qlat + (row_base + lrow(rb)) * D + ks * 32 + q16 * 8)
-                  : bf16x8{};
+      for (int e = 0; e < 8; ++e) {
+        const float x = lrow < row_count ? qlat[(row_base + lrow) * D + ks * 16 + h2 * 8 + e] : 0.f;
+        hi[e] = f32_to_bf16_finite(x);
+        lo[e] = f32_to_bf16_finite(x - bf16_to_f32(hi[e]));
       }
-      if (ks < KSQ) {
-        qf[rb][ks < KSQ ? ks : 0] = hi8;
-        if constexpr (QF32) qlo[rb][ks < KSQ ? ks : 0] = lo8;
-      } else {
-        *q_slot(0, rb, ks, r16, q16) = hi8;
-        if constexpr (QF32) *q_slot(1, rb, ks, r16, q16) = lo8;
-      }
+      __builtin_memcpy(&hi8, hi, 16);
+      __builtin_memcpy(&lo8, lo, 16);
+    } else {
+      const bf16_t* qlat = static_cast<const bf16_t*>(p.q_lat);
+      hi8 = lrow < row_count ? *reinterpret_cast<const bf16x8*>(qlat + (row_base + lrow) * D + ks * 16 + h2 * 8)
+                             : bf16x8{};
     }
-
-  f32x4 oacc[CB][2];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    oacc[cb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    oacc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ks < KSQ) {
+      qf[ks < KSQ ? ks : 0] = hi8;
+      if constexpr (QF32) qlo[ks < KSQ ? ks : 0] = lo8;
+    } else {
+      *q_slot(0, ks, r32, h2) = hi8;
+      if constexpr (QF32) *q_slot(1, ks, r32, h2) = lo8;
+    }
   }
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_part[2] = {0.f, 0.f};
+
+  f32x16 oacc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
 
   const char* cache = static_cast<const char*>(p.cache);
   const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
@@ -422,16 +422,15 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       const int pg = page_begin + rel / kPage;
       if (rel % kPage == 0 && ((pg - page_begin) & 63) == 0 && pg != page_begin) ids = load_ids(pg);
       const int t0 = page_begin * kPage + rel;
-      return Dma(dst, page_ptr(ids, pg) + (rel % kPage) * (D * 2), min(TROWS, key_end - t0), true, wave);
+      return Dma(dst, page_ptr(ids, pg) + (rel % kPage) * ROWB, min(TROWS, key_end - t0), true, wave);
     };
     if (ntile > 0) tile_dma(0, lds0).issue_all(lane, wave);
     if (ntile > 1) tile_dma(1, lds1).issue_all(lane, wave);
     // One tile: wait for `cur` (the next tile's DMA stays in flight), make it
     // visible to all waves, then compute on `cur` while issuing the DMA two
     // tiles ahead into `nx2` (the buffer every wave finished reading one step
-    // ago).
-    // The three buffers are distinct LDS objects, so the compiler can see
-    // that the DMAs in flight never alias the reads.
+    // ago).  The three buffers are distinct LDS objects, so the compiler can
+    // see that the DMAs in flight never alias the reads.
     auto tile = [&](int it, char* cur, char* nx2) {
       if (it + 1 < ntile)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(G));
@@ -443,8 +442,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       // the DMA two tiles ahead; its instructions are spread over the K steps below
       const Dma dma = it + 2 < ntile ? tile_dma(it + 2, nx2) : Dma(nx2, cache, 1, false, wave);
-      const char* buf = cur;
       const int sb = TW == 1 ? 0 : tw;  // this wave's 32-row sub-block of the tile
+      const char* buf = cur + sb * 32 * ROWB;
       const int t0 = page_begin * kPage + it * TROWS + sb * 32;
       [&] {
         // skip sub-blocks no row of this wave can see (wave-uniform)
@@ -452,43 +451,48 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
           dma.issue_all(lane, wave);
           return;
         }
-        // Per-lane LDS byte offsets inside the tile, recomputed here from an
-        // opaque lane id rather than held in registers across the loop; the
-        // chunk group and the sub-block enter as immediates.
+        // Per-lane LDS byte offsets inside the sub-block, recomputed here
+        // from an opaque lane id rather than held in registers across the
+        // loop; swizzle groups, token halves and column blocks enter as
+        // immediates (rows 16 apart share a swizzle).
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        const int lq16 = ln >> 4, lr16 = ln & 15;
-        // Rows 16 apart share a swizzle (swz depends on r mod 8), so the
-        // second 16-token block is a constant offset away.
-        constexpr int TB_OFF = 16 * D * 2;
-        int k_off[2], k_tail, v_off[4];
+        const int lr = ln & 31, lh = ln >> 5;
+        // K (A operand) of k-step ks: token row lr, chunk 2*ks + lh; group ks/4
+        int k_off[4], k_tail[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) k_off[kb] = lr16 * (D * 2) + phys_chunk<D>(lr16, kb * 4 + lq16) * 16;
-        k_tail = lr16 * (D * 2) + (phys_chunk<D>(lr16, CHF8 + lq16) - CHF8) * 16;
-        const int vrow = lq16 * 4 + (lr16 >> 2);
+        for (int kq = 0; kq < 4; ++kq) k_off[kq] = lr * ROWB + phys_chunk<D>(lr, 2 * kq + lh) * 16;
 #pragma unroll
-        for (int cl = 0; cl < 4; ++cl)
-          v_off[cl] = vrow * (D * 2) + phys_chunk<D>(vrow, cl * 2 + ((lr16 & 3) >> 1)) * 16 + (lr16 & 1) * 8;
-        // ---- S^T = K . Q^T over D
-        f32x4 sacc[2][2];
-        // K fragments run KPF steps ahead of the MFMAs that consume them.
-        constexpr int KPF = 2;
-        bf16x8 ka[KS][2];
-        bf16x8 qr[KS][2], qrlo[QF32 ? KS : 1][2];
-        auto load_k = [&](int ks) {
+        for (int kq = 0; kq < 2; ++kq) k_tail[kq] = lr * ROWB + phys_chunk<D>(lr, CHF8 + 2 * kq + lh) * 16;
+        // V^T (A operand) of k-step kp, column block cb, transpose read s:
+        // supplier lane 16g + 4k + q reads token row 16kp + 8s + 4(g/2) + k,
+        // columns cb*32 + 16(g%2) + 4q .. +3; the result gives lane l the
+        // column cb*32 + l%32 at tokens 16kp + 8s + 4h + 0..3, the order in
+        // which the lane holds P.
+        int v_off[2][2];
+        {
+          const int vg = ln >> 4, vk = (ln >> 2) & 3, vq = ln & 3;
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            // chunk ks*4 + q16 of row krow: group ks/2 (immediate), in-group slot from k_off
-            const char* a = (ks / 2) * 128 < CHF8 * 16 ? buf + k_off[ks & 1] + (ks / 2) * 128
-                                                       : buf + k_tail + (ks / 2) * 128;
-            ka[ks][tb] = *reinterpret_cast<const bf16x8*>(a + sb * 32 * (D * 2) + tb * TB_OFF);
+          for (int s = 0; s < 2; ++s) {
+            const int vrow = 8 * s + 4 * (vg >> 1) + vk;
+#pragma unroll
+            for (int co = 0; co < 2; ++co)
+              v_off[s][co] = vrow * ROWB + phys_chunk<D>(vrow, 4 * co + 2 * (vg & 1) + (vq >> 1)) * 16 + (vq & 1) * 8;
           }
+        }
+        // ---- S^T = K . Q^T over D, one accumulator (dependent accumulation
+        // issues back to back at full rate)
+        f32x16 sacc;
+        // K fragments run KPF steps ahead of the MFMAs that consume them.
+        constexpr int KPF = 8;
+        bf16x8 ka[KS];
+        bf16x8 qr[KS], qrlo[QF32 ? KS : 1];
+        auto load_k = [&](int ks) {
+          const char* a = 2 * ks < CHF8 ? buf + k_off[ks & 3] + (ks / 4) * 128 : buf + k_tail[(ks - CHF8 / 2) & 1];
+          ka[ks] = *reinterpret_cast<const bf16x8*>(a);
           if (ks >= KSQ) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-              qr[ks][rb] = *q_slot(0, rb, ks, lr16, lq16);
-              if constexpr (QF32) qrlo[ks][rb] = *q_slot(1, rb, ks, lr16, lq16);
-            }
+            qr[ks] = *q_slot(0, ks, lr, lh);
+            if constexpr (QF32) qrlo[ks] = *q_slot(1, ks, lr, lh);
           }
         };
 #pragma unroll
@@ -497,115 +501,99 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           if (ks + KPF < KS) load_k(ks + KPF);
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-              const bf16x8& qb = ks < KSQ ? qf[rb][ks < KSQ ? ks : 0] : qr[ks][rb];
-              if (ks == 0)
-                mfma_qk_first(sacc[tb][rb], ka[ks][tb], qb);
-              else
-                mfma_qk(sacc[tb][rb], ka[ks][tb], qb);
-              if constexpr (QF32)
-                mfma_qk(sacc[tb][rb], ka[ks][tb], ks < KSQ ? qlo[rb][ks < KSQ ? ks : 0] : qrlo[QF32 ? ks : 0][rb]);
-            }
+          const bf16x8& qb = ks < KSQ ? qf[ks < KSQ ? ks : 0] : qr[ks];
+          if (ks == 0)
+            mfma_qk_first(sacc, ka[ks], qb);
+          else
+            mfma_qk(sacc, ka[ks], qb);
+          if constexpr (QF32) mfma_qk(sacc, ka[ks], ks < KSQ ? qlo[ks < KSQ ? ks : 0] : qrlo[QF32 ? ks : 0]);
 #pragma unroll
           for (int i = ks * Dma::N / KS; i < (ks + 1) * Dma::N / KS; ++i) dma.issue(i, lane, wave);
-          __builtin_amdgcn_sched_barrier(0);  // likewise for the K reads of step ks + KPF
+          __builtin_amdgcn_sched_barrier(0);  // keep the K reads of step ks + KPF above the MFMA of step ks
         }
         mfma_qk_drain(sacc);
         // ---- reference max.  Raw scores stay unscaled; the scale (times log2 e)
-        // is folded into the exponent's FMA.  Only sub-blocks that cross a
-        // row's last visible key are masked.  The cross-lane row max (two
-        // shuffles) is needed only while a row has no reference yet (its first
-        // visible sub-block) and in the max-only pass; otherwise each lane just
-        // checks its own scores against the reference for overflow.
+        // is folded into the exponent's FMA.  Lane (row lr, half lh) holds
+        // tokens 8g + 4lh + e at register 4g + e.  Only sub-blocks that cross a
+        // row's last visible key are masked.  The cross-lane row max (one
+        // swap with lane l ^ 32) is needed only while a row has no reference
+        // yet (its first visible sub-block) and in the max-only pass;
+        // otherwise each lane just checks its own scores for overflow.
+        float sv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
         const bool partial = t0 + 32 > lim_min;
         if (partial) {
           float ninf = -INFINITY;  // materialised here, not held across the loop
           asm volatile("" : "+v"(ninf));
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
+          for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int t = t0 + tb * 16 + lq16 * 4 + e;
-                if (t >= (PREFILL ? limit[rb] : key_end)) sacc[tb][rb][e] = ninf;
-              }
+            for (int e = 0; e < 4; ++e) {
+              const int t = t0 + 8 * g + 4 * lh + e;
+              if (t >= (PREFILL ? limit : key_end)) sv[4 * g + e] = ninf;
+            }
         }
-        float lmx[2];
+        float lmx = -INFINITY;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          float m = -INFINITY;
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = fmaxf(m, sacc[tb][rb][e]);
-          lmx[rb] = m * p.scale_log2;  // this lane's max (scale > 0 keeps the order)
-        }
-        const bool need_ref = MODE == 1 || __ballot(m_run[0] == -INFINITY || m_run[1] == -INFINITY) != 0;
+        for (int i = 0; i < 16; ++i) lmx = fmaxf(lmx, sv[i]);
+        lmx *= p.scale_log2;  // this lane's max (scale > 0 keeps the order)
+        const bool need_ref = MODE == 1 || __ballot(m_run == -INFINITY) != 0;
         if (need_ref) {
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            const float m = pair32_max(pair16_max(lmx[rb]));
-            if constexpr (MODE == 1)
-              m_run[rb] = fmaxf(m_run[rb], m);
-            else if (m_run[rb] == -INFINITY)
-              m_run[rb] = m;  // O and l are still zero: exact
-          }
+          const float m = pair32_max(lmx);
+          if constexpr (MODE == 1)
+            m_run = fmaxf(m_run, m);
+          else if (m_run == -INFINITY)
+            m_run = m;  // O and l are still zero: exact
         }
         if constexpr (MODE == 1) return;
-        if constexpr (MODE == 0)
-          overflow |= __ballot(lmx[0] > m_run[0] + kOverflowLog2 || lmx[1] > m_run[1] + kOverflowLog2) != 0;
-        // ---- P = 2^(scale*log2e*s - m) rounded to bf16 (hardware RNE, two at a time)
+        if constexpr (MODE == 0) overflow |= __ballot(lmx > m_run + kOverflowLog2) != 0;
+        // ---- P = 2^(scale*log2e*s - m) rounded to bf16 (hardware RNE, two at a
+        // time); registers 8kp .. 8kp+7 are the B operand of k-step kp.
         bf16x8 pb[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        {
           // a row still without a reference has only masked (-inf) scores here,
           // which give 0 against any finite reference
-          const float m_use = __builtin_fmaxf(m_run[rb], -FLT_MAX);
-          float pf[8];
+          const float m_use = __builtin_fmaxf(m_run, -FLT_MAX);
+          float pf[16];
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              pf[tb * 4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][rb][e], p.scale_log2, -m_use));
+          for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], p.scale_log2, -m_use));
           float lsum = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) lsum += pf[i];
-          l_part[rb] += lsum;
+          for (int i = 0; i < 16; ++i) lsum += pf[i];
+          l_part += lsum;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < 8; ++i) {
             const bf16x2 pair = __builtin_convertvector((f32x2){pf[2 * i], pf[2 * i + 1]}, bf16x2);
-            pb[rb][2 * i] = pair[0];
-            pb[rb][2 * i + 1] = pair[1];
+            pb[i / 4][(2 * i) % 8] = pair[0];
+            pb[i / 4][(2 * i) % 8 + 1] = pair[1];
           }
         }
-        // V^T fragments run VPF column blocks ahead of their MFMAs.
+        // ---- O^T += V^T . P^T: k-step kp (16 tokens) outer, column block cb
+        // inner, so an accumulator's two MFMAs are CB apart.  V^T fragments
+        // run VPF blocks ahead of their MFMAs.
+        constexpr int NV = 2 * CB;
         constexpr int VPF = 4;
-        i16x4 vt[CB][2];
-        auto load_v = [&](int cb) {
+        i16x4 vt[NV][2];
+        auto load_v = [&](int idx) {
+          const int kp = idx / CB, cb = idx % CB;
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            // columns cb*16 + 4*(r16&3): chunk cb*2 + ((r16&3)>>1) = group cb/4, slot from v_off
-            const char* a = buf + v_off[cb & 3] + (cb / 4) * 128 + sb * 32 * (D * 2) + tb * TB_OFF;
-            vt[cb][tb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
+          for (int s = 0; s < 2; ++s) {
+            const char* a = buf + v_off[s][cb & 1] + (cb / 2) * 128 + kp * 16 * ROWB;
+            vt[idx][s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
           }
         };
 #pragma unroll
-        for (int cb = 0; cb < VPF; ++cb) load_v(cb);
+        for (int idx = 0; idx < VPF; ++idx) load_v(idx);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          if (cb + VPF < CB) load_v(cb + VPF);
+        for (int idx = 0; idx < NV; ++idx) {
+          if (idx + VPF < NV) load_v(idx + VPF);
           bf16x8 va;
-          __builtin_memcpy(&va, &vt[cb][0], 8);
-          __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vt[cb][1], 8);
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            oacc[cb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb], oacc[cb][rb], 0, 0, 0);
-          // Keep source order: the reads of block cb + VPF stay above the MFMAs
-          // of block cb (the scheduler would otherwise sink them to their use).
+          __builtin_memcpy(&va, &vt[idx][0], 8);
+          __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vt[idx][1], 8);
+          oacc[idx % CB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[idx / CB], oacc[idx % CB], 0, 0, 0);
+          // Keep source order: the reads of block idx + VPF stay above the MFMA
+          // of block idx (the scheduler would otherwise sink them to their use).
           __builtin_amdgcn_sched_barrier(0);
         }
       }();
@@ -630,15 +618,12 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     // Rare: some row's scores rose by more than 2^kOverflowLog2 over its first
     // visible key.  Redo the split exactly: true max first, then accumulate.
     __syncthreads();
-    m_run[0] = m_run[1] = -INFINITY;
+    m_run = -INFINITY;
     run_pass(std::integral_constant<int, 1>{});
     __syncthreads();
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      oacc[cb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      oacc[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    l_part[0] = l_part[1] = 0.f;
+    for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
+    l_part = 0.f;
     run_pass(std::integral_constant<int, 2>{});
     __syncthreads();  // the epilogue stages through the tile buffers
   }
@@ -646,88 +631,87 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   // ---- combine the two token lanes of a head group (TW == 2)
   if constexpr (TW == 2) {
     __syncthreads();
-    static_assert((HG * CB * 2 * 64 * 4 + HG * 2 * 64 * 2) * 4 <= TILE, "exchange must fit one page buffer");
-    float* xo = reinterpret_cast<float*>(lds0);  // [hg][cb][rb][lane][4]
-    float* xs = xo + HG * CB * 2 * 64 * 4;       // [hg][rb][lane][m, l]
+    static_assert((HG * CB * 64 * 16 + HG * 64 * 2) * 4 <= TILE, "exchange must fit one page buffer");
+    float* xo = reinterpret_cast<float*>(lds0);  // [hg][cb][lane][16]
+    float* xs = xo + HG * CB * 64 * 16;          // [hg][lane][m, l]
     if (tw == 1) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          *reinterpret_cast<f32x4*>(&xo[(((hg * CB + cb) * 2 + rb) * 64 + lane) * 4]) = oacc[cb][rb];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        xs[((hg * 2 + rb) * 64 + lane) * 2 + 0] = m_run[rb];
-        xs[((hg * 2 + rb) * 64 + lane) * 2 + 1] = l_part[rb];
-      }
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<f32x4*>(&xo[((hg * CB + cb) * 64 + lane) * 16 + 4 * i]) =
+              f32x4{oacc[cb][4 * i], oacc[cb][4 * i + 1], oacc[cb][4 * i + 2], oacc[cb][4 * i + 3]};
+      xs[(hg * 64 + lane) * 2 + 0] = m_run;
+      xs[(hg * 64 + lane) * 2 + 1] = l_part;
     }
     __syncthreads();
     if (tw == 1) return;
+    const float m1 = xs[(hg * 64 + lane) * 2 + 0];
+    const float l1 = xs[(hg * 64 + lane) * 2 + 1];
+    const float m = fmaxf(m_run, m1);
+    const float mu = m == -INFINITY ? 0.f : m;
+    const float f0 = __builtin_amdgcn_exp2f(m_run - mu);
+    const float f1 = __builtin_amdgcn_exp2f(m1 - mu);
+    l_part = l_part * f0 + l1 * f1;
+    m_run = m;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float m1 = xs[((hg * 2 + rb) * 64 + lane) * 2 + 0];
-      const float l1 = xs[((hg * 2 + rb) * 64 + lane) * 2 + 1];
-      const float m = fmaxf(m_run[rb], m1);
-      const float mu = m == -INFINITY ? 0.f : m;
-      const float f0 = __builtin_amdgcn_exp2f(m_run[rb] - mu);
-      const float f1 = __builtin_amdgcn_exp2f(m1 - mu);
-      l_part[rb] = l_part[rb] * f0 + l1 * f1;
-      m_run[rb] = m;
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[(((hg * CB + cb) * 2 + rb) * 64 + lane) * 4]);
-        oacc[cb][rb] = oacc[cb][rb] * f0 + o1 * f1;
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[((hg * CB + cb) * 64 + lane) * 16 + 4 * i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[cb][4 * i + e] = oacc[cb][4 * i + e] * f0 + o1[e] * f1;
       }
-    }
   }
 
-  // ---- normalise and store.  O^T lane layout: row r16, c = cb*16 + 4*q16 + e,
-  // so a lane holds 4 columns of one row per column block.  Each wave stages
-  // 16 rows at a time (bf16) in its own part of an idle tile buffer, then
-  // writes whole rows (2*d_c contiguous bytes) with 16-byte stores.  Partial
-  // results of a split are stored normalised in bf16, like the final ones.
-  constexpr int SROW = DC * 2 + 32;  // staging row stride in bytes (padding spreads the rows over the banks)
-  static_assert(2 * 16 * SROW <= TILE && HG <= 4, "staging must fit two waves per idle tile buffer");
-  char* stage = (hg < 2 ? lds1 : lds2) + (hg % 2) * 16 * SROW;
+  // ---- normalise and store.  O^T lane layout: lane (row r32, half h2) holds
+  // columns cb*32 + 8g + 4h2 + e at oacc[cb][4g + e].  Each wave stages its 32
+  // rows (bf16), half of the columns at a time, in its own part of an idle
+  // tile buffer, then writes whole half-rows (d_c contiguous bytes) with
+  // 16-byte stores.  Partial results of a split are stored normalised in
+  // bf16, like the final ones.
+  constexpr int SROW = DC + 16;  // staging row stride in bytes (d_c/2 bf16 + padding against bank conflicts)
+  static_assert(2 * 32 * SROW <= TILE && HG <= 4, "staging must fit two waves per idle tile buffer");
+  char* stage = (hg < 2 ? lds1 : lds2) + (hg % 2) * 32 * SROW;
   bf16_t* const out_base = final_out ? static_cast<bf16_t*>(p.out_latent) : p.ws_o;
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    float l = l_part[rb];
-    l = pair32_sum(pair16_sum(l));
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse_v = l > 0.f ? (m_run[rb] + log2f(l)) * kLn2 : -INFINITY;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      uint2 pk;
-      pk.x = f32_to_bf16(oacc[cb][rb][0] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][rb][1] * inv)) << 16);
-      pk.y = f32_to_bf16(oacc[cb][rb][2] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][rb][3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(stage + r16 * SROW + (cb * 16 + 4 * q16) * 2) = pk;
+  const float l = pair32_sum(l_part);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (lrow < row_count && h2 == 0) {
+    const float lse_v = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    const int64_t row_g = row_base + lrow;
+    if (final_out) {
+      if (p.lse != nullptr) p.lse[row_g] = lse_v;
+    } else {
+      p.ws_lse[static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H)] = lse_v;
     }
-    if (lrow(rb) < row_count && q16 == 0) {
-      const int64_t row_g = row_base + lrow(rb);
-      if (final_out) {
-        if (p.lse != nullptr) p.lse[row_g] = lse_v;
-      } else {
-        p.ws_lse[static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H)] = lse_v;
+  }
+  constexpr int PIECES = DC / 16;  // 16-byte pieces per half-row
+  static_assert(64 % PIECES == 0, "half-row pieces must tile a wave");
+  constexpr int RPI = 64 / PIECES;  // half-rows per store instruction
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int cbl = 0; cbl < CB / 2; ++cbl) {
+      const int cb = half * (CB / 2) + cbl;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 pk;
+        pk.x = f32_to_bf16(oacc[cb][4 * g] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][4 * g + 1] * inv)) << 16);
+        pk.y = f32_to_bf16(oacc[cb][4 * g + 2] * inv) |
+               (static_cast<uint32_t>(f32_to_bf16(oacc[cb][4 * g + 3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(stage + r32 * SROW + (cbl * 32 + 8 * g + 4 * h2) * 2) = pk;
       }
     }
-    // rows hg*32 + rb*16 + i of the workgroup, one 16-byte piece per lane
-    constexpr int PIECES = DC * 2 / 16;  // 16-byte pieces per row
-    static_assert(64 % PIECES == 0 || PIECES % 64 == 0, "row pieces must tile a wave");
-    constexpr int RPI = PIECES >= 64 ? 1 : 64 / PIECES;  // rows per store instruction
 #pragma unroll
-    for (int i0 = 0; i0 < 16; i0 += RPI) {
-#pragma unroll
-      for (int pc0 = 0; pc0 < (PIECES >= 64 ? PIECES : 64); pc0 += 64) {
-        const int i = i0 + (PIECES >= 64 ? 0 : lane / PIECES);
-        const int pc = pc0 + (PIECES >= 64 ? lane : lane % PIECES);
-        const int lr = hg * 32 + rb * 16 + i;
-        const i32x4 v = *reinterpret_cast<const i32x4*>(stage + i * SROW + pc * 16);
-        if (lr < row_count) {
-          const int64_t row_g = row_base + lr;
-          const int64_t orow = final_out ? row_g : static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
-          *reinterpret_cast<i32x4*>(out_base + orow * DC + pc * 8) = v;
-        }
+    for (int i0 = 0; i0 < 32; i0 += RPI) {
+      const int i = i0 + lane / PIECES;
+      const int pc = lane % PIECES;
+      const int lr = hg * 32 + i;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(stage + i * SROW + pc * 16);
+      if (lr < row_count) {
+        const int64_t row_g = row_base + lr;
+        const int64_t orow = final_out ? row_g : static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
+        *reinterpret_cast<i32x4*>(out_base + orow * DC + half * (DC / 2) + pc * 8) = v;
       }
     }
   }
