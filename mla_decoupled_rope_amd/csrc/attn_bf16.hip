@@ -175,9 +175,8 @@ constexpr int dma_groups() { return TROWS / (576 / (D / 8)); }
 template <int D, int NW, int TROWS>
 constexpr int dma_loads() { return 9 * (dma_groups<D, TROWS>() >= NW ? dma_groups<D, TROWS>() / NW : 1); }
 
-// One tile's DMA, prepared once and issued one 1 KiB instruction at a time,
-// so the issue (tens of cycles per instruction) can be spread over the MFMA
-// work of the tile being computed instead of stalling the wave in one burst.
+// One tile's DMA: the source resource and valid rows prepared once, then
+// issued as N 1 KiB wave instructions.
 template <int D, int NW, int TROWS>
 struct TileDma {
   static constexpr int CH = D / 8;
@@ -427,9 +426,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     if (ntile > 0) tile_dma(0, lds0).issue_all(lane, wave);
     if (ntile > 1) tile_dma(1, lds1).issue_all(lane, wave);
     // One tile: wait for `cur` (the next tile's DMA stays in flight), make it
-    // visible to all waves, then compute on `cur` while issuing the DMA two
-    // tiles ahead into `nx2` (the buffer every wave finished reading one step
-    // ago).  The three buffers are distinct LDS objects, so the compiler can
+    // visible to all waves, start the DMA two tiles ahead into `nx2` (the
+    // buffer every wave finished reading one step ago), compute on `cur`.  The three buffers are distinct LDS objects, so the compiler can
     // see that the DMAs in flight never alias the reads.
     auto tile = [&](int it, char* cur, char* nx2) {
       if (it + 1 < ntile)
@@ -440,17 +438,15 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       // flight.  Every LDS read of the previous tile has been consumed by an
       // MFMA by now; the memory clobber keeps this tile's reads below it.
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      // the DMA two tiles ahead; its instructions are spread over the K steps below
-      const Dma dma = it + 2 < ntile ? tile_dma(it + 2, nx2) : Dma(nx2, cache, 1, false, wave);
+      // the DMA two tiles ahead, issued in one burst here: spread over the
+      // score loop, its instructions were measured to slow the loop more
+      if (it + 2 < ntile) tile_dma(it + 2, nx2).issue_all(lane, wave);
       const int sb = TW == 1 ? 0 : tw;  // this wave's 32-row sub-block of the tile
       const char* buf = cur + sb * 32 * ROWB;
       const int t0 = page_begin * kPage + it * TROWS + sb * 32;
       [&] {
         // skip sub-blocks no row of this wave can see (wave-uniform)
-        if (t0 >= lim_max) {
-          dma.issue_all(lane, wave);
-          return;
-        }
+        if (t0 >= lim_max) return;
         // Per-lane LDS byte offsets inside the sub-block, recomputed here
         // from an opaque lane id rather than held in registers across the
         // loop; swizzle groups, token halves and column blocks enter as
@@ -507,8 +503,6 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
           else
             mfma_qk(sacc, ka[ks], qb);
           if constexpr (QF32) mfma_qk(sacc, ka[ks], ks < KSQ ? qlo[ks < KSQ ? ks : 0] : qrlo[QF32 ? ks : 0]);
-#pragma unroll
-          for (int i = ks * Dma::N / KS; i < (ks + 1) * Dma::N / KS; ++i) dma.issue(i, lane, wave);
           __builtin_amdgcn_sched_barrier(0);  // keep the K reads of step ks + KPF above the MFMA of step ks
         }
         mfma_qk_drain(sacc);
