@@ -690,9 +690,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2 pk;
-        pk.x = f32_to_bf16(oacc[cb][4 * g] * inv) | (static_cast<uint32_t>(f32_to_bf16(oacc[cb][4 * g + 1] * inv)) << 16);
-        pk.y = f32_to_bf16(oacc[cb][4 * g + 2] * inv) |
-               (static_cast<uint32_t>(f32_to_bf16(oacc[cb][4 * g + 3] * inv)) << 16);
+        pk.x = pack_bf16x2(oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv);
+        pk.y = pack_bf16x2(oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
         *reinterpret_cast<uint2*>(stage + r32 * SROW + (cbl * 32 + 8 * g + 4 * h2) * 2) = pk;
       }
     }
@@ -741,25 +740,44 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
   if (head >= H || ns_b == 1 || base + ns_b > p.n_items) return;
   const int64_t row = static_cast<int64_t>(b) * H + head;
   bf16_t* out = static_cast<bf16_t*>(p.out_latent) + row * DC;
+  const float* lse_s = p.ws_lse + static_cast<int64_t>(base) * H + head;  // split s at lse_s[s * H]
+  const bf16_t* part = p.ws_o + (static_cast<int64_t>(base) * H + head) * DC + lane * PER;
+  // max of the splits' lse, the lanes taking splits side by side
+  float m = -INFINITY;
+  for (int s0 = 0; s0 < ns_b; s0 += 64)
+    if (s0 + lane < ns_b) m = fmaxf(m, lse_s[static_cast<int64_t>(s0 + lane) * H]);
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  float m = -INFINITY;
-  for (int s = 0; s < ns_b; ++s) m = fmaxf(m, p.ws_lse[static_cast<int64_t>(base + s) * H + head]);
   float wsum = 0.f;
   if (m != -INFINITY) {
-    for (int s = 0; s < ns_b; ++s) {
-      const int64_t srow = static_cast<int64_t>(base + s) * H + head;
-      const float w = __expf(p.ws_lse[srow] - m);
-      wsum += w;
-      const bf16_t* src = p.ws_o + srow * DC + lane * PER;
+    // four splits a round, every load of the round issued before its use
+    constexpr int U = 4;
+    for (int s0 = 0; s0 < ns_b; s0 += U) {
+      bf16_t v[U][PER];
+      float w[U];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, bf16_to_f32(src[i]), acc[i]);
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u < ns_b ? s0 + u : s0;
+        __builtin_memcpy(v[u], part + static_cast<int64_t>(s) * H * DC, PER * sizeof(bf16_t));
+        w[u] = s0 + u < ns_b ? lse_s[static_cast<int64_t>(s) * H] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wu = __expf(w[u] - m);
+        wsum += wu;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, bf16_to_f32(v[u][i]), acc[i]);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  uint32_t o[PER / 2];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) out[lane * PER + i] = f32_to_bf16(acc[i] * inv);
+  for (int i = 0; i < PER / 2; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  __builtin_memcpy(out + lane * PER, o, PER * sizeof(bf16_t));
   if (p.lse != nullptr && lane == 0) p.lse[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 

@@ -24,12 +24,16 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// Round-to-nearest-even float -> bf16 (NaN stays NaN).
+// Round-to-nearest-even float -> bf16 by the hardware conversion
+// (v_cvt_pk_bf16_f32; NaN stays NaN).  A software rounding with a NaN test
+// costs a branch per value, which dominated the epilogues.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+
+// Two floats to a packed bf16 pair (lo in bits 0-15), one conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Round-to-nearest-even float -> bf16 for values known to be finite.

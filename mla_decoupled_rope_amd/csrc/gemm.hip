@@ -117,8 +117,8 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
           *reinterpret_cast<f32x4*>(out + (n * H + h) * D + j) = acc[jb][nb];
         } else {
           uint2 packed;
-          packed.x = f32_to_bf16(acc[jb][nb][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[jb][nb][1])) << 16);
-          packed.y = f32_to_bf16(acc[jb][nb][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[jb][nb][3])) << 16);
+          packed.x = pack_bf16x2(acc[jb][nb][0], acc[jb][nb][1]);
+          packed.y = pack_bf16x2(acc[jb][nb][2], acc[jb][nb][3]);
           *reinterpret_cast<uint2*>(out + (n * H + h) * D + j) = packed;
         }
       }
