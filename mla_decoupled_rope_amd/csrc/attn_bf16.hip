@@ -199,27 +199,54 @@ struct TileDma {
       : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), 0, TROWS * ROWB, kBufferWord3)),
         lds_buf(dst), valid_rows(valid), active(on && (NG >= NW || wave < NG)) {}
 
-  // Instruction i (0 <= i < N, a compile-time constant at every call site).
-  __device__ __forceinline__ void issue(int i, int lane, int wave) const {
-    if (!active) return;
+  // Byte offset in the tile of a lane's 16 bytes in instruction i (0 <= i <
+  // N, a compile-time constant at every call site) of wave `wave`, for a
+  // tile whose rows >= valid repeat row valid - 1.
+  __device__ __forceinline__ static uint32_t offset(int i, int lane, int wave, int valid) {
     const int gg = i / 9, kk = i % 9;
     const int g = NG >= NW ? wave * GPW + gg : wave;
-    // An opaque copy of the lane id keeps the per-lane offsets from being
-    // hoisted out of the tile loop (they are cheap; registers are not).
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int c = kk * 64 + ln;
+    const int c = kk * 64 + lane;
     const int rig = c / CH;
     const int r = g * RG + rig;
     const int j = phys_chunk<D>(r, c - rig * CH);
-    const int rs = r < valid_rows ? r : valid_rows - 1;
-    const uint32_t off = static_cast<uint32_t>(rs * ROWB + j * 16);
+    const int rs = r < valid ? r : valid - 1;
+    return static_cast<uint32_t>(rs * ROWB + j * 16);
+  }
+  // A full tile's offsets depend on the lane and the wave only, so they are
+  // computed once per kernel and kept two 16-bit values to a register; the
+  // division and swizzle behind them cost far more than the DMA issue.
+  static_assert(TROWS * ROWB <= 65536, "tile offsets must fit 16 bits");
+  struct Full {
+    uint32_t v[(N + 1) / 2];
+  };
+  __device__ __forceinline__ static Full full_offsets(int lane, int wave) {
+    Full f;
+#pragma unroll
+    for (int i = 0; i < N; i += 2)
+      f.v[i / 2] = offset(i, lane, wave, TROWS) | (i + 1 < N ? offset(i + 1, lane, wave, TROWS) << 16 : 0u);
+    return f;
+  }
+  __device__ __forceinline__ void issue_at(int i, int wave, uint32_t off) const {
+    const int gg = i / 9, kk = i % 9;
+    const int g = NG >= NW ? wave * GPW + gg : wave;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_buf + g * RG * ROWB + kk * 1024), 16, off, 0, 0,
                                              0);
   }
-  __device__ __forceinline__ void issue_all(int lane, int wave) const {
+  __device__ __forceinline__ void issue_all(int lane, int wave, const Full& f) const {
+    if (!active) return;
+    if (valid_rows == TROWS) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) issue(i, lane, wave);
+      for (int i = 0; i < N; ++i) issue_at(i, wave, (f.v[i / 2] >> (16 * (i % 2))) & 0xffffu);
+    } else {
+      // the last tile of a sequence: offsets recomputed from an opaque lane
+      // id (not hoisted into more registers)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        issue_at(i, wave, offset(i, ln, wave, valid_rows));
+      }
+    }
   }
 };
 
@@ -254,13 +281,21 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   constexpr int NT = 64 * HG * TW;
   constexpr int ROWS = 32 * HG;
   constexpr int KS = D / 16;        // 16-wide k steps of the score contraction
-  // Q k-steps kept in LDS: the position part, plus (at d_c = 512) eight
-  // content k-steps, which keeps the page loop within the register file.
-  constexpr int KSL = DR / 16 + (DC >= 512 ? 8 : 0);
+  // Four head groups of one token lane split P.V by columns of O: each wave
+  // accumulates all 128 rows over d_c/4 columns, so one V^T transpose read
+  // serves four head groups (a quarter of the transpose traffic), and P
+  // (32 tokens x 128 rows, bf16) is exchanged through LDS once per tile.
+  constexpr bool DSPLIT = HG == 4 && TW == 1;
+  // Q k-steps kept in LDS: the position part, plus (at d_c = 512) content
+  // k-steps, which keeps the page loop within the register file (two fewer
+  // with the column split, whose P buffer takes their LDS).
+  constexpr int KSL = DR / 16 + (DC >= 512 ? (DSPLIT ? 6 : 8) : 0);
   constexpr int KSQ = KS - KSL;     // Q k-steps kept in VGPRs
   constexpr int QCH = KSL * 2;      // 16-byte chunks per row of the LDS part of Q
-  static_assert(DR % 16 == 0 && (QCH % 8 == 0 || QCH == 4), "LDS part of Q must swizzle within its row");
+  static_assert(DR % 16 == 0 && QCH % 4 == 0, "LDS part of Q must swizzle within its row");
   constexpr int CB = DC / 32;       // 32-wide column blocks of O
+  constexpr int CBW = DSPLIT ? CB / 4 : CB;  // column blocks a wave accumulates
+  static_assert(!DSPLIT || CBW % 2 == 0, "a wave's columns must cover whole swizzle groups");
   constexpr int PAGE_BYTES = kPage * D * 2;
   // LDS tiles of TROWS cache rows (32 per wave token lane), in a ring of three:
   // one being read, two in flight.
@@ -273,6 +308,9 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   __shared__ __attribute__((aligned(16))) char lds1[TILE];
   __shared__ __attribute__((aligned(16))) char lds2[TILE];
   __shared__ bf16x8 ldsq[(QF32 ? 2 : 1) * ROWS * QCH];
+  // P^T of a tile for the column split: entry (kp * 2 + h) * ROWS + row holds
+  // row's P at the 8 tokens that half h of k-step kp covers
+  __shared__ bf16x8 ldsp[DSPLIT ? 4 * ROWS : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -325,11 +363,12 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     limit = key_end;
   }
   if (b >= p.num_seqs) return;
-  // wave-uniform bound on the visible keys of this wave's rows
+  // wave-uniform bound on the visible keys of this wave's rows (of the whole
+  // workgroup with the column split, whose tiles every wave must take)
   int lim_max = limit;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) lim_max = max(lim_max, __shfl_xor(lim_max, m, 64));
-  lim_max = __builtin_amdgcn_readfirstlane(lim_max);
+  lim_max = __builtin_amdgcn_readfirstlane(DSPLIT ? key_end : lim_max);
   // wave-uniform lower bound: sub-blocks entirely below it need no mask
   int lim_min = lrow < row_count ? limit : INT32_MAX;
 #pragma unroll
@@ -344,11 +383,15 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   // barrier), XOR-swizzled like the cache tiles.
   bf16x8 qf[KSQ];
   bf16x8 qlo[QF32 ? KSQ : 1];
-  // this lane's LDS home of a fragment of k-step ks; lr, lh are the lane's r32, h2
+  // this lane's LDS home of a fragment of k-step ks; lr, lh are the lane's r32, h2.
+  // Rows of a multiple of 8 chunks take the cache tiles' swizzle; other rows
+  // (a stride of 16 banks mod 64) XOR with bits 2-3 of the row.  Either way
+  // the 16 rows of every read phase land on distinct banks.
   auto q_slot = [&](int term, int ks, int lr, int lh) -> bf16x8* {
     const int row = hg * 32 + lr;
     const int ch = (ks - KSQ) * 2 + lh;
-    return &ldsq[(term * ROWS + row) * QCH + (ch ^ (swz(row) & (QCH >= 8 ? 7 : QCH - 1)))];
+    const int x = QCH % 8 == 0 ? (swz(row) & 7) : ((row >> 2) & 3);
+    return &ldsq[(term * ROWS + row) * QCH + (ch ^ x)];
   };
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -410,12 +453,13 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   // climb further sets `overflow`.  MODE 1: running max only (no PV).
   // MODE 2: P = 2^(s - m) with the true max m from a MODE 1 pass.
   // O is never rescaled inside the loop.
+  using Dma = TileDma<D, NT / 64, TROWS>;
+  const typename Dma::Full dma_full = Dma::full_offsets(lane, wave);
   auto run_pass = [&](auto mode_tag) -> bool {
     constexpr int MODE = decltype(mode_tag)::value;
     bool overflow = false;
     int ids = load_ids(page_begin);
     // source of tile h: page page_begin + h*TROWS/64, from row (h*TROWS) % 64
-    using Dma = TileDma<D, NT / 64, TROWS>;
     auto tile_dma = [&](int h, char* dst) -> Dma {
       const int rel = h * TROWS;
       const int pg = page_begin + rel / kPage;
@@ -423,8 +467,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       const int t0 = page_begin * kPage + rel;
       return Dma(dst, page_ptr(ids, pg) + (rel % kPage) * ROWB, min(TROWS, key_end - t0), true, wave);
     };
-    if (ntile > 0) tile_dma(0, lds0).issue_all(lane, wave);
-    if (ntile > 1) tile_dma(1, lds1).issue_all(lane, wave);
+    if (ntile > 0) tile_dma(0, lds0).issue_all(lane, wave, dma_full);
+    if (ntile > 1) tile_dma(1, lds1).issue_all(lane, wave, dma_full);
     // One tile: wait for `cur` (the next tile's DMA stays in flight), make it
     // visible to all waves, start the DMA two tiles ahead into `nx2` (the
     // buffer every wave finished reading one step ago), compute on `cur`.  The three buffers are distinct LDS objects, so the compiler can
@@ -440,7 +484,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       // the DMA two tiles ahead, issued in one burst here: spread over the
       // score loop, its instructions were measured to slow the loop more
-      if (it + 2 < ntile) tile_dma(it + 2, nx2).issue_all(lane, wave);
+      if (it + 2 < ntile) tile_dma(it + 2, nx2).issue_all(lane, wave, dma_full);
       const int sb = TW == 1 ? 0 : tw;  // this wave's 32-row sub-block of the tile
       const char* buf = cur + sb * 32 * ROWB;
       const int t0 = page_begin * kPage + it * TROWS + sb * 32;
@@ -563,32 +607,72 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
             pb[i / 4][(2 * i) % 8 + 1] = pair[1];
           }
         }
-        // ---- O^T += V^T . P^T: k-step kp (16 tokens) outer, column block cb
-        // inner, so an accumulator's two MFMAs are CB apart.  V^T fragments
-        // run VPF blocks ahead of their MFMAs.
-        constexpr int NV = 2 * CB;
-        constexpr int VPF = 4;
-        i16x4 vt[NV][2];
-        auto load_v = [&](int idx) {
-          const int kp = idx / CB, cb = idx % CB;
+        // ---- O^T += V^T . P^T: k-step kp (16 tokens) outer, column block
+        // inner, so an accumulator's MFMAs are several blocks apart.  V^T
+        // fragments run VPF blocks ahead of their MFMAs.
+        if constexpr (DSPLIT) {
+          // every wave's P to LDS; this wave then takes its d_c/4 columns of
+          // all four head groups: block idx = (kp, cbl) is column block
+          // hg * CBW + cbl, whose swizzle groups start hg * CBW / 2 groups in
+          ldsp[(0 * 2 + lh) * ROWS + hg * 32 + lr] = pb[0];
+          ldsp[(1 * 2 + lh) * ROWS + hg * 32 + lr] = pb[1];
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          const char* vbuf = buf + hg * (CBW / 2) * 128;
+          constexpr int NV = 2 * CBW;
+          constexpr int VPF = 4;
+          i16x4 vt[NV][2];
+          auto load_v = [&](int idx) {
+            const int kp = idx / CBW, cbl = idx % CBW;
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const char* a = buf + v_off[s][cb & 1] + (cb / 2) * 128 + kp * 16 * ROWB;
-            vt[idx][s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
+            for (int s = 0; s < 2; ++s) {
+              const char* a = vbuf + v_off[s][cbl & 1] + (cbl / 2) * 128 + kp * 16 * ROWB;
+              vt[idx][s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
+            }
+          };
+#pragma unroll
+          for (int idx = 0; idx < VPF; ++idx) load_v(idx);
+          bf16x8 px[2][4];
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) px[kp][g] = ldsp[(kp * 2 + lh) * ROWS + g * 32 + lr];
+#pragma unroll
+          for (int idx = 0; idx < NV; ++idx) {
+            if (idx + VPF < NV) load_v(idx + VPF);
+            const int kp = idx / CBW, cbl = idx % CBW;
+            bf16x8 va;
+            __builtin_memcpy(&va, &vt[idx][0], 8);
+            __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vt[idx][1], 8);
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              oacc[g * CBW + cbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, px[kp][g], oacc[g * CBW + cbl], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
           }
-        };
+        } else {
+          constexpr int NV = 2 * CB;
+          constexpr int VPF = 4;
+          i16x4 vt[NV][2];
+          auto load_v = [&](int idx) {
+            const int kp = idx / CB, cb = idx % CB;
 #pragma unroll
-        for (int idx = 0; idx < VPF; ++idx) load_v(idx);
+            for (int s = 0; s < 2; ++s) {
+              const char* a = buf + v_off[s][cb & 1] + (cb / 2) * 128 + kp * 16 * ROWB;
+              vt[idx][s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
+            }
+          };
 #pragma unroll
-        for (int idx = 0; idx < NV; ++idx) {
-          if (idx + VPF < NV) load_v(idx + VPF);
-          bf16x8 va;
-          __builtin_memcpy(&va, &vt[idx][0], 8);
-          __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vt[idx][1], 8);
-          oacc[idx % CB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[idx / CB], oacc[idx % CB], 0, 0, 0);
-          // Keep source order: the reads of block idx + VPF stay above the MFMA
-          // of block idx (the scheduler would otherwise sink them to their use).
-          __builtin_amdgcn_sched_barrier(0);
+          for (int idx = 0; idx < VPF; ++idx) load_v(idx);
+#pragma unroll
+          for (int idx = 0; idx < NV; ++idx) {
+            if (idx + VPF < NV) load_v(idx + VPF);
+            bf16x8 va;
+            __builtin_memcpy(&va, &vt[idx][0], 8);
+            __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vt[idx][1], 8);
+            oacc[idx % CB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[idx / CB], oacc[idx % CB], 0, 0, 0);
+            // Keep source order: the reads of block idx + VPF stay above the MFMA
+            // of block idx (the scheduler would otherwise sink them to their use).
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }();
     };
@@ -679,32 +763,88 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       p.ws_lse[static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H)] = lse_v;
     }
   }
-  constexpr int PIECES = DC / 16;  // 16-byte pieces per half-row
-  static_assert(64 % PIECES == 0, "half-row pieces must tile a wave");
-  constexpr int RPI = 64 / PIECES;  // half-rows per store instruction
+  if constexpr (DSPLIT) {
+    // This wave holds columns (hg * CBW + cbl) * 32 + 8g' + 4h2 + e of rows
+    // g * 32 + r32 at oacc[g * CBW + cbl][4g' + e].  Every row's 1/l goes to
+    // LDS (the P buffer is idle now); then the rows are staged a quarter (32
+    // rows, all d_c columns, bf16) at a time in the idle tile buffers and
+    // written as whole rows by all 256 threads with 16-byte stores.
+    float* ldsl = reinterpret_cast<float*>(ldsp);
+    if (h2 == 0) ldsl[lrow] = inv;
+    __syncthreads();
+    float inv_g[4];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+    for (int g = 0; g < 4; ++g) inv_g[g] = ldsl[g * 32 + r32];
+    constexpr int SROWQ = DC * 2 + 16;  // staging row stride in bytes
+    static_assert(32 * SROWQ <= TILE, "a quarter of the rows must fit one tile buffer");
+    auto stage_quarter = [&](int g, char* st) {
 #pragma unroll
-    for (int cbl = 0; cbl < CB / 2; ++cbl) {
-      const int cb = half * (CB / 2) + cbl;
+      for (int cbl = 0; cbl < CBW; ++cbl)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 pk;
-        pk.x = pack_bf16x2(oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv);
-        pk.y = pack_bf16x2(oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(stage + r32 * SROW + (cbl * 32 + 8 * g + 4 * h2) * 2) = pk;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x16& o = oacc[g * CBW + cbl];
+          uint2 pk;
+          pk.x = pack_bf16x2(o[4 * g4] * inv_g[g], o[4 * g4 + 1] * inv_g[g]);
+          pk.y = pack_bf16x2(o[4 * g4 + 2] * inv_g[g], o[4 * g4 + 3] * inv_g[g]);
+          *reinterpret_cast<uint2*>(st + r32 * SROWQ + ((hg * CBW + cbl) * 32 + 8 * g4 + 4 * h2) * 2) = pk;
+        }
+    };
+    auto store_quarter = [&](int g, const char* st) {
+      constexpr int PIECES = DC * 2 / 16;  // 16-byte pieces per row
+      static_assert(NT % PIECES == 0, "row pieces must tile the workgroup");
+      constexpr int RPI = NT / PIECES;     // rows per store instruction
+#pragma unroll
+      for (int i0 = 0; i0 < 32; i0 += RPI) {
+        const int i = i0 + tid / PIECES;
+        const int pc = tid % PIECES;
+        const int lr = g * 32 + i;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(st + i * SROWQ + pc * 16);
+        if (lr < row_count) {
+          const int64_t row_g = row_base + lr;
+          const int64_t orow = final_out ? row_g : static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
+          *reinterpret_cast<i32x4*>(out_base + orow * DC + pc * 8) = v;
+        }
       }
-    }
-#pragma unroll
-    for (int i0 = 0; i0 < 32; i0 += RPI) {
-      const int i = i0 + lane / PIECES;
-      const int pc = lane % PIECES;
-      const int lr = hg * 32 + i;
-      const i32x4 v = *reinterpret_cast<const i32x4*>(stage + i * SROW + pc * 16);
-      if (lr < row_count) {
-        const int64_t row_g = row_base + lr;
-        const int64_t orow = final_out ? row_g : static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
-        *reinterpret_cast<i32x4*>(out_base + orow * DC + half * (DC / 2) + pc * 8) = v;
+    };
+    stage_quarter(0, lds0);
+    stage_quarter(1, lds1);
+    stage_quarter(2, lds2);
+    __syncthreads();
+    store_quarter(0, lds0);
+    store_quarter(1, lds1);
+    store_quarter(2, lds2);
+    __syncthreads();
+    stage_quarter(3, lds0);
+    __syncthreads();
+    store_quarter(3, lds0);
+  } else {
+    constexpr int PIECES = DC / 16;  // 16-byte pieces per half-row
+    static_assert(64 % PIECES == 0, "half-row pieces must tile a wave");
+    constexpr int RPI = 64 / PIECES;  // half-rows per store instruction
+  #pragma unroll
+    for (int half = 0; half < 2; ++half) {
+  #pragma unroll
+      for (int cbl = 0; cbl < CB / 2; ++cbl) {
+        const int cb = half * (CB / 2) + cbl;
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2 pk;
+          pk.x = pack_bf16x2(oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv);
+          pk.y = pack_bf16x2(oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(stage + r32 * SROW + (cbl * 32 + 8 * g + 4 * h2) * 2) = pk;
+        }
+      }
+  #pragma unroll
+      for (int i0 = 0; i0 < 32; i0 += RPI) {
+        const int i = i0 + lane / PIECES;
+        const int pc = lane % PIECES;
+        const int lr = hg * 32 + i;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(stage + i * SROW + pc * 16);
+        if (lr < row_count) {
+          const int64_t row_g = row_base + lr;
+          const int64_t orow = final_out ? row_g : static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
+          *reinterpret_cast<i32x4*>(out_base + orow * DC + half * (DC / 2) + pc * 8) = v;
+        }
       }
     }
   }
