@@ -47,7 +47,7 @@ namespace mla {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kOverflowLog2 = 64.0f;  // P may reach 2^64 before a split is redone
+constexpr float kOverflowMax = 18446744073709551616.0f;  // 2^64: a lane's sum of P beyond it redoes the split
 // Word 3 of a raw (untyped) buffer resource on gfx9-family parts: 32-bit data
 // format, no swizzle, no index/thread-id addressing.
 constexpr int kBufferWord3 = 0x00020000;
@@ -448,10 +448,11 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   const int ntile = key_hi > page_begin * kPage ? (key_hi - page_begin * kPage + TROWS - 1) / TROWS : 0;
 
   // One pass over the split's pages.  MODE 0: the reference max of a row is
-  // fixed at its first visible key and P = 2^(s - m_ref) may grow up to
-  // 2^kOverflowLog2 (bf16 and float32 hold that easily); a row whose scores
-  // climb further sets `overflow`.  MODE 1: running max only (no PV).
-  // MODE 2: P = 2^(s - m) with the true max m from a MODE 1 pass.
+  // fixed at its first visible key and P = 2^(s - m_ref) may grow; a lane
+  // whose sum of P ends above kOverflowMax (or not finite) sets `overflow`.
+  // Below that bound every P and every partial of O stay far inside the
+  // float32 and bf16 ranges, so the pass is exact.  MODE 1: running max only
+  // (no PV).  MODE 2: P = 2^(s - m) with the true max m from a MODE 1 pass.
   // O is never rescaled inside the loop.
   using Dma = TileDma<D, NT / 64, TROWS>;
   const typename Dma::Full dma_full = Dma::full_offsets(lane, wave);
@@ -553,10 +554,9 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
         // ---- reference max.  Raw scores stay unscaled; the scale (times log2 e)
         // is folded into the exponent's FMA.  Lane (row lr, half lh) holds
         // tokens 8g + 4lh + e at register 4g + e.  Only sub-blocks that cross a
-        // row's last visible key are masked.  The cross-lane row max (one
-        // swap with lane l ^ 32) is needed only while a row has no reference
-        // yet (its first visible sub-block) and in the max-only pass;
-        // otherwise each lane just checks its own scores for overflow.
+        // row's last visible key are masked.  The row max (with one swap with
+        // lane l ^ 32) is needed only while a row has no reference yet (its
+        // first visible sub-block) and in the max-only pass.
         float sv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
@@ -572,12 +572,12 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
               if (t >= (PREFILL ? limit : key_end)) sv[4 * g + e] = ninf;
             }
         }
-        float lmx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) lmx = fmaxf(lmx, sv[i]);
-        lmx *= p.scale_log2;  // this lane's max (scale > 0 keeps the order)
         const bool need_ref = MODE == 1 || __ballot(m_run == -INFINITY) != 0;
         if (need_ref) {
+          float lmx = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) lmx = fmaxf(lmx, sv[i]);
+          lmx *= p.scale_log2;  // this lane's max (scale > 0 keeps the order)
           const float m = pair32_max(lmx);
           if constexpr (MODE == 1)
             m_run = fmaxf(m_run, m);
@@ -585,7 +585,6 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
             m_run = m;  // O and l are still zero: exact
         }
         if constexpr (MODE == 1) return;
-        if constexpr (MODE == 0) overflow |= __ballot(lmx > m_run + kOverflowLog2) != 0;
         // ---- P = 2^(scale*log2e*s - m) rounded to bf16 (hardware RNE, two at a
         // time); registers 8kp .. 8kp+7 are the B operand of k-step kp.
         bf16x8 pb[2];
@@ -681,6 +680,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       if (it + 1 < ntile) tile(it + 1, lds1, lds0);
       if (it + 2 < ntile) tile(it + 2, lds2, lds1);
     }
+    if constexpr (MODE == 0) overflow = __ballot(!(l_part <= kOverflowMax)) != 0;
     return overflow;
   };
 
@@ -693,8 +693,9 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) any_overflow |= reinterpret_cast<const int*>(lds0)[w];
   if (any_overflow) {
-    // Rare: some row's scores rose by more than 2^kOverflowLog2 over its first
-    // visible key.  Redo the split exactly: true max first, then accumulate.
+    // Rare: some row's scores rose so far above its first visible key that
+    // its sum of P passed kOverflowMax.  Redo the split exactly: true max
+    // first, then accumulate.
     __syncthreads();
     m_run = -INFINITY;
     run_pass(std::integral_constant<int, 1>{});
