@@ -454,6 +454,32 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   // float32 and bf16 ranges, so the pass is exact.  MODE 1: running max only
   // (no PV).  MODE 2: P = 2^(s - m) with the true max m from a MODE 1 pass.
   // O is never rescaled inside the loop.
+  // Per-lane LDS byte offsets inside a 32-row sub-block, the same for every
+  // tile: swizzle groups, token halves and column blocks enter as
+  // immediates (rows 16 apart share a swizzle).
+  // K (A operand) of k-step ks: token row r32, chunk 2*ks + h2; group ks/4
+  int k_off[4], k_tail[2];
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) k_off[kq] = r32 * ROWB + phys_chunk<D>(r32, 2 * kq + h2) * 16;
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq) k_tail[kq] = r32 * ROWB + phys_chunk<D>(r32, CHF8 + 2 * kq + h2) * 16;
+  // V^T (A operand) of k-step kp, column block cb, transpose read s:
+  // supplier lane 16g + 4k + q reads token row 16kp + 8s + 4(g/2) + k,
+  // columns cb*32 + 16(g%2) + 4q .. +3; the result gives lane l the
+  // column cb*32 + l%32 at tokens 16kp + 8s + 4h + 0..3, the order in
+  // which the lane holds P.
+  int v_off[2][2];
+  {
+    const int vg = lane >> 4, vk = (lane >> 2) & 3, vq = lane & 3;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int vrow = 8 * s + 4 * (vg >> 1) + vk;
+#pragma unroll
+      for (int co = 0; co < 2; ++co)
+        v_off[s][co] = vrow * ROWB + phys_chunk<D>(vrow, 4 * co + 2 * (vg & 1) + (vq >> 1)) * 16 + (vq & 1) * 8;
+    }
+  }
+
   using Dma = TileDma<D, NT / 64, TROWS>;
   const typename Dma::Full dma_full = Dma::full_offsets(lane, wave);
   auto run_pass = [&](auto mode_tag) -> bool {
@@ -492,35 +518,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       [&] {
         // skip sub-blocks no row of this wave can see (wave-uniform)
         if (t0 >= lim_max) return;
-        // Per-lane LDS byte offsets inside the sub-block, recomputed here
-        // from an opaque lane id rather than held in registers across the
-        // loop; swizzle groups, token halves and column blocks enter as
-        // immediates (rows 16 apart share a swizzle).
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int lr = ln & 31, lh = ln >> 5;
-        // K (A operand) of k-step ks: token row lr, chunk 2*ks + lh; group ks/4
-        int k_off[4], k_tail[2];
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) k_off[kq] = lr * ROWB + phys_chunk<D>(lr, 2 * kq + lh) * 16;
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) k_tail[kq] = lr * ROWB + phys_chunk<D>(lr, CHF8 + 2 * kq + lh) * 16;
-        // V^T (A operand) of k-step kp, column block cb, transpose read s:
-        // supplier lane 16g + 4k + q reads token row 16kp + 8s + 4(g/2) + k,
-        // columns cb*32 + 16(g%2) + 4q .. +3; the result gives lane l the
-        // column cb*32 + l%32 at tokens 16kp + 8s + 4h + 0..3, the order in
-        // which the lane holds P.
-        int v_off[2][2];
-        {
-          const int vg = ln >> 4, vk = (ln >> 2) & 3, vq = ln & 3;
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const int vrow = 8 * s + 4 * (vg >> 1) + vk;
-#pragma unroll
-            for (int co = 0; co < 2; ++co)
-              v_off[s][co] = vrow * ROWB + phys_chunk<D>(vrow, 4 * co + 2 * (vg & 1) + (vq >> 1)) * 16 + (vq & 1) * 8;
-          }
-        }
+        const int lr = lane & 31, lh = lane >> 5;
         // ---- S^T = K . Q^T over D, one accumulator (dependent accumulation
         // issues back to back at full rate)
         f32x16 sacc;
@@ -883,6 +881,20 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
   bf16_t* out = static_cast<bf16_t*>(p.out_latent) + row * DC;
   const float* lse_s = p.ws_lse + static_cast<int64_t>(base) * H + head;  // split s at lse_s[s * H]
   const bf16_t* part = p.ws_o + (static_cast<int64_t>(base) * H + head) * DC + lane * PER;
+  // Splits go four a round, every load of a round issued before its use; the
+  // first round's loads go out before the lse max, so they share its wait.
+  constexpr int U = 4;
+  bf16_t v[U][PER];
+  float w[U];
+  auto load_round = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u < ns_b ? s0 + u : s0;
+      __builtin_memcpy(v[u], part + static_cast<int64_t>(s) * H * DC, PER * sizeof(bf16_t));
+      w[u] = s0 + u < ns_b ? lse_s[static_cast<int64_t>(s) * H] : -INFINITY;
+    }
+  };
+  load_round(0);
   // max of the splits' lse, the lanes taking splits side by side
   float m = -INFINITY;
   for (int s0 = 0; s0 < ns_b; s0 += 64)
@@ -894,17 +906,8 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float wsum = 0.f;
   if (m != -INFINITY) {
-    // four splits a round, every load of the round issued before its use
-    constexpr int U = 4;
     for (int s0 = 0; s0 < ns_b; s0 += U) {
-      bf16_t v[U][PER];
-      float w[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = s0 + u < ns_b ? s0 + u : s0;
-        __builtin_memcpy(v[u], part + static_cast<int64_t>(s) * H * DC, PER * sizeof(bf16_t));
-        w[u] = s0 + u < ns_b ? lse_s[static_cast<int64_t>(s) * H] : -INFINITY;
-      }
+      if (s0 > 0) load_round(s0);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float wu = __expf(w[u] - m);
