@@ -80,6 +80,18 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Workgroup order on the XCDs.  Consecutive workgroups are dealt to the eight
+// XCDs in turn, and each XCD has its own L2; when the grid is a multiple of
+// 32, workgroup x takes work index xcd_local(x), which puts every run of four
+// consecutive work indices (the splits of one sequence, or neighbouring query
+// blocks, which read the same rows) on one XCD while dispatch still follows
+// the index order to within 32.  A bijection on [0, n).
+__device__ __forceinline__ int64_t xcd_local(int64_t x, int64_t n) {
+  if (n % 32 != 0) return x;
+  const int64_t k = x % 8, j = x / 8;
+  return ((j / 4) * 8 + k) * 4 + j % 4;
+}
+
 struct DecodeItem {
   int b, s, n_s, slot;
   bool ok;
@@ -332,7 +344,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   int slot = 0;
   const int lrow = hg * 32 + r32;
   if constexpr (PREFILL) {
-    const PrefillBlock pb = find_prefill_block(p, p.n_blocks - 1 - static_cast<int64_t>(blockIdx.x), ROWS);
+    const int64_t wg = xcd_local(blockIdx.x, gridDim.x);
+    const PrefillBlock pb = find_prefill_block(p, p.n_blocks - 1 - wg, ROWS);
     if (!pb.ok) return;
     b = __builtin_amdgcn_readfirstlane(pb.b);
     const int nq = __builtin_amdgcn_readfirstlane(p.cu_q[b + 1] - p.cu_q[b]);
@@ -346,8 +359,9 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     row_count = nq * H - r0;
     limit = lrow < row_count ? q0 + (r0 + lrow) / H + 1 : 0;
   } else {
-    const int64_t item = static_cast<int64_t>(blockIdx.x) / p.n_head_chunks;
-    const int hc = static_cast<int>(static_cast<int64_t>(blockIdx.x) % p.n_head_chunks);
+    const int64_t wg = xcd_local(blockIdx.x, gridDim.x);
+    const int64_t item = wg / p.n_head_chunks;
+    const int hc = static_cast<int>(wg % p.n_head_chunks);
     const DecodeItem it = find_decode_item(p, item);
     if (!it.ok || it.slot >= p.n_items) return;
     // the item is wave-uniform: keep it in scalar registers
