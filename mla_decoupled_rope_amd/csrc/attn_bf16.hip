@@ -199,7 +199,7 @@ struct TileDma {
   static constexpr int N = 9 * GPW;  // instructions per issuing wave
   static_assert(RG * CH == 576 && TROWS % RG == 0 && (NG < NW || NG % NW == 0), "tile must split into row groups");
   __amdgpu_buffer_rsrc_t rsrc;
-  char* lds_buf;
+  lds_char_t* lds_buf;  // LDS address of the tile buffer
   int valid_rows;
   bool active;  // wave-uniform: this wave has instructions to issue for this tile
 
@@ -209,7 +209,7 @@ struct TileDma {
   // tile would read zeros; none are formed.
   __device__ __forceinline__ TileDma(char* dst, const char* src, int valid, bool on, int wave)
       : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), 0, TROWS * ROWB, kBufferWord3)),
-        lds_buf(dst), valid_rows(valid), active(on && (NG >= NW || wave < NG)) {}
+        lds_buf(reinterpret_cast<lds_char_t*>(reinterpret_cast<uintptr_t>(dst))), valid_rows(valid), active(on && (NG >= NW || wave < NG)) {}
 
   // Byte offset in the tile of a lane's 16 bytes in instruction i (0 <= i <
   // N, a compile-time constant at every call site) of wave `wave`, for a
@@ -241,14 +241,19 @@ struct TileDma {
   __device__ __forceinline__ void issue_at(int i, int wave, uint32_t off) const {
     const int gg = i / 9, kk = i % 9;
     const int g = NG >= NW ? wave * GPW + gg : wave;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds_buf + g * RG * ROWB + kk * 1024), 16, off, 0, 0,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_buf + g * RG * ROWB + kk * 1024, 16, off, 0, 0,
                                              0);
+  }
+  // A full tile (valid_rows == TROWS) from the precomputed offsets.
+  __device__ __forceinline__ void issue_full(int wave, const Full& f) const {
+    if (!active) return;
+#pragma unroll
+    for (int i = 0; i < N; ++i) issue_at(i, wave, (f.v[i / 2] >> (16 * (i % 2))) & 0xffffu);
   }
   __device__ __forceinline__ void issue_all(int lane, int wave, const Full& f) const {
     if (!active) return;
     if (valid_rows == TROWS) {
-#pragma unroll
-      for (int i = 0; i < N; ++i) issue_at(i, wave, (f.v[i / 2] >> (16 * (i % 2))) & 0xffffu);
+      issue_full(wave, f);
     } else {
       // the last tile of a sequence: offsets recomputed from an opaque lane
       // id (not hoisted into more registers)
@@ -291,6 +296,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   constexpr int D = DC + DR;
   constexpr int ROWB = D * 2;       // bytes per cache row
   constexpr int NT = 64 * HG * TW;
+  constexpr int NW = NT / 64;       // waves
   constexpr int ROWS = 32 * HG;
   constexpr int KS = D / 16;        // 16-wide k steps of the score contraction
   // Four head groups of one token lane split P.V by columns of O: each wave
@@ -494,7 +500,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     }
   }
 
-  using Dma = TileDma<D, NT / 64, TROWS>;
+  using Dma = TileDma<D, NW, TROWS>;
   const typename Dma::Full dma_full = Dma::full_offsets(lane, wave);
   auto run_pass = [&](auto mode_tag) -> bool {
     constexpr int MODE = decltype(mode_tag)::value;
@@ -523,15 +529,25 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       // flight.  Every LDS read of the previous tile has been consumed by an
       // MFMA by now; the memory clobber keeps this tile's reads below it.
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      // the DMA two tiles ahead, issued in one burst here: spread over the
-      // score loop, its instructions were measured to slow the loop more
-      if (it + 2 < ntile) tile_dma(it + 2, nx2).issue_all(lane, wave, dma_full);
+      // The DMA two tiles ahead.  The CU's address unit takes a 1 KiB
+      // instruction about every 16 cycles and stalls the issuing wave while
+      // busy, so the waves take turns: wave w issues its burst at score
+      // k-step w * KS / NW, while the others keep their MFMAs going.
+      const bool dma_on = it + 2 < ntile;
+      const Dma dma = tile_dma(dma_on ? it + 2 : ntile - 1, nx2);  // issued only when dma_on
+      constexpr int DMA_KSTEP = KS / NW;
+      // a sequence's last, partial tile takes the slow offsets, in one burst here
+      const bool dma_turn = dma_on && dma.valid_rows == TROWS;
+      if (dma_on && !dma_turn) dma.issue_all(lane, wave, dma_full);
       const int sb = TW == 1 ? 0 : tw;  // this wave's 32-row sub-block of the tile
       const char* buf = cur + sb * 32 * ROWB;
       const int t0 = page_begin * kPage + it * TROWS + sb * 32;
       [&] {
         // skip sub-blocks no row of this wave can see (wave-uniform)
-        if (t0 >= lim_max) return;
+        if (t0 >= lim_max) {
+          if (dma_turn) dma.issue_full(wave, dma_full);
+          return;
+        }
         const int lr = lane & 31, lh = lane >> 5;
         // ---- S^T = K . Q^T over D, one accumulator (dependent accumulation
         // issues back to back at full rate)
@@ -554,6 +570,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           if (ks + KPF < KS) load_k(ks + KPF);
+          if (ks % DMA_KSTEP == 0 && ks / DMA_KSTEP < NW && ks / DMA_KSTEP == wave && dma_turn)
+            dma.issue_full(wave, dma_full);
           const bf16x8& qb = ks < KSQ ? qf[ks < KSQ ? ks : 0] : qr[ks];
           if (ks == 0)
             mfma_qk_first(sacc, ka[ks], qb);
