@@ -640,43 +640,47 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
         // inner, so an accumulator's MFMAs are several blocks apart.  V^T
         // fragments run VPF blocks ahead of their MFMAs.
         if constexpr (DSPLIT) {
-          // every wave's P to LDS; this wave then takes its d_c/4 columns of
-          // all four head groups: block idx = (kp, cbl) is column block
-          // hg * CBW + cbl, whose swizzle groups start hg * CBW / 2 groups in
-          ldsp[(0 * 2 + lh) * ROWS + hg * 32 + lr] = pb[0];
-          ldsp[(1 * 2 + lh) * ROWS + hg * 32 + lr] = pb[1];
-          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          // This wave takes its d_c/4 columns of all four head groups: block
+          // idx = (kp, cbl) is column block hg * CBW + cbl, whose swizzle
+          // groups start hg * CBW / 2 groups in.  Accumulator slot j holds
+          // head group (hg + j) mod 4, so slot 0 is the wave's own group,
+          // whose P is already in registers: its MFMAs go first and run
+          // while the waves meet at the barrier that publishes every P.
+          // Every V^T fragment of the tile is read up front (the tile has
+          // been visible since the ring barrier).
           const char* vbuf = buf + hg * (CBW / 2) * 128;
           constexpr int NV = 2 * CBW;
-          constexpr int VPF = 4;
-          i16x4 vt[NV][2];
-          auto load_v = [&](int idx) {
+          bf16x8 va[NV];
+#pragma unroll
+          for (int idx = 0; idx < NV; ++idx) {
             const int kp = idx / CBW, cbl = idx % CBW;
+            i16x4 t[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
               const char* a = vbuf + v_off[s][cbl & 1] + (cbl / 2) * 128 + kp * 16 * ROWB;
-              vt[idx][s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
+              t[s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
             }
-          };
+            __builtin_memcpy(&va[idx], &t[0], 8);
+            __builtin_memcpy(reinterpret_cast<char*>(&va[idx]) + 8, &t[1], 8);
+          }
+          ldsp[(0 * 2 + lh) * ROWS + hg * 32 + lr] = pb[0];
+          ldsp[(1 * 2 + lh) * ROWS + hg * 32 + lr] = pb[1];
 #pragma unroll
-          for (int idx = 0; idx < VPF; ++idx) load_v(idx);
+          for (int idx = 0; idx < NV; ++idx)
+            oacc[idx % CBW] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[idx], pb[idx / CBW], oacc[idx % CBW], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           bf16x8 px[2][4];
 #pragma unroll
           for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) px[kp][g] = ldsp[(kp * 2 + lh) * ROWS + g * 32 + lr];
+            for (int j = 1; j < 4; ++j) px[kp][j] = ldsp[(kp * 2 + lh) * ROWS + ((hg + j) & 3) * 32 + lr];
 #pragma unroll
-          for (int idx = 0; idx < NV; ++idx) {
-            if (idx + VPF < NV) load_v(idx + VPF);
-            const int kp = idx / CBW, cbl = idx % CBW;
-            bf16x8 va;
-            __builtin_memcpy(&va, &vt[idx][0], 8);
-            __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vt[idx][1], 8);
+          for (int idx = 0; idx < NV; ++idx)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-              oacc[g * CBW + cbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, px[kp][g], oacc[g * CBW + cbl], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+            for (int j = 1; j < 4; ++j)
+              oacc[j * CBW + idx % CBW] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[idx], px[idx / CBW][j], oacc[j * CBW + idx % CBW], 0, 0, 0);
         } else {
           constexpr int NV = 2 * CB;
           constexpr int VPF = 4;
@@ -796,31 +800,32 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   }
   if constexpr (DSPLIT) {
     // This wave holds columns (hg * CBW + cbl) * 32 + 8g' + 4h2 + e of rows
-    // g * 32 + r32 at oacc[g * CBW + cbl][4g' + e].  Every row's 1/l goes to
-    // LDS (the P buffer is idle now); then the rows are staged a quarter (32
-    // rows, all d_c columns, bf16) at a time in the idle tile buffers and
-    // written as whole rows by all 256 threads with 16-byte stores.
+    // q * 32 + r32, q = (hg + j) mod 4, at oacc[j * CBW + cbl][4g' + e].
+    // Every row's 1/l goes to LDS (the P buffer is idle now); then the rows
+    // are staged a quarter (32 rows, all d_c columns, bf16) per idle tile
+    // buffer and written as whole rows by all threads with 16-byte stores:
+    // quarters 0-2 first, then quarter 3.
     float* ldsl = reinterpret_cast<float*>(ldsp);
     if (h2 == 0) ldsl[lrow] = inv;
     __syncthreads();
-    float inv_g[4];
+    float inv_s[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) inv_g[g] = ldsl[g * 32 + r32];
+    for (int j = 0; j < 4; ++j) inv_s[j] = ldsl[((hg + j) & 3) * 32 + r32];
     constexpr int SROWQ = DC * 2 + 16;  // staging row stride in bytes
     static_assert(32 * SROWQ <= TILE, "a quarter of the rows must fit one tile buffer");
-    auto stage_quarter = [&](int g, char* st) {
+    auto stage_slot = [&](int j, char* st) {
 #pragma unroll
       for (int cbl = 0; cbl < CBW; ++cbl)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x16& o = oacc[g * CBW + cbl];
+          const f32x16& o = oacc[j * CBW + cbl];
           uint2 pk;
-          pk.x = pack_bf16x2(o[4 * g4] * inv_g[g], o[4 * g4 + 1] * inv_g[g]);
-          pk.y = pack_bf16x2(o[4 * g4 + 2] * inv_g[g], o[4 * g4 + 3] * inv_g[g]);
+          pk.x = pack_bf16x2(o[4 * g4] * inv_s[j], o[4 * g4 + 1] * inv_s[j]);
+          pk.y = pack_bf16x2(o[4 * g4 + 2] * inv_s[j], o[4 * g4 + 3] * inv_s[j]);
           *reinterpret_cast<uint2*>(st + r32 * SROWQ + ((hg * CBW + cbl) * 32 + 8 * g4 + 4 * h2) * 2) = pk;
         }
     };
-    auto store_quarter = [&](int g, const char* st) {
+    auto store_quarter = [&](int q, const char* st) {
       constexpr int PIECES = DC * 2 / 16;  // 16-byte pieces per row
       static_assert(NT % PIECES == 0, "row pieces must tile the workgroup");
       constexpr int RPI = NT / PIECES;     // rows per store instruction
@@ -828,7 +833,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       for (int i0 = 0; i0 < 32; i0 += RPI) {
         const int i = i0 + tid / PIECES;
         const int pc = tid % PIECES;
-        const int lr = g * 32 + i;
+        const int lr = q * 32 + i;
         const i32x4 v = *reinterpret_cast<const i32x4*>(st + i * SROWQ + pc * 16);
         if (lr < row_count) {
           const int64_t row_g = row_base + lr;
@@ -837,15 +842,19 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
         }
       }
     };
-    stage_quarter(0, lds0);
-    stage_quarter(1, lds1);
-    stage_quarter(2, lds2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = (hg + j) & 3;  // wave-uniform
+      if (q < 3) stage_slot(j, q == 0 ? lds0 : (q == 1 ? lds1 : lds2));
+    }
     __syncthreads();
     store_quarter(0, lds0);
     store_quarter(1, lds1);
     store_quarter(2, lds2);
     __syncthreads();
-    stage_quarter(3, lds0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (((hg + j) & 3) == 3) stage_slot(j, lds0);
     __syncthreads();
     store_quarter(3, lds0);
   } else {
