@@ -618,24 +618,25 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
         // ---- P = 2^(scale*log2e*s - m) rounded to bf16 (hardware RNE, two at a
         // time); registers 8kp .. 8kp+7 are the B operand of k-step kp.
         bf16x8 pb[2];
-        {
-          // a row still without a reference has only masked (-inf) scores here,
-          // which give 0 against any finite reference
-          const float m_use = __builtin_fmaxf(m_run, -FLT_MAX);
-          float pf[16];
+        // a row still without a reference has only masked (-inf) scores here,
+        // which give 0 against any finite reference
+        const float m_use = __builtin_fmaxf(m_run, -FLT_MAX);
+        // P of k-step kp into pb[kp]; returns its float32 sum
+        auto p_half = [&](int kp) -> float {
+          float pf[8];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], p.scale_log2, -m_use));
-          float lsum = 0.f;
+          for (int e = 0; e < 8; ++e) pf[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[8 * kp + e], p.scale_log2, -m_use));
 #pragma unroll
-          for (int i = 0; i < 16; ++i) lsum += pf[i];
-          l_part += lsum;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
+          for (int i = 0; i < 4; ++i) {
             const bf16x2 pair = __builtin_convertvector((f32x2){pf[2 * i], pf[2 * i + 1]}, bf16x2);
-            pb[i / 4][(2 * i) % 8] = pair[0];
-            pb[i / 4][(2 * i) % 8 + 1] = pair[1];
+            pb[kp][2 * i] = pair[0];
+            pb[kp][2 * i + 1] = pair[1];
           }
-        }
+          float sum = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum += pf[e];
+          return sum;
+        };
         // ---- O^T += V^T . P^T: k-step kp (16 tokens) outer, column block
         // inner, so an accumulator's MFMAs are several blocks apart.  V^T
         // fragments run VPF blocks ahead of their MFMAs.
@@ -663,12 +664,17 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
             __builtin_memcpy(&va[idx], &t[0], 8);
             __builtin_memcpy(reinterpret_cast<char*>(&va[idx]) + 8, &t[1], 8);
           }
-          ldsp[(0 * 2 + lh) * ROWS + hg * 32 + lr] = pb[0];
-          ldsp[(1 * 2 + lh) * ROWS + hg * 32 + lr] = pb[1];
+          // P a k-step at a time: the exponentials of k-step 1 issue under the
+          // own-group MFMAs of k-step 0
 #pragma unroll
-          for (int idx = 0; idx < NV; ++idx)
-            oacc[idx % CBW] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[idx], pb[idx / CBW], oacc[idx % CBW], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int kp = 0; kp < 2; ++kp) {
+            l_part += p_half(kp);
+            ldsp[(kp * 2 + lh) * ROWS + hg * 32 + lr] = pb[kp];
+#pragma unroll
+            for (int cbl = 0; cbl < CBW; ++cbl)
+              oacc[cbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kp * CBW + cbl], pb[kp], oacc[cbl], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           bf16x8 px[2][4];
 #pragma unroll
@@ -682,6 +688,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
               oacc[j * CBW + idx % CBW] =
                   __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[idx], px[idx / CBW][j], oacc[j * CBW + idx % CBW], 0, 0, 0);
         } else {
+          l_part += p_half(0);
+          l_part += p_half(1);
           constexpr int NV = 2 * CB;
           constexpr int VPF = 4;
           i16x4 vt[NV][2];
