@@ -12,30 +12,30 @@
 // Every head of a query reads the same cache row ("Latent Attention Meets
 // RoPE": one latent and one shared position key per token), so a workgroup
 // takes 32*HG rows (heads, or (query, head) pairs in prefill) against one
-// stream of 64-token pages, and both products are dense MFMA contractions:
-//   S^T[token, row]  = K[token, 0:D]  . Q^T[0:D, row]    (v_mfma 16x16x32 bf16)
+// stream of cache tiles, and both products are dense MFMA contractions:
+//   S^T[token, row]  = K[token, 0:D]  . Q^T[0:D, row]    (v_mfma 32x32x16 bf16)
 //   O^T[c, row]     += V^T[c, token] . P^T[token, row]
 // Layout per workgroup:
-//   * Q for the wave's 32 rows stays in VGPRs for the whole split (D/4 regs);
-//   * O (32 rows x d_c, float32) stays in accumulators (d_c/2 regs);
-//   * each page (64 x D bf16, 72 KB at D = 576) is copied HBM -> LDS once by
-//     16-byte global_load_lds DMA, double buffered, and read by every wave;
-//     16-byte chunks are XOR-swizzled within groups of 8 by bits 1-2 of the
-//     row.  With 64 four-byte banks and 1152-byte rows (odd rows start half
-//     way round the banks), that puts every phase of a K read (16 lanes: 16
-//     rows, one chunk each) and every half-wave of a V transpose read (8 rows
-//     x 2 chunks x 8 bytes) on distinct banks;
-//   * V^T fragments come from the same page with ds_read_tr16_b64, which
+//   * Q for a wave's 32 rows: most k-steps in VGPRs, the rest in LDS;
+//   * O in float32 accumulators (AGPRs).  With four head groups the P.V
+//     product is split by columns: each wave accumulates d_c/4 columns of
+//     all rows, P is exchanged through LDS once per tile, and one V^T
+//     transpose read serves four head groups;
+//   * the cache streams HBM -> LDS by 16-byte buffer-load DMA into a ring of
+//     three 32-row tiles, read by every wave; 16-byte chunks are
+//     XOR-swizzled so every K read phase and V^T transpose half-wave hits
+//     distinct banks;
+//   * V^T fragments come from the same tile with ds_read_tr16_b64, which
 //     turns four 8-byte row pieces into one token-contiguous column piece;
 //   * softmax in base 2 without rescaling O inside the loop: each row's
 //     reference max is fixed at its first visible key and P = 2^(s - m_ref)
-//     may grow to 2^64 (bf16 and float32 hold it); if a row's scores climb
-//     further the workgroup redoes the split exactly in two passes (true max,
-//     then accumulate).  The same data always takes the same path, so the
-//     result is deterministic.  (A VALU rescale of the 256 accumulator
-//     registers would force them out of AGPRs and spill.)
+//     may grow; a lane whose sum of P ends too large makes the workgroup redo
+//     the split exactly in two passes (true max, then accumulate).  The same
+//     data always takes the same path, so the result is deterministic.  (A
+//     VALU rescale of the 256 accumulator registers would force them out of
+//     AGPRs and spill.)
 // Tokens past the end of a sequence are masked; their LDS rows are filled
-// from the last valid row of the page, so garbage or NaN in unused page
+// from the last valid row of the tile, so garbage or NaN in unused page
 // slots never reaches the accumulators.
 #include <cfloat>
 #include <type_traits>
