@@ -56,6 +56,51 @@ def prefill_flops(case) -> float:
     return 2.0 * s.n_heads * (s.row + s.d_latent) * pairs
 
 
+class DeviceEvents:
+    """HIP events on the launch stream, recorded with a device-scope release.
+
+    torch's events take a system-scope release at every record, which writes
+    back L2 and stalls the queue for several microseconds around the timed
+    call; a device-scope release (hipEventReleaseToDevice) orders the same
+    work without that flush.  The events come from the HIP runtime the
+    process has loaded (the one torch and libmla share).
+    """
+
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self, n: int):
+        import ctypes
+
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+        self.hip = ctypes.CDLL(path)
+        self.ct = ctypes
+        self.events = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(self.RELEASE_TO_DEVICE)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.events.append(e)
+        self.used = 0
+
+    def record(self, stream_handle: int):
+        e = self.events[self.used]
+        self.used += 1
+        if self.hip.hipEventRecord(e, self.ct.c_void_p(stream_handle)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
 def load_traffic(config_name: str):
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -142,6 +187,8 @@ def main():
     w_uk, w_uv = dev(case.w_uk), dev(case.w_uv)
     q_nope, q_rope = dev(case.qc), dev(case.qr)
     stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    events = DeviceEvents(2 * args.steps)
     ev = []
 
     if case.kind == "decode":
@@ -155,13 +202,11 @@ def main():
                          kv_latent=new_lat, k_rope=new_kr, kv_seq=st.kv_seq, kv_pos=st.q_pos)
             B.absorb_q(dims, q_nope, w_uk, st.q_lat)
             if timed:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
+                e0 = events.record(sh)
             B.decode(dims, st.cache.data, st.cache.block_table, st.q_lat, st.seq_lens, st.seq_lens_host,
                      st.out_latent, st.lse, st.workspace)
             if timed:
-                e1.record(stream)
-                ev.append((e0, e1))
+                ev.append((e0, events.record(sh)))
             B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = case.batch
         kernel_name = "mla_decode (split attention + merge)"
@@ -176,13 +221,11 @@ def main():
             B.rope_apply(dims, None, None, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat)
             B.absorb_q(dims, q_nope, w_uk, st.q_lat)
             if timed:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
+                e0 = events.record(sh)
             B.prefill(dims, st.cache.data, st.cache.block_table, st.q_lat, st.cu_q, st.q_start, st.cu_q_host,
                       st.q_start_host, st.out_latent, st.lse)
             if timed:
-                e1.record(stream)
-                ev.append((e0, e1))
+                ev.append((e0, events.record(sh)))
             B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = int(case.cu_q[-1])
         kernel_name = "mla_prefill (causal attention)"
@@ -198,7 +241,8 @@ def main():
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_per_step = el / args.steps * 1e3
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kern_ms = float(np.mean([events.elapsed_ms(a, b) for a, b in ev]))
+    events.close()
     achieved = algo / (kern_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
     traffic = load_traffic(args.config)
     out = {

@@ -270,6 +270,8 @@ mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache, co
     p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
     p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
   }
+  p.q_vec = dims->d_rope % 8 == 0 && reinterpret_cast<uintptr_t>(q_rope) % 16 == 0 &&
+            reinterpret_cast<uintptr_t>(q_lat) % 16 == 0;
   for (int j = 0; j < dims->d_rope / 2; ++j) p.theta[j] = std::pow(dims->rope_base, -2.0 * j / dims->d_rope);
   const hipError_t e = mla::launch_rope(p, as_stream(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "rope launch");

@@ -74,6 +74,7 @@ struct RopeParams {
   const void* q_rope; const int32_t* q_pos; int64_t n_q; void* q_lat;
   const void* kv_latent; const void* k_rope; const int32_t* kv_seq; const int32_t* kv_pos; int64_t n_kv;
   void* cache; int64_t num_pages; const int32_t* block_table; int32_t num_seqs; int32_t max_pages;
+  int q_vec;  // query pairs in 16-byte vectors: d_rope % 8 == 0 and q_rope, q_lat 16-byte aligned
   double theta[64];  // theta_j, j < d_rope / 2 (float64, from the host)
 };
 

@@ -7,10 +7,13 @@
 // position, so decode needs no positions at all (R_m^T R_t depends only on
 // t - m, "Detailed Illustration of the Problem", Step 3).
 //
-// One 64-lane wave per row: a query row (n, h) rotates q^R into the tail of
-// q_lat; a cache row copies c_t and writes R_t k^R_t into its page slot.
+// A query n is one workgroup: every head of a query shares its position, so
+// the d_r/2 angles are computed once (float64) into LDS and all heads'
+// pairs are rotated from there with 16-byte loads and stores.  A cache row
+// is one 64-lane wave: it copies c_t and writes R_t k^R_t into its page slot.
 // Angles p * theta_j and sin / cos are float64 (positions reach 2^17, where a
-// float32 angle would be off by ~1e-2 rad).
+// float32 angle would be off by ~1e-2 rad); the rotation is float64 too,
+// rounded once to the output type.
 #include "common.hpp"
 
 namespace mla {
@@ -37,20 +40,53 @@ __device__ __forceinline__ void rotate_pairs(const RopeParams& p, const T* src, 
   }
 }
 
+// Blocks [0, n_q): one query each.  Blocks after that: four cache rows each.
+// Queries without 16-byte vectors (q_vec == 0) take one wave per row.
 template <typename T, typename TQ>
 __global__ void __launch_bounds__(256) rope_kernel(RopeParams p) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
-  const int64_t nq_rows = p.n_q * p.n_heads;
   const int64_t width = p.d_latent + p.d_rope;
-  if (row < nq_rows) {
-    const int pos = p.q_pos[row / p.n_heads];
-    const T* src = static_cast<const T*>(p.q_rope) + row * p.d_rope;
-    TQ* dst = static_cast<TQ*>(p.q_lat) + row * width + p.d_latent;
-    rotate_pairs<T, TQ>(p, src, dst, pos, lane);
+  const int half = p.d_rope / 2;
+  const bool vec = p.q_vec != 0;
+  const int64_t q_blocks = vec ? p.n_q : (p.n_q * p.n_heads + 3) / 4;
+  if (static_cast<int64_t>(blockIdx.x) < q_blocks) {
+    if (!vec) {
+      const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / 64;
+      if (row >= p.n_q * p.n_heads) return;
+      const T* src = static_cast<const T*>(p.q_rope) + row * p.d_rope;
+      TQ* dst = static_cast<TQ*>(p.q_lat) + row * width + p.d_latent;
+      rotate_pairs<T, TQ>(p, src, dst, p.q_pos[row / p.n_heads], lane);
+      return;
+    }
+    __shared__ double cs[64], sn[64];
+    const int64_t n = blockIdx.x;
+    const int pos = p.q_pos[n];
+    if (threadIdx.x < half) sincos(static_cast<double>(pos) * p.theta[threadIdx.x], &sn[threadIdx.x], &cs[threadIdx.x]);
+    __syncthreads();
+    // 8 consecutive elements (4 pairs) of one head per step
+    const int per_head = p.d_rope / 8;
+    const int pieces = p.n_heads * per_head;
+    for (int k = threadIdx.x; k < pieces; k += 256) {
+      const int h = k / per_head, e0 = (k % per_head) * 8;
+      const int64_t row = n * p.n_heads + h;
+      const T* src = static_cast<const T*>(p.q_rope) + row * p.d_rope + e0;
+      TQ* dst = static_cast<TQ*>(p.q_lat) + row * width + p.d_latent + e0;
+      T x[8];
+      __builtin_memcpy(x, __builtin_assume_aligned(src, 16), sizeof(x));
+      TQ y[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = e0 / 2 + i;
+        const double x0 = ld(x, 2 * i), x1 = ld(x, 2 * i + 1);
+        const double c = cs[j], sj = sn[j];
+        st(y, 2 * i, x0 * c - x1 * sj);
+        st(y, 2 * i + 1, x0 * sj + x1 * c);
+      }
+      __builtin_memcpy(__builtin_assume_aligned(dst, 16), y, sizeof(y));
+    }
     return;
   }
-  const int64_t m = row - nq_rows;
+  const int64_t m = (static_cast<int64_t>(blockIdx.x) - q_blocks) * 4 + threadIdx.x / 64;
   if (m >= p.n_kv) return;
   const int b = p.kv_seq[m];
   const int pos = p.kv_pos[m];
@@ -66,9 +102,10 @@ __global__ void __launch_bounds__(256) rope_kernel(RopeParams p) {
 }
 
 hipError_t launch_rope(const RopeParams& p, hipStream_t s) {
-  const int64_t rows = p.n_q * p.n_heads + p.n_kv;
-  if (rows == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  const int64_t q_blocks = p.q_vec ? p.n_q : (p.n_q * p.n_heads + 3) / 4;
+  const int64_t blocks = q_blocks + (p.n_kv + 3) / 4;
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(blocks));
   if (p.dtype == 0)
     hipLaunchKernelGGL((rope_kernel<float, float>), grid, dim3(256), 0, s, p);
   else if (p.q_lat_dtype == 0)
