@@ -31,9 +31,13 @@ __device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
 }
 
 // W_UK tile [d_head rows (i), 128 cols (j)] in LDS; each wave owns 32 j x 64 n.
+// A 64-token chunk of q^C goes through LDS once per workgroup (rows padded to
+// 288 bytes: conflict-free fragment reads) instead of once per wave.
 template <int DH, typename TQ>
 __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t w_lds[DH * kAbsorbLdsStride];
+  constexpr int QS = DH + 16;  // q^C row stride in LDS (elements)
+  __shared__ __attribute__((aligned(16))) bf16_t q_lds[64 * QS];
   const int h = blockIdx.y;
   const int j0 = blockIdx.x * kAbsorbJTile;
   const int tid = threadIdx.x;
@@ -49,16 +53,27 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
   const int64_t n_end = min(p.n, n_begin + kAbsorbNChunk);
   const int q16 = lane >> 4, r16 = lane & 15;
   const int jw = wave * 32;  // this wave's j offset inside the tile
-  // The B fragments (64 tokens x DH) of a chunk, all in flight at once.
-  bf16x8 bq[DH / 32][4];
+  // A chunk of q^C (64 tokens x DH): this thread's 16-byte pieces, loaded
+  // together and then stored to LDS.
+  constexpr int QPT = 64 * (DH / 8) / 256;  // pieces per thread
+  static_assert(QPT * 256 == 64 * (DH / 8), "q chunk pieces must split evenly over the threads");
+  bf16x8 qv[QPT];
   auto load_q = [&](int64_t nb0) {
 #pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks)
+    for (int k = 0; k < QPT; ++k) {
+      const int c = tid + k * 256;
+      const int r = c / (DH / 8), cc = c % (DH / 8);
+      const int64_t n = nb0 + r;
+      qv[k] = n < n_end ? load8(q + (n * H + h) * DH + cc * 8) : bf16x8{};
+    }
+  };
+  auto store_q = [&] {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int64_t n = nb0 + nb * 16 + r16;
-        bq[ks][nb] = n < n_end ? load8(q + (n * H + h) * DH + ks * 32 + q16 * 8) : bf16x8{};
-      }
+    for (int k = 0; k < QPT; ++k) {
+      const int c = tid + k * 256;
+      const int r = c / (DH / 8), cc = c % (DH / 8);
+      *reinterpret_cast<bf16x8*>(&q_lds[r * QS + cc * 8]) = qv[k];
+    }
   };
   // The first chunk's queries load together with the W tile: one memory round trip.
   load_q(n_begin);
@@ -77,9 +92,22 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
     const int row = c / (kAbsorbJTile / 8), cc = c % (kAbsorbJTile / 8);
     *reinterpret_cast<bf16x8*>(&w_lds[row * kAbsorbLdsStride + cc * 8]) = wv[k];
   }
+  store_q();
   __syncthreads();
   for (int64_t nb0 = n_begin; nb0 < n_end; nb0 += 64) {
-    if (nb0 != n_begin) load_q(nb0);
+    if (nb0 != n_begin) {
+      load_q(nb0);
+      __syncthreads();  // every wave is done with the previous chunk
+      store_q();
+      __syncthreads();
+    }
+    // B fragments of the chunk: token nb*16 + r16, i = ks*32 + q16*8 .. +7
+    bf16x8 bq[DH / 32][4];
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        bq[ks][nb] = *reinterpret_cast<const bf16x8*>(&q_lds[(nb * 16 + r16) * QS + ks * 32 + q16 * 8]);
     f32x4 acc[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
