@@ -158,6 +158,40 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const
                        const int32_t* q_start_pos_host, int32_t batch, void* out_latent, float* lse,
                        void* stream);
 
+/* Bytes of workspace mla_prefill_mha needs: the up-projected keys and values
+ * of every position 0 .. q_start_pos[b] + n_q(b) - 1 of every sequence,
+ * 2 * n_heads * sum_b (q_start_pos[b] + n_q(b)) * 128 float16 values (0
+ * when the arguments are rejected; mla_last_error() says why). */
+size_t mla_prefill_mha_workspace_size(const mla_dims* dims, int32_t batch, const int32_t* cu_q_host,
+                                      const int32_t* q_start_pos_host);
+
+/* mla_prefill_mha -- the same causal chunked prefill in the materialised
+ * form ("Multi-Head Latent Attention" (talalahmed.dev), the MLA dataflow:
+ * each head's key is [W_UK c_t ; R_t k^R_t] and its value W_UV c_t; the
+ * "ropeabsorb" README: this and the absorbed form are the same result).  It
+ * up-projects every visible position's latent once per head into the
+ * workspace, then runs standard causal attention per head (score width
+ * d_head + d_rope, value width d_v), which costs 2 n_h (d_h + d_r + d_v) flop
+ * per visible (query, key) pair instead of 2 n_h (2 d_c + d_r) -- the cheaper
+ * form for long chunks -- and writes the layer output directly.
+ *   Queries and positions as in mla_prefill.  q_nope [cu_q[batch], H, d_head]
+ *   (the un-absorbed content query); q_lat [cu_q[batch], H, d_latent + d_rope]
+ *   of which only the rotated tail [d_latent, d_latent + d_rope) is read
+ *   (mla_rope_apply writes it); w_uk [H, d_head, d_latent]; w_uv
+ *   [H, d_v, d_latent]; out [cu_q[batch], H, d_v] float32 gets
+ *   o = sum_t alpha_t W_UV c_t; lse [cu_q[batch], H] float32 or NULL.
+ * workspace: device memory of at least mla_prefill_mha_workspace_size()
+ * bytes (otherwise MLA_ERR_WORKSPACE).  The up-projected keys and values,
+ * the content query and the softmax weights are rounded to float16 (keys and
+ * values must stay below 65504 in magnitude); the rotated part stays bf16.
+ * bf16 inputs only, d_head = d_v = 128,
+ * (n_heads, d_latent, d_rope) = (128, 512, 64) or (16, 256, 32); other
+ * shapes return MLA_ERR_UNSUPPORTED. */
+mla_status mla_prefill_mha(const mla_dims* dims, const mla_paged_cache* cache, const void* q_nope, const void* q_lat,
+                           const void* w_uk, const void* w_uv, const int32_t* cu_q, const int32_t* q_start_pos,
+                           const int32_t* cu_q_host, const int32_t* q_start_pos_host, int32_t batch, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* mla_out_proj -- output absorption ("AI decoupled RoPE MLA", recap section:
  * Attn_m = W^UV sum_t alpha_mt c_t).
  *   out[n, h, :] = W_UV[h] out_latent[n, h, :]

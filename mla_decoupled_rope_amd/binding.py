@@ -57,6 +57,7 @@ def _load():
         "mla_prefill": [pd, pc, vp, vp, vp, vp, vp, i32, vp, vp, vp],
         "mla_out_proj": [pd, vp, vp, i64, vp, vp],
         "mla_decode_plan": [pd, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(i64)],
+        "mla_prefill_mha": [pd, pc, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -64,6 +65,8 @@ def _load():
         fn.restype = ctypes.c_int
     lib.mla_decode_workspace_size.argtypes = [pd, i32, vp]
     lib.mla_decode_workspace_size.restype = sz
+    lib.mla_prefill_mha_workspace_size.argtypes = [pd, i32, vp, vp]
+    lib.mla_prefill_mha_workspace_size.restype = sz
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -74,7 +77,8 @@ def _load():
 LIB = _load()
 
 EXPORTS = ("mla_rope_apply", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode", "mla_prefill",
-           "mla_out_proj", "mla_status_string", "mla_last_error", "mla_decode_plan")
+           "mla_out_proj", "mla_status_string", "mla_last_error", "mla_decode_plan",
+           "mla_prefill_mha_workspace_size", "mla_prefill_mha")
 
 
 def _check(status: int):
@@ -245,6 +249,53 @@ def prefill(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat
     _check(LIB.mla_prefill(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), cu_q.data_ptr(),
                            q_start.data_ptr(), cu_q_host.data_ptr(), q_start_host.data_ptr(), batch,
                            out_latent.data_ptr(), _ptr(lse), _stream()))
+
+
+def prefill_mha_workspace_size(dims: MLADims, cu_q_host: torch.Tensor, q_start_host: torch.Tensor) -> int:
+    _host_i32(cu_q_host, "cu_q_host")
+    _host_i32(q_start_host, "q_start_host")
+    d = dims.c()
+    n = int(LIB.mla_prefill_mha_workspace_size(ctypes.byref(d), q_start_host.numel(), cu_q_host.data_ptr(),
+                                               q_start_host.data_ptr()))
+    if n == 0 and int(cu_q_host[-1]) + int(q_start_host.sum()) > 0:
+        raise MLAError(2, LIB.mla_last_error().decode())
+    return n
+
+
+def prefill_mha_workspace(dims: MLADims, cu_q_host: torch.Tensor, q_start_host: torch.Tensor,
+                          device="cuda") -> torch.Tensor | None:
+    n = prefill_mha_workspace_size(dims, cu_q_host, q_start_host)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def prefill_mha(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_nope: torch.Tensor,
+                q_lat: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor, cu_q: torch.Tensor,
+                q_start: torch.Tensor, cu_q_host: torch.Tensor, q_start_host: torch.Tensor, out: torch.Tensor,
+                lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> None:
+    """mla_prefill_mha: causal prefill in the materialised form; out[n, h] = sum_t alpha_t W_UV[h] c_t (float32)."""
+    batch = q_start_host.numel()
+    cstruct = _cache(dims, cache, block_table)
+    _host_i32(cu_q_host, "cu_q_host")
+    _host_i32(q_start_host, "q_start_host")
+    if cu_q_host.numel() != batch + 1:
+        raise ValueError("cu_q must have batch + 1 entries")
+    n = int(cu_q_host[-1])
+    _dev(q_nope, "q_nope", dims.dtype, (n, dims.n_heads, dims.d_head))
+    _dev(q_lat, "q_lat", dims.qdtype, (n, dims.n_heads, dims.row))
+    _dev(w_uk, "w_uk", dims.dtype, (dims.n_heads, dims.d_head, dims.d_latent))
+    _dev(w_uv, "w_uv", dims.dtype, (dims.n_heads, dims.d_v, dims.d_latent))
+    _dev(cu_q, "cu_q", torch.int32, (batch + 1,))
+    _dev(q_start, "q_start", torch.int32, (batch,))
+    _dev(out, "out", torch.float32, (n, dims.n_heads, dims.d_v))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (n, dims.n_heads))
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+    d = dims.c()
+    _check(LIB.mla_prefill_mha(ctypes.byref(d), ctypes.byref(cstruct), q_nope.data_ptr(), q_lat.data_ptr(),
+                               w_uk.data_ptr(), w_uv.data_ptr(), cu_q.data_ptr(), q_start.data_ptr(),
+                               cu_q_host.data_ptr(), q_start_host.data_ptr(), batch, out.data_ptr(), _ptr(lse),
+                               _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
 
 
 def out_proj(dims: MLADims, out_latent: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor) -> None:

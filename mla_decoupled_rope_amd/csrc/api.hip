@@ -435,4 +435,97 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const
   return e == hipSuccess ? MLA_OK : hip_fail(e, "prefill launch");
 }
 
+// ---------------------------------------------------- materialised prefill
+
+namespace {
+
+struct MhaPlan {
+  int64_t n_keys = 0, n_key_tiles = 0, n_q_blocks = 0;
+};
+
+mla_status plan_mha(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch, const int32_t* cu_q_host,
+                    const int32_t* q_start_pos_host, MhaPlan* plan) {
+  MLA_TRY(check_dims(dims));
+  if (dims->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "the materialised prefill is bf16 only");
+  if (dims->d_head != 128 || dims->d_v != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "the materialised prefill needs d_head = d_v = 128 (got %d, %d)", dims->d_head,
+                dims->d_v);
+  const bool dsv2 = dims->n_heads == 128 && dims->d_latent == 512 && dims->d_rope == 64;
+  const bool tiny = dims->n_heads == 16 && dims->d_latent == 256 && dims->d_rope == 32;
+  if (!dsv2 && !tiny)
+    return fail(MLA_ERR_UNSUPPORTED, "materialised prefill supports (n_heads, d_latent, d_rope) = (128, 512, 64) or "
+                "(16, 256, 32); got (%d, %d, %d)", dims->n_heads, dims->d_latent, dims->d_rope);
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch > 0 && (cu_q_host == nullptr || q_start_pos_host == nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "cu_q_host and q_start_pos_host must be non-NULL");
+  if (batch > 0 && cu_q_host[0] != 0) return fail(MLA_ERR_INVALID_ARG, "cu_q[0] must be 0");
+  if (cache != nullptr && batch > cache->num_seqs)
+    return fail(MLA_ERR_INVALID_ARG, "batch (%d) exceeds the block table's rows (%d)", batch, cache->num_seqs);
+  MhaPlan pl;
+  for (int b = 0; b < batch; ++b) {
+    const int nq = cu_q_host[b + 1] - cu_q_host[b];
+    if (nq < 0) return fail(MLA_ERR_INVALID_ARG, "cu_q must be non-decreasing (at %d)", b);
+    if (q_start_pos_host[b] < 0) return fail(MLA_ERR_INVALID_ARG, "q_start_pos[%d] is negative", b);
+    const int64_t T = static_cast<int64_t>(q_start_pos_host[b]) + nq;
+    if (cache != nullptr && T > static_cast<int64_t>(cache->max_pages_per_seq) * mla::kPage)
+      return fail(MLA_ERR_INVALID_ARG, "sequence %d reaches position %lld beyond its block table", b,
+                  static_cast<long long>(T - 1));
+    if (cache != nullptr && T > 0 && cache->num_pages == 0)
+      return fail(MLA_ERR_INVALID_ARG, "sequence %d has tokens but the cache has no pages", b);
+    pl.n_keys += T;
+    pl.n_key_tiles += (T + 127) / 128;
+    pl.n_q_blocks += (nq + 127) / 128 * dims->n_heads;
+  }
+  if (pl.n_key_tiles > (1LL << 31) - 1 || pl.n_q_blocks > (1LL << 31) - 1)
+    return fail(MLA_ERR_UNSUPPORTED, "too many workgroups for one launch");
+  *plan = pl;
+  return MLA_OK;
+}
+
+size_t mha_ws_half(const mla_dims* dims, int64_t n_keys) {
+  const size_t half = static_cast<size_t>(dims->n_heads) * static_cast<size_t>(n_keys) * 128 * sizeof(uint16_t);
+  return (half + kWsAlign - 1) / kWsAlign * kWsAlign;
+}
+
+}  // namespace
+
+size_t mla_prefill_mha_workspace_size(const mla_dims* dims, int32_t batch, const int32_t* cu_q_host,
+                                      const int32_t* q_start_pos_host) {
+  g_err.clear();
+  MhaPlan pl;
+  if (plan_mha(dims, nullptr, batch, cu_q_host, q_start_pos_host, &pl) != MLA_OK) return 0;
+  return 2 * mha_ws_half(dims, pl.n_keys);
+}
+
+mla_status mla_prefill_mha(const mla_dims* dims, const mla_paged_cache* cache, const void* q_nope, const void* q_lat,
+                           const void* w_uk, const void* w_uv, const int32_t* cu_q, const int32_t* q_start_pos,
+                           const int32_t* cu_q_host, const int32_t* q_start_pos_host, int32_t batch, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  MLA_TRY(check_cache(cache));
+  MhaPlan pl;
+  MLA_TRY(plan_mha(dims, cache, batch, cu_q_host, q_start_pos_host, &pl));
+  if (pl.n_keys == 0) return MLA_OK;
+  if (q_nope == nullptr || q_lat == nullptr || w_uk == nullptr || w_uv == nullptr || cu_q == nullptr ||
+      q_start_pos == nullptr || out == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "q_nope, q_lat, w_uk, w_uv, cu_q, q_start_pos and out must be non-NULL");
+  const size_t half = mha_ws_half(dims, pl.n_keys);
+  if (workspace == nullptr || workspace_bytes < 2 * half)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, 2 * half);
+  mla::MhaParams p{};
+  p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
+  p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);
+  p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
+  p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
+  p.cu_q = cu_q; p.q_start = q_start_pos; p.batch = batch;
+  p.q_nope = q_nope; p.q_lat = q_lat; p.w_uk = w_uk; p.w_uv = w_uv;
+  p.ws_k = static_cast<uint16_t*>(workspace);
+  p.ws_v = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + half);
+  p.n_keys = pl.n_keys; p.n_key_tiles = pl.n_key_tiles; p.n_q_blocks = pl.n_q_blocks;
+  p.out = out; p.lse = lse;
+  const hipError_t e = mla::launch_mha_prefill(p, as_stream(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "materialised prefill launch");
+}
+
 }  // extern "C"

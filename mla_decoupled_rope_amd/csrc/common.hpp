@@ -12,6 +12,8 @@ constexpr int kPage = 64;  // tokens per cache page (one attention tile)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -103,6 +105,24 @@ struct AttnParams {
   bf16_t* ws_o; float* ws_lse;  // split partials: normalised obar (bf16) [slot, H, d_latent] / lse [slot, H]
 };
 
+// Materialised-form prefill: per-head keys and values up-projected from the
+// latent cache into a workspace, then causal attention over them.
+struct MhaParams {
+  int n_heads, d_latent, d_rope;
+  float scale_log2;  // softmax_scale * log2(e)
+  const void* cache; int64_t num_pages;
+  const int32_t* block_table; int32_t num_seqs; int32_t max_pages;
+  const int32_t* cu_q; const int32_t* q_start; int32_t batch;
+  const void* q_nope;  // [n_q, H, 128] bf16
+  const void* q_lat;   // [n_q, H, d_latent + d_rope] bf16; only the rotated tail is read
+  const void* w_uk; const void* w_uv;  // [H, 128, d_latent] bf16
+  uint16_t* ws_k; uint16_t* ws_v;      // [H, n_keys, 128] float16
+  int64_t n_keys;                      // sum over sequences of q_start + n_q
+  int64_t n_key_tiles;                 // 128-key tiles of the up-projection
+  int64_t n_q_blocks;                  // (sequence, 128-query block) pairs
+  float* out; float* lse;              // [n_q, H, 128] float32 / [n_q, H]
+};
+
 // Launchers (each returns hipGetLastError() after the launch).
 hipError_t launch_rope(const RopeParams& p, hipStream_t s);
 hipError_t launch_absorb(const GemmParams& p, hipStream_t s);
@@ -112,5 +132,6 @@ hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t s);
 hipError_t launch_merge(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_decode_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_prefill_f32(const AttnParams& p, hipStream_t s);
+hipError_t launch_mha_prefill(const MhaParams& p, hipStream_t s);
 
 }  // namespace mla

@@ -102,3 +102,19 @@ class PrefillStep:
                   self.q_start_host, self.out_latent, self.lse)
         B.out_proj(d, self.out_latent, w_uv, self.out)
         return self.out
+
+    def run_materialised(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
+        """The same chunk through mla_prefill_mha (per-head keys and values up-projected)."""
+        d = self.dims
+        if new_latent is not None:
+            B.rope_apply(d, self.cache.data, self.cache.block_table, q_rope=q_rope, q_pos=self.q_pos,
+                         q_lat=self.q_lat, kv_latent=new_latent, k_rope=new_k_rope, kv_seq=self.kv_seq,
+                         kv_pos=self.q_pos)
+        else:
+            B.rope_apply(d, None, None, q_rope=q_rope, q_pos=self.q_pos, q_lat=self.q_lat)
+        if getattr(self, "mha_workspace", None) is None:
+            self.mha_workspace = B.prefill_mha_workspace(d, self.cu_q_host, self.q_start_host,
+                                                         device=self.q_lat.device)
+        B.prefill_mha(d, self.cache.data, self.cache.block_table, q_nope, self.q_lat, w_uk, w_uv, self.cu_q,
+                      self.q_start, self.cu_q_host, self.q_start_host, self.out, self.lse, self.mha_workspace)
+        return self.out

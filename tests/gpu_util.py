@@ -71,6 +71,17 @@ def run_prefill(case, cache=None, precise=None):
     return {"o": to64(out), "obar": to64(step.out_latent), "lse": to64(step.lse), "q_lat": to64(step.q_lat)}
 
 
+def run_prefill_mha(case, cache=None):
+    """The prefill step in the materialised form (mla_prefill_mha).  Returns float64 numpy dict with o, lse."""
+    dims = dims_of(case, precise=False)
+    cache = build_cache(case) if cache is None else cache
+    step = mla.PrefillStep(dims, cache, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
+    dt = tdtype(case)
+    out = step.run_materialised(dev(case.qc, dt), dev(case.qr, dt), dev(case.w_uk, dt), dev(case.w_uv, dt))
+    torch.cuda.synchronize()
+    return {"o": to64(out), "lse": to64(step.lse)}
+
+
 def rel_errors(got: np.ndarray, want: np.ndarray):
     """(max over output rows of max|err| / rms(that row of want), rms(err) / rms(want)).
 

@@ -111,6 +111,28 @@ def test_other_calls_validate():
     assert B.LIB.mla_status_string(3).decode().startswith("workspace")
 
 
+def test_materialised_prefill_validates():
+    d = _dims()
+    cache = B.PagedCache(FAKE.value, 4, FAKE.value, 2, 4)
+    cu = (ctypes.c_int32 * 3)(0, 5, 9)
+    st = (ctypes.c_int32 * 2)(0, 10)
+
+    def call(dims=d, cu=cu, st=st, ws=FAKE, ws_bytes=1 << 40):
+        return B.LIB.mla_prefill_mha(ctypes.byref(dims), ctypes.byref(cache), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     cu, st, 2, FAKE, None, ws, ws_bytes, None)
+
+    need = B.LIB.mla_prefill_mha_workspace_size(ctypes.byref(d), 2, cu, st)
+    assert need == 2 * 128 * (5 + 14) * 128 * 2  # keys 0..4 and 0..13, keys and values in bf16
+    assert call(ws_bytes=need - 1) == 3
+    assert call(ws=None) == 3
+    assert call(dims=_dims(d_head=64)) == 2
+    assert call(dims=_dims(dtype=0, q_lat_dtype=0)) == 2
+    assert call(cu=(ctypes.c_int32 * 3)(1, 5, 9)) == 1  # cu_q[0] != 0
+    assert call(cu=(ctypes.c_int32 * 3)(0, 5, 2)) == 1  # decreasing
+    assert call(st=(ctypes.c_int32 * 2)(0, 300)) == 1   # beyond the block table (4 pages of 64)
+    assert B.LIB.mla_prefill_mha_workspace_size(ctypes.byref(_dims(d_head=64)), 2, cu, st) == 0
+
+
 def _plan(lens, dims=None):
     dims = dims or mla.MLADims(128, 128, 128, 512, 64)
     return mla.decode_plan(dims, torch.tensor(lens, dtype=torch.int32))
