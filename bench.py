@@ -56,6 +56,21 @@ def prefill_flops(case) -> float:
     return 2.0 * s.n_heads * (s.row + s.d_latent) * pairs
 
 
+def prefill_mha_flops(case) -> float:
+    """Materialised form: 2 * n_h * (d_h + d_v) * d_c per visible key position for
+    the up-projection, plus 2 * n_h * (d_h + d_r + d_v) per visible (query, key)
+    pair for the attention."""
+    s = case.shape
+    pairs = keys = 0
+    for b in range(case.batch):
+        n = int(case.cu_q[b + 1] - case.cu_q[b])
+        p0 = int(case.q_start[b])
+        pairs += n * p0 + n * (n + 1) // 2
+        keys += p0 + n
+    return (2.0 * s.n_heads * (s.d_head + s.d_v) * s.d_latent * keys
+            + 2.0 * s.n_heads * (s.d_head + s.d_rope + s.d_v) * pairs)
+
+
 class DeviceEvents:
     """HIP events on the launch stream, recorded with a device-scope release.
 
@@ -138,6 +153,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--prefill-form", default="absorbed", choices=["absorbed", "materialised"],
+                    help="prefill workloads: absorbed latent attention (mla_prefill) or per-head keys and "
+                         "values up-projected first (mla_prefill_mha)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="run one plain 256 MiB copy kernel before timing (HBM counter calibration under rocprofv3)")
@@ -212,6 +230,24 @@ def main():
         kernel_name = "mla_decode (split attention + merge)"
         algo = decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope)
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+    elif args.prefill_form == "materialised":
+        steps = [mla.PrefillStep(dims, c, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
+                 for c in caches]
+        mha_ws = B.prefill_mha_workspace(dims, steps[0].cu_q_host, steps[0].q_start_host)
+
+        def step(i, timed):
+            st = steps[i % len(steps)]
+            B.rope_apply(dims, None, None, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat)
+            if timed:
+                e0 = events.record(sh)
+            B.prefill_mha(dims, st.cache.data, st.cache.block_table, q_nope, st.q_lat, w_uk, w_uv, st.cu_q,
+                          st.q_start, st.cu_q_host, st.q_start_host, st.out, st.lse, mha_ws)
+            if timed:
+                ev.append((e0, events.record(sh)))
+        tokens_per_step = int(case.cu_q[-1])
+        kernel_name = "mla_prefill_mha (key/value up-projection + causal attention)"
+        algo = prefill_mha_flops(case)
+        bound, unit, peak = "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
     else:
         steps = [mla.PrefillStep(dims, c, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
                  for c in caches]
@@ -244,9 +280,12 @@ def main():
     kern_ms = float(np.mean([events.elapsed_ms(a, b) for a, b in ev]))
     events.close()
     achieved = algo / (kern_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
-    traffic = load_traffic(args.config)
+    traffic = load_traffic(args.config if case.kind == "decode" or args.prefill_form == "absorbed"
+                           else args.config + "_mha")
     out = {
-        "metric": METRIC if case.kind == "decode" else "absorbed MLA causal prefill tokens/s + % MFMA roofline",
+        "metric": (METRIC if case.kind == "decode" else
+                   "absorbed MLA causal prefill tokens/s + % MFMA roofline" if args.prefill_form == "absorbed" else
+                   "MLA causal prefill, materialised form, tokens/s + % MFMA roofline"),
         "value": tokens_per_step / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -261,7 +300,9 @@ def main():
         "config": {"workload": case.note.get("workload", args.config), "config": args.config,
                    "batch": case.batch, "seq_len": int(np.max(case.seq_lens)), "total_kv_tokens": case.total_tokens,
                    "n_heads": s.n_heads, "d_latent": s.d_latent, "d_rope": s.d_rope, "page_size": s.page_size,
-                   "cache_copies": len(caches), "step": "rope_apply + absorb_q + decode/prefill + out_proj"},
+                   "cache_copies": len(caches),
+                   "step": ("rope_apply + prefill_mha" if case.kind != "decode" and args.prefill_form == "materialised"
+                            else "rope_apply + absorb_q + decode/prefill + out_proj")},
         "roofline": {"kernel": kernel_name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic, "algorithmic_per_launch": algo,
                      "avg_launch_ms": kern_ms},
