@@ -159,9 +159,11 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const
                        void* stream);
 
 /* Bytes of workspace mla_prefill_mha needs: the up-projected keys and values
- * of every position 0 .. q_start_pos[b] + n_q(b) - 1 of every sequence,
- * 2 * n_heads * sum_b (q_start_pos[b] + n_q(b)) * 128 float16 values (0
- * when the arguments are rejected; mla_last_error() says why). */
+ * of every position 0 .. T_b - 1 (T_b = q_start_pos[b] + n_q(b)) of every
+ * sequence, each sequence's range padded to a multiple of 128 positions:
+ * 2 * n_heads * sum_b ceil(T_b / 128) * 128 * 128 float16 values (0 when
+ * the arguments are rejected; mla_last_error() says why).  The padded total
+ * may not exceed 2^24 - 128 positions. */
 size_t mla_prefill_mha_workspace_size(const mla_dims* dims, int32_t batch, const int32_t* cu_q_host,
                                       const int32_t* q_start_pos_host);
 

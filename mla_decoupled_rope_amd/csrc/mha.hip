@@ -13,17 +13,26 @@
 // for a long causal chunk.
 //
 // Kernel 1 (upproj_kernel): for every key position t of every sequence,
-//   K^C[h][t][:] = W_UK[h] c_t,   V[h][t][:] = W_UV[h] c_t      (float16, head-major)
-// one workgroup per (128 keys, head, K or V): D^T[i][t] = W[i][:] . c_t on
-// v_mfma_f32_32x32x16_bf16, both operands staged through LDS in 64-wide
-// slices of d_c, double buffered.
+//   K^C[h][t][:] = W_UK[h] c_t      (float16, [head][key][128])
+//   V^T[h][:][t] = W_UV[h] c_t      (float16, [head][128][key], transposed)
+// one workgroup per (128 keys, head), one launch for K^C and one for V^T, on
+// v_mfma_f32_32x32x16_bf16,
+// both operands staged through LDS in 64-wide slices of d_c, double
+// buffered.  Each sequence's keys take a range padded to a multiple of 128;
+// the padding rows repeat the sequence's last latent, so every value in the
+// workspace is finite.  V is stored transposed so that the P.V operand is a
+// plain 16-byte LDS read (a transpose read would make the compiler wait for
+// every LDS DMA in flight before it); within each 16-key group the keys are
+// stored in the order 0-3, 8-11, 4-7, 12-15, the order in which a lane holds
+// its softmax weights.
 // Kernel 2 (mha_prefill_kernel): one workgroup per (sequence, head, 128
 // queries); wave w owns queries 32w .. 32w+31.  Keys stream in 32-key tiles
-// [K^C | R_t k^R_t | V] through a ring of three LDS buffers filled by
+// [K^C | R_t k^R_t | V^T] through a ring of four LDS buffers filled by
 // buffer-load DMA (the position part straight from the cache rows); scores
-// S^T = K . Q^T, online softmax in base 2 with O rescaled when a row's max
-// rises, O^T += V^T . P^T with V^T from transpose reads.  Two workgroups
-// share a CU (8 waves), so one wave's softmax overlaps another's MFMAs.
+// S^T = K . Q^T, online softmax in base 2 with O rescaled only when a row's
+// max rises by more than 2^8, O^T += V^T . P^T.  Each wave issues the next
+// tile's score MFMAs between the current tile's exponentials, and two
+// workgroups share a CU (8 waves), so softmax work overlaps MFMAs.
 // The up-projected keys and values, the content part of q and P are float16
 // (11-bit significands: this form rounds keys and values the absorbed form
 // never forms, and float16 keeps that rounding 8x below bf16's); the position
@@ -55,6 +64,16 @@ __device__ __forceinline__ int64_t wave_scan64(int64_t v) {
   return v;
 }
 
+// A wave-uniform 64-bit value moved to scalar registers, so the buffer
+// descriptors built from it stay scalar (a vector descriptor makes the
+// compiler wrap every buffer load in a loop over the distinct values).
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(u)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(u >> 32)));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 struct SeqUnit {
   int b;
   int64_t u;         // unit index within the sequence
@@ -63,9 +82,10 @@ struct SeqUnit {
 };
 
 // Sequence b has n_q = cu_q[b+1] - cu_q[b] queries and T = q_start[b] + n_q
-// keys.  Units per sequence: KIND 0 -> ceil(T / 128) key tiles, KIND 1 ->
+// keys, which occupy a workspace range of pad(T) = ceil(T / 128) * 128 keys.
+// Units per sequence: KIND 0 -> ceil(T / 128) key tiles, KIND 1 ->
 // ceil(n_q / 128) * n_heads attention blocks.  Returns the sequence of a
-// global unit index (sequence order) and its key offset sum_{b' < b} T_b'.
+// global unit index (sequence order) and its key offset sum_{b' < b} pad(T_b').
 template <int KIND>
 __device__ SeqUnit find_unit(const MhaParams& p, int64_t unit) {
   const int lane = threadIdx.x & 63;
@@ -78,7 +98,8 @@ __device__ SeqUnit find_unit(const MhaParams& p, int64_t unit) {
       T = max(0, p.q_start[b]) + nq;
     }
     const int64_t n = KIND == 0 ? (T + kBlk - 1) / kBlk : (nq + kBlk - 1) / kBlk * p.n_heads;
-    const int64_t incl_u = wave_scan64(n), incl_k = wave_scan64(T);
+    const int64_t Tp = (T + kBlk - 1) / kBlk * kBlk;
+    const int64_t incl_u = wave_scan64(n), incl_k = wave_scan64(Tp);
     const int64_t lo = base_u + incl_u - n;
     const bool hit = n > 0 && unit >= lo && unit < lo + n;
     const unsigned long long mask = __ballot(hit);
@@ -87,7 +108,7 @@ __device__ SeqUnit find_unit(const MhaParams& p, int64_t unit) {
       SeqUnit r;
       r.b = b0 + src;
       r.u = unit - __shfl(lo, src, 64);
-      r.key_base = base_k + __shfl(incl_k, src, 64) - __shfl(T, src, 64);
+      r.key_base = base_k + __shfl(incl_k, src, 64) - __shfl(Tp, src, 64);
       r.ok = true;
       return r;
     }
@@ -105,7 +126,7 @@ __device__ SeqUnit find_unit(const MhaParams& p, int64_t unit) {
 // fragment-read phase on distinct banks.
 __device__ __forceinline__ int up_slot(int r, int ch) { return ch ^ ((r >> 1) & 7); }
 
-template <int DC, int DR>
+template <int DC, int DR, bool IS_V>
 __global__ void __launch_bounds__(256) upproj_kernel(MhaParams p) {
   constexpr int KC = 64;            // d_c per slice
   constexpr int NSL = DC / KC;      // slices
@@ -120,16 +141,15 @@ __global__ void __launch_bounds__(256) upproj_kernel(MhaParams p) {
   if (!su.ok) return;
   const int b = __builtin_amdgcn_readfirstlane(su.b);
   const int t0 = __builtin_amdgcn_readfirstlane(static_cast<int>(su.u)) * kBlk;
-  const int64_t key_base = su.key_base;
+  const int64_t key_base = uniform_i64(su.key_base);
   const int nq = p.cu_q[b + 1] - p.cu_q[b];
   const int T = __builtin_amdgcn_readfirstlane(max(0, p.q_start[b]) + nq);
   const int tvalid = min(kBlk, T - t0);
-  const int H = p.n_heads;
-  const int yb = blockIdx.y;
-  const bool is_v = yb >= H;
-  const int h = is_v ? yb - H : yb;
-  const bf16_t* w = static_cast<const bf16_t*>(is_v ? p.w_uv : p.w_uk) + static_cast<int64_t>(h) * kDh * DC;
-  uint16_t* out = (is_v ? p.ws_v : p.ws_k) + (static_cast<int64_t>(h) * p.n_keys + key_base + t0) * kDh;
+  const int h = blockIdx.y;
+  const bf16_t* w = static_cast<const bf16_t*>(IS_V ? p.w_uv : p.w_uk) + static_cast<int64_t>(h) * kDh * DC;
+  // K^C rows of this tile: ws_k[h][key_base + t0 + t][:]; V^T columns: ws_v[h][i][key_base + t0 + t]
+  uint16_t* out_k = p.ws_k + (static_cast<int64_t>(h) * p.n_keys + key_base + t0) * kDh;
+  uint16_t* out_v = p.ws_v + static_cast<int64_t>(h) * kDh * p.n_keys + key_base + t0;
 
   // This thread's four 16-byte pieces of each slice: piece c = tid + 256 k is
   // row c / 8, chunk c % 8.  The cache row of a token row comes from the
@@ -164,7 +184,10 @@ __global__ void __launch_bounds__(256) upproj_kernel(MhaParams p) {
       *reinterpret_cast<bf16x8*>(&lds_c[buf][r * RB + up_slot(r, ch) * 16]) = rc[k];
     }
   };
-  // wave (wi, wt) takes output rows i = 64 wi .. +63 and tokens 64 wt .. +63
+  // wave (wi, wt) takes output rows i = 64 wi .. +63 and tokens 64 wt .. +63.
+  // K^C: acc[a][c] = D[i][t] (W rows as the A operand); V: acc[a][c] = D[t][i]
+  // (the operands swapped), so a lane holds four consecutive tokens of one
+  // output row, the layout of V^T.
   const int wi = wave >> 1, wt = wave & 1;
   const int r32 = lane & 31, kh = lane >> 5;
   f32x16 acc[2][2];
@@ -195,44 +218,71 @@ __global__ void __launch_bounds__(256) upproj_kernel(MhaParams p) {
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fc[c], acc[a][c], 0, 0, 0);
+        for (int c = 0; c < 2; ++c)
+          acc[a][c] = IS_V ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc[c], fa[a], acc[a][c], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fc[c], acc[a][c], 0, 0, 0);
     }
     if (sl + 1 < NSL) store(buf ^ 1);
     __syncthreads();
   }
-  // D[i][t]: lane (t = r32, half kh) holds i = 8g + 4kh + e at register 4g + e
+  // Every row of the tile is stored, the padding rows included.
+  auto h2pack = [](float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
+  };
+  if constexpr (!IS_V) {
+    // D[i][t]: lane (t = r32, half kh) holds i = 8g + 4kh + e at register 4g + e
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int t = wt * 64 + c * 32 + r32;
-    if (t >= tvalid) continue;
+    for (int c = 0; c < 2; ++c) {
+      const int t = wt * 64 + c * 32 + r32;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int i = wi * 64 + a * 32 + 8 * g + 4 * kh;
-        uint2 pk;
-        pk.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){acc[a][c][4 * g], acc[a][c][4 * g + 1]}, f16x2));
-        pk.y = __builtin_bit_cast(uint32_t,
-                                  __builtin_convertvector((f32x2){acc[a][c][4 * g + 2], acc[a][c][4 * g + 3]}, f16x2));
-        *reinterpret_cast<uint2*>(out + static_cast<int64_t>(t) * kDh + i) = pk;
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int i = wi * 64 + a * 32 + 8 * g + 4 * kh;
+          uint2 pk;
+          pk.x = h2pack(acc[a][c][4 * g], acc[a][c][4 * g + 1]);
+          pk.y = h2pack(acc[a][c][4 * g + 2], acc[a][c][4 * g + 3]);
+          *reinterpret_cast<uint2*>(out_k + static_cast<int64_t>(t) * kDh + i) = pk;
+        }
+    }
+  } else {
+    // D[t][i]: lane (i = r32, half kh) holds t = 16q + 8s + 4kh + e at register
+    // 4(2q + s) + e; stored at position 16q + 8kh + 4s + e of its 16-key group
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int i = wi * 64 + a * 32 + r32;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int tpos = wt * 64 + c * 32 + 16 * q + 8 * kh;
+          const f32x16& v = acc[a][c];
+          uint4 pk;
+          pk.x = h2pack(v[8 * q], v[8 * q + 1]);
+          pk.y = h2pack(v[8 * q + 2], v[8 * q + 3]);
+          pk.z = h2pack(v[8 * q + 4], v[8 * q + 5]);
+          pk.w = h2pack(v[8 * q + 6], v[8 * q + 7]);
+          *reinterpret_cast<uint4*>(out_v + static_cast<int64_t>(i) * p.n_keys + tpos) = pk;
+        }
+    }
   }
 }
 
 // -------------------------------------------------------------- attention
 
 // LDS tile of 32 keys: K^C [32][128] (256-byte rows), the rotated position
-// key [32][d_r], V [32][128].  Swizzles (16-byte chunk ch of row r):
-//   K^C: slot ch ^ (r & 15)        -- 16 rows of a b128 read phase, distinct banks
+// key [32][d_r], V^T [128][32] (64-byte rows).  Swizzles (16-byte chunk ch of
+// row r), each putting the 16 rows of a b128 read phase on distinct banks:
+//   K^C: slot ch ^ (r & 15)
 //   k^R: slot ch ^ ((r >> 1) & 7)  (128-byte rows), ch ^ ((r >> 2) & 3) (64-byte rows)
-//   V:   slot ch ^ 4 (r & 3)       -- the 4 rows of a transpose-read half-wave
+//   V^T: slot ch ^ ((r >> 2) & 3)
 __device__ __forceinline__ int kc_slot(int r, int ch) { return ch ^ (r & 15); }
 template <int DR>
 __device__ __forceinline__ int kr_slot(int r, int ch) {
   if constexpr (DR * 2 == 128) return ch ^ ((r >> 1) & 7);
   return ch ^ ((r >> 2) & 3);
 }
-__device__ __forceinline__ int v_slot(int r, int ch) { return ch ^ (4 * (r & 3)); }
+__device__ __forceinline__ int vt_slot(int r, int ch) { return ch ^ ((r >> 2) & 3); }
 
 template <int DC, int DR>
 struct MhaTile {
@@ -243,53 +293,63 @@ struct MhaTile {
   static constexpr int KR_ROWS = 1024 / (DR * 2);  // key rows per 1 KiB DMA instruction
   static constexpr int N_KC = KC_B / 1024, N_KR = KR_B / 1024, N_V = V_B / 1024;
   static constexpr int N = N_KC + N_KR + N_V;      // wave instructions per tile
+  static constexpr int NW = 4;
+  static constexpr int NPW = (N + NW - 1) / NW;    // instructions of the busiest wave
   static_assert(KR_B % 1024 == 0, "the position part must fill whole DMA instructions");
+  static_assert(N >= NW * (NPW - 1), "every wave issues NPW or NPW - 1 instructions");
 };
 
 // The DMA of one key tile into an LDS buffer.  Instruction n of a tile:
-// n < N_KC -> K^C rows 4n .. 4n+3; n < N_KC + N_V -> V rows; else the
-// position part, KR_ROWS rows each.  Wave w issues instructions w, w + 4,
-// w + 8, ...  Per-lane source offsets place each 16-byte chunk in its
-// swizzled slot; rows past `valid` repeat the last valid row.
+// n < N_KC -> K^C rows 4n .. 4n+3; n < N_KC + N_V -> V^T rows (value
+// dimensions) 16m .. 16m+15; else the position part, KR_ROWS key rows each.
+// Wave w issues instructions w, w + 4, w + 8, ...  Every tile lies inside
+// its sequence's padded key range and inside one cache page, so a lane's
+// source offset within an instruction's buffer depends only on the lane,
+// the instruction and the workspace row length: it is computed once.
 template <int DC, int DR>
-__device__ __forceinline__ void mha_issue_tile(const MhaParams& p, int h, int64_t key_base, int t0, int valid, int page,
-                                               char* dst, int wave, int lane) {
+__device__ __forceinline__ uint32_t mha_dma_offset(int n, int lane, int64_t n_keys) {
   using Tl = MhaTile<DC, DR>;
-  constexpr int NW = 4;
-  constexpr int NPW = (Tl::N + NW - 1) / NW;
+  constexpr int ROWB = (DC + DR) * 2;
+  if (n < Tl::N_KC) {
+    const int r = 4 * n + (lane >> 4), slot = lane & 15;
+    return static_cast<uint32_t>(r * 256 + kc_slot(r, slot) * 16);
+  }
+  if (n < Tl::N_KC + Tl::N_V) {
+    const int m = n - Tl::N_KC;
+    const int r = 16 * m + (lane >> 2), slot = lane & 3;
+    return static_cast<uint32_t>(r * n_keys * 2 + vt_slot(r, slot) * 16);
+  }
+  const int m = n - Tl::N_KC - Tl::N_V;
+  constexpr int CPR = DR * 2 / 16;  // chunks per position row
+  const int r = Tl::KR_ROWS * m + lane / CPR, slot = lane % CPR;
+  return static_cast<uint32_t>(r * ROWB + kr_slot<DR>(r, slot) * 16);
+}
+
+// rk / rv cover the sequence's K^C rows / V^T columns of head h; the tile
+// starts t0 keys in (scalar offsets t0 * 256 and t0 * 2 bytes).
+template <int DC, int DR>
+__device__ __forceinline__ void mha_issue_tile(const MhaParams& p, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                               int t0, int page, char* dst, int wave,
+                                               const uint32_t (&off)[MhaTile<DC, DR>::NPW]) {
+  using Tl = MhaTile<DC, DR>;
   constexpr int ROWB = (DC + DR) * 2;
   const char* cache = static_cast<const char*>(p.cache);
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      p.ws_k + (static_cast<int64_t>(h) * p.n_keys + key_base + t0) * kDh, 0, Tl::KC_B, kBufWord3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      p.ws_v + (static_cast<int64_t>(h) * p.n_keys + key_base + t0) * kDh, 0, Tl::V_B, kBufWord3);
   const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(cache) + (static_cast<int64_t>(page) * kPage + t0 % kPage) * ROWB + DC * 2, 0,
       kKeyTile * ROWB, kBufWord3);
   lds_char_t* ldst = reinterpret_cast<lds_char_t*>(reinterpret_cast<uintptr_t>(dst));
 #pragma unroll
-  for (int k = 0; k < NPW; ++k) {
-    const int n = wave + NW * k;  // wave-uniform
+  for (int k = 0; k < Tl::NPW; ++k) {
+    const int n = wave + Tl::NW * k;  // wave-uniform
     if (n >= Tl::N) break;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
     if (n < Tl::N_KC) {
-      const int r = 4 * n + (ln >> 4), slot = ln & 15;
-      const int rs = min(r, valid - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, ldst + n * 1024, 16, rs * 256 + kc_slot(r, slot) * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, ldst + n * 1024, 16, off[k], t0 * (kDh * 2), 0, 0);
     } else if (n < Tl::N_KC + Tl::N_V) {
-      const int m = n - Tl::N_KC;
-      const int r = 4 * m + (ln >> 4), slot = ln & 15;
-      const int rs = min(r, valid - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, ldst + Tl::KC_B + Tl::KR_B + m * 1024, 16,
-                                               rs * 256 + v_slot(r, slot) * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, ldst + Tl::KC_B + Tl::KR_B + (n - Tl::N_KC) * 1024, 16, off[k],
+                                               t0 * 2, 0, 0);
     } else {
-      const int m = n - Tl::N_KC - Tl::N_V;
-      constexpr int CPR = DR * 2 / 16;  // chunks per position row
-      const int r = Tl::KR_ROWS * m + ln / CPR, slot = ln % CPR;
-      const int rs = min(r, valid - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, ldst + Tl::KC_B + m * 1024, 16,
-                                               rs * ROWB + kr_slot<DR>(r, slot) * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, ldst + Tl::KC_B + (n - Tl::N_KC - Tl::N_V) * 1024, 16, off[k], 0,
+                                               0, 0);
     }
   }
 }
@@ -300,12 +360,9 @@ __global__ void __launch_bounds__(256, 2) mha_prefill_kernel(MhaParams p) {
   constexpr int D = kDh + DR;      // score width
   constexpr int KS = D / 16;       // k-steps
   constexpr int KSC = kDh / 16;    // k-steps from K^C
-  constexpr int ROWB = (DC + DR) * 2;
-  constexpr int NW = 4;
-  constexpr int NPW = (Tl::N + NW - 1) / NW;  // DMA instructions of the busiest wave
-  __shared__ __attribute__((aligned(16))) char lds0[Tl::BYTES];
-  __shared__ __attribute__((aligned(16))) char lds1[Tl::BYTES];
-  __shared__ __attribute__((aligned(16))) char lds2[Tl::BYTES];
+  constexpr int NW = Tl::NW;
+  constexpr int NPW = Tl::NPW;
+  __shared__ __attribute__((aligned(16))) char lds_ring[4 * Tl::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -321,9 +378,16 @@ __global__ void __launch_bounds__(256, 2) mha_prefill_kernel(MhaParams p) {
   const int qpos0 = __builtin_amdgcn_readfirstlane(max(0, p.q_start[b]));
   const int nqb = (nq + kBlk - 1) / kBlk;
   const int u = __builtin_amdgcn_readfirstlane(static_cast<int>(su.u));
-  const int h = u % H;
-  const int qb = nqb - 1 - u / H;  // the latest query blocks (most keys) go first
-  const int64_t key_base = su.key_base;
+  // Placement: a sequence's nqb * H units start at a multiple of 8 (H is), and
+  // consecutive workgroups go to the 8 XCDs in turn, so unit u runs on XCD
+  // u % 8.  Each XCD takes the query blocks of heads u % 8, u % 8 + 8, ... one
+  // head at a time, so the blocks that stream the same keys and values run
+  // together and share that XCD's L2.  Within a head the latest query blocks
+  // (most keys) go first.
+  const int j8 = u >> 3;
+  const int h = (j8 / nqb) * 8 + (u & 7);
+  const int qb = nqb - 1 - j8 % nqb;
+  const int64_t key_base = uniform_i64(su.key_base);
   // this lane's query (row r32 of the wave), its position, validity
   const int jq = qb * kBlk + wave * 32 + r32;
   const bool qvalid = jq < nq;
@@ -358,9 +422,19 @@ __global__ void __launch_bounds__(256, 2) mha_prefill_kernel(MhaParams p) {
     }
   }
 
-  // ---- tile DMA (mha_issue_tile)
+  // ---- tile DMA
   const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
   const int my_n = __builtin_amdgcn_readfirstlane((Tl::N - wave + NW - 1) / NW);  // this wave's count
+  uint32_t doff[NPW];
+#pragma unroll
+  for (int k = 0; k < NPW; ++k) doff[k] = mha_dma_offset<DC, DR>(min(wave + NW * k, Tl::N - 1), lane, p.n_keys);
+  const int Tpad = (wg_last + kBlk) / kBlk * kBlk;  // keys of the padded range this workgroup may read
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      p.ws_k + (static_cast<int64_t>(h) * p.n_keys + key_base) * kDh, 0,
+      static_cast<int>(static_cast<uint32_t>(min(static_cast<int64_t>(Tpad) * kDh * 2, int64_t{0xffffffff}))), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      p.ws_v + static_cast<int64_t>(h) * kDh * p.n_keys + key_base, 0,
+      static_cast<int>(static_cast<uint32_t>(((kDh - 1) * p.n_keys + Tpad) * 2)), kBufWord3);
   // Page ids 64 at a time: lane j holds page (ids_base + j); a tile reads its
   // id with readlane, so the tile loop issues no other vector loads (a load
   // there would make the compiler wait for every DMA in flight).
@@ -379,7 +453,7 @@ __global__ void __launch_bounds__(256, 2) mha_prefill_kernel(MhaParams p) {
       ids = load_ids(pg);
     }
     const int page = __builtin_amdgcn_readlane(ids, pg - ids_base);
-    mha_issue_tile<DC, DR>(p, h, key_base, t0, min(kKeyTile, wg_last + 1 - t0), page, dst, wave, lane);
+    mha_issue_tile<DC, DR>(p, rk, rv, t0, page, dst, wave, doff);
   };
   auto wait_tile = [&](bool newer_in_flight) {
     // this wave's instructions of the newer tile may stay in flight
@@ -391,108 +465,149 @@ __global__ void __launch_bounds__(256, 2) mha_prefill_kernel(MhaParams p) {
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  static_assert(Tl::N >= NW * (NPW - 1), "every wave issues NPW or NPW - 1 instructions");
 
-  // ---- per-lane LDS offsets (rows r32; K^C and k^R chunks ks*2 + h2)
+  // ---- per-lane LDS read offsets: K^C / k^R row r32, chunk 2 ks + h2; V^T
+  // row 32 cb + r32, chunk 2 kp + h2
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int ch = ks * 2 + h2;
+    koff[ks] = ks < KSC ? r32 * 256 + kc_slot(r32, ch) * 16
+                        : Tl::KC_B + r32 * (DR * 2) + kr_slot<DR>(r32, ch - 2 * KSC) * 16;
+  }
+  int voff[2];
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) voff[kp] = Tl::KC_B + Tl::KR_B + r32 * 64 + vt_slot(r32, 2 * kp + h2) * 16;
+
   f32x16 oacc[kDh / 32];
 #pragma unroll
   for (int c = 0; c < kDh / 32; ++c) oacc[c] = f32x16{};
   float m_run = -INFINITY, l_part = 0.f;
 
-  if (ntile > 0) issue_tile(0, lds0);
-  if (ntile > 1) issue_tile(1, lds1);
-  auto tile = [&](int it, char* cur, char* nx2) {
-    wait_tile(it + 1 < ntile);
-    if (it + 2 < ntile) issue_tile(it + 2, nx2);
-    const int t0 = it * kKeyTile;
-    if (!wave_live || t0 > w_last) return;  // nothing this wave can see
-    // ---- S^T = K . Q^T
-    f32x16 sacc = f32x16{};
-    constexpr int KPF = 4;
+  // ---- the pipeline.  Tiles go round a ring of four LDS buffers.  Step it
+  // waits for tile it+1, meets the other waves at the barrier (after which
+  // nobody reads buffer (it+3) % 4 = (it-1) % 4 any more) and issues tile
+  // it+3 there; then it issues the score MFMAs of tile it+1 with the
+  // exponentials of tile it between them, and ends with tile it's P.V.
+  // The waves see a prefix of the tiles: wave_tiles of them.
+  const int wave_tiles = wave_live ? w_last / kKeyTile + 1 : 0;
+  auto buf = [&](int it) { return lds_ring + (it & 3) * Tl::BYTES; };
+  auto qk_load = [&](const char* cur, bf16x8 (&ka)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(cur + koff[ks]);
+  };
+  auto qk_step = [&](int ks, const bf16x8 (&ka)[KS], f32x16 s) {
+    if (ks < KSC)
+      return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, ka[ks]), qc[ks < KSC ? ks : 0], s, 0, 0,
+                                                    0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qr[ks >= KSC ? ks - KSC : 0], s, 0, 0, 0);
+  };
+
+  for (int k = 0; k < 3 && k < ntile; ++k) issue_tile(k, buf(k));
+  {
+    // tile 0 lands; tiles 1 and 2 may stay in flight
+    const int newer = min(2, ntile - 1);
+    const int n = newer * my_n;
+    if (n >= 2 * NPW) __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * NPW));
+    else if (n >= 2 * NPW - 2) __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * NPW - 2));
+    else if (n >= NPW) __builtin_amdgcn_s_waitcnt(vmcnt_wait(NPW));
+    else if (n >= NPW - 1) __builtin_amdgcn_s_waitcnt(vmcnt_wait(NPW - 1));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  f32x16 sacc = f32x16{};
+  if (wave_tiles > 0) {
     bf16x8 ka[KS];
-    auto load_k = [&](int ks) {
-      const int ch = ks * 2 + h2;
-      const char* a = ks < KSC ? cur + r32 * 256 + kc_slot(r32, ch) * 16
-                               : cur + Tl::KC_B + r32 * (DR * 2) + kr_slot<DR>(r32, ch - 2 * KSC) * 16;
-      ka[ks] = *reinterpret_cast<const bf16x8*>(a);
-    };
+    qk_load(buf(0), ka);
 #pragma unroll
-    for (int ks = 0; ks < KPF; ++ks) load_k(ks);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + KPF < KS) load_k(ks + KPF);
-      if (ks < KSC)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, ka[ks]), qc[ks < KSC ? ks : 0], sacc,
-                                                      0, 0, 0);
-      else
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qr[ks >= KSC ? ks - KSC : 0], sacc, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) sacc = qk_step(ks, ka, sacc);
+  }
+
+  for (int it = 0; it < ntile; ++it) {
+    if (it + 1 < ntile) {
+      wait_tile(it + 2 < ntile);
+      if (it + 3 < ntile) issue_tile(it + 3, buf(it + 3));
     }
-    // ---- online softmax (base 2).  Lane (row r32, half h2) holds keys
+    if (it >= wave_tiles) continue;  // keeps meeting the barriers
+    const int t0 = it * kKeyTile;
+    const char* cur = buf(it);
+    // V^T fragments of tile it, read first: they have the whole step to land
+    f16x8 va[2][kDh / 32];
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+      for (int cb = 0; cb < kDh / 32; ++cb)
+        va[kp][cb] = *reinterpret_cast<const f16x8*>(cur + voff[kp] + cb * 32 * 64);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- row max of tile it.  Lane (row r32, half h2) holds keys
     // t0 + 8g + 4h2 + e at register 4g + e.
     float sv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
-    if (t0 + kKeyTile - 1 > w_min) {  // the tile crosses some query's diagonal
+    if (t0 + kKeyTile - 1 > w_min) {  // the tile crosses some query's diagonal (or the sequence end)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (t0 + 8 * g + 4 * h2 + e > mpos) sv[4 * g + e] = -INFINITY;
     }
+    // The row's reference m_run moves only when this tile's max exceeds it by
+    // more than 8 (base 2): weights up to 2^8 stay far inside float16 and the
+    // float32 sums, and O is rescaled on few tiles instead of on every rise.
     float lmx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) lmx = fmaxf(lmx, sv[i]);
-    const float m_new = fmaxf(m_run, pair32_max(lmx) * p.scale_log2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = m_run == m_new ? 1.f : __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    if (alpha != 1.f) {
+    const float m_tile = pair32_max(lmx) * p.scale_log2;
+    if (m_tile > m_run + 8.f) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_tile);  // 0 while m_run is -inf
+      m_run = m_tile;
       l_part *= alpha;
 #pragma unroll
       for (int c = 0; c < kDh / 32; ++c)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
     }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    // ---- scores of tile it+1 (MFMA) with the weights of tile it (VALU)
+    // between them: k-step ks carries key pair ks of this lane.
+    const bool next = it + 1 < wave_tiles;
     f16x8 pb[2];
     float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    auto weights = [&](int i) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], p.scale_log2, -m_use));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], p.scale_log2, -m_use));
       psum += p0 + p1;
       const f16x2 pair = __builtin_convertvector((f32x2){p0, p1}, f16x2);
       pb[i / 4][(2 * i) % 8] = pair[0];
       pb[i / 4][(2 * i) % 8 + 1] = pair[1];
+    };
+    if (next) {
+      bf16x8 ka[KS];
+      qk_load(buf(it + 1), ka);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 sn = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sn = qk_step(ks, ka, sn);
+        if (ks < 8) weights(ks);
+      }
+#pragma unroll
+      for (int i = KS; i < 8; ++i) weights(i);
+      sacc = sn;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) weights(i);
     }
     l_part += psum;
-    // ---- O^T += V^T . P^T.  Transpose read: supplier lane 16g + 4k + q reads
-    // key row 16kp + 8s + 4(g/2) + k, columns cb*32 + 16(g%2) + 4q .. +3; lane
-    // l receives column cb*32 + l%32 at keys 16kp + 8s + 4h + 0..3, the order
-    // of its P registers 8kp + 4s + e.
-    const char* vb = cur + Tl::KC_B + Tl::KR_B;
-    const int vg = lane >> 4, vk = (lane >> 2) & 3, vq = lane & 3;
+    // ---- O^T += V^T . P^T.  In k-step kp, position 8h + 4s + e of the
+    // sixteen holds key 16kp + 8s + 4h + e on both sides: the V^T rows store
+    // their keys in that order, and pb[kp] packs this lane's registers
+    // 4(2kp + s) + e.
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
-      for (int cb = 0; cb < kDh / 32; ++cb) {
-        i16x4 t[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int vrow = 16 * kp + 8 * s + 4 * (vg >> 1) + vk;
-          const int ch = cb * 4 + 2 * (vg & 1) + (vq >> 1);
-          const char* a = vb + vrow * 256 + v_slot(vrow, ch) * 16 + (vq & 1) * 8;
-          t[s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a));
-        }
-        f16x8 va;
-        __builtin_memcpy(&va, &t[0], 8);
-        __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &t[1], 8);
-        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kp], oacc[cb], 0, 0, 0);
-      }
-  };
-  for (int it = 0; it < ntile; it += 3) {
-    tile(it, lds0, lds2);
-    if (it + 1 < ntile) tile(it + 1, lds1, lds0);
-    if (it + 2 < ntile) tile(it + 2, lds2, lds1);
+      for (int cb = 0; cb < kDh / 32; ++cb)
+        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[kp][cb], pb[kp], oacc[cb], 0, 0, 0);
   }
   // ---- normalise and store o (float32) and lse
   const float l = pair32_sum(l_part);
@@ -514,9 +629,13 @@ __global__ void __launch_bounds__(256, 2) mha_prefill_kernel(MhaParams p) {
 template <int DC, int DR>
 hipError_t launch_mha(const MhaParams& p, hipStream_t s) {
   if (p.n_key_tiles > 0) {
-    hipLaunchKernelGGL((upproj_kernel<DC, DR>), dim3(static_cast<unsigned>(p.n_key_tiles), 2 * p.n_heads), dim3(256),
-                       0, s, p);
-    const hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL((upproj_kernel<DC, DR, false>), dim3(static_cast<unsigned>(p.n_key_tiles), p.n_heads),
+                       dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((upproj_kernel<DC, DR, true>), dim3(static_cast<unsigned>(p.n_key_tiles), p.n_heads),
+                       dim3(256), 0, s, p);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.n_q_blocks > 0)

@@ -122,7 +122,7 @@ def test_materialised_prefill_validates():
                                      cu, st, 2, FAKE, None, ws, ws_bytes, None)
 
     need = B.LIB.mla_prefill_mha_workspace_size(ctypes.byref(d), 2, cu, st)
-    assert need == 2 * 128 * (5 + 14) * 128 * 2  # keys 0..4 and 0..13, keys and values in bf16
+    assert need == 2 * 128 * (128 + 128) * 128 * 2  # keys 0..4 and 0..13, each range padded to 128, float16
     assert call(ws_bytes=need - 1) == 3
     assert call(ws=None) == 3
     assert call(dims=_dims(d_head=64)) == 2
@@ -131,6 +131,12 @@ def test_materialised_prefill_validates():
     assert call(cu=(ctypes.c_int32 * 3)(0, 5, 2)) == 1  # decreasing
     assert call(st=(ctypes.c_int32 * 2)(0, 300)) == 1   # beyond the block table (4 pages of 64)
     assert B.LIB.mla_prefill_mha_workspace_size(ctypes.byref(_dims(d_head=64)), 2, cu, st) == 0
+    # padded key positions are limited to 2^24 - 128 (32-bit offsets into the transposed values)
+    one = (ctypes.c_int32 * 2)(0, 1)
+    lim = (1 << 24) - 128
+    at_limit = B.LIB.mla_prefill_mha_workspace_size(ctypes.byref(d), 1, one, (ctypes.c_int32 * 1)(lim - 1))
+    assert at_limit == 2 * 128 * lim * 128 * 2
+    assert B.LIB.mla_prefill_mha_workspace_size(ctypes.byref(d), 1, one, (ctypes.c_int32 * 1)(lim)) == 0
 
 
 def _plan(lens, dims=None):

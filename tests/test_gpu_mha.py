@@ -85,7 +85,7 @@ def test_mha_workspace_is_checked():
     dims = G.dims_of(case, precise=False)
     cu, st = torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start)
     need = mla.prefill_mha_workspace_size(dims, cu, st)
-    assert need == 2 * 128 * 30 * 128 * 2  # keys and values of 30 positions, float16
+    assert need == 2 * 128 * 128 * 128 * 2  # keys and values of 30 positions, padded to 128, float16
     cache = G.build_cache(case)
     step = mla.PrefillStep(dims, cache, cu, st)
     step.mha_workspace = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
