@@ -11,4 +11,4 @@ from .binding import (  # noqa: F401
     decode_workspace_size, out_proj, prefill, prefill_mha, prefill_mha_workspace, prefill_mha_workspace_size,
     rope_apply,
 )
-from .pipeline import DecodeStep, LatentCache, PrefillStep  # noqa: F401
+from .pipeline import DecodeStep, LatentCache, PrefillStep, choose_prefill_form  # noqa: F401

@@ -5,7 +5,8 @@
                       (split + merge) -> out_proj, with every buffer
                       preallocated so a step launches kernels only.
 * ``PrefillStep``  -- rope_apply (chunk rows + q^R) -> absorb_q -> prefill ->
-                      out_proj.
+                      out_proj, or rope_apply -> prefill_mha (the materialised
+                      form); ``choose_prefill_form`` picks between them.
 """
 
 from __future__ import annotations
@@ -13,6 +14,49 @@ from __future__ import annotations
 import torch
 
 from . import binding as B
+
+
+# Sustained rates measured on one MI355X (2048-token chunk after 16384 cached
+# tokens, n_h = 128): the absorbed prefill attention, the materialised form's
+# attention and its key/value up-projection, in flop/s.
+ABSORBED_PREFILL_RATE = 1.25e15
+MATERIALISED_ATTENTION_RATE = 0.92e15
+UPPROJECTION_RATE = 0.57e15
+
+
+def choose_prefill_form(dims: B.MLADims, cu_q_host: torch.Tensor, q_start_host: torch.Tensor,
+                        workspace_limit: int = 8 << 30) -> str:
+    """'materialised' or 'absorbed': the form with the smaller estimated time for this chunk.
+
+    Both forms compute one result ("ropeabsorb" README: absorption is exact).
+    The absorbed form spends 2 n_h (2 d_c + d_r) flop per visible (query, key)
+    pair; the materialised form 2 n_h (d_h + d_r + d_v) per pair plus
+    2 n_h (d_h + d_v) d_c per visible key to form the keys and values
+    ("Multi-Head Latent Attention", the MLA dataflow).  Long chunks favour the
+    materialised form, a few queries over a long prefix the absorbed one.  The
+    materialised form is chosen only where mla_prefill_mha supports the shape
+    and its workspace fits ``workspace_limit`` bytes.
+    """
+    cu = [int(x) for x in cu_q_host]
+    st = [int(x) for x in q_start_host]
+    pairs = keys = 0
+    for b in range(len(st)):
+        n = cu[b + 1] - cu[b]
+        pairs += n * st[b] + n * (n + 1) // 2
+        keys += st[b] + n
+    if pairs == 0:
+        return "absorbed"
+    try:
+        ws = B.prefill_mha_workspace_size(dims, cu_q_host, q_start_host)
+    except B.MLAError:
+        return "absorbed"
+    if ws == 0 or ws > workspace_limit:
+        return "absorbed"
+    h, dc, dr, dh, dv = dims.n_heads, dims.d_latent, dims.d_rope, dims.d_head, dims.d_v
+    t_abs = 2.0 * h * (2 * dc + dr) * pairs / ABSORBED_PREFILL_RATE
+    t_mat = (2.0 * h * (dh + dr + dv) * pairs / MATERIALISED_ATTENTION_RATE
+             + 2.0 * h * (dh + dv) * dc * keys / UPPROJECTION_RATE)
+    return "materialised" if t_mat < t_abs else "absorbed"
 
 
 class LatentCache:
@@ -102,6 +146,14 @@ class PrefillStep:
                   self.q_start_host, self.out_latent, self.lse)
         B.out_proj(d, self.out_latent, w_uv, self.out)
         return self.out
+
+    def run_best(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
+        """run() or run_materialised(), whichever choose_prefill_form picks for this chunk."""
+        if getattr(self, "form", None) is None:
+            self.form = choose_prefill_form(self.dims, self.cu_q_host, self.q_start_host)
+        if self.form == "materialised":
+            return self.run_materialised(q_nope, q_rope, w_uk, w_uv, new_latent, new_k_rope)
+        return self.run(q_nope, q_rope, w_uk, w_uv, new_latent, new_k_rope)
 
     def run_materialised(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
         """The same chunk through mla_prefill_mha (per-head keys and values up-projected)."""

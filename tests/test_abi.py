@@ -165,3 +165,18 @@ def test_plan_shapes_of_the_named_workloads():
 def test_plan_env_override(monkeypatch):
     monkeypatch.setenv("MLA_DECODE_SPLIT_PAGES", "3")
     assert _plan([64 * 7, 1, 0]) == (3, 3 + 1)
+
+
+def test_choose_prefill_form():
+    """The per-shape choice between the absorbed and the materialised prefill (host logic only)."""
+    dsv2 = mla.MLADims(128, 128, 128, 512, 64)
+    i32 = lambda *v: torch.tensor(v, dtype=torch.int32)  # noqa: E731
+    # a long chunk: 35.7 M visible pairs over 18,432 keys -> the materialised form
+    assert mla.choose_prefill_form(dsv2, i32(0, 2048), i32(16384)) == "materialised"
+    # a few queries over a long prefix: forming 100 k keys costs more than it saves
+    assert mla.choose_prefill_form(dsv2, i32(0, 4), i32(100000)) == "absorbed"
+    # nothing to do, a workspace over the limit, a shape the materialised form does not take
+    assert mla.choose_prefill_form(dsv2, i32(0, 0), i32(0)) == "absorbed"
+    assert mla.choose_prefill_form(dsv2, i32(0, 2048), i32(16384), workspace_limit=1 << 20) == "absorbed"
+    f32 = mla.MLADims(16, 128, 128, 256, 32, dtype=torch.float32)
+    assert mla.choose_prefill_form(f32, i32(0, 1024), i32(0)) == "absorbed"
