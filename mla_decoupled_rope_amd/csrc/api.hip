@@ -473,10 +473,10 @@ mla_status plan_mha(const mla_dims* dims, const mla_paged_cache* cache, int32_t 
     if (cache != nullptr && T > 0 && cache->num_pages == 0)
       return fail(MLA_ERR_INVALID_ARG, "sequence %d has tokens but the cache has no pages", b);
     pl.n_keys += (T + 127) / 128 * 128;  // each sequence's keys take a range padded to 128
-    pl.n_key_tiles += (T + 127) / 128;
+    pl.n_key_tiles += (T + 255) / 256;
     pl.n_q_blocks += (nq + 127) / 128 * dims->n_heads;
   }
-  if (pl.n_key_tiles > (1LL << 31) - 1 || pl.n_q_blocks > (1LL << 31) - 1)
+  if (pl.n_key_tiles * dims->n_heads > (1LL << 31) - 1 || pl.n_q_blocks > (1LL << 31) - 1)
     return fail(MLA_ERR_UNSUPPORTED, "too many workgroups for one launch");
   // the transposed values are addressed with 32-bit byte offsets within a head: 127 rows of n_keys
   // plus one sequence's range

@@ -118,7 +118,7 @@ struct MhaParams {
   const void* w_uk; const void* w_uv;  // [H, 128, d_latent] bf16
   uint16_t* ws_k; uint16_t* ws_v;      // [H, n_keys, 128] float16
   int64_t n_keys;                      // sum over sequences of q_start + n_q
-  int64_t n_key_tiles;                 // 128-key tiles of the up-projection
+  int64_t n_key_tiles;                 // 256-key tiles of the up-projection (per head)
   int64_t n_q_blocks;                  // (sequence, 128-query block) pairs
   float* out; float* lse;              // [n_q, H, 128] float32 / [n_q, H]
 };

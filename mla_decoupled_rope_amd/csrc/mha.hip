@@ -83,7 +83,7 @@ struct SeqUnit {
 
 // Sequence b has n_q = cu_q[b+1] - cu_q[b] queries and T = q_start[b] + n_q
 // keys, which occupy a workspace range of pad(T) = ceil(T / 128) * 128 keys.
-// Units per sequence: KIND 0 -> ceil(T / 128) key tiles, KIND 1 ->
+// Units per sequence: KIND 0 -> ceil(T / 256) key tiles, KIND 1 ->
 // ceil(n_q / 128) * n_heads attention blocks.  Returns the sequence of a
 // global unit index (sequence order) and its key offset sum_{b' < b} pad(T_b').
 template <int KIND>
@@ -97,7 +97,7 @@ __device__ SeqUnit find_unit(const MhaParams& p, int64_t unit) {
       nq = max(0, p.cu_q[b + 1] - p.cu_q[b]);
       T = max(0, p.q_start[b]) + nq;
     }
-    const int64_t n = KIND == 0 ? (T + kBlk - 1) / kBlk : (nq + kBlk - 1) / kBlk * p.n_heads;
+    const int64_t n = KIND == 0 ? (T + 255) / 256 : (nq + kBlk - 1) / kBlk * p.n_heads;
     const int64_t Tp = (T + kBlk - 1) / kBlk * kBlk;
     const int64_t incl_u = wave_scan64(n), incl_k = wave_scan64(Tp);
     const int64_t lo = base_u + incl_u - n;
@@ -121,149 +121,240 @@ __device__ SeqUnit find_unit(const MhaParams& p, int64_t unit) {
 
 // ------------------------------------------------------------ up-projection
 
-// LDS slices are 128 rows x 64 bf16 (128-byte rows); 16-byte chunk ch of row
-// r sits in slot ch ^ ((r >> 1) & 7), which puts the 16 rows of every
-// fragment-read phase on distinct banks.
-__device__ __forceinline__ int up_slot(int r, int ch) { return ch ^ ((r >> 1) & 7); }
+// One workgroup per (256 keys, head): 4 waves, wave (wt, wo) takes keys
+// 128 wt .. +127 and wo = 0: the 128 K^C outputs (D[i][t] = W_UK[h][i] . c_t,
+// W rows as the A operand), wo = 1: the 128 V outputs (D[t][i], c rows as the
+// A operand, so a lane holds consecutive keys of one value dimension, the
+// layout of V^T).  Each wave holds 4 x 4 blocks of 32 x 32 (AGPRs), so every
+// fragment read from LDS serves four MFMAs.  d_c goes in 32-wide slices: a
+// slice is the 256 latent rows and the 256 weight rows (W_UK[h] then
+// W_UV[h]), 64 bytes each, 32 KiB, brought in by buffer-load DMA into a ring
+// of four; chunk ch of row r sits in slot ch ^ ((r >> 2) & 3).
+constexpr int kUpKeys = 256;  // keys per up-projection workgroup
+constexpr int kUpSl = 32;     // d_c per slice
 
-template <int DC, int DR, bool IS_V>
-__global__ void __launch_bounds__(256) upproj_kernel(MhaParams p) {
-  constexpr int KC = 64;            // d_c per slice
-  constexpr int NSL = DC / KC;      // slices
-  constexpr int RB = KC * 2;        // LDS row bytes
+__device__ __forceinline__ int up_slot(int r, int ch) { return ch ^ ((r >> 2) & 3); }
+
+// D += A . B on an accumulator pinned to AGPRs (inline asm): the 256
+// accumulator registers fill the AGPR file and the fragments the VGPRs; with
+// the builtin the compiler splits the accumulators across both files and
+// moves them every slice.
+__device__ __forceinline__ void mfma_up(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+template <int DC, int DR>
+__global__ void __launch_bounds__(256, 1) upproj_kernel(MhaParams p) {
+  constexpr int NSL = DC / kUpSl;         // slices
+  constexpr int RB = kUpSl * 2;           // LDS row bytes (64)
+  constexpr int SLB = 2 * kUpKeys * RB;   // slice bytes: latent rows then weight rows
   constexpr int ROWB = (DC + DR) * 2;
-  __shared__ __attribute__((aligned(16))) char lds_w[2][kDh * RB];
-  __shared__ __attribute__((aligned(16))) char lds_c[2][kBlk * RB];
+  constexpr int NR = 4;                   // ring depth
+  static_assert(NSL >= 2, "at least two slices");
+  __shared__ __attribute__((aligned(16))) char lds_ring[NR * SLB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const SeqUnit su = find_unit<0>(p, blockIdx.x);
+  const int r32 = lane & 31, kh = lane >> 5;
+  // Placement: consecutive workgroups go to the 8 XCDs in turn; XCD x takes
+  // heads x, x + 8, ... so its heads' weights stay in its L2, and walks the
+  // key tiles with those heads innermost, so a latent tile is read by
+  // consecutive workgroups.
+  const int H = p.n_heads;
+  const int hpx = H / 8;
+  const int x = blockIdx.x;
+  const int j8 = x >> 3;
+  const int h = (j8 % hpx) * 8 + (x & 7);
+  const SeqUnit su = find_unit<0>(p, j8 / hpx);
   if (!su.ok) return;
   const int b = __builtin_amdgcn_readfirstlane(su.b);
-  const int t0 = __builtin_amdgcn_readfirstlane(static_cast<int>(su.u)) * kBlk;
+  const int t0 = __builtin_amdgcn_readfirstlane(static_cast<int>(su.u)) * kUpKeys;
   const int64_t key_base = uniform_i64(su.key_base);
   const int nq = p.cu_q[b + 1] - p.cu_q[b];
   const int T = __builtin_amdgcn_readfirstlane(max(0, p.q_start[b]) + nq);
-  const int tvalid = min(kBlk, T - t0);
-  const int h = blockIdx.y;
-  const bf16_t* w = static_cast<const bf16_t*>(IS_V ? p.w_uv : p.w_uk) + static_cast<int64_t>(h) * kDh * DC;
-  // K^C rows of this tile: ws_k[h][key_base + t0 + t][:]; V^T columns: ws_v[h][i][key_base + t0 + t]
-  uint16_t* out_k = p.ws_k + (static_cast<int64_t>(h) * p.n_keys + key_base + t0) * kDh;
-  uint16_t* out_v = p.ws_v + static_cast<int64_t>(h) * kDh * p.n_keys + key_base + t0;
+  const int Tp = (T + kBlk - 1) / kBlk * kBlk - t0;  // rows of this tile inside the padded range
 
-  // This thread's four 16-byte pieces of each slice: piece c = tid + 256 k is
-  // row c / 8, chunk c % 8.  The cache row of a token row comes from the
-  // block table (rows past the sequence repeat its last row).
+  // ---- DMA.  Instruction n of a slice: n < 16 -> latent rows 16n .. 16n+15
+  // (one cache page: 16 consecutive keys, rows past the sequence repeat its
+  // last row); n >= 16 -> weight rows 16(n-16) .. +15.  Wave w issues n = w +
+  // 4k, k = 0..7: latent for k < 4, W_UK for k = 4, 5, W_UV for k = 6, 7.  Each
+  // lane's source offset within the instruction's buffer is fixed; slices
+  // advance through the scalar offset.
   const char* cache = static_cast<const char*>(p.cache);
   const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_pages;
-  const char* crow[4];
+  __amdgpu_buffer_rsrc_t rc[4];
+  uint32_t off[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int r = (tid + 256 * k) >> 3;
-    const int t = t0 + min(r, tvalid - 1);
-    int page = bt[t / kPage];
+    const int n = wave + 4 * k;
+    const int row = 16 * n + (lane >> 2), slot = lane & 3;
+    const int ts = min(t0 + row, T - 1);
+    const int first = min(t0 + 16 * n, T - 1);  // every row of the instruction is in this row's page
+    int page = bt[first / kPage];
     page = page < 0 || page >= p.num_pages ? 0 : page;
-    crow[k] = cache + (static_cast<int64_t>(page) * kPage + t % kPage) * ROWB;
+    page = __builtin_amdgcn_readfirstlane(page);
+    rc[k] = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(cache) + static_cast<int64_t>(page) * kPage * ROWB, 0,
+                                              kPage * ROWB, kBufWord3);
+    off[k] = static_cast<uint32_t>((ts % kPage) * ROWB + up_slot(row, slot) * 16);
   }
-  bf16x8 rw[4], rc[4];
-  auto load = [&](int sl) {
+  const __amdgpu_buffer_rsrc_t rwk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(static_cast<const bf16_t*>(p.w_uk)) + static_cast<int64_t>(h) * kDh * DC, 0, kDh * DC * 2,
+      kBufWord3);
+  const __amdgpu_buffer_rsrc_t rwv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(static_cast<const bf16_t*>(p.w_uv)) + static_cast<int64_t>(h) * kDh * DC, 0, kDh * DC * 2,
+      kBufWord3);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = tid + 256 * k;
-      const int r = c >> 3, ch = c & 7;
-      rw[k] = *reinterpret_cast<const bf16x8*>(w + static_cast<int64_t>(r) * DC + sl * KC + ch * 8);
-      rc[k] = *reinterpret_cast<const bf16x8*>(crow[k] + (sl * KC + ch * 8) * 2);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = tid + 256 * k;
-      const int r = c >> 3, ch = c & 7;
-      *reinterpret_cast<bf16x8*>(&lds_w[buf][r * RB + up_slot(r, ch) * 16]) = rw[k];
-      *reinterpret_cast<bf16x8*>(&lds_c[buf][r * RB + up_slot(r, ch) * 16]) = rc[k];
-    }
-  };
-  // wave (wi, wt) takes output rows i = 64 wi .. +63 and tokens 64 wt .. +63.
-  // K^C: acc[a][c] = D[i][t] (W rows as the A operand); V: acc[a][c] = D[t][i]
-  // (the operands swapped), so a lane holds four consecutive tokens of one
-  // output row, the layout of V^T.
-  const int wi = wave >> 1, wt = wave & 1;
-  const int r32 = lane & 31, kh = lane >> 5;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) acc[a][c] = f32x16{};
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int sl = 0; sl < NSL; ++sl) {
-    const int buf = sl & 1;
-    if (sl + 1 < NSL) load(sl + 1);
-#pragma unroll
-    for (int ks = 0; ks < KC / 16; ++ks) {
-      const int ch = ks * 2 + kh;
-      bf16x8 fa[2], fc[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int r = wi * 64 + a * 32 + r32;
-        fa[a] = *reinterpret_cast<const bf16x8*>(&lds_w[buf][r * RB + up_slot(r, ch) * 16]);
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int r = wt * 64 + c * 32 + r32;
-        fc[c] = *reinterpret_cast<const bf16x8*>(&lds_c[buf][r * RB + up_slot(r, ch) * 16]);
-      }
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc[a][c] = IS_V ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc[c], fa[a], acc[a][c], 0, 0, 0)
-                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fc[c], acc[a][c], 0, 0, 0);
-    }
-    if (sl + 1 < NSL) store(buf ^ 1);
-    __syncthreads();
+  for (int k = 4; k < 8; ++k) {
+    const int n = wave + 4 * k - 16;
+    const int row = 16 * n + (lane >> 2), slot = lane & 3;
+    off[k] = static_cast<uint32_t>((row % kDh) * DC * 2 + up_slot(row, slot) * 16);
   }
-  // Every row of the tile is stored, the padding rows included.
-  auto h2pack = [](float x, float y) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
+  auto buf = [&](int s) { return lds_ring + (s % NR) * SLB; };
+  auto issue = [&](int s) {
+    lds_char_t* dst = reinterpret_cast<lds_char_t*>(reinterpret_cast<uintptr_t>(buf(s)));
+    const int so = s * RB;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int n = wave + 4 * k;
+      const __amdgpu_buffer_rsrc_t r = k < 4 ? rc[k] : (k < 6 ? rwk : rwv);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + n * 1024, 16, off[k], so, 0, 0);
+    }
   };
-  if constexpr (!IS_V) {
-    // D[i][t]: lane (t = r32, half kh) holds i = 8g + 4kh + e at register 4g + e
+
+  // ---- fragments: wave (wt, wo); A rows and B rows of block a / c are
+  // base + 32 a + r32; chunk 2 ks + kh
+  const int wt = wave & 1, wo = wave >> 1;
+  const int a_base = wo == 0 ? kUpKeys * RB : wt * 128 * RB;                 // W_UK rows, or latent rows
+  const int b_base = wo == 0 ? wt * 128 * RB : (kUpKeys + 128) * RB;        // latent rows, or W_UV rows
+  int foff[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int t = wt * 64 + c * 32 + r32;
+  for (int ks = 0; ks < 2; ++ks) foff[ks] = r32 * RB + up_slot(r32, 2 * ks + kh) * 16;
+  // Only LDS reads (ordered by s_waitcnt) write the fragment registers: the
+  // inline-asm MFMAs are invisible to the hazard recognizer, so a VALU write
+  // (a register copy, say) feeding one could be read stale.
+  bf16x8 fa[2][4], fb[2][4];
+  auto load_frags = [&](const char* sl) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        fa[ks][a] = *reinterpret_cast<const bf16x8*>(sl + a_base + foff[ks] + a * 32 * RB);
+        fb[ks][a] = *reinterpret_cast<const bf16x8*>(sl + b_base + foff[ks] + a * 32 * RB);
+      }
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = f32x16{};
+
+  // ---- slices: step s waits for slice s+1 and meets the barrier (after which
+  // buffer (s+3) % 4 = (s-1) % 4 is free), issues slice s+3 (this wave's turn
+  // after its a-row `wave` of MFMAs), computes slice s from the fragments
+  // read at the end of step s-1, and reads slice s+1's fragments.
+  issue(0);
+  issue(1);
+  if (NSL > 2) issue(2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(NSL > 2 ? 16 : 8));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  load_frags(buf(0));
+  for (int s = 0; s < NSL; ++s) {
+    if (s + 1 < NSL) {
+      // this wave's DMAs of slice s+2 may stay in flight
+      if (s + 2 < NSL) __builtin_amdgcn_s_waitcnt(vmcnt_wait(8));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      asm volatile("s_barrier" ::: "memory");
+    }
+    const bool dma = s + 3 < NSL;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mfma_up(acc[a][c], fa[ks][a], fb[ks][c]);
+        if (ks == 0 && a == wave && dma) issue(s + 3);
+      }
+    if (s + 1 < NSL) load_frags(buf(s + 1));
+  }
+
+  // ---- store, rows of the padded range only.  The tile goes through the idle
+  // ring first (K^C as its 256-byte rows [t][i], V^T as 512-byte rows [i][t] in
+  // the stored key order), so the global writes are whole rows: the K^C tile
+  // is one contiguous 64 KiB run, each V^T row 512 contiguous bytes.
+  auto h2pack = [](float u, float v) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){u, v}, f16x2));
+  };
+  constexpr int KROW = kDh * 2;        // K^C row bytes (256)
+  constexpr int VROW = kUpKeys * 2;    // V^T row bytes in the tile (512)
+  char* stk = lds_ring;                // K^C tile, 64 KiB
+  char* stv = lds_ring + kUpKeys * KROW;  // V^T tile, 64 KiB
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave is done with the ring
+  if (wo == 0) {
+    // D[i][t]: lane (t = r32, half kh) holds i = 32a + 8g + 4kh + e at register 4g + e.
+    // 8-byte pieces of row t; the piece index is XOR-swizzled by the row so the
+    // 32 rows of a store land on distinct banks.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int t = wt * 128 + c * 32 + r32;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int i = wi * 64 + a * 32 + 8 * g + 4 * kh;
           uint2 pk;
           pk.x = h2pack(acc[a][c][4 * g], acc[a][c][4 * g + 1]);
           pk.y = h2pack(acc[a][c][4 * g + 2], acc[a][c][4 * g + 3]);
-          *reinterpret_cast<uint2*>(out_k + static_cast<int64_t>(t) * kDh + i) = pk;
+          const int piece = (a * 32 + 8 * g + 4 * kh) / 4;  // 0..31
+          *reinterpret_cast<uint2*>(stk + t * KROW + ((piece ^ (t & 31)) * 8)) = pk;
         }
     }
   } else {
-    // D[t][i]: lane (i = r32, half kh) holds t = 16q + 8s + 4kh + e at register
-    // 4(2q + s) + e; stored at position 16q + 8kh + 4s + e of its 16-key group
+    // D[t][i]: lane (i = r32, half kh) holds t = 32a + 16q + 8s + 4kh + e at
+    // register 4(2q + s) + e; it goes to position 16q + 8kh + 4s + e of its
+    // 16-key group, a 16-byte piece of row i (XOR-swizzled by the row).
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int i = wi * 64 + a * 32 + r32;
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const int tpos = wt * 64 + c * 32 + 16 * q + 8 * kh;
           const f32x16& v = acc[a][c];
           uint4 pk;
           pk.x = h2pack(v[8 * q], v[8 * q + 1]);
           pk.y = h2pack(v[8 * q + 2], v[8 * q + 3]);
           pk.z = h2pack(v[8 * q + 4], v[8 * q + 5]);
           pk.w = h2pack(v[8 * q + 6], v[8 * q + 7]);
-          *reinterpret_cast<uint4*>(out_v + static_cast<int64_t>(i) * p.n_keys + tpos) = pk;
+          const int i = c * 32 + r32;
+          const int piece = (wt * 128 + a * 32 + 16 * q + 8 * kh) / 8;  // 0..31
+          *reinterpret_cast<uint4*>(stv + i * VROW + ((piece ^ (i & 31)) * 16)) = pk;
         }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // K^C: rows t < Tp, 16 pieces of 16 bytes a row, 256 threads -> 16 rows a pass
+  {
+    char* out = reinterpret_cast<char*>(p.ws_k + (static_cast<int64_t>(h) * p.n_keys + key_base + t0) * kDh);
+    const int rows = min(kUpKeys, Tp);
+#pragma unroll 4
+    for (int r0 = 0; r0 < kUpKeys; r0 += 16) {
+      const int t = r0 + (tid >> 4), q16 = tid & 15;
+      if (t < rows) {
+        // 16-byte piece q16 = 8-byte pieces 2 q16, 2 q16 + 1 (swizzled separately)
+        const uint2 lo = *reinterpret_cast<const uint2*>(stk + t * KROW + (((2 * q16) ^ (t & 31)) * 8));
+        const uint2 hi = *reinterpret_cast<const uint2*>(stk + t * KROW + (((2 * q16 + 1) ^ (t & 31)) * 8));
+        *reinterpret_cast<uint4*>(out + static_cast<int64_t>(t) * KROW + q16 * 16) = uint4{lo.x, lo.y, hi.x, hi.y};
+      }
+    }
+  }
+  // V^T: 128 rows, the first min(256, Tp) keys of each (Tp is a multiple of 128)
+  {
+    uint16_t* out = p.ws_v + static_cast<int64_t>(h) * kDh * p.n_keys + key_base + t0;
+    const int pieces = min(kUpKeys, Tp) / 8;  // 16-byte pieces a row: 16 or 32
+#pragma unroll 4
+    for (int r0 = 0; r0 < kDh; r0 += 8) {
+      const int i = r0 + (tid >> 5), pc = tid & 31;
+      if (pc < pieces)
+        *reinterpret_cast<uint4*>(out + static_cast<int64_t>(i) * p.n_keys + pc * 8) =
+            *reinterpret_cast<const uint4*>(stv + i * VROW + ((pc ^ (i & 31)) * 16));
     }
   }
 }
@@ -629,13 +720,9 @@ __global__ void __launch_bounds__(256, 2) mha_prefill_kernel(MhaParams p) {
 template <int DC, int DR>
 hipError_t launch_mha(const MhaParams& p, hipStream_t s) {
   if (p.n_key_tiles > 0) {
-    hipLaunchKernelGGL((upproj_kernel<DC, DR, false>), dim3(static_cast<unsigned>(p.n_key_tiles), p.n_heads),
-                       dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((upproj_kernel<DC, DR, true>), dim3(static_cast<unsigned>(p.n_key_tiles), p.n_heads),
-                       dim3(256), 0, s, p);
-    e = hipGetLastError();
+    hipLaunchKernelGGL((upproj_kernel<DC, DR>), dim3(static_cast<unsigned>(p.n_key_tiles * p.n_heads)), dim3(256), 0,
+                       s, p);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.n_q_blocks > 0)
