@@ -30,10 +30,11 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "attn_bf16.hip")
+MHA_SRC = os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "mha.hip")
 
 
-def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_hash(src: str = KERNEL_SRC) -> str:
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
 def decode_bytes(seq_lens, n_heads=128, d_latent=512, d_rope=64) -> int:
@@ -116,11 +117,12 @@ class DeviceEvents:
         self.events = []
 
 
-def load_traffic(config_name: str):
+def load_traffic(config_name: str, src: str = KERNEL_SRC):
+    """Measured HBM bytes per call, if profiled on the current kernel source (else None)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE)).get(config_name)
-    if not rec or rec.get("kernel_sha") != kernel_hash():
+    if not rec or rec.get("kernel_sha") != kernel_hash(src):
         return None
     return rec.get("bytes_per_launch")
 
@@ -280,8 +282,10 @@ def main():
     kern_ms = float(np.mean([events.elapsed_ms(a, b) for a, b in ev]))
     events.close()
     achieved = algo / (kern_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
-    traffic = load_traffic(args.config if case.kind == "decode" or args.prefill_form == "absorbed"
-                           else args.config + "_mha")
+    if case.kind == "decode" or args.prefill_form == "absorbed":
+        traffic = load_traffic(args.config)
+    else:
+        traffic = load_traffic(args.config + "_mha", MHA_SRC)
     out = {
         "metric": (METRIC if case.kind == "decode" else
                    "absorbed MLA causal prefill tokens/s + % MFMA roofline" if args.prefill_form == "absorbed" else
