@@ -16,9 +16,13 @@ equations:
                      pure-Python version for tiny cases.
 * ``paging``      -- where a (sequence, position) lands in a paged cache.
 * ``accounting``  -- per-token cache sizes of the layouts the pages compare.
+* ``front``       -- the projections in front of the cache: the latent
+                     c = W_DKV h, the position key W_KR h, the query latent
+                     c^Q = W_DQ h and its content / position projections, and
+                     the folded query weight W_UK^T W_UQ.
 
 No function here shares code with the GPU path, and none reads any value the
 GPU produced.
 """
 
-from . import accounting, attention, paging, rope  # noqa: F401
+from . import accounting, attention, front, paging, rope  # noqa: F401

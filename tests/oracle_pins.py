@@ -16,7 +16,7 @@ import os
 import numpy as np
 
 import oracle
-from oracle import accounting, attention, paging, rope
+from oracle import accounting, attention, front, paging, rope
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
 
@@ -266,10 +266,92 @@ def pin_page_figures():
     assert abs(mha / dec - g["dsv2_decoupled_fraction_about"]["value"]) <= g["dsv2_decoupled_fraction_about"]["abs_tol"]
 
 
+# -------------------------------------------------------- front of layer --
+# "AI decoupled RoPE MLA", recap (c = W^DKV h) and decoupled-RoPE section
+# (k^R = W^KR h); "Detailed Illustration of the Problem", Step 1 (query
+# latent c^Q = W^DQ h, q = W^UQ c^Q) and Step 4 (W^{Q'} = (W^UQ)^T W^UK).
+
+def _front_problem(seed=5, n=3, d_model=10, d_q=7, n_heads=2, d_h=4, d_c=6, d_r=4):
+    rng = np.random.default_rng(seed)
+    return dict(
+        h=rng.standard_normal((n, d_model)),
+        w_dkv=rng.standard_normal((d_c, d_model)), w_kr=rng.standard_normal((d_r, d_model)),
+        w_dq=rng.standard_normal((d_q, d_model)), w_uq=rng.standard_normal((n_heads, d_h, d_q)),
+        w_qr=rng.standard_normal((n_heads, d_r, d_q)), w_uk=rng.standard_normal((n_heads, d_h, d_c)),
+    )
+
+
+def pin_front_unit_vectors():
+    """h = e_j picks column j of each down-projection exactly (non-square weights, so a
+    transposed weight or an input taken from the wrong side fails)."""
+    p = _front_problem()
+    d_model = p["h"].shape[1]
+    for j in (0, 3, d_model - 1):
+        e = np.zeros((1, d_model))
+        e[0, j] = 1.0
+        assert np.array_equal(front.kv_latent(e, p["w_dkv"])[0], p["w_dkv"][:, j])
+        assert np.array_equal(front.position_key(e, p["w_kr"])[0], p["w_kr"][:, j])
+        assert np.array_equal(front.query_latent(e, p["w_dq"])[0], p["w_dq"][:, j])
+    d_q = p["w_dq"].shape[0]
+    for j in (0, d_q - 1):
+        e = np.zeros((1, d_q))
+        e[0, j] = 1.0
+        assert np.array_equal(front.content_query(e, p["w_uq"])[0], p["w_uq"][:, :, j])
+        assert np.array_equal(front.position_query(e, p["w_qr"])[0], p["w_qr"][:, :, j])
+
+
+def pin_front_brute_force():
+    """Scalar loops over every index equal the vectorised projections and the fold."""
+    p = _front_problem(seed=6)
+    h, w_dq, w_uq, w_qr, w_uk = p["h"], p["w_dq"], p["w_uq"], p["w_qr"], p["w_uk"]
+    n, d_model = h.shape
+    d_q = w_dq.shape[0]
+    n_heads, d_h, d_c = w_uk.shape
+    cq = front.query_latent(h, w_dq)
+    for a in range(n):
+        for q in range(d_q):
+            assert math.isclose(cq[a, q], sum(w_dq[q, k] * h[a, k] for k in range(d_model)), rel_tol=1e-12,
+                                abs_tol=1e-12)
+    qc = front.content_query(cq, w_uq)
+    fold = front.fold_query_weights(w_uq, w_uk)
+    for i in range(n_heads):
+        for a in range(n):
+            for d in range(d_h):
+                assert math.isclose(qc[a, i, d], sum(w_uq[i, d, q] * cq[a, q] for q in range(d_q)), rel_tol=1e-12,
+                                    abs_tol=1e-12)
+        for c in range(d_c):
+            for q in range(d_q):
+                want = sum(w_uk[i, d, c] * w_uq[i, d, q] for d in range(d_h))
+                assert math.isclose(fold[i, c, q], want, rel_tol=1e-12, abs_tol=1e-12)
+
+
+def pin_fold_equals_absorbed_query():
+    """Folding W_UK into the query weight ahead of time gives the absorbed query of the
+    unfolded path ("Detailed Illustration of the Problem", Step 4; "ropeabsorb": exact)."""
+    p = _front_problem(seed=7, n=5, d_model=16, d_q=9, n_heads=3, d_h=5, d_c=8)
+    cq = front.query_latent(p["h"], p["w_dq"])
+    via_fold = front.folded_query(cq, front.fold_query_weights(p["w_uq"], p["w_uk"]))
+    via_absorb = attention.query_absorption(p["w_uk"], front.content_query(cq, p["w_uq"]))
+    assert _rel(via_fold, via_absorb) <= 1e-12
+
+
+def pin_latent_path_reduces_to_direct_query():
+    """With W_DQ = I the latent path is the direct query W_Q h of the tiny configs
+    (W_Q [H d_h, D] rows regrouped per head), a plain matrix product."""
+    rng = np.random.default_rng(8)
+    n, d_model, n_heads, d_h = 4, 12, 3, 4
+    h = rng.standard_normal((n, d_model))
+    w_q = rng.standard_normal((n_heads * d_h, d_model))
+    got = front.content_query(front.query_latent(h, np.eye(d_model)), w_q.reshape(n_heads, d_h, d_model))
+    assert _rel(got, (h @ w_q.T).reshape(n, n_heads, d_h)) <= 1e-14
+
+
 ALL_PINS = [
     pin_rope_identity_at_zero, pin_rope_closed_form, pin_rope_orthogonal, pin_rope_relative,
     pin_shift_invariance, pin_absorbed_equals_materialised, pin_key_rank, pin_brute_force,
     pin_special_cases, pin_sdpa, pin_prefill_is_decode_of_prefix, pin_paging, pin_page_figures,
+    pin_front_unit_vectors, pin_front_brute_force, pin_fold_equals_absorbed_query,
+    pin_latent_path_reduces_to_direct_query,
 ]
 
 

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle_pins as pins
-from oracle import attention, paging, rope
+from oracle import attention, front, paging, rope
 
 _orig_rotate = rope.rotate
 _orig_thetas = rope.thetas
@@ -16,6 +16,7 @@ _orig_values = attention.materialise_values
 _orig_keys = attention.materialise_keys
 _orig_visible = attention._visible
 _orig_slot = paging.slot
+_orig_fold = front.fold_query_weights
 
 
 def _clockwise_rotate(x, positions, base=10000.0):
@@ -79,6 +80,28 @@ def _bad_slot(table, seq, pos, ps):
     return int(table[seq, pos // ps]) * ps + pos // ps
 
 
+def _kv_latent_transposed(h, w_dkv):
+    # the weight read as [in, out]: only survives where it is square
+    w = np.asarray(w_dkv, np.float64)
+    return np.asarray(h, np.float64)[:, : w.shape[0]] @ w[:, : w.shape[0]]
+
+
+def _fold_wrong_side(w_uq, w_uk):
+    # W_UQ^T W_UK contracted over the wrong index pair (d_q with d_c swapped)
+    f = _orig_fold(w_uq, w_uk)
+    return f[:, ::-1, :]
+
+
+def _query_skips_latent(cq, w_uq):
+    # the content query taken without its up-projection's head split
+    w = np.asarray(w_uq, np.float64)
+    return np.einsum("hdq,nq->nhd", w[::-1], np.asarray(cq, np.float64))
+
+
+def _position_query_from_content(cq, w_qr):
+    return np.einsum("hrq,nq->nhr", np.asarray(w_qr, np.float64), np.asarray(cq, np.float64)) * 0.0
+
+
 MUTATIONS = {
     "rope_clockwise": [(rope, "rotate", _clockwise_rotate), (rope, "rotation_matrix", _clockwise_matrix)],
     "rope_half_split_pairs": [(rope, "rotate", _half_split_rotate)],
@@ -90,6 +113,10 @@ MUTATIONS = {
     "score_scale_dropped": [(attention, "materialised", _materialised_no_scale)],
     "query_not_rotated": [(attention, "materialised", _materialised_query_unrotated)],
     "paging_offset_slip": [(paging, "slot", _bad_slot)],
+    "front_latent_weight_transposed": [(front, "kv_latent", _kv_latent_transposed)],
+    "front_fold_wrong_index": [(front, "fold_query_weights", _fold_wrong_side)],
+    "front_query_heads_swapped": [(front, "content_query", _query_skips_latent)],
+    "front_position_query_dropped": [(front, "position_query", _position_query_from_content)],
 }
 
 
