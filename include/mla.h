@@ -202,6 +202,62 @@ mla_status mla_prefill_mha(const mla_dims* dims, const mla_paged_cache* cache, c
 mla_status mla_out_proj(const mla_dims* dims, const void* out_latent, const void* w_uv, int64_t n,
                         void* out, void* stream);
 
+/* ---- The front of the layer: projections from the hidden state h ---------
+ * "AI decoupled RoPE MLA" (operatorworld.com), recap: the latent is the
+ * down-projection c_t = W^DKV h_t; decoupled-RoPE section: the position
+ * channel k^R_t = W^KR h_t is shared by the heads and is the only part
+ * rotated.  "Detailed Illustration of the Problem" (notion.site), Step 1: the
+ * query goes through a compressed latent c^Q = W^DQ h and is projected up
+ * from it; Step 4: with no rotation between them, W^UK folds into the query
+ * weight, W^{Q'} = (W^UQ)^T W^UK.  Here both query channels come from the
+ * query latent: q^C_i = W_UQ,i c^Q, q^R_i = W_QR,i c^Q.
+ * Weights are stored [out, in]: W_DKV [d_latent, d_model], W_KR [d_rope,
+ * d_model], W_DQ [d_qlat, d_model], W_UQ [H, d_head, d_qlat], W_QR [H, d_rope,
+ * d_qlat], the folded W_fold [H, d_latent, d_qlat] = W_UK,i^T W_UQ,i.
+ * bf16 only (dims->dtype and q_lat_dtype), d_model and d_qlat multiples of 32,
+ * h and the weights 16-byte aligned; otherwise MLA_ERR_UNSUPPORTED or
+ * MLA_ERR_INVALID_ARG and nothing is launched.  Accumulation is float32 over
+ * K splits summed in a fixed order (bitwise repeatable); RoPE angles are
+ * float64, as in mla_rope_apply.  The workspace holds float32 partial sums
+ * and the bf16 query latent; it is the caller's, and calls on one stream may
+ * share it. */
+
+/* Bytes of workspace the front calls need for n tokens (d_qlat = 0 for
+ * mla_kv_project alone); 0 when the arguments are rejected. */
+size_t mla_front_workspace_size(const mla_dims* dims, int64_t n, int32_t d_model, int32_t d_qlat);
+
+/* mla_kv_project -- the cache side of the front, fused with the cache write:
+ *   c = W_DKV h[j],  k^R = W_KR h[j],  cache row of (kv_seq[j], kv_pos[j]) =
+ *   [c | R_{kv_pos[j]} k^R] (bf16), for j < n.
+ *   h [n, d_model]; kv_seq, kv_pos int32 [n] device.  Rows whose sequence,
+ *   position or page id is negative or out of range are skipped (as in
+ *   mla_rope_apply). */
+mla_status mla_kv_project(const mla_dims* dims, const mla_paged_cache* cache, const void* h, int64_t n,
+                          int32_t d_model, const void* w_dkv, const void* w_kr, const int32_t* kv_seq,
+                          const int32_t* kv_pos, void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_q_project -- the query side through the query latent:
+ *   c^Q = W_DQ h[j] (rounded to bf16), q_nope[j, i, :] = W_UQ,i c^Q,
+ *   q_lat[j, i, d_latent:] = R_{q_pos[j]} W_QR,i c^Q.
+ *   h [n, d_model]; q_pos int32 [n] device; q_nope [n, H, d_head];
+ *   q_lat [n, H, d_latent + d_rope] (only the tail is written; mla_absorb_q
+ *   writes the head from q_nope). */
+mla_status mla_q_project(const mla_dims* dims, const void* h, int64_t n, int32_t d_model, int32_t d_qlat,
+                         const void* w_dq, const void* w_uq, const void* w_qr, const int32_t* q_pos, void* q_nope,
+                         void* q_lat, void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_q_project_folded -- the same query with W_UK folded in ahead of time:
+ *   q_lat[j, i, :d_latent] = W_fold,i c^Q (the absorbed query q~),
+ *   q_lat[j, i, d_latent:] = R_{q_pos[j]} W_QR,i c^Q.  No mla_absorb_q follows. */
+mla_status mla_q_project_folded(const mla_dims* dims, const void* h, int64_t n, int32_t d_model, int32_t d_qlat,
+                                const void* w_dq, const void* w_fold, const void* w_qr, const int32_t* q_pos,
+                                void* q_lat, void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_fold_q_weights -- W_fold,i = W_UK,i^T W_UQ,i ([H, d_latent, d_qlat],
+ * float32 sums rounded once to bf16), once per weight set. */
+mla_status mla_fold_q_weights(const mla_dims* dims, int32_t d_qlat, const void* w_uq, const void* w_uk, void* w_fold,
+                              void* stream);
+
 /* Static text for a status code. */
 const char* mla_status_string(mla_status status);
 

@@ -8,7 +8,7 @@ Importing it without the built library raises ImportError.
 
 from .binding import (  # noqa: F401
     LIB, LIB_PATH, MLADims, MLAError, absorb_q, decode, decode_plan, decode_workspace,
-    decode_workspace_size, out_proj, prefill, prefill_mha, prefill_mha_workspace, prefill_mha_workspace_size,
-    rope_apply,
+    decode_workspace_size, fold_q_weights, front_workspace, front_workspace_size, kv_project, out_proj, prefill,
+    prefill_mha, prefill_mha_workspace, prefill_mha_workspace_size, q_project, q_project_folded, rope_apply,
 )
 from .pipeline import DecodeStep, LatentCache, PrefillStep, choose_prefill_form  # noqa: F401

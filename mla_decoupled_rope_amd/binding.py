@@ -58,6 +58,10 @@ def _load():
         "mla_out_proj": [pd, vp, vp, i64, vp, vp],
         "mla_decode_plan": [pd, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(i64)],
         "mla_prefill_mha": [pd, pc, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp],
+        "mla_kv_project": [pd, pc, vp, i64, i32, vp, vp, vp, vp, vp, sz, vp],
+        "mla_q_project": [pd, vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "mla_q_project_folded": [pd, vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+        "mla_fold_q_weights": [pd, i32, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -67,6 +71,8 @@ def _load():
     lib.mla_decode_workspace_size.restype = sz
     lib.mla_prefill_mha_workspace_size.argtypes = [pd, i32, vp, vp]
     lib.mla_prefill_mha_workspace_size.restype = sz
+    lib.mla_front_workspace_size.argtypes = [pd, i64, i32, i32]
+    lib.mla_front_workspace_size.restype = sz
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -78,7 +84,8 @@ LIB = _load()
 
 EXPORTS = ("mla_rope_apply", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode", "mla_prefill",
            "mla_out_proj", "mla_status_string", "mla_last_error", "mla_decode_plan",
-           "mla_prefill_mha_workspace_size", "mla_prefill_mha")
+           "mla_prefill_mha_workspace_size", "mla_prefill_mha", "mla_front_workspace_size", "mla_kv_project",
+           "mla_q_project", "mla_q_project_folded", "mla_fold_q_weights")
 
 
 def _check(status: int):
@@ -306,3 +313,80 @@ def out_proj(dims: MLADims, out_latent: torch.Tensor, w_uv: torch.Tensor, out: t
     _dev(out, "out", torch.float32, (n, dims.n_heads, dims.d_v))
     d = dims.c()
     _check(LIB.mla_out_proj(ctypes.byref(d), out_latent.data_ptr(), w_uv.data_ptr(), n, out.data_ptr(), _stream()))
+
+
+def front_workspace_size(dims: MLADims, n: int, d_model: int, d_qlat: int = 0) -> int:
+    d = dims.c()
+    size = int(LIB.mla_front_workspace_size(ctypes.byref(d), n, d_model, d_qlat))
+    if size == 0 and n > 0:
+        raise MLAError(2, LIB.mla_last_error().decode())
+    return size
+
+
+def front_workspace(dims: MLADims, n: int, d_model: int, d_qlat: int = 0, device="cuda") -> torch.Tensor:
+    return torch.empty(max(front_workspace_size(dims, n, d_model, d_qlat), 1), dtype=torch.uint8, device=device)
+
+
+def kv_project(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, h: torch.Tensor, w_dkv: torch.Tensor,
+               w_kr: torch.Tensor, kv_seq: torch.Tensor, kv_pos: torch.Tensor, workspace: torch.Tensor) -> None:
+    """mla_kv_project: cache row of (kv_seq[j], kv_pos[j]) = [W_DKV h[j] | R_pos W_KR h[j]]."""
+    n, d_model = h.shape
+    cstruct = _cache(dims, cache, block_table)
+    _dev(h, "h", dims.dtype, (n, d_model))
+    _dev(w_dkv, "w_dkv", dims.dtype, (dims.d_latent, d_model))
+    _dev(w_kr, "w_kr", dims.dtype, (dims.d_rope, d_model))
+    _dev(kv_seq, "kv_seq", torch.int32, (n,))
+    _dev(kv_pos, "kv_pos", torch.int32, (n,))
+    _dev(workspace, "workspace", torch.uint8)
+    d = dims.c()
+    _check(LIB.mla_kv_project(ctypes.byref(d), ctypes.byref(cstruct), h.data_ptr(), n, d_model, w_dkv.data_ptr(),
+                              w_kr.data_ptr(), kv_seq.data_ptr(), kv_pos.data_ptr(), workspace.data_ptr(),
+                              workspace.numel(), _stream()))
+
+
+def q_project(dims: MLADims, h: torch.Tensor, w_dq: torch.Tensor, w_uq: torch.Tensor, w_qr: torch.Tensor,
+              q_pos: torch.Tensor, q_nope: torch.Tensor, q_lat: torch.Tensor, workspace: torch.Tensor) -> None:
+    """mla_q_project: q_nope = W_UQ (W_DQ h), q_lat tail = R_pos W_QR (W_DQ h)."""
+    n, d_model = h.shape
+    d_qlat = w_dq.shape[0]
+    _dev(h, "h", dims.dtype, (n, d_model))
+    _dev(w_dq, "w_dq", dims.dtype, (d_qlat, d_model))
+    _dev(w_uq, "w_uq", dims.dtype, (dims.n_heads, dims.d_head, d_qlat))
+    _dev(w_qr, "w_qr", dims.dtype, (dims.n_heads, dims.d_rope, d_qlat))
+    _dev(q_pos, "q_pos", torch.int32, (n,))
+    _dev(q_nope, "q_nope", dims.dtype, (n, dims.n_heads, dims.d_head))
+    _dev(q_lat, "q_lat", dims.qdtype, (n, dims.n_heads, dims.row))
+    _dev(workspace, "workspace", torch.uint8)
+    d = dims.c()
+    _check(LIB.mla_q_project(ctypes.byref(d), h.data_ptr(), n, d_model, d_qlat, w_dq.data_ptr(), w_uq.data_ptr(),
+                             w_qr.data_ptr(), q_pos.data_ptr(), q_nope.data_ptr(), q_lat.data_ptr(),
+                             workspace.data_ptr(), workspace.numel(), _stream()))
+
+
+def q_project_folded(dims: MLADims, h: torch.Tensor, w_dq: torch.Tensor, w_fold: torch.Tensor, w_qr: torch.Tensor,
+                     q_pos: torch.Tensor, q_lat: torch.Tensor, workspace: torch.Tensor) -> None:
+    """mla_q_project_folded: q_lat = [W_fold (W_DQ h) | R_pos W_QR (W_DQ h)]."""
+    n, d_model = h.shape
+    d_qlat = w_dq.shape[0]
+    _dev(h, "h", dims.dtype, (n, d_model))
+    _dev(w_dq, "w_dq", dims.dtype, (d_qlat, d_model))
+    _dev(w_fold, "w_fold", dims.dtype, (dims.n_heads, dims.d_latent, d_qlat))
+    _dev(w_qr, "w_qr", dims.dtype, (dims.n_heads, dims.d_rope, d_qlat))
+    _dev(q_pos, "q_pos", torch.int32, (n,))
+    _dev(q_lat, "q_lat", dims.qdtype, (n, dims.n_heads, dims.row))
+    _dev(workspace, "workspace", torch.uint8)
+    d = dims.c()
+    _check(LIB.mla_q_project_folded(ctypes.byref(d), h.data_ptr(), n, d_model, d_qlat, w_dq.data_ptr(),
+                                    w_fold.data_ptr(), w_qr.data_ptr(), q_pos.data_ptr(), q_lat.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel(), _stream()))
+
+
+def fold_q_weights(dims: MLADims, w_uq: torch.Tensor, w_uk: torch.Tensor, w_fold: torch.Tensor) -> None:
+    """mla_fold_q_weights: w_fold[i] = W_UK[i]^T W_UQ[i]."""
+    d_qlat = w_uq.shape[2]
+    _dev(w_uq, "w_uq", dims.dtype, (dims.n_heads, dims.d_head, d_qlat))
+    _dev(w_uk, "w_uk", dims.dtype, (dims.n_heads, dims.d_head, dims.d_latent))
+    _dev(w_fold, "w_fold", dims.dtype, (dims.n_heads, dims.d_latent, d_qlat))
+    d = dims.c()
+    _check(LIB.mla_fold_q_weights(ctypes.byref(d), d_qlat, w_uq.data_ptr(), w_uk.data_ptr(), w_fold.data_ptr(),
+                                  _stream()))

@@ -534,3 +534,178 @@ mla_status mla_prefill_mha(const mla_dims* dims, const mla_paged_cache* cache, c
 }
 
 }  // extern "C"
+
+namespace {
+
+// ---- front of the layer ---------------------------------------------------
+
+// Splits of K for an [m x n x k] projection: the first count (a divisor of
+// k / 32, at most k / 256) that gives two workgroups per CU, else the largest.
+int front_splits(int64_t m, int64_t n, int k) {
+  const int64_t tiles = ((m + 63) / 64) * ((n + 127) / 128);
+  int best = 1;
+  for (int s = 1; s <= k / 256 && s <= 64; ++s) {
+    if (k % (32 * s) != 0) continue;
+    best = s;
+    if (tiles * s >= 2 * kPlanCUs) break;
+  }
+  return best;
+}
+
+size_t front_part_bytes(int64_t m, int64_t n, int k) {
+  return static_cast<size_t>(front_splits(m, n, k)) * static_cast<size_t>(m) * static_cast<size_t>(n) * 4;
+}
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+mla_status check_front(const mla_dims* d, int64_t n, int32_t d_model, int32_t d_qlat, bool need_q) {
+  MLA_TRY(check_dims(d));
+  if (d->dtype != MLA_BF16 || d->q_lat_dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "the front projections are bf16 only");
+  if (n < 0) return fail(MLA_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > 65535LL * 64) return fail(MLA_ERR_UNSUPPORTED, "more than %lld tokens in one call", 65535LL * 64);
+  if (d_model <= 0 || d_model % 32 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "d_model must be a positive multiple of 32 (got %d)", d_model);
+  if ((need_q && d_qlat <= 0) || d_qlat < 0 || d_qlat % 32 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "d_qlat must be a positive multiple of 32 (got %d)", d_qlat);
+  if (d->d_latent % 16 != 0 || (d->n_heads * d->d_head) % 16 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "d_latent and n_heads * d_head must be multiples of 16");
+  const int64_t widest = static_cast<int64_t>(d->n_heads) * (d->d_latent + d->d_rope);
+  if (widest > (1LL << 30) || static_cast<int64_t>(d_model) * (d->d_latent + d->d_rope) * 2 > 0xffffffffLL ||
+      static_cast<int64_t>(d_qlat) * widest * 2 > 0xffffffffLL)
+    return fail(MLA_ERR_UNSUPPORTED, "a weight over 4 GiB");
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+size_t front_ws(const mla_dims* d, int64_t n, int32_t d_model, int32_t d_qlat) {
+  const int64_t kv_n = d->d_latent + d->d_rope;
+  size_t part = front_part_bytes(n, kv_n, d_model);
+  if (d_qlat > 0) {
+    part = std::max(part, front_part_bytes(n, d_qlat, d_model));
+    part = std::max(part, front_part_bytes(n, static_cast<int64_t>(d->n_heads) * (d->d_head + d->d_rope), d_qlat));
+    part = std::max(part, front_part_bytes(n, static_cast<int64_t>(d->n_heads) * (d->d_latent + d->d_rope), d_qlat));
+  }
+  return align_up(part) + align_up(static_cast<size_t>(n) * static_cast<size_t>(d_qlat) * 2);
+}
+
+void set_theta(const mla_dims* d, double* theta) {
+  for (int j = 0; j < d->d_rope / 2; ++j) theta[j] = std::pow(d->rope_base, -2.0 * j / d->d_rope);
+}
+
+// One projection: Y = X [m, k] W^T with W rows [0, n1) from w1 and [n1, n) from w2,
+// then the reduce that writes its destination.
+mla_status front_project(const mla::bf16_t* x, int64_t ldx, int64_t m, int k, const void* w1, const void* w2, int64_t n,
+                         int64_t n1, float* part, mla::FrontReduceParams rp, int mode, hipStream_t st) {
+  mla::GemmNtParams g{};
+  g.x = x; g.ldx = ldx;
+  g.w1 = static_cast<const mla::bf16_t*>(w1); g.w2 = static_cast<const mla::bf16_t*>(w2 != nullptr ? w2 : w1);
+  g.m = static_cast<int>(m); g.n = static_cast<int>(n); g.n1 = static_cast<int>(n1); g.k = k;
+  const int splits = front_splits(m, n, k);
+  g.k_split = k / splits;
+  g.part = part;
+  hipError_t e = mla::launch_gemm_nt(g, splits, st);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  rp.part = part; rp.splits = splits; rp.m = static_cast<int>(m); rp.n = static_cast<int>(n);
+  e = mla::launch_front_reduce(rp, mode, st);
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "projection reduce launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_front_workspace_size(const mla_dims* dims, int64_t n, int32_t d_model, int32_t d_qlat) {
+  g_err.clear();
+  if (check_front(dims, n, d_model, d_qlat, false) != MLA_OK) return 0;
+  return front_ws(dims, n, d_model, d_qlat);
+}
+
+mla_status mla_kv_project(const mla_dims* dims, const mla_paged_cache* cache, const void* h, int64_t n,
+                          int32_t d_model, const void* w_dkv, const void* w_kr, const int32_t* kv_seq,
+                          const int32_t* kv_pos, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  MLA_TRY(check_front(dims, n, d_model, 0, false));
+  if (n == 0) return MLA_OK;
+  MLA_TRY(check_cache(cache));
+  if (h == nullptr || w_dkv == nullptr || w_kr == nullptr || kv_seq == nullptr || kv_pos == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "h, w_dkv, w_kr, kv_seq and kv_pos must be non-NULL");
+  if (!aligned16(h) || !aligned16(w_dkv) || !aligned16(w_kr))
+    return fail(MLA_ERR_INVALID_ARG, "h and the weights must be 16-byte aligned");
+  const size_t need = front_ws(dims, n, d_model, 0);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  mla::FrontReduceParams rp{};
+  rp.n_heads = dims->n_heads; rp.d_head = dims->d_head; rp.d_latent = dims->d_latent; rp.d_rope = dims->d_rope;
+  rp.cache = cache->data; rp.num_pages = cache->num_pages; rp.block_table = cache->block_table;
+  rp.max_pages = cache->max_pages_per_seq; rp.kv_seq = kv_seq; rp.kv_pos = kv_pos;
+  set_theta(dims, rp.theta);
+  return front_project(static_cast<const mla::bf16_t*>(h), d_model, n, d_model, w_dkv, w_kr,
+                       dims->d_latent + dims->d_rope, dims->d_latent, static_cast<float*>(workspace), rp,
+                       mla::kFrontKv, as_stream(stream));
+}
+
+static mla_status q_project_impl(const mla_dims* dims, const void* h, int64_t n, int32_t d_model, int32_t d_qlat,
+                                 const void* w_dq, const void* w_up, const void* w_qr, const int32_t* q_pos,
+                                 void* q_nope, void* q_lat, void* workspace, size_t workspace_bytes, void* stream,
+                                 bool folded) {
+  g_err.clear();
+  MLA_TRY(check_front(dims, n, d_model, d_qlat, true));
+  if (n == 0) return MLA_OK;
+  if (h == nullptr || w_dq == nullptr || w_up == nullptr || w_qr == nullptr || q_pos == nullptr ||
+      q_lat == nullptr || (!folded && q_nope == nullptr))
+    return fail(MLA_ERR_INVALID_ARG, folded ? "h, w_dq, w_fold, w_qr, q_pos and q_lat must be non-NULL"
+                                            : "h, w_dq, w_uq, w_qr, q_pos, q_nope and q_lat must be non-NULL");
+  if (!aligned16(h) || !aligned16(w_dq) || !aligned16(w_up) || !aligned16(w_qr))
+    return fail(MLA_ERR_INVALID_ARG, "h and the weights must be 16-byte aligned");
+  const size_t need = front_ws(dims, n, d_model, d_qlat);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  const size_t part_bytes = need - align_up(static_cast<size_t>(n) * static_cast<size_t>(d_qlat) * 2);
+  float* part = static_cast<float*>(workspace);
+  mla::bf16_t* cq = reinterpret_cast<mla::bf16_t*>(static_cast<char*>(workspace) + part_bytes);
+  const hipStream_t st = as_stream(stream);
+  // the query latent c^Q = W_DQ h, kept in bf16
+  mla::FrontReduceParams rp{};
+  rp.n_heads = dims->n_heads; rp.d_head = dims->d_head; rp.d_latent = dims->d_latent; rp.d_rope = dims->d_rope;
+  rp.y = cq; rp.ldy = d_qlat;
+  set_theta(dims, rp.theta);
+  MLA_TRY(front_project(static_cast<const mla::bf16_t*>(h), d_model, n, d_model, w_dq, nullptr, d_qlat, d_qlat, part, rp,
+                        mla::kFrontPlain, st));
+  // the content (or folded) and position queries from c^Q
+  rp.y = nullptr;
+  rp.q_nope = static_cast<mla::bf16_t*>(q_nope); rp.q_lat = static_cast<mla::bf16_t*>(q_lat); rp.q_pos = q_pos;
+  const int64_t w0 = folded ? dims->d_latent : dims->d_head;
+  return front_project(cq, d_qlat, n, d_qlat, w_up, w_qr, static_cast<int64_t>(dims->n_heads) * (w0 + dims->d_rope),
+                       static_cast<int64_t>(dims->n_heads) * w0, part, rp, folded ? mla::kFrontQFolded : mla::kFrontQ,
+                       st);
+}
+
+mla_status mla_q_project(const mla_dims* dims, const void* h, int64_t n, int32_t d_model, int32_t d_qlat,
+                         const void* w_dq, const void* w_uq, const void* w_qr, const int32_t* q_pos, void* q_nope,
+                         void* q_lat, void* workspace, size_t workspace_bytes, void* stream) {
+  return q_project_impl(dims, h, n, d_model, d_qlat, w_dq, w_uq, w_qr, q_pos, q_nope, q_lat, workspace,
+                        workspace_bytes, stream, false);
+}
+
+mla_status mla_q_project_folded(const mla_dims* dims, const void* h, int64_t n, int32_t d_model, int32_t d_qlat,
+                                const void* w_dq, const void* w_fold, const void* w_qr, const int32_t* q_pos,
+                                void* q_lat, void* workspace, size_t workspace_bytes, void* stream) {
+  return q_project_impl(dims, h, n, d_model, d_qlat, w_dq, w_fold, w_qr, q_pos, nullptr, q_lat, workspace,
+                        workspace_bytes, stream, true);
+}
+
+mla_status mla_fold_q_weights(const mla_dims* dims, int32_t d_qlat, const void* w_uq, const void* w_uk, void* w_fold,
+                              void* stream) {
+  g_err.clear();
+  MLA_TRY(check_front(dims, 0, 32, d_qlat, true));
+  if (w_uq == nullptr || w_uk == nullptr || w_fold == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "w_uq, w_uk and w_fold must be non-NULL");
+  mla::FoldParams p{static_cast<const mla::bf16_t*>(w_uq), static_cast<const mla::bf16_t*>(w_uk), static_cast<mla::bf16_t*>(w_fold),
+                    dims->n_heads, dims->d_head, dims->d_latent, d_qlat};
+  const hipError_t e = mla::launch_fold(p, as_stream(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "fold launch");
+}
+
+}  // extern "C"

@@ -85,6 +85,40 @@ struct GemmParams {
   const void* a; const void* w; void* out; int64_t n;
 };
 
+// Front of the layer: Y = X W^T in split-K partials, then a reduce that
+// writes the projection's destination.
+struct GemmNtParams {
+  const bf16_t* x; int64_t ldx;           // [M, K] activations, row stride ldx elements
+  const bf16_t* w1; const bf16_t* w2;     // weight rows [0, n1) from w1, [n1, n) from w2, each [rows, K]
+  int m, n, n1, k, k_split;               // k_split: K elements per split (a multiple of 32)
+  float* part;                            // [splits, M, N] float32
+};
+
+enum FrontMode { kFrontPlain = 0, kFrontKv = 1, kFrontQ = 2, kFrontQFolded = 3 };
+
+struct FrontReduceParams {
+  const float* part; int splits; int m, n;
+  // plain: bf16 y [M, ldy]
+  bf16_t* y; int64_t ldy;
+  // shape
+  int n_heads, d_head, d_latent, d_rope;
+  // kv: the cache row [c | R_p k^R] of (kv_seq, kv_pos)
+  void* cache; int64_t num_pages; const int32_t* block_table; int32_t max_pages;
+  const int32_t* kv_seq; const int32_t* kv_pos;
+  // q: q_nope [M, H, d_head], q_lat [M, H, d_latent + d_rope], positions
+  bf16_t* q_nope; bf16_t* q_lat; const int32_t* q_pos;
+  double theta[64];
+};
+
+struct FoldParams {
+  const bf16_t* w_uq; const bf16_t* w_uk; bf16_t* w_fold;  // [H, d_h, d_q], [H, d_h, d_c] -> [H, d_c, d_q]
+  int n_heads, d_head, d_latent, d_qlat;
+};
+
+hipError_t launch_gemm_nt(const GemmNtParams& p, int splits, hipStream_t s);
+hipError_t launch_front_reduce(const FrontReduceParams& p, int mode, hipStream_t s);
+hipError_t launch_fold(const FoldParams& p, hipStream_t s);
+
 // Decode / prefill attention over the paged latent cache.
 struct AttnParams {
   // shape

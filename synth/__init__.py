@@ -271,3 +271,63 @@ def config5_prefill(seed: int = 5) -> Case:
     case = direct_prefill(DSV2, "bf16", [16384], [2048], seed + 1000)
     case.note["workload"] = "MLA chunked causal prefill bf16, 2048 new over 16384 cached"
     return case
+
+
+@dataclass
+class FrontCase:
+    """Hidden states and the projection weights of one layer (the front of the layer).
+
+    h [total tokens, d_model] in (sequence, position) row order; the weights
+    W_DKV [d_c, d_model], W_KR [d_r, d_model], W_DQ [d_q, d_model],
+    W_UQ [H, d_h, d_q], W_QR [H, d_r, d_q], W_UK [H, d_h, d_c], W_UV [H, d_v, d_c].
+    """
+    shape: Shape
+    d_model: int
+    d_qlat: int
+    seq_lens: np.ndarray
+    h: np.ndarray
+    w_dkv: np.ndarray
+    w_kr: np.ndarray
+    w_dq: np.ndarray
+    w_uq: np.ndarray
+    w_qr: np.ndarray
+    w_uk: np.ndarray
+    w_uv: np.ndarray
+    block_table: np.ndarray
+    num_pages: int
+    seed: int = 0
+
+    @property
+    def row_offsets(self) -> np.ndarray:
+        return _offsets(self.seq_lens)
+
+    def kv_seq_pos(self):
+        seqs = np.repeat(np.arange(len(self.seq_lens), dtype=np.int32), self.seq_lens)
+        pos = np.concatenate([np.arange(t, dtype=np.int32) for t in self.seq_lens]) \
+            if len(self.seq_lens) else np.zeros(0, np.int32)
+        return seqs, pos
+
+
+def front_layer(shape: Shape, seq_lens, d_model: int, d_qlat: int, seed: int, shuffle: bool = True,
+                dtype: str = "bf16") -> FrontCase:
+    """h ~ N(0,1); every weight ~ N(0,1)/sqrt(fan_in) (fan_in = its input width).
+    Draw order: h, W_DKV, W_KR, W_DQ, W_UQ, W_QR, W_UK, W_UV, then the page permutation.
+    All values rounded to the storage dtype."""
+    s = shape
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    rng = np.random.default_rng(seed)
+    total = int(seq_lens.sum())
+
+    def w(shape_, fan_in):
+        return to_storage(rng.standard_normal(shape_) / math.sqrt(fan_in), dtype)
+
+    h = to_storage(rng.standard_normal((total, d_model)), dtype)
+    w_dkv = w((s.d_latent, d_model), d_model)
+    w_kr = w((s.d_rope, d_model), d_model)
+    w_dq = w((d_qlat, d_model), d_model)
+    w_uq = w((s.n_heads, s.d_head, d_qlat), d_qlat)
+    w_qr = w((s.n_heads, s.d_rope, d_qlat), d_qlat)
+    w_uk = w((s.n_heads, s.d_head, s.d_latent), s.d_latent)
+    w_uv = w((s.n_heads, s.d_v, s.d_latent), s.d_latent)
+    table, pool = allocate_pages(seq_lens, s.page_size, rng, shuffle)
+    return FrontCase(s, d_model, d_qlat, seq_lens, h, w_dkv, w_kr, w_dq, w_uq, w_qr, w_uk, w_uv, table, pool, seed)

@@ -180,3 +180,44 @@ def test_choose_prefill_form():
     assert mla.choose_prefill_form(dsv2, i32(0, 2048), i32(16384), workspace_limit=1 << 20) == "absorbed"
     f32 = mla.MLADims(16, 128, 128, 256, 32, dtype=torch.float32)
     assert mla.choose_prefill_form(f32, i32(0, 1024), i32(0)) == "absorbed"
+
+
+def test_front_projections_validate():
+    """The front-of-layer calls: workspace sizing and every rejection, before any launch."""
+    d = _dims()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    ws_kv = B.LIB.mla_front_workspace_size(ctypes.byref(d), 64, 5120, 0)
+    ws_q = B.LIB.mla_front_workspace_size(ctypes.byref(d), 64, 5120, 1536)
+    assert 0 < ws_kv < ws_q
+    assert ws_q % 256 == 0
+    assert B.LIB.mla_front_workspace_size(ctypes.byref(d), 64, 5000, 1536) == 0      # d_model % 32
+    assert B.LIB.mla_front_workspace_size(ctypes.byref(d), 64, 5120, 1500) == 0      # d_qlat % 32
+    assert B.LIB.mla_front_workspace_size(ctypes.byref(_dims(dtype=0, q_lat_dtype=0)), 64, 5120, 1536) == 0
+    cache = B.PagedCache(FAKE.value, 4, FAKE.value, 2, 4)
+    seq = ctypes.cast(FAKE, i32p)
+
+    def kv(dims=d, n=64, d_model=5120, h=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return B.LIB.mla_kv_project(ctypes.byref(dims), ctypes.byref(cache), h, n, d_model, FAKE, FAKE, seq, seq,
+                                    ws, ws_bytes, None)
+
+    assert kv(n=0) == 0                      # nothing to do, nothing launched
+    assert kv(d_model=100) == 1
+    assert kv(dims=_dims(dtype=0, q_lat_dtype=0)) == 2
+    assert kv(h=None) == 1
+    assert kv(h=ctypes.c_void_p(FAKE.value + 2)) == 1  # misaligned
+    assert kv(ws_bytes=ws_kv - 1) == 3
+    assert kv(ws=None) == 3
+
+    def q(folded=False, n=64, d_qlat=1536, q_nope=FAKE, ws_bytes=1 << 40):
+        if folded:
+            return B.LIB.mla_q_project_folded(ctypes.byref(d), FAKE, n, 5120, d_qlat, FAKE, FAKE, FAKE, seq, FAKE,
+                                              FAKE, ws_bytes, None)
+        return B.LIB.mla_q_project(ctypes.byref(d), FAKE, n, 5120, d_qlat, FAKE, FAKE, FAKE, seq, q_nope, FAKE, FAKE,
+                                   ws_bytes, None)
+
+    assert q(n=0) == 0 and q(folded=True, n=0) == 0
+    assert q(d_qlat=0) == 1 and q(folded=True, d_qlat=0) == 1
+    assert q(q_nope=None) == 1               # the unfolded form writes q_nope
+    assert q(ws_bytes=ws_q - 1) == 3 and q(folded=True, ws_bytes=ws_q - 1) == 3
+    assert B.LIB.mla_fold_q_weights(ctypes.byref(d), 1536, None, FAKE, FAKE, None) == 1
+    assert B.LIB.mla_fold_q_weights(ctypes.byref(d), 100, FAKE, FAKE, FAKE, None) == 1
