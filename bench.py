@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "absorbed MLA decode tokens/s + % HBM roofline (n_h=128,d_c=512,d_r=64)"
 HBM_PEAK_GBS = 8000.0
+QUERY_LATENT = 1536  # the query latent width of the DeepSeek-V2-like layer
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "attn_bf16.hip")
@@ -155,6 +156,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--front", default="none", choices=["none", "unfolded", "folded"],
+                    help="decode workloads: start the step from hidden states (d_model 5120, query latent 1536): "
+                         "kv_project + q_project + absorb_q (or q_project_folded) + decode + out_proj")
     ap.add_argument("--prefill-form", default="absorbed", choices=["absorbed", "materialised"],
                     help="prefill workloads: absorbed latent attention (mla_prefill) or per-head keys and "
                          "values up-projected first (mla_prefill_mha)")
@@ -208,10 +212,47 @@ def main():
     q_nope, q_rope = dev(case.qc), dev(case.qr)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    events = DeviceEvents(2 * args.steps)
+    events = DeviceEvents(3 * args.steps)
     ev = []
 
-    if case.kind == "decode":
+    front_ev = []
+    front_bytes = 0
+    if case.kind == "decode" and args.front != "none":
+        d_model, d_qlat = s.hidden, QUERY_LATENT
+        folded = args.front == "folded"
+        fc = synth.front_layer(s, np.ones(case.batch, np.int32), d_model, d_qlat, seed=case.seed + 100, shuffle=False)
+        w_dkv, w_kr, w_dq, w_qr = dev(fc.w_dkv), dev(fc.w_kr), dev(fc.w_dq), dev(fc.w_qr)
+        w_uk, w_uv = dev(fc.w_uk), dev(fc.w_uv)
+        w_up = dev(fc.w_uq)
+        if folded:  # weight preparation, once, outside the timed region
+            w_fold = torch.empty((s.n_heads, s.d_latent, d_qlat), dtype=dt, device="cuda")
+            B.fold_q_weights(dims, w_up, w_uk, w_fold)
+            w_up = w_fold
+        h_new = dev(fc.h)
+        steps = [mla.LayerDecodeStep(dims, c, torch.from_numpy(case.seq_lens), d_model, d_qlat, folded)
+                 for c in caches]
+        front_bytes = 2 * (w_dkv.numel() + w_kr.numel() + w_dq.numel() + w_qr.numel() + w_up.numel()
+                           + (0 if folded else w_uk.numel()))
+
+        def step(i, timed):
+            st = steps[i % len(steps)]
+            f0 = events.record(sh) if timed else None
+            st.kv(h_new, w_dkv, w_kr)
+            st.query(h_new, w_dq, w_up, w_qr, w_uk)
+            if timed:
+                e0 = events.record(sh)
+                front_ev.append((f0, e0))
+            inner = st.inner
+            B.decode(dims, inner.cache.data, inner.cache.block_table, inner.q_lat, inner.seq_lens,
+                     inner.seq_lens_host, inner.out_latent, inner.lse, inner.workspace)
+            if timed:
+                ev.append((e0, events.record(sh)))
+            B.out_proj(dims, inner.out_latent, w_uv, inner.out)
+        tokens_per_step = case.batch
+        kernel_name = "mla_decode (split attention + merge)"
+        algo = decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope)
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+    elif case.kind == "decode":
         steps = [mla.DecodeStep(dims, c, torch.from_numpy(case.seq_lens)) for c in caches]
         last = case.row_offsets + np.maximum(case.seq_lens - 1, 0)
         new_lat, new_kr = dev(case.c_rows[last]), dev(case.kr_rows[last])
@@ -280,6 +321,7 @@ def main():
     el = time.perf_counter() - t0
     ms_per_step = el / args.steps * 1e3
     kern_ms = float(np.mean([events.elapsed_ms(a, b) for a, b in ev]))
+    front_ms = float(np.mean([events.elapsed_ms(a, b) for a, b in front_ev])) if front_ev else None
     events.close()
     achieved = algo / (kern_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
     if case.kind == "decode" or args.prefill_form == "absorbed":
@@ -287,7 +329,9 @@ def main():
     else:
         traffic = load_traffic(args.config + "_mha", MHA_SRC)
     out = {
-        "metric": (METRIC if case.kind == "decode" else
+        "metric": (METRIC if case.kind == "decode" and args.front == "none" else
+                   "MLA decode layer step from hidden states tokens/s + % HBM roofline of mla_decode"
+                   if case.kind == "decode" else
                    "absorbed MLA causal prefill tokens/s + % MFMA roofline" if args.prefill_form == "absorbed" else
                    "MLA causal prefill, materialised form, tokens/s + % MFMA roofline"),
         "value": tokens_per_step / (ms_per_step * 1e-3),
@@ -306,12 +350,17 @@ def main():
                    "n_heads": s.n_heads, "d_latent": s.d_latent, "d_rope": s.d_rope, "page_size": s.page_size,
                    "cache_copies": len(caches),
                    "step": ("rope_apply + prefill_mha" if case.kind != "decode" and args.prefill_form == "materialised"
+                            else f"kv_project + q_project ({args.front}) + decode + out_proj" if args.front != "none"
                             else "rope_apply + absorb_q + decode/prefill + out_proj")},
         "roofline": {"kernel": kernel_name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic, "algorithmic_per_launch": algo,
                      "avg_launch_ms": kern_ms},
     }
-    if case.kind == "decode" and not args.no_cpu_baseline:
+    if front_ms is not None:
+        out["front"] = {"form": args.front, "d_model": s.hidden, "d_qlat": QUERY_LATENT, "avg_ms": front_ms,
+                        "weight_bytes": front_bytes, "weight_GBps": front_bytes / (front_ms * 1e-3) / 1e9,
+                        "calls": "kv_project + q_project" + (" + absorb_q" if args.front == "unfolded" else "")}
+    if case.kind == "decode" and not args.no_cpu_baseline and args.front == "none":
         out["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(out), flush=True)
 

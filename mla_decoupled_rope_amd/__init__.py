@@ -11,4 +11,4 @@ from .binding import (  # noqa: F401
     decode_workspace_size, fold_q_weights, front_workspace, front_workspace_size, kv_project, out_proj, prefill,
     prefill_mha, prefill_mha_workspace, prefill_mha_workspace_size, q_project, q_project_folded, rope_apply,
 )
-from .pipeline import DecodeStep, LatentCache, PrefillStep, choose_prefill_form  # noqa: F401
+from .pipeline import DecodeStep, LatentCache, LayerDecodeStep, PrefillStep, choose_prefill_form  # noqa: F401

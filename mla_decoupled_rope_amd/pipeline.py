@@ -4,6 +4,9 @@
 * ``DecodeStep``   -- rope_apply (new token + q^R) -> absorb_q -> decode
                       (split + merge) -> out_proj, with every buffer
                       preallocated so a step launches kernels only.
+* ``LayerDecodeStep`` -- the same step from hidden states: kv_project (the new
+                      token's cache row) -> q_project -> absorb_q (or
+                      q_project_folded) -> decode -> out_proj.
 * ``PrefillStep``  -- rope_apply (chunk rows + q^R) -> absorb_q -> prefill ->
                       out_proj, or rope_apply -> prefill_mha (the materialised
                       form); ``choose_prefill_form`` picks between them.
@@ -170,3 +173,46 @@ class PrefillStep:
         B.prefill_mha(d, self.cache.data, self.cache.block_table, q_nope, self.q_lat, w_uk, w_uv, self.cu_q,
                       self.q_start, self.cu_q_host, self.q_start_host, self.out, self.lse, self.mha_workspace)
         return self.out
+
+
+class LayerDecodeStep:
+    """One decode step from hidden states h [B, d_model] of each sequence's newest token.
+
+    The token sits at position seq_lens[b] - 1: kv_project writes its cache row,
+    the query goes through the query latent (q_project + absorb_q, or
+    q_project_folded with a pre-folded W_UK), then decode and out_proj.
+    """
+
+    def __init__(self, dims: B.MLADims, cache: LatentCache, seq_lens_host: torch.Tensor, d_model: int, d_qlat: int,
+                 folded: bool = False, device="cuda"):
+        self.inner = DecodeStep(dims, cache, seq_lens_host, device)
+        self.dims, self.cache, self.folded = dims, cache, folded
+        n = self.inner.seq_lens_host.numel()
+        self.q_nope = torch.empty((n, dims.n_heads, dims.d_head), dtype=dims.dtype, device=device)
+        self.front_ws = B.front_workspace(dims, n, d_model, d_qlat, device)
+
+    def kv(self, h, w_dkv, w_kr):
+        s = self.inner
+        B.kv_project(self.dims, self.cache.data, self.cache.block_table, h, w_dkv, w_kr, s.kv_seq, s.q_pos,
+                     self.front_ws)
+
+    def query(self, h, w_dq, w_up, w_qr, w_uk):
+        """w_up is W_UQ, or W_fold when the step is folded."""
+        s = self.inner
+        if self.folded:
+            B.q_project_folded(self.dims, h, w_dq, w_up, w_qr, s.q_pos, s.q_lat, self.front_ws)
+        else:
+            B.q_project(self.dims, h, w_dq, w_up, w_qr, s.q_pos, self.q_nope, s.q_lat, self.front_ws)
+            B.absorb_q(self.dims, self.q_nope, w_uk, s.q_lat)
+
+    def attend(self, w_uv):
+        s, d = self.inner, self.dims
+        B.decode(d, self.cache.data, self.cache.block_table, s.q_lat, s.seq_lens, s.seq_lens_host, s.out_latent,
+                 s.lse, s.workspace)
+        B.out_proj(d, s.out_latent, w_uv, s.out)
+        return s.out
+
+    def run(self, h, w_dkv, w_kr, w_dq, w_up, w_qr, w_uk, w_uv):
+        self.kv(h, w_dkv, w_kr)
+        self.query(h, w_dq, w_up, w_qr, w_uk)
+        return self.attend(w_uv)
