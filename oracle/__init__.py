@@ -20,9 +20,12 @@ equations:
                      c = W_DKV h, the position key W_KR h, the query latent
                      c^Q = W_DQ h and its content / position projections, and
                      the folded query weight W_UK^T W_UQ.
+* ``obstruction`` -- why the rotated key cannot be absorbed: the position-
+                     operator family W_QR^T R_delta W_UKR, its span over the
+                     shifts, and the best single matrix with its residual.
 
 No function here shares code with the GPU path, and none reads any value the
 GPU produced.
 """
 
-from . import accounting, attention, front, paging, rope  # noqa: F401
+from . import accounting, attention, front, obstruction, paging, rope  # noqa: F401

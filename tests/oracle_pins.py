@@ -16,7 +16,7 @@ import os
 import numpy as np
 
 import oracle
-from oracle import accounting, attention, front, paging, rope
+from oracle import accounting, attention, front, obstruction, paging, rope
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
 
@@ -346,12 +346,112 @@ def pin_latent_path_reduces_to_direct_query():
     assert _rel(got, (h @ w_q.T).reshape(n, n_heads, d_h)) <= 1e-14
 
 
+# ------------------------------------------------- the RoPE obstruction ----
+# "ropeabsorb" README, "RoPE spans exactly d_R dimensions and cannot be folded"
+# and "Partial absorption is impossible".
+
+def _obstruction_weights(seed, d_r, d_q=6, d_c=5):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((d_r, d_q)), rng.standard_normal((d_r, d_c))
+
+
+def pin_obstruction_one_pair_by_hand():
+    """d_R = 2 (theta = 1) expanded by hand: with W_QR rows q0, q1 and W_UKR rows k0, k1,
+    F_delta = cos(delta) (q0 k0^T + q1 k1^T) + sin(delta) (q1 k0^T - q0 k1^T).  Both the
+    family and its per-frequency decomposition must equal this, entry by entry."""
+    w_qr, w_ukr = _obstruction_weights(11, 2)
+    q0, q1, k0, k1 = w_qr[0], w_qr[1], w_ukr[0], w_ukr[1]
+    deltas = [0, 1, 2, 7, -3]
+    fam = obstruction.family(w_qr, w_ukr, deltas)
+    mc, ms = obstruction.frequency_components(w_qr, w_ukr)
+    via = obstruction.family_from_components(mc, ms, [1.0], deltas)
+    for n, d in enumerate(deltas):
+        c, s = math.cos(d), math.sin(d)
+        for a in range(w_qr.shape[1]):
+            for b in range(w_ukr.shape[1]):
+                want = c * (q0[a] * k0[b] + q1[a] * k1[b]) + s * (q1[a] * k0[b] - q0[a] * k1[b])
+                assert math.isclose(fam[n, a, b], want, rel_tol=1e-12, abs_tol=1e-12)
+                assert math.isclose(via[n, a, b], want, rel_tol=1e-12, abs_tol=1e-12)
+
+
+def pin_obstruction_is_the_rotated_score():
+    """The family at delta = t - m is the operator inside the rotated score: for a query input x
+    at position m and a key input y at t, (R_m W_QR x) . (R_t W_UKR y) = x^T F_{t-m} y.  The same
+    holds for coupled RoPE with W_UQ, W_UK over the whole head, so that family is the coupled one."""
+    rng = np.random.default_rng(12)
+    for d_r, fam_fn in ((8, obstruction.family), (12, obstruction.coupled_family)):
+        w_q, w_k = _obstruction_weights(13 + d_r, d_r)
+        for m, t in ((0, 0), (3, 10), (10, 3), (100, 4095)):
+            x = rng.standard_normal(w_q.shape[1])
+            y = rng.standard_normal(w_k.shape[1])
+            want = float(rope.rotate(w_q @ x, m) @ rope.rotate(w_k @ y, t))
+            got = float(x @ fam_fn(w_q, w_k, [t - m])[0] @ y)
+            assert math.isclose(got, want, rel_tol=1e-11, abs_tol=1e-11), (d_r, m, t, got, want)
+
+
+def pin_obstruction_decomposition():
+    """The family is the sum of its per-frequency cosine and sine parts at RoFormer's
+    frequencies, for several d_R and signed shifts."""
+    for d_r in (4, 8, 16):
+        w_qr, w_ukr = _obstruction_weights(d_r, d_r)
+        deltas = np.array([0, 1, 5, 64, 1000, -17])
+        mc, ms = obstruction.frequency_components(w_qr, w_ukr)
+        th = np.array([10000.0 ** (-2.0 * j / d_r) for j in range(d_r // 2)])
+        assert _rel(obstruction.family(w_qr, w_ukr, deltas),
+                    obstruction.family_from_components(mc, ms, th, deltas)) <= 1e-12
+
+
+def pin_obstruction_span():
+    """The span over the shifts is exactly d_R = 2L for distinct nonzero frequencies and never
+    more, whatever the weights' scale; the no-RoPE control spans 1; equal frequencies (base 1,
+    every theta = 1) span 2 however many pairs there are."""
+    deltas = np.arange(4096)
+    for d_r in (2, 4, 8, 16):
+        w_qr, w_ukr = _obstruction_weights(20 + d_r, d_r, d_q=9, d_c=7)
+        for scale in (1.0, 1e-14, 1e6):
+            rank, _, gap = obstruction.span(obstruction.family(w_qr * scale, w_ukr, deltas))
+            assert rank == d_r and gap < 1e-12, (d_r, scale, rank, gap)
+        assert obstruction.span(obstruction.family(w_qr, w_ukr, np.zeros(16)))[0] == 1
+        assert obstruction.span(obstruction.family(w_qr, w_ukr, deltas[:64], base=1.0))[0] == min(2, d_r)
+    w_uq, w_uk = _obstruction_weights(29, 24, d_q=9, d_c=7)
+    assert obstruction.span(obstruction.coupled_family(w_uq, w_uk, deltas))[0] == 24
+
+
+def pin_obstruction_best_single_matrix():
+    """The returned constant minimises the summed squared error (a random step away from it
+    raises the error, computed member by member); a frequency sampled over whole periods has
+    no constant part (share 1); the no-RoPE control is absorbed exactly (share 0); and the
+    residual grows with the range of shifts, as the page reports."""
+    w_qr, w_ukr = _obstruction_weights(31, 8)
+    fam = obstruction.family(w_qr, w_ukr, np.arange(300))
+    m, share = obstruction.best_single_matrix(fam)
+
+    def err(x):
+        return sum(float(np.sum((f - x) ** 2)) for f in fam)
+
+    total = sum(float(np.sum(f * f)) for f in fam)
+    assert math.isclose(share, err(m) / total, rel_tol=1e-12)
+    rng = np.random.default_rng(32)
+    for _ in range(4):
+        e = rng.standard_normal(m.shape)
+        assert err(m + 1e-3 * e) > err(m) and err(m - 1e-3 * e) > err(m)
+    mc, ms = obstruction.frequency_components(w_qr[:2], w_ukr[:2])
+    periodic = obstruction.family_from_components(mc, ms, [2.0 * math.pi / 8.0], np.arange(64))
+    assert abs(obstruction.best_single_matrix(periodic)[1] - 1.0) <= 1e-12
+    control = obstruction.family(w_qr, w_ukr, np.zeros(5))
+    assert obstruction.best_single_matrix(control)[1] <= 1e-28
+    r = obstruction.report()["residual_by_window"]
+    assert 0.0 < r[128] < r[1024] < r[4096] < 1.0
+
+
 ALL_PINS = [
     pin_rope_identity_at_zero, pin_rope_closed_form, pin_rope_orthogonal, pin_rope_relative,
     pin_shift_invariance, pin_absorbed_equals_materialised, pin_key_rank, pin_brute_force,
     pin_special_cases, pin_sdpa, pin_prefill_is_decode_of_prefix, pin_paging, pin_page_figures,
     pin_front_unit_vectors, pin_front_brute_force, pin_fold_equals_absorbed_query,
-    pin_latent_path_reduces_to_direct_query,
+    pin_latent_path_reduces_to_direct_query, pin_obstruction_one_pair_by_hand, pin_obstruction_is_the_rotated_score,
+    pin_obstruction_decomposition,
+    pin_obstruction_span, pin_obstruction_best_single_matrix,
 ]
 
 

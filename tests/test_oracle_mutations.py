@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle_pins as pins
-from oracle import attention, front, paging, rope
+from oracle import attention, front, obstruction, paging, rope
 
 _orig_rotate = rope.rotate
 _orig_thetas = rope.thetas
@@ -17,6 +17,9 @@ _orig_keys = attention.materialise_keys
 _orig_visible = attention._visible
 _orig_slot = paging.slot
 _orig_fold = front.fold_query_weights
+_orig_components = obstruction.frequency_components
+_orig_family = obstruction.family
+_orig_span = obstruction.span
 
 
 def _clockwise_rotate(x, positions, base=10000.0):
@@ -102,6 +105,40 @@ def _position_query_from_content(cq, w_qr):
     return np.einsum("hrq,nq->nhr", np.asarray(w_qr, np.float64), np.asarray(cq, np.float64)) * 0.0
 
 
+def _components_sine_flipped(w_qr, w_ukr):
+    # J taken as the clockwise quarter turn
+    mc, ms = _orig_components(w_qr, w_ukr)
+    return mc, -ms
+
+
+def _family_ignores_shift(w_qr, w_ukr, deltas, base=10000.0):
+    return _orig_family(w_qr, w_ukr, np.zeros(len(deltas)), base)
+
+
+def _family_half_the_pairs(w_qr, w_ukr, deltas, base=10000.0):
+    # only the first half of the rotated dimensions carried into the family
+    h = max(2, (np.asarray(w_qr).shape[0] // 4) * 2)
+    return _orig_family(np.asarray(w_qr)[:h], np.asarray(w_ukr)[:h], deltas, base)
+
+
+def _family_reversed_shift(w_qr, w_ukr, deltas, base=10000.0):
+    # delta taken as query position minus key position
+    return _orig_family(w_qr, w_ukr, -np.asarray(deltas), base)
+
+
+def _span_absolute_cliff(fam, cliff=1e-10):
+    rows = np.asarray(fam, np.float64).reshape(len(fam), -1)
+    sv = np.linalg.svd(rows, compute_uv=False)
+    rank = int(np.sum(sv > cliff))
+    return rank, sv, float(sv[rank] / sv[0]) if 0 < rank < sv.size else 0.0
+
+
+def _dc_first_member(fam):
+    fam = np.asarray(fam, np.float64)
+    m = fam[0]
+    return m, float(np.sum((fam - m) ** 2) / np.sum(fam * fam))
+
+
 MUTATIONS = {
     "rope_clockwise": [(rope, "rotate", _clockwise_rotate), (rope, "rotation_matrix", _clockwise_matrix)],
     "rope_half_split_pairs": [(rope, "rotate", _half_split_rotate)],
@@ -117,6 +154,12 @@ MUTATIONS = {
     "front_fold_wrong_index": [(front, "fold_query_weights", _fold_wrong_side)],
     "front_query_heads_swapped": [(front, "content_query", _query_skips_latent)],
     "front_position_query_dropped": [(front, "position_query", _position_query_from_content)],
+    "obstruction_sine_flipped": [(obstruction, "frequency_components", _components_sine_flipped)],
+    "obstruction_family_ignores_shift": [(obstruction, "family", _family_ignores_shift)],
+    "obstruction_family_reversed_shift": [(obstruction, "family", _family_reversed_shift)],
+    "obstruction_family_half_pairs": [(obstruction, "family", _family_half_the_pairs)],
+    "obstruction_absolute_cliff": [(obstruction, "span", _span_absolute_cliff)],
+    "obstruction_dc_first_member": [(obstruction, "best_single_matrix", _dc_first_member)],
 }
 
 
