@@ -34,9 +34,11 @@ cases only.
 
 Readings where the pages are silent (each also used by the GPU path):
 
-* One softmax scale on the summed score (the operatorworld.com page writes
-  separate 1/sqrt(d) and 1/sqrt(d_r) factors; a caller reaches that form by
-  pre-scaling q^R).
+* One softmax scale on the summed score by default.  The operatorworld.com
+  page's decoupled-RoPE section writes the score with its own factor on each
+  channel (content over sqrt(d), position over sqrt(d_r)); every evaluation
+  here takes that form when ``position_scale`` is given:
+      s_t = scale * (q^C . k^C_t) + position_scale * (R_m q^R . R_t k^R_t).
 * Key t sits at position t; a decode query sees keys 0 .. T-1 (its own token
   is already in the cache); a causal query at position m sees keys t <= m.
 * A query with no visible key has obar = 0, o = 0 and lse = -inf.
@@ -73,12 +75,18 @@ def _softmax(s: np.ndarray, visible: np.ndarray):
 def materialise_keys(c, kr, w_uk, key_pos, base=10000.0):
     """K_i[t] = [W_UK,i c_t ; R_{pos t} k^R_t] for every head i.  Returns [T, H, d_h + d_r].
 
-    The position part is one vector per token, the same for every head.
+    kr [T, d_r]: one position key per token, the same for every head (the
+    decoupled design).  kr [T, H, d_r]: one position key per head and token,
+    K_i[t] = [W_UK,i c_t ; R_{pos t} k^R_{t,i}] (the simplified MLA-style
+    cache of "Multi-Head Latent Attention", "A concrete size comparison").
     """
     c = np.asarray(c, np.float64)
     w_uk = np.asarray(w_uk, np.float64)
+    kr = np.asarray(kr, np.float64)
     h, d_h, _ = w_uk.shape
     k_content = (c @ w_uk.reshape(h * d_h, -1).T).reshape(c.shape[0], h, d_h)
+    if kr.ndim == 3:
+        return np.concatenate([k_content, rope.rotate(kr, np.asarray(key_pos)[:, None], base)], axis=-1)
     k_rope = rope.rotate(kr, np.asarray(key_pos), base)
     return np.concatenate(
         [k_content, np.broadcast_to(k_rope[:, None, :], (c.shape[0], h, k_rope.shape[-1]))], axis=-1)
@@ -93,13 +101,17 @@ def materialise_values(c, w_uv):
 
 
 def materialised(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False,
-                 key_chunk=2048, key_offset=0):
+                 key_chunk=2048, key_offset=0, position_scale=None):
     """The definition: materialise K and V per head, then plain softmax attention.
 
     qc [N, H, d_h] and qr [N, H, d_r] (q^R un-rotated), q_pos [N] int;
     c [T, d_c], kr [T, d_r] (k^R un-rotated; key t is at position
     key_offset + t); w_uk [H, d_h, d_c], w_uv [H, d_v, d_c] (weights stored
-    [out, in]).  Returns dict(o [N, H, d_v], obar [N, H, d_c], lse [N, H]).
+    [out, in]).  kr may also be [T, H, d_r], one position key per head
+    (``materialise_keys``).  With ``position_scale`` the two channels' dot products take
+    their own scales (the two-scale score); without it one scale multiplies the
+    [content ; position] dot product.  Returns dict(o [N, H, d_v],
+    obar [N, H, d_c], lse [N, H]).
     """
     qc = np.asarray(qc, np.float64)
     qr = np.asarray(qr, np.float64)
@@ -116,7 +128,13 @@ def materialised(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=F
         t1 = min(t_all, t0 + key_chunk)
         k_full = materialise_keys(c[t0:t1], kr[t0:t1], w_uk, key_pos[t0:t1], base)
         k_h = np.ascontiguousarray(k_full.transpose(1, 2, 0))  # [H, D, Tc]
-        s[:, :, t0:t1] = (scale * (q_h @ k_h)).transpose(1, 0, 2)
+        if position_scale is None:
+            s[:, :, t0:t1] = (scale * (q_h @ k_h)).transpose(1, 0, 2)
+        else:
+            d_h = qc.shape[2]
+            content = q_h[:, :, :d_h] @ k_h[:, :d_h, :]
+            position = q_h[:, :, d_h:] @ k_h[:, d_h:, :]
+            s[:, :, t0:t1] = (scale * content + position_scale * position).transpose(1, 0, 2)
     alpha, lse = _softmax(s, _visible(q_pos, key_pos, causal))
     o = np.zeros((n, h, d_v), dtype=np.float64)
     for t0 in range(0, t_all, key_chunk):
@@ -141,10 +159,12 @@ def output_absorption(w_uv, obar):
     return np.einsum("hvc,nhc->nhv", np.asarray(w_uv, np.float64), np.asarray(obar, np.float64))
 
 
-def absorbed(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False, key_offset=0):
+def absorbed(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False, key_offset=0,
+             position_scale=None):
     """The weight-absorbed evaluation order (self-check of ``materialised`` only).
 
-    q~ = W_UK^T q^C (per head), s_t = scale (q~ . c_t + R_m q^R . R_t k^R_t),
+    q~ = W_UK^T q^C (per head), s_t = scale (q~ . c_t + R_m q^R . R_t k^R_t)
+    (or scale q~ . c_t + position_scale R_m q^R . R_t k^R_t),
     obar = sum_t alpha_t c_t, o = W_UV obar.
     """
     qc = np.asarray(qc, np.float64)
@@ -155,19 +175,28 @@ def absorbed(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False
     key_pos = key_offset + np.arange(c.shape[0])
     q_tilde = query_absorption(w_uk, qc)  # W_UK^T q^C
     q_rot = rope.rotate(qr, q_pos[:, None], base)
-    k_rot = rope.rotate(kr, key_pos, base)
-    s = scale * (q_tilde @ c.T + q_rot @ k_rot.T)
+    kr = np.asarray(kr, np.float64)
+    if kr.ndim == 3:  # one position key per head: [T, H, d_r]
+        k_rot = rope.rotate(kr, key_pos[:, None], base)
+        pos_dot = np.einsum("nhr,thr->nht", q_rot, k_rot)
+    else:
+        pos_dot = q_rot @ rope.rotate(kr, key_pos, base).T
+    if position_scale is None:
+        s = scale * (q_tilde @ c.T + pos_dot)
+    else:
+        s = scale * (q_tilde @ c.T) + position_scale * pos_dot
     alpha, lse = _softmax(s, _visible(q_pos, key_pos, causal))
     obar = alpha @ c
     o = output_absorption(w_uv, obar)
     return {"o": o, "obar": obar, "lse": lse, "q_tilde": q_tilde, "q_rot": q_rot}
 
 
-def brute_force(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False):
+def brute_force(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False, position_scale=None):
     """Scalar pure-Python loops over the materialised definition (tiny inputs only).
 
     Uses only ``math`` and Python lists: no numpy arithmetic, no shared helper.
     """
+    per_head = np.asarray(kr).ndim == 3  # kr [T, H, d_r]: one position key per head
     qc, qr, c, kr = (np.asarray(a, np.float64).tolist() for a in (qc, qr, c, kr))
     w_uk = np.asarray(w_uk, np.float64).tolist()
     w_uv = np.asarray(w_uv, np.float64).tolist()
@@ -189,14 +218,19 @@ def brute_force(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=Fa
     lse = [[-math.inf] * h for _ in range(n)]
     for qi in range(n):
         for hi in range(h):
-            qvec = qc[qi][hi] + rot(qr[qi][hi], q_pos[qi])
+            qrot = rot(qr[qi][hi], q_pos[qi])
             scores = []
             for t in range(t_all):
                 if causal and t > q_pos[qi]:
                     continue
-                kvec = [sum(w_uk[hi][a][b] * c[t][b] for b in range(d_c)) for a in range(d_h)]
-                kvec = kvec + rot(kr[t], t)
-                scores.append((t, scale * sum(x * y for x, y in zip(qvec, kvec))))
+                kc = [sum(w_uk[hi][a][b] * c[t][b] for b in range(d_c)) for a in range(d_h)]
+                krot = rot(kr[t][hi] if per_head else kr[t], t)
+                dot_c = sum(x * y for x, y in zip(qc[qi][hi], kc))
+                dot_r = sum(x * y for x, y in zip(qrot, krot))
+                if position_scale is None:
+                    scores.append((t, scale * (dot_c + dot_r)))
+                else:
+                    scores.append((t, scale * dot_c + position_scale * dot_r))
             if not scores:
                 continue
             mx = max(sv for _, sv in scores)
@@ -212,7 +246,7 @@ def brute_force(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=Fa
 
 
 def decode_batch(seq_lens, c_rows, kr_rows, row_offsets, qc, qr, w_uk, w_uv, scale,
-                 base=10000.0, seqs=None, evaluate=materialised):
+                 base=10000.0, seqs=None, evaluate=materialised, position_scale=None):
     """Decode for a batch: query b sits at position T_b - 1 and sees keys 0 .. T_b - 1.
 
     c_rows [sum T, d_c] and kr_rows [sum T, d_r] hold each sequence's tokens in
@@ -225,12 +259,13 @@ def decode_batch(seq_lens, c_rows, kr_rows, row_offsets, qc, qr, w_uk, w_uv, sca
         t = int(seq_lens[b])
         r0 = int(row_offsets[b])
         outs.append(evaluate(qc[b:b + 1], qr[b:b + 1], np.array([t - 1]), c_rows[r0:r0 + t],
-                             kr_rows[r0:r0 + t], w_uk, w_uv, scale, base=base, causal=False))
+                             kr_rows[r0:r0 + t], w_uk, w_uv, scale, base=base, causal=False,
+                             position_scale=position_scale))
     return {k: np.concatenate([r[k] for r in outs], axis=0) for k in ("o", "obar", "lse")}
 
 
 def prefill_batch(cu_q, q_start, c_rows, kr_rows, row_offsets, qc, qr, w_uk, w_uv, scale,
-                  base=10000.0, queries=None, evaluate=materialised):
+                  base=10000.0, queries=None, evaluate=materialised, position_scale=None):
     """Causal chunked prefill: query j of sequence b sits at position q_start[b] + j.
 
     c_rows / kr_rows hold positions 0 .. q_start[b] + n_b - 1 of sequence b from
@@ -249,7 +284,7 @@ def prefill_batch(cu_q, q_start, c_rows, kr_rows, row_offsets, qc, qr, w_uk, w_u
         t = int(pos.max()) + 1
         r0 = int(row_offsets[b])
         res = evaluate(qc[sel], qr[sel], pos, c_rows[r0:r0 + t], kr_rows[r0:r0 + t],
-                       w_uk, w_uv, scale, base=base, causal=True)
+                       w_uk, w_uv, scale, base=base, causal=True, position_scale=position_scale)
         for i, g in enumerate(sel):
             outs[int(g)] = {k: res[k][i] for k in ("o", "obar", "lse")}
     return {k: np.stack([outs[int(g)][k] for g in want]) for k in ("o", "obar", "lse")}

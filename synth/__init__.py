@@ -79,7 +79,7 @@ class Case:
     seq_lens: np.ndarray           # int32 [B]: cached tokens per sequence (incl. new ones)
     row_offsets: np.ndarray        # int64 [B]
     c_rows: np.ndarray             # [sum T, d_c]
-    kr_rows: np.ndarray            # [sum T, d_r]  (un-rotated)
+    kr_rows: np.ndarray            # [sum T, d_r], or [sum T, H, d_r] with per-head keys (un-rotated)
     qc: np.ndarray                 # [N, H, d_h]
     qr: np.ndarray                 # [N, H, d_r]   (un-rotated)
     q_pos: np.ndarray              # int32 [N]
@@ -138,18 +138,19 @@ def _offsets(seq_lens):
 
 
 def direct_decode(shape: Shape, dtype: str, seq_lens, seed: int, shuffle: bool = False,
-                  weight_seed_offset: int = 0) -> Case:
+                  weight_seed_offset: int = 0, per_head_rope: bool = False) -> Case:
     """Decode inputs drawn directly: c, k^R, q^C, q^R ~ N(0,1); W ~ N(0,1)/sqrt(d_c).
 
     Draw order: c rows, k^R rows, q^C, q^R, W_UK, W_UV, then the page
-    permutation.  Query b sits at position T_b - 1.
+    permutation.  Query b sits at position T_b - 1.  per_head_rope draws one
+    position key per head and token ([sum T, H, d_r]) in place of one per token.
     """
     rng = np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     total = int(seq_lens.sum(dtype=np.int64))
     h, s = shape.n_heads, shape
     c = to_storage(_normal(rng, (total, s.d_latent)), dtype)
-    kr = to_storage(_normal(rng, (total, s.d_rope)), dtype)
+    kr = to_storage(_normal(rng, (total, h, s.d_rope) if per_head_rope else (total, s.d_rope)), dtype)
     qc = to_storage(_normal(rng, (len(seq_lens), h, s.d_head)), dtype)
     qr = to_storage(_normal(rng, (len(seq_lens), h, s.d_rope)), dtype)
     w_uk = to_storage(_normal(rng, (h, s.d_head, s.d_latent), np.float64) / math.sqrt(s.d_latent), dtype)

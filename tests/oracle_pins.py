@@ -346,6 +346,89 @@ def pin_latent_path_reduces_to_direct_query():
     assert _rel(got, (h @ w_q.T).reshape(n, n_heads, d_h)) <= 1e-14
 
 
+# ------------------------------------------------------ two-scale score ----
+# "AI decoupled RoPE MLA", decoupled-RoPE section: each channel's dot product
+# takes its own factor, content over sqrt(d) and position over sqrt(d_r).
+
+def pin_two_scale_brute_force():
+    """Scalar loops with the two factors equal the vectorised materialised and absorbed forms
+    (causal, with a key offset of 0), and equal factors give the one-scale score."""
+    p = _small_problem(seed=40, t=12, n=3)
+    args = (p["qc"], p["qr"], np.array([3, 7, 11]), p["c"], p["kr"], p["w_uk"], p["w_uv"], 1.0 / math.sqrt(8))
+    ps = 1.0 / math.sqrt(8 // 2)
+    want = attention.brute_force(*args, causal=True, position_scale=ps)
+    for form in (attention.materialised, attention.absorbed):
+        got = form(*args, causal=True, position_scale=ps)
+        for k in ("o", "obar", "lse"):
+            assert _rel(got[k], want[k]) <= 1e-12, (form.__name__, k)
+    same = attention.materialised(*args, causal=True, position_scale=args[-1])
+    one = attention.materialised(*args, causal=True)
+    for k in ("o", "obar", "lse"):
+        assert _rel(same[k], one[k]) <= 1e-14
+
+
+def pin_two_scale_special_cases():
+    """With q^R = 0 the position factor has no effect (bitwise); with q^C = 0 the layer is
+    textbook attention of the rotated position query over the rotated position keys with
+    scale position_scale and values W_UV c (torch's scaled_dot_product_attention, float64)."""
+    import torch
+
+    p = _small_problem(seed=41, t=30, n=2)
+    pos = np.array([29, 29])
+    zr = np.zeros_like(p["qr"])
+    a = attention.materialised(p["qc"], zr, pos, p["c"], p["kr"], p["w_uk"], p["w_uv"], 0.3, position_scale=0.05)
+    b = attention.materialised(p["qc"], zr, pos, p["c"], p["kr"], p["w_uk"], p["w_uv"], 0.3, position_scale=2.0)
+    for k in ("o", "obar", "lse"):
+        assert np.array_equal(a[k], b[k])
+    zc = np.zeros_like(p["qc"])
+    ps = 0.7
+    got = attention.materialised(zc, p["qr"], pos, p["c"], p["kr"], p["w_uk"], p["w_uv"], 0.3, position_scale=ps)
+    q = torch.from_numpy(rope.rotate(p["qr"], pos[:, None]).transpose(1, 0, 2).copy())  # [H, N, d_r]
+    k = torch.from_numpy(rope.rotate(p["kr"], np.arange(30)))[None].expand(q.shape[0], -1, -1)
+    v = torch.from_numpy(np.einsum("hvc,tc->htv", p["w_uv"], p["c"]))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=ps).numpy().transpose(1, 0, 2)
+    assert _rel(got["o"], ref) <= 1e-12
+
+
+# ---------------------------------------------------- per-head position keys ----
+# "Multi-Head Latent Attention", "A concrete size comparison": the simplified
+# MLA-style cache keeps the latent plus one RoPE key per head (256 + 16 x 32).
+
+def pin_per_head_keys_brute_force():
+    """Scalar loops over per-head position keys equal the materialised and absorbed forms,
+    causal and not, with one scale and with two."""
+    p = _small_problem(seed=50, t=14, n=3)
+    rng = np.random.default_rng(51)
+    kr = rng.standard_normal((14, 3, 8))
+    for causal, ps in ((False, None), (True, 0.4)):
+        args = (p["qc"], p["qr"], np.array([13, 5, 9]), p["c"], kr, p["w_uk"], p["w_uv"], p["scale"])
+        want = attention.brute_force(*args, causal=causal, position_scale=ps)
+        for form in (attention.materialised, attention.absorbed):
+            got = form(*args, causal=causal, position_scale=ps)
+            for k in ("o", "obar", "lse"):
+                assert _rel(got[k], want[k]) <= 1e-12, (form.__name__, causal, k)
+
+
+def pin_per_head_keys_reduce_to_shared():
+    """Every head holding the same position key is the shared-key layout; per-head keys that
+    differ change only their own head (head 1's key perturbed leaves heads 0 and 2 bitwise)."""
+    p = _small_problem(seed=52, t=20, n=2)
+    pos = np.array([19, 19])
+    args = (p["qc"], p["qr"], pos, p["c"])
+    shared = attention.materialised(*args, p["kr"], p["w_uk"], p["w_uv"], p["scale"])
+    tiled = np.repeat(p["kr"][:, None, :], 3, axis=1)
+    per = attention.materialised(*args, tiled, p["w_uk"], p["w_uv"], p["scale"])
+    for k in ("o", "obar", "lse"):
+        assert _rel(per[k], shared[k]) <= 1e-14
+    moved = tiled.copy()
+    moved[:, 1, :] += 1.0
+    per2 = attention.materialised(*args, moved, p["w_uk"], p["w_uv"], p["scale"])
+    for k in ("o", "obar", "lse"):
+        assert np.array_equal(per2[k][:, [0, 2]], per[k][:, [0, 2]])
+        assert not np.allclose(per2[k][:, 1], per[k][:, 1])
+    assert accounting.mla_per_head_rope(256, 16, 32) == 768
+
+
 # ------------------------------------------------- the RoPE obstruction ----
 # "ropeabsorb" README, "RoPE spans exactly d_R dimensions and cannot be folded"
 # and "Partial absorption is impossible".
@@ -451,7 +534,8 @@ ALL_PINS = [
     pin_front_unit_vectors, pin_front_brute_force, pin_fold_equals_absorbed_query,
     pin_latent_path_reduces_to_direct_query, pin_obstruction_one_pair_by_hand, pin_obstruction_is_the_rotated_score,
     pin_obstruction_decomposition,
-    pin_obstruction_span, pin_obstruction_best_single_matrix,
+    pin_obstruction_span, pin_obstruction_best_single_matrix, pin_two_scale_brute_force,
+    pin_two_scale_special_cases, pin_per_head_keys_brute_force, pin_per_head_keys_reduce_to_shared,
 ]
 
 

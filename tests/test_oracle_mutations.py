@@ -53,6 +53,14 @@ def _keys_without_rope(c, kr, w_uk, key_pos, base=10000.0):
     return k
 
 
+def _per_head_keys_take_head0(c, kr, w_uk, key_pos, base=10000.0):
+    # per-head position keys read as head 0's key for every head
+    kr = np.asarray(kr)
+    if kr.ndim == 3:
+        kr = np.repeat(kr[:, :1, :], kr.shape[1], axis=1)
+    return _orig_keys(c, kr, w_uk, key_pos, base)
+
+
 def _keys_unrotated(c, kr, w_uk, key_pos, base=10000.0):
     return _orig_keys(c, kr, w_uk, np.zeros_like(np.asarray(key_pos)), base)
 
@@ -73,6 +81,15 @@ def _materialised_no_scale(*a, **k):
     else:
         k["scale"] = 1.0
     return _orig_materialised(*a, **k)
+
+
+def _materialised_scales_swapped(*a, position_scale=None, **k):
+    # the two factors applied to the wrong channels
+    if position_scale is None:
+        return _orig_materialised(*a, **k)
+    a = list(a)
+    a[7], position_scale = position_scale, a[7]
+    return _orig_materialised(*a, position_scale=position_scale, **k)
 
 
 def _materialised_query_unrotated(qc, qr, q_pos, *a, **k):
@@ -144,10 +161,12 @@ MUTATIONS = {
     "rope_half_split_pairs": [(rope, "rotate", _half_split_rotate)],
     "rope_theta_exponent": [(rope, "thetas", _wrong_thetas)],
     "keys_drop_rope_term": [(attention, "materialise_keys", _keys_without_rope)],
+    "per_head_keys_head0_only": [(attention, "materialise_keys", _per_head_keys_take_head0)],
     "keys_not_rotated": [(attention, "materialise_keys", _keys_unrotated)],
     "values_wrong_rows": [(attention, "materialise_values", _values_from_uk)],
     "causal_excludes_diagonal": [(attention, "_visible", _strict_causal)],
     "score_scale_dropped": [(attention, "materialised", _materialised_no_scale)],
+    "two_scale_swapped": [(attention, "materialised", _materialised_scales_swapped)],
     "query_not_rotated": [(attention, "materialised", _materialised_query_unrotated)],
     "paging_offset_slip": [(paging, "slot", _bad_slot)],
     "front_latent_weight_transposed": [(front, "kv_latent", _kv_latent_transposed)],
