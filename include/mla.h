@@ -79,7 +79,19 @@ typedef struct {
                         * MFMA work, bf16 rounding of q~ removed.  Supported
                         * for d_latent + d_rope <= 288.  With dtype MLA_F32
                         * it must be MLA_F32.                             */
-  float softmax_scale; /* one scale on the summed score                  */
+  float softmax_scale; /* scale on the content part of the score          */
+  float position_scale; /* scale on the position part of the score.  Equal
+                        * to softmax_scale: one scale on the summed score.
+                        * The two-scale score of "AI decoupled RoPE MLA"
+                        * (decoupled-RoPE section: content over sqrt(d),
+                        * position over sqrt(d_r)) sets them apart.  The
+                        * calls that write the rotated query (mla_rope_apply,
+                        * mla_q_project, mla_q_project_folded) multiply it
+                        * by position_scale / softmax_scale before its one
+                        * rounding, so the attention calls score
+                        * softmax_scale * (q~ . c_t) + position_scale *
+                        * (R_m q^R . R_t k^R_t) with no extra work.  Finite
+                        * and positive.                                    */
   double rope_base;    /* theta_j = rope_base^(-2j/d_r)                  */
 } mla_dims;
 
@@ -193,6 +205,39 @@ mla_status mla_prefill_mha(const mla_dims* dims, const mla_paged_cache* cache, c
                            const void* w_uk, const void* w_uv, const int32_t* cu_q, const int32_t* q_start_pos,
                            const int32_t* cu_q_host, const int32_t* q_start_pos_host, int32_t batch, float* out,
                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Per-head position keys ------------------------------------------------
+ * The simplified MLA-style cache of "Multi-Head Latent Attention"
+ * (talalahmed.dev), "A concrete size comparison": each token keeps the latent
+ * and one RoPE key per head, d_latent + n_heads * d_rope numbers (256 + 16 x 32
+ * = 768 for that page's example), where the decoupled design keeps one key
+ * shared by every head.  Supported for that example's shape only: bf16,
+ * n_heads 16, d_latent 256, d_rope 32 (else MLA_ERR_UNSUPPORTED).
+ *
+ * Cache rows are [ c_t | R_t k^R_{t,0} | ... | R_t k^R_{t,H-1} ], each key
+ * rotated to its own position; paging as in mla_paged_cache, with rows of
+ * d_latent + n_heads * d_rope elements.  The query side is unchanged: q_lat
+ * rows are [ q~_i | R_m q^R_i ] as written by mla_absorb_q and mla_rope_apply
+ * (which also applies position_scale). */
+
+/* mla_cache_write_per_head -- write n_kv token rows.
+ *   kv_latent [n_kv, d_latent] bf16; k_rope [n_kv, n_heads, d_rope] bf16
+ *   (un-rotated); kv_seq / kv_pos [n_kv] int32 device arrays.  Rows whose
+ *   (sequence, position) has no page in the block table are skipped.  Angles
+ *   and rotation in float64, rounded once. */
+mla_status mla_cache_write_per_head(const mla_dims* dims, const mla_paged_cache* cache, const void* kv_latent,
+                                    const void* k_rope, const int32_t* kv_seq, const int32_t* kv_pos, int64_t n_kv,
+                                    void* stream);
+
+/* mla_decode_per_head -- decode over a per-head-key cache: head i scores
+ * softmax_scale * (q~_i . c_t + R_m q^R_i . R_t k^R_{t,i}) over keys
+ * 0 .. T_b - 1 and returns obar_i = sum_t alpha_{i,t} c_t and lse, with the
+ * arguments, output layout, workspace (mla_decode_workspace_size with the same
+ * dims and lengths) and errors of mla_decode.  q_lat may be bf16 or float32
+ * (q_lat_dtype; float32 enters as a two-term bf16 split). */
+mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                               const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* out_latent,
+                               float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /* mla_out_proj -- output absorption ("AI decoupled RoPE MLA", recap section:
  * Attn_m = W^UV sum_t alpha_mt c_t).

@@ -7,8 +7,11 @@ Importing it without the built library raises ImportError.
 """
 
 from .binding import (  # noqa: F401
-    LIB, LIB_PATH, MLADims, MLAError, absorb_q, decode, decode_plan, decode_workspace,
+    LIB, LIB_PATH, MLADims, MLAError, absorb_q, cache_write_per_head, decode, decode_per_head, decode_plan,
+    decode_workspace, per_head_row,
     decode_workspace_size, fold_q_weights, front_workspace, front_workspace_size, kv_project, out_proj, prefill,
     prefill_mha, prefill_mha_workspace, prefill_mha_workspace_size, q_project, q_project_folded, rope_apply,
 )
-from .pipeline import DecodeStep, LatentCache, LayerDecodeStep, PrefillStep, choose_prefill_form  # noqa: F401
+from .pipeline import (  # noqa: F401
+    DecodeStep, LatentCache, LayerDecodeStep, PerHeadDecodeStep, PrefillStep, choose_prefill_form,
+)

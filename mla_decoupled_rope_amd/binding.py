@@ -33,7 +33,7 @@ class Dims(ctypes.Structure):
         ("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32), ("d_v", ctypes.c_int32),
         ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("page_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("q_lat_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-        ("rope_base", ctypes.c_double),
+        ("position_scale", ctypes.c_float), ("rope_base", ctypes.c_double),
     ]
 
 
@@ -62,6 +62,8 @@ def _load():
         "mla_q_project": [pd, vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "mla_q_project_folded": [pd, vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         "mla_fold_q_weights": [pd, i32, vp, vp, vp, vp],
+        "mla_cache_write_per_head": [pd, pc, vp, vp, vp, vp, i64, vp],
+        "mla_decode_per_head": [pd, pc, vp, vp, vp, i32, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -85,7 +87,8 @@ LIB = _load()
 EXPORTS = ("mla_rope_apply", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode", "mla_prefill",
            "mla_out_proj", "mla_status_string", "mla_last_error", "mla_decode_plan",
            "mla_prefill_mha_workspace_size", "mla_prefill_mha", "mla_front_workspace_size", "mla_kv_project",
-           "mla_q_project", "mla_q_project_folded", "mla_fold_q_weights")
+           "mla_q_project", "mla_q_project_folded", "mla_fold_q_weights", "mla_cache_write_per_head",
+           "mla_decode_per_head")
 
 
 def _check(status: int):
@@ -104,6 +107,7 @@ class MLADims:
     d_rope: int
     dtype: torch.dtype = torch.bfloat16
     softmax_scale: float | None = None
+    position_scale: float | None = None  # None: softmax_scale (one scale on the summed score)
     rope_base: float = 10000.0
     page_size: int = 64
     q_lat_dtype: torch.dtype | None = None  # None: same as dtype
@@ -120,7 +124,8 @@ class MLADims:
         scale = self.softmax_scale if self.softmax_scale is not None else 1.0 / math.sqrt(self.d_head + self.d_rope)
         code = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}
         return Dims(self.n_heads, self.d_head, self.d_v, self.d_latent, self.d_rope, self.page_size,
-                    code[self.dtype], code[self.qdtype], scale, self.rope_base)
+                    code[self.dtype], code[self.qdtype], scale,
+                    scale if self.position_scale is None else self.position_scale, self.rope_base)
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -147,10 +152,11 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _cache(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor) -> PagedCache:
+def _cache(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, row: int | None = None) -> PagedCache:
+    row = dims.row if row is None else row
     _dev(cache, "cache", dims.dtype)
-    if cache.dim() != 3 or cache.shape[1] != dims.page_size or cache.shape[2] != dims.row:
-        raise ValueError(f"cache must be [num_pages, {dims.page_size}, {dims.row}]")
+    if cache.dim() != 3 or cache.shape[1] != dims.page_size or cache.shape[2] != row:
+        raise ValueError(f"cache must be [num_pages, {dims.page_size}, {row}]")
     _dev(block_table, "block_table", torch.int32)
     if block_table.dim() != 2:
         raise ValueError("block_table must be [num_seqs, max_pages_per_seq]")
@@ -233,6 +239,45 @@ def decode(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat:
     _check(LIB.mla_decode(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), seq_lens.data_ptr(),
                           seq_lens_host.data_ptr(), batch, out_latent.data_ptr(), _ptr(lse), _ptr(workspace),
                           0 if workspace is None else workspace.numel(), _stream()))
+
+
+def per_head_row(dims: MLADims) -> int:
+    """Elements per cache row with one position key per head: d_latent + n_heads * d_rope."""
+    return dims.d_latent + dims.n_heads * dims.d_rope
+
+
+def cache_write_per_head(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, kv_latent: torch.Tensor,
+                         k_rope: torch.Tensor, kv_seq: torch.Tensor, kv_pos: torch.Tensor) -> None:
+    """mla_cache_write_per_head: rows [c | R_t k^R_{t,0} | ... | R_t k^R_{t,H-1}] into a per-head-key cache."""
+    n = kv_latent.shape[0]
+    cstruct = _cache(dims, cache, block_table, per_head_row(dims))
+    _dev(kv_latent, "kv_latent", dims.dtype, (n, dims.d_latent))
+    _dev(k_rope, "k_rope", dims.dtype, (n, dims.n_heads, dims.d_rope))
+    _dev(kv_seq, "kv_seq", torch.int32, (n,))
+    _dev(kv_pos, "kv_pos", torch.int32, (n,))
+    d = dims.c()
+    _check(LIB.mla_cache_write_per_head(ctypes.byref(d), ctypes.byref(cstruct), kv_latent.data_ptr(),
+                                        k_rope.data_ptr(), kv_seq.data_ptr(), kv_pos.data_ptr(), n, _stream()))
+
+
+def decode_per_head(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat: torch.Tensor,
+                    seq_lens: torch.Tensor, seq_lens_host: torch.Tensor, out_latent: torch.Tensor,
+                    lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> None:
+    """mla_decode_per_head: decode over a cache with one position key per head."""
+    batch = seq_lens_host.numel()
+    cstruct = _cache(dims, cache, block_table, per_head_row(dims))
+    _dev(q_lat, "q_lat", dims.qdtype, (batch, dims.n_heads, dims.row))
+    _dev(seq_lens, "seq_lens", torch.int32, (batch,))
+    _host_i32(seq_lens_host, "seq_lens_host")
+    _dev(out_latent, "out_latent", dims.dtype, (batch, dims.n_heads, dims.d_latent))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (batch, dims.n_heads))
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+    d = dims.c()
+    _check(LIB.mla_decode_per_head(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), seq_lens.data_ptr(),
+                                   seq_lens_host.data_ptr(), batch, out_latent.data_ptr(), _ptr(lse),
+                                   _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
 
 
 def prefill(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat: torch.Tensor,

@@ -43,6 +43,12 @@ mla_status hip_fail(hipError_t e, const char* what) {
 constexpr int kPlanCUs = 256;
 constexpr size_t kWsAlign = 256;
 
+// The rotated query carries the position part's scale relative to the
+// content part's, so one softmax_scale on the summed score gives both.
+double position_ratio(const mla_dims* d) {
+  return static_cast<double>(d->position_scale) / static_cast<double>(d->softmax_scale);
+}
+
 mla_status check_dims(const mla_dims* d) {
   if (d == nullptr) return fail(MLA_ERR_INVALID_ARG, "dims is NULL");
   if (d->n_heads <= 0 || d->d_head <= 0 || d->d_v <= 0 || d->d_latent <= 0 || d->d_rope <= 0)
@@ -58,6 +64,8 @@ mla_status check_dims(const mla_dims* d) {
     return fail(MLA_ERR_INVALID_ARG, "float32 inputs need a float32 q_lat");
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f))
     return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
+  if (!(std::isfinite(d->position_scale) && d->position_scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "position_scale must be finite and positive");
   if (!(std::isfinite(d->rope_base) && d->rope_base > 0.0))
     return fail(MLA_ERR_INVALID_ARG, "rope_base must be finite and positive");
   return MLA_OK;
@@ -273,6 +281,7 @@ mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache, co
   p.q_vec = dims->d_rope % 8 == 0 && reinterpret_cast<uintptr_t>(q_rope) % 16 == 0 &&
             reinterpret_cast<uintptr_t>(q_lat) % 16 == 0;
   for (int j = 0; j < dims->d_rope / 2; ++j) p.theta[j] = std::pow(dims->rope_base, -2.0 * j / dims->d_rope);
+  p.q_scale = position_ratio(dims);
   const hipError_t e = mla::launch_rope(p, as_stream(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "rope launch");
 }
@@ -380,6 +389,94 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
   }
   hipError_t e = mla::launch_decode_bf16(p, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (plan.needs_merge) {
+    e = mla::launch_merge(p, dims->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return MLA_OK;
+}
+
+// ---- per-head position keys (rows [c | R k^R_0 | ... | R k^R_{H-1}])
+
+namespace {
+
+mla_status check_per_head_shape(const mla_dims* d) {
+  if (d->dtype != MLA_BF16 || d->n_heads != 16 || d->d_latent != 256 || d->d_rope != 32)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "per-head position keys need bf16, 16 heads, d_latent 256 and d_rope 32 (got %d heads, %d, %d)",
+                d->n_heads, d->d_latent, d->d_rope);
+  return MLA_OK;
+}
+
+}  // namespace
+
+mla_status mla_cache_write_per_head(const mla_dims* dims, const mla_paged_cache* cache, const void* kv_latent,
+                                    const void* k_rope, const int32_t* kv_seq, const int32_t* kv_pos, int64_t n_kv,
+                                    void* stream) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  MLA_TRY(check_per_head_shape(dims));
+  if (n_kv < 0) return fail(MLA_ERR_INVALID_ARG, "n_kv must be >= 0");
+  if (n_kv == 0) return MLA_OK;
+  MLA_TRY(check_cache(cache));
+  if (kv_latent == nullptr || k_rope == nullptr || kv_seq == nullptr || kv_pos == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "kv_latent, k_rope, kv_seq and kv_pos must be non-NULL");
+  if (n_kv > (static_cast<int64_t>(UINT32_MAX) - 3) * 4) return fail(MLA_ERR_UNSUPPORTED, "too many rows for one launch");
+  mla::RopeParams p{};
+  p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
+  p.dtype = dims->dtype; p.q_lat_dtype = dims->q_lat_dtype;
+  p.kv_latent = kv_latent; p.k_rope = k_rope; p.kv_seq = kv_seq; p.kv_pos = kv_pos; p.n_kv = n_kv;
+  p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
+  p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
+  p.q_scale = 1.0;
+  for (int j = 0; j < dims->d_rope / 2; ++j) p.theta[j] = std::pow(dims->rope_base, -2.0 * j / dims->d_rope);
+  const hipError_t e = mla::launch_perhead_cache_write(p, as_stream(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "per-head cache write launch");
+}
+
+mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                               const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* out_latent,
+                               float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  MLA_TRY(check_per_head_shape(dims));
+  MLA_TRY(check_cache(cache));
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch == 0) return MLA_OK;
+  if (batch > cache->num_seqs)
+    return fail(MLA_ERR_INVALID_ARG, "batch (%d) exceeds the block table's rows (%d)", batch, cache->num_seqs);
+  if (q_lat == nullptr || seq_lens == nullptr || seq_lens_host == nullptr || out_latent == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "q_lat, seq_lens, seq_lens_host and out_latent must be non-NULL");
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens_host[b] < 0 ||
+        static_cast<int64_t>(seq_lens_host[b]) > static_cast<int64_t>(cache->max_pages_per_seq) * mla::kPage)
+      return fail(MLA_ERR_INVALID_ARG, "seq_lens_host[%d] = %d is negative or beyond the block table", b,
+                  seq_lens_host[b]);
+    if (seq_lens_host[b] > 0 && cache->num_pages == 0)
+      return fail(MLA_ERR_INVALID_ARG, "sequence %d has tokens but the cache has no pages", b);
+  }
+  const Plan plan = make_plan(dims, batch, seq_lens_host);
+  const size_t need = workspace_bytes(dims, plan);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "decode needs %zu bytes of workspace, got %zu", need, workspace ? ws_bytes : 0);
+  if (plan.n_items > (1LL << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
+  mla::AttnParams p{};
+  p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
+  p.q_f32 = dims->q_lat_dtype == MLA_F32;
+  p.scale = dims->softmax_scale;
+  p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);
+  p.q_lat = q_lat; p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
+  p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
+  p.seq_lens = seq_lens; p.batch = batch; p.out_latent = out_latent; p.lse = lse;
+  p.split_pages = plan.split_pages; p.n_full = plan.n_full; p.n_items = plan.n_items; p.n_head_chunks = 1;
+  if (need > 0) {
+    const size_t o = static_cast<size_t>(plan.n_items) * dims->n_heads * dims->d_latent * sizeof(uint16_t);
+    p.ws_o = static_cast<mla::bf16_t*>(workspace);
+    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (o + kWsAlign - 1) / kWsAlign * kWsAlign);
+  }
+  const hipStream_t s = as_stream(stream);
+  hipError_t e = mla::launch_perhead_decode(p, s);
+  if (e != hipSuccess) return hip_fail(e, "per-head decode launch");
   if (plan.needs_merge) {
     e = mla::launch_merge(p, dims->dtype, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
@@ -676,6 +773,7 @@ static mla_status q_project_impl(const mla_dims* dims, const void* h, int64_t n,
   // the content (or folded) and position queries from c^Q
   rp.y = nullptr;
   rp.q_nope = static_cast<mla::bf16_t*>(q_nope); rp.q_lat = static_cast<mla::bf16_t*>(q_lat); rp.q_pos = q_pos;
+  rp.q_scale = position_ratio(dims);
   const int64_t w0 = folded ? dims->d_latent : dims->d_head;
   return front_project(cq, d_qlat, n, d_qlat, w_up, w_qr, static_cast<int64_t>(dims->n_heads) * (w0 + dims->d_rope),
                        static_cast<int64_t>(dims->n_heads) * w0, part, rp, folded ? mla::kFrontQFolded : mla::kFrontQ,

@@ -77,6 +77,7 @@ struct RopeParams {
   const void* kv_latent; const void* k_rope; const int32_t* kv_seq; const int32_t* kv_pos; int64_t n_kv;
   void* cache; int64_t num_pages; const int32_t* block_table; int32_t num_seqs; int32_t max_pages;
   int q_vec;  // query pairs in 16-byte vectors: d_rope % 8 == 0 and q_rope, q_lat 16-byte aligned
+  double q_scale;    // rotated query times position_scale / softmax_scale (1 for one scale)
   double theta[64];  // theta_j, j < d_rope / 2 (float64, from the host)
 };
 
@@ -107,6 +108,7 @@ struct FrontReduceParams {
   const int32_t* kv_seq; const int32_t* kv_pos;
   // q: q_nope [M, H, d_head], q_lat [M, H, d_latent + d_rope], positions
   bf16_t* q_nope; bf16_t* q_lat; const int32_t* q_pos;
+  double q_scale;  // rotated query times position_scale / softmax_scale (1 for one scale)
   double theta[64];
 };
 
@@ -159,6 +161,8 @@ struct MhaParams {
 
 // Launchers (each returns hipGetLastError() after the launch).
 hipError_t launch_rope(const RopeParams& p, hipStream_t s);
+hipError_t launch_perhead_decode(const AttnParams& p, hipStream_t s);
+hipError_t launch_perhead_cache_write(const RopeParams& p, hipStream_t s);
 hipError_t launch_absorb(const GemmParams& p, hipStream_t s);
 hipError_t launch_out_proj(const GemmParams& p, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s);

@@ -204,6 +204,8 @@ __global__ void __launch_bounds__(256) front_reduce_kernel(FrontReduceParams p) 
     } else {
       const int g = f - split, h = g / p.d_rope, d = g % p.d_rope;
       rot(p.q_pos[m], d / 2, v0, v1);
+      v0 *= p.q_scale;  // the two-scale score's ratio, inside the one rounding
+      v1 *= p.q_scale;
       put(p.q_lat + (static_cast<int64_t>(m) * p.n_heads + h) * row_w + p.d_latent + d, v0, v1);
     }
   }

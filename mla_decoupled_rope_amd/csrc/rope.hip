@@ -13,7 +13,10 @@
 // is one 64-lane wave: it copies c_t and writes R_t k^R_t into its page slot.
 // Angles p * theta_j and sin / cos are float64 (positions reach 2^17, where a
 // float32 angle would be off by ~1e-2 rad); the rotation is float64 too,
-// rounded once to the output type.
+// rounded once to the output type.  The rotated query also takes the ratio
+// of the position scale to the content scale (1 for one scale on the summed
+// score), inside the same float64 product, so the two-scale score costs no
+// extra rounding and no extra work in the attention kernels.
 #include "common.hpp"
 
 namespace mla {
@@ -29,14 +32,15 @@ template <> __device__ __forceinline__ void st<bf16_t>(bf16_t* p, int64_t i, dou
 }
 
 template <typename T, typename TO>
-__device__ __forceinline__ void rotate_pairs(const RopeParams& p, const T* src, TO* dst, int pos, int lane) {
+__device__ __forceinline__ void rotate_pairs(const RopeParams& p, const T* src, TO* dst, int pos, int lane,
+                                             double scale) {
   const int half = p.d_rope / 2;
   for (int j = lane; j < half; j += 64) {
     double s, c;
     sincos(static_cast<double>(pos) * p.theta[j], &s, &c);
     const double x0 = ld(src, 2 * j), x1 = ld(src, 2 * j + 1);
-    st(dst, 2 * j, x0 * c - x1 * s);
-    st(dst, 2 * j + 1, x0 * s + x1 * c);
+    st(dst, 2 * j, (x0 * c - x1 * s) * scale);
+    st(dst, 2 * j + 1, (x0 * s + x1 * c) * scale);
   }
 }
 
@@ -55,7 +59,7 @@ __global__ void __launch_bounds__(256) rope_kernel(RopeParams p) {
       if (row >= p.n_q * p.n_heads) return;
       const T* src = static_cast<const T*>(p.q_rope) + row * p.d_rope;
       TQ* dst = static_cast<TQ*>(p.q_lat) + row * width + p.d_latent;
-      rotate_pairs<T, TQ>(p, src, dst, p.q_pos[row / p.n_heads], lane);
+      rotate_pairs<T, TQ>(p, src, dst, p.q_pos[row / p.n_heads], lane, p.q_scale);
       return;
     }
     __shared__ double cs[64], sn[64];
@@ -79,8 +83,8 @@ __global__ void __launch_bounds__(256) rope_kernel(RopeParams p) {
         const int j = e0 / 2 + i;
         const double x0 = ld(x, 2 * i), x1 = ld(x, 2 * i + 1);
         const double c = cs[j], sj = sn[j];
-        st(y, 2 * i, x0 * c - x1 * sj);
-        st(y, 2 * i + 1, x0 * sj + x1 * c);
+        st(y, 2 * i, (x0 * c - x1 * sj) * p.q_scale);
+        st(y, 2 * i + 1, (x0 * sj + x1 * c) * p.q_scale);
       }
       __builtin_memcpy(__builtin_assume_aligned(dst, 16), y, sizeof(y));
     }
@@ -98,7 +102,7 @@ __global__ void __launch_bounds__(256) rope_kernel(RopeParams p) {
   T* dst = static_cast<T*>(p.cache) + (static_cast<int64_t>(page) * kPage + pos % kPage) * width;
   const T* lat = static_cast<const T*>(p.kv_latent) + m * p.d_latent;
   for (int c = lane; c < p.d_latent; c += 64) dst[c] = lat[c];
-  rotate_pairs<T, T>(p, static_cast<const T*>(p.k_rope) + m * p.d_rope, dst + p.d_latent, pos, lane);
+  rotate_pairs<T, T>(p, static_cast<const T*>(p.k_rope) + m * p.d_rope, dst + p.d_latent, pos, lane, 1.0);
 }
 
 hipError_t launch_rope(const RopeParams& p, hipStream_t s) {

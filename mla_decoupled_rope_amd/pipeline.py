@@ -114,6 +114,44 @@ class DecodeStep:
         return self.out
 
 
+class PerHeadDecodeStep:
+    """One decode step over a cache that keeps one position key per head (rows of
+    d_latent + n_heads * d_rope): the same query path, mla_decode_per_head for
+    attention.  Buffers, the cache included, are allocated once here."""
+
+    def __init__(self, dims: B.MLADims, block_table, num_pages: int, seq_lens_host: torch.Tensor, device="cuda",
+                 fill: float = 0.0):
+        self.dims = dims
+        self.cache = torch.full((num_pages, dims.page_size, B.per_head_row(dims)), fill, dtype=dims.dtype,
+                                device=device)
+        self.block_table = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
+        self.seq_lens_host = seq_lens_host.to(torch.int32).contiguous()
+        self.seq_lens = self.seq_lens_host.to(device)
+        n = self.seq_lens_host.numel()
+        self.q_pos = (self.seq_lens - 1).clamp_min(0).to(torch.int32)
+        self.q_lat = torch.empty((n, dims.n_heads, dims.row), dtype=dims.qdtype, device=device)
+        self.out_latent = torch.empty((n, dims.n_heads, dims.d_latent), dtype=dims.dtype, device=device)
+        self.lse = torch.empty((n, dims.n_heads), dtype=torch.float32, device=device)
+        self.out = torch.empty((n, dims.n_heads, dims.d_v), dtype=torch.float32, device=device)
+        self.workspace = B.decode_workspace(dims, self.seq_lens_host, device)
+
+    def write(self, kv_latent, k_rope, kv_seq, kv_pos):
+        """Cache rows [c | R_t k^R_{t,0} | ... ] for tokens (kv_seq, kv_pos); k_rope [n, H, d_r]."""
+        B.cache_write_per_head(self.dims, self.cache, self.block_table, kv_latent, k_rope, kv_seq, kv_pos)
+
+    def attend(self):
+        B.decode_per_head(self.dims, self.cache, self.block_table, self.q_lat, self.seq_lens, self.seq_lens_host,
+                          self.out_latent, self.lse, self.workspace)
+
+    def run(self, q_nope, q_rope, w_uk, w_uv):
+        d = self.dims
+        B.rope_apply(d, None, None, q_rope=q_rope, q_pos=self.q_pos, q_lat=self.q_lat)
+        B.absorb_q(d, q_nope, w_uk, self.q_lat)
+        self.attend()
+        B.out_proj(d, self.out_latent, w_uv, self.out)
+        return self.out
+
+
 class PrefillStep:
     """Causal chunked prefill for fixed chunk sizes: buffers are allocated once here."""
 

@@ -13,16 +13,20 @@ def tdtype(case) -> torch.dtype:
     return torch.float32 if case.dtype == "f32" else torch.bfloat16
 
 
-def dims_of(case, precise=None) -> mla.MLADims:
+def dims_of(case, precise=None, scales=None) -> mla.MLADims:
     """Library dims for a case.  precise=True keeps q_lat in float32 (two-term
     bf16 scores); by default the tiny shape takes it and the DeepSeek-V2 shape
-    keeps a bf16 q_lat."""
+    keeps a bf16 q_lat.  scales = (content, position) gives each part of the
+    score its own factor (the two-scale score); None keeps the shape's one
+    scale on the summed score."""
     s = case.shape
     if precise is None:
         precise = s.row <= 288
     qdt = torch.float32 if (case.dtype == "f32" or precise) else torch.bfloat16
     return mla.MLADims(s.n_heads, s.d_head, s.d_v, s.d_latent, s.d_rope, dtype=tdtype(case),
-                       softmax_scale=s.scale, rope_base=s.rope_base, page_size=s.page_size, q_lat_dtype=qdt)
+                       softmax_scale=s.scale if scales is None else scales[0],
+                       position_scale=None if scales is None else scales[1], rope_base=s.rope_base,
+                       page_size=s.page_size, q_lat_dtype=qdt)
 
 
 def dev(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
@@ -49,9 +53,9 @@ def build_cache(case, block_table=None, fill=float("nan")) -> mla.LatentCache:
     return cache
 
 
-def run_decode(case, cache=None, block_table=None, precise=None):
+def run_decode(case, cache=None, block_table=None, precise=None, scales=None):
     """Full decode step (q^R rotation, absorption, decode, out_proj).  Returns float64 numpy dict."""
-    dims = dims_of(case, precise)
+    dims = dims_of(case, precise, scales)
     cache = build_cache(case, block_table) if cache is None else cache
     step = mla.DecodeStep(dims, cache, torch.from_numpy(case.seq_lens))
     dt = tdtype(case)
@@ -61,8 +65,8 @@ def run_decode(case, cache=None, block_table=None, precise=None):
     return {"o": to64(out), "obar": to64(step.out_latent), "lse": to64(step.lse), "q_lat": to64(step.q_lat)}
 
 
-def run_prefill(case, cache=None, precise=None):
-    dims = dims_of(case, precise)
+def run_prefill(case, cache=None, precise=None, scales=None):
+    dims = dims_of(case, precise, scales)
     cache = build_cache(case) if cache is None else cache
     step = mla.PrefillStep(dims, cache, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
     dt = tdtype(case)
@@ -71,9 +75,9 @@ def run_prefill(case, cache=None, precise=None):
     return {"o": to64(out), "obar": to64(step.out_latent), "lse": to64(step.lse), "q_lat": to64(step.q_lat)}
 
 
-def run_prefill_mha(case, cache=None):
+def run_prefill_mha(case, cache=None, scales=None):
     """The prefill step in the materialised form (mla_prefill_mha).  Returns float64 numpy dict with o, lse."""
-    dims = dims_of(case, precise=False)
+    dims = dims_of(case, precise=False, scales=scales)
     cache = build_cache(case) if cache is None else cache
     step = mla.PrefillStep(dims, cache, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
     dt = tdtype(case)

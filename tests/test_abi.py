@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def _dims(**kw):
     base = dict(n_heads=128, d_head=128, d_v=128, d_latent=512, d_rope=64, page_size=64, dtype=B.MLA_BF16,
-                q_lat_dtype=B.MLA_BF16, softmax_scale=0.0722, rope_base=10000.0)
+                q_lat_dtype=B.MLA_BF16, softmax_scale=0.0722, position_scale=0.0722, rope_base=10000.0)
     base.update(kw)
     return B.Dims(**base)
 
@@ -56,7 +56,8 @@ def status_of_decode(d, batch=1, lens=(10,), ws=None, ws_bytes=0, cache_kw=None)
 
 @pytest.mark.parametrize("kw, status", [
     (dict(d_rope=63), 1), (dict(n_heads=0), 1), (dict(page_size=32), 2), (dict(dtype=7), 1),
-    (dict(softmax_scale=float("nan")), 1), (dict(rope_base=-1.0), 1), (dict(n_heads=64), 2),
+    (dict(softmax_scale=float("nan")), 1), (dict(position_scale=0.0), 1), (dict(position_scale=float("inf")), 1),
+    (dict(rope_base=-1.0), 1), (dict(n_heads=64), 2),
     (dict(d_rope=256), 2), (dict(q_lat_dtype=B.MLA_F32), 2), (dict(dtype=B.MLA_F32), 1),
     (dict(q_lat_dtype=5), 1),
 ])
