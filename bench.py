@@ -47,6 +47,16 @@ def decode_bytes(seq_lens, n_heads=128, d_latent=512, d_rope=64) -> int:
     return int(np.sum(row * t + per_q + 4 * ((t + 63) // 64)))
 
 
+def per_head_decode_bytes(seq_lens, n_heads=16, d_latent=256, d_rope=32) -> int:
+    """Algorithmic HBM bytes of one per-head-key decode call: rows of the latent and
+    one position key per head read once, the query read once, the latent output
+    written once, the block table read once."""
+    row = (d_latent + n_heads * d_rope) * 2
+    t = np.asarray(seq_lens, np.int64)
+    per_q = n_heads * (d_latent + d_rope) * 2 + n_heads * d_latent * 2
+    return int(np.sum(row * t + per_q + 4 * ((t + 63) // 64)))
+
+
 def prefill_flops(case) -> float:
     """2 * n_h * (576 + 512) per visible (query, key) pair, causal."""
     s = case.shape
@@ -162,6 +172,12 @@ def main():
     ap.add_argument("--prefill-form", default="absorbed", choices=["absorbed", "materialised"],
                     help="prefill workloads: absorbed latent attention (mla_prefill) or per-head keys and "
                          "values up-projected first (mla_prefill_mha)")
+    ap.add_argument("--score", default="one", choices=["one", "two"],
+                    help="one scale on the summed score, or the two-scale score (content over sqrt(d_h), "
+                         "position over sqrt(d_r)) through position_scale")
+    ap.add_argument("--cache-layout", default="shared", choices=["shared", "per-head"],
+                    help="per-head: decode over a cache with one position key per head (16 heads, d_c 256, "
+                         "d_r 32, 768-element rows; 64 sequences x 4096 tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="run one plain 256 MiB copy kernel before timing (HBM counter calibration under rocprofv3)")
@@ -181,26 +197,46 @@ def main():
     torch.cuda.set_device(0)
     maker = {"c1": synth.config1, "c2": synth.config2, "c3": synth.config3, "c4": synth.config4,
              "c5a": synth.config5_decode, "c5b": synth.config5_prefill}[args.config]
-    case = maker()
+    per_head = args.cache_layout == "per-head"
+    if per_head:
+        case = synth.direct_decode(synth.TINY, "bf16", [4096] * 64, seed=31, shuffle=True, per_head_rope=True)
+        case.note["workload"] = "per-head position keys: 64 x 4096 decode, n_h=16, d_c=256, d_r=32 per head"
+    else:
+        case = maker()
     s = case.shape
     dt = torch.float32 if case.dtype == "f32" else torch.bfloat16
-    dims = mla.MLADims(s.n_heads, s.d_head, s.d_v, s.d_latent, s.d_rope, dtype=dt, softmax_scale=s.scale)
+    scale, position_scale = s.scale, None
+    if args.score == "two":
+        scale, position_scale = 1.0 / np.sqrt(s.d_head), 1.0 / np.sqrt(s.d_rope)
+    dims = mla.MLADims(s.n_heads, s.d_head, s.d_v, s.d_latent, s.d_rope, dtype=dt, softmax_scale=scale,
+                       position_scale=position_scale)
 
     def dev(x, dtype=dt):
         return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(dtype).contiguous()
 
     seqs, pos = case.kv_seq_pos()
-    cache0 = mla.LatentCache(dims, case.block_table, case.num_pages)
     chunk = 1 << 20
-    for r0 in range(0, len(seqs), chunk):
-        r1 = min(len(seqs), r0 + chunk)
-        cache0.write(dev(case.c_rows[r0:r1]), dev(case.kr_rows[r0:r1]), torch.from_numpy(seqs[r0:r1]).cuda(),
-                     torch.from_numpy(pos[r0:r1]).cuda())
-    caches = [cache0]
-    for _ in range(1, max(1, args.copies)):
-        c = mla.LatentCache(dims, case.block_table, case.num_pages)
-        c.data.copy_(cache0.data)
-        caches.append(c)
+    if per_head:
+        ph_steps = [mla.PerHeadDecodeStep(dims, case.block_table, case.num_pages, torch.from_numpy(case.seq_lens))
+                    for _ in range(max(1, args.copies))]
+        for r0 in range(0, len(seqs), chunk):
+            r1 = min(len(seqs), r0 + chunk)
+            ph_steps[0].write(dev(case.c_rows[r0:r1]), dev(case.kr_rows[r0:r1]), torch.from_numpy(seqs[r0:r1]).cuda(),
+                              torch.from_numpy(pos[r0:r1]).cuda())
+        for st in ph_steps[1:]:
+            st.cache.copy_(ph_steps[0].cache)
+        caches = [st.cache for st in ph_steps]
+    else:
+        cache0 = mla.LatentCache(dims, case.block_table, case.num_pages)
+        for r0 in range(0, len(seqs), chunk):
+            r1 = min(len(seqs), r0 + chunk)
+            cache0.write(dev(case.c_rows[r0:r1]), dev(case.kr_rows[r0:r1]), torch.from_numpy(seqs[r0:r1]).cuda(),
+                         torch.from_numpy(pos[r0:r1]).cuda())
+        caches = [cache0]
+        for _ in range(1, max(1, args.copies)):
+            c = mla.LatentCache(dims, case.block_table, case.num_pages)
+            c.data.copy_(cache0.data)
+            caches.append(c)
     if args.calibrate:
         # a plain streaming kernel of known size: reads 256 MiB, writes 256 MiB
         cal_src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")
@@ -217,7 +253,27 @@ def main():
 
     front_ev = []
     front_bytes = 0
-    if case.kind == "decode" and args.front != "none":
+    if per_head:
+        last = case.row_offsets + np.maximum(case.seq_lens - 1, 0)
+        new_lat, new_kr = dev(case.c_rows[last]), dev(case.kr_rows[last])
+        kv_seq = torch.arange(case.batch, dtype=torch.int32, device="cuda")
+
+        def step(i, timed):
+            st = ph_steps[i % len(ph_steps)]
+            st.write(new_lat, new_kr, kv_seq, st.q_pos)
+            B.rope_apply(dims, None, None, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat)
+            B.absorb_q(dims, q_nope, w_uk, st.q_lat)
+            if timed:
+                e0 = events.record(sh)
+            st.attend()
+            if timed:
+                ev.append((e0, events.record(sh)))
+            B.out_proj(dims, st.out_latent, w_uv, st.out)
+        tokens_per_step = case.batch
+        kernel_name = "mla_decode_per_head (split attention + merge)"
+        algo = per_head_decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope)
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+    elif case.kind == "decode" and args.front != "none":
         d_model, d_qlat = s.hidden, QUERY_LATENT
         folded = args.front == "folded"
         fc = synth.front_layer(s, np.ones(case.batch, np.int32), d_model, d_qlat, seed=case.seed + 100, shuffle=False)
@@ -324,12 +380,17 @@ def main():
     front_ms = float(np.mean([events.elapsed_ms(a, b) for a, b in front_ev])) if front_ev else None
     events.close()
     achieved = algo / (kern_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
-    if case.kind == "decode" or args.prefill_form == "absorbed":
+    if per_head:
+        traffic = load_traffic("per_head", os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "perhead.hip"))
+    elif case.kind == "decode" or args.prefill_form == "absorbed":
         traffic = load_traffic(args.config)
     else:
         traffic = load_traffic(args.config + "_mha", MHA_SRC)
     out = {
-        "metric": (METRIC if case.kind == "decode" and args.front == "none" else
+        "metric": ("MLA decode over per-head position keys tokens/s + % HBM roofline" if per_head else
+                   METRIC if case.kind == "decode" and args.front == "none" and args.score == "one" else
+                   "absorbed MLA decode, two-scale score, tokens/s + % HBM roofline"
+                   if case.kind == "decode" and args.front == "none" else
                    "MLA decode layer step from hidden states tokens/s + % HBM roofline of mla_decode"
                    if case.kind == "decode" else
                    "absorbed MLA causal prefill tokens/s + % MFMA roofline" if args.prefill_form == "absorbed" else
@@ -348,8 +409,10 @@ def main():
         "config": {"workload": case.note.get("workload", args.config), "config": args.config,
                    "batch": case.batch, "seq_len": int(np.max(case.seq_lens)), "total_kv_tokens": case.total_tokens,
                    "n_heads": s.n_heads, "d_latent": s.d_latent, "d_rope": s.d_rope, "page_size": s.page_size,
-                   "cache_copies": len(caches),
-                   "step": ("rope_apply + prefill_mha" if case.kind != "decode" and args.prefill_form == "materialised"
+                   "cache_copies": len(caches), "score": "two-scale" if args.score == "two" else "one scale",
+                   "cache_layout": args.cache_layout,
+                   "step": ("cache_write_per_head + rope_apply + absorb_q + decode_per_head + out_proj" if per_head
+                            else "rope_apply + prefill_mha" if case.kind != "decode" and args.prefill_form == "materialised"
                             else f"kv_project + q_project ({args.front}) + decode + out_proj" if args.front != "none"
                             else "rope_apply + absorb_q + decode/prefill + out_proj")},
         "roofline": {"kernel": kernel_name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
@@ -360,7 +423,8 @@ def main():
         out["front"] = {"form": args.front, "d_model": s.hidden, "d_qlat": QUERY_LATENT, "avg_ms": front_ms,
                         "weight_bytes": front_bytes, "weight_GBps": front_bytes / (front_ms * 1e-3) / 1e9,
                         "calls": "kv_project + q_project" + (" + absorb_q" if args.front == "unfolded" else "")}
-    if case.kind == "decode" and not args.no_cpu_baseline and args.front == "none":
+    if case.kind == "decode" and not args.no_cpu_baseline and args.front == "none" and not per_head \
+            and args.score == "one":
         out["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(out), flush=True)
 
