@@ -222,3 +222,36 @@ def test_front_projections_validate():
     assert q(ws_bytes=ws_q - 1) == 3 and q(folded=True, ws_bytes=ws_q - 1) == 3
     assert B.LIB.mla_fold_q_weights(ctypes.byref(d), 1536, None, FAKE, FAKE, None) == 1
     assert B.LIB.mla_fold_q_weights(ctypes.byref(d), 100, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_per_head_calls_validate():
+    """The per-head-key calls: the supported shape only, and every rejection before any launch."""
+    tiny = _dims(n_heads=16, d_head=128, d_v=128, d_latent=256, d_rope=32)
+    cache = B.PagedCache(FAKE.value, 4, FAKE.value, 2, 4)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    seq = ctypes.cast(FAKE, i32p)
+
+    def write(dims=tiny, n=8, lat=FAKE):
+        return B.LIB.mla_cache_write_per_head(ctypes.byref(dims), ctypes.byref(cache), lat, FAKE, seq, seq, n, None)
+
+    assert write(n=0) == 0
+    assert write(dims=_dims()) == 2                           # the DeepSeek-V2 shape has no per-head kernel
+    assert write(dims=_dims(n_heads=16, d_latent=256, d_rope=32, dtype=0, q_lat_dtype=0)) == 2
+    assert write(n=-1) == 1
+    assert write(lat=None) == 1
+    assert B.LIB.mla_last_error().decode()
+
+    def decode(dims=tiny, lens=(100, 3), batch=None, ws=None, ws_bytes=0, q=FAKE):
+        lens_host = (ctypes.c_int32 * len(lens))(*lens)
+        return B.LIB.mla_decode_per_head(ctypes.byref(dims), ctypes.byref(cache), q, seq, lens_host,
+                                         len(lens) if batch is None else batch, FAKE, None, ws, ws_bytes, None)
+
+    assert decode(batch=0) == 0
+    assert decode(dims=_dims()) == 2
+    assert decode(q=None) == 1
+    assert decode(lens=(300, 3)) == 1                          # beyond 4 pages of 64
+    assert decode(lens=(1, 1, 1)) == 1                         # more rows than the block table
+    lens = (ctypes.c_int32 * 2)(100, 3)
+    need = B.LIB.mla_decode_workspace_size(ctypes.byref(tiny), 2, lens)
+    if need:                                                   # a plan that splits needs the workspace
+        assert decode(ws=FAKE, ws_bytes=need - 1) == 3
