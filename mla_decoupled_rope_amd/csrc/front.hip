@@ -155,8 +155,22 @@ __global__ void __launch_bounds__(256) front_reduce_kernel(FrontReduceParams p) 
   const float* src = p.part + static_cast<int64_t>(m) * p.n + f;
   double v0 = 0.0, v1 = 0.0;
   {
+    // Splits are added in order; their loads go out eight at a time, so a
+    // round costs one memory latency instead of eight.
+    constexpr int U = 8;
     float s0 = 0.f, s1 = 0.f;
-    for (int s = 0; s < p.splits; ++s) {  // splits in order
+    int s = 0;
+    for (; s + U <= p.splits; s += U) {
+      float2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const float2*>(src + (s + u) * stride);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        s0 += v[u].x;
+        s1 += v[u].y;
+      }
+    }
+    for (; s < p.splits; ++s) {
       const float2 v = *reinterpret_cast<const float2*>(src + s * stride);
       s0 += v.x;
       s1 += v.y;
