@@ -638,15 +638,24 @@ namespace {
 
 // Splits of K for an [m x n x k] projection: the first count (a divisor of
 // k / 32, at most k / 256) that gives two workgroups per CU, else the largest.
+// Split-K factor of a projection: the smallest s (a divisor of k / 32, at
+// least eight slices a split) that gives two workgroups a CU; when that count
+// leaves the CUs unevenly loaded and a larger s still fits three a CU (all
+// resident at once) with an even count, that s, so no CU streams a third
+// more weights than the rest.
 int front_splits(int64_t m, int64_t n, int k) {
   const int64_t tiles = ((m + 63) / 64) * ((n + 127) / 128);
-  int best = 1;
+  int best = 1, fallback = 0;
   for (int s = 1; s <= k / 256 && s <= 64; ++s) {
     if (k % (32 * s) != 0) continue;
-    best = s;
-    if (tiles * s >= 2 * kPlanCUs) break;
+    const int64_t wgs = tiles * s;
+    if (fallback == 0) best = s;
+    if (wgs < 2 * kPlanCUs) continue;
+    if (wgs > 3 * kPlanCUs) break;
+    if (wgs % kPlanCUs == 0) return s;
+    if (fallback == 0) fallback = s;
   }
-  return best;
+  return fallback != 0 ? fallback : best;
 }
 
 size_t front_part_bytes(int64_t m, int64_t n, int k) {
