@@ -106,8 +106,10 @@ def test_kv_project_writes_cache_rows(shape, d_model, d_qlat):
 
 @pytest.mark.parametrize("shape,d_model,d_qlat", SMALL, ids=["tiny", "dsv2"])
 @pytest.mark.parametrize("folded", [False, True], ids=["unfolded", "folded"])
-def test_q_project(shape, d_model, d_qlat, folded):
-    fc = _front_case(shape, [9, 40], d_model, d_qlat, seed=13)
+@pytest.mark.parametrize("lens", [[9, 40], [200, 100, 3]], ids=["one-tile", "prefill-sized"])
+def test_q_project(shape, d_model, d_qlat, folded, lens):
+    """Single- and multi-tile token counts (303 tokens: five 64-token tiles, the last ragged)."""
+    fc = _front_case(shape, lens, d_model, d_qlat, seed=13)
     dims = _dims(shape)
     n = fc.h.shape[0]
     q_pos = np.arange(n, dtype=np.int32) * 37 % 5000
