@@ -255,3 +255,19 @@ def test_per_head_calls_validate():
     need = B.LIB.mla_decode_workspace_size(ctypes.byref(tiny), 2, lens)
     if need:                                                   # a plan that splits needs the workspace
         assert decode(ws=FAKE, ws_bytes=need - 1) == 3
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    """include/mla.h is a plain C header: it compiles as strict C99 and as C++17, warning-free."""
+    import shutil
+    import subprocess
+
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "mla.h"\nint main(void) { mla_dims d; (void)d; return 0; }\n')
+    for cc, args in (("gcc", ["-std=c99", "-pedantic"]), ("g++", ["-std=c++17", "-x", "c++"])):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} is not installed")
+        res = subprocess.run([cc, *args, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I", inc, str(src)],
+                             capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr
