@@ -13,5 +13,5 @@ from .binding import (  # noqa: F401
     prefill_mha, prefill_mha_workspace, prefill_mha_workspace_size, q_project, q_project_folded, rope_apply,
 )
 from .pipeline import (  # noqa: F401
-    DecodeStep, LatentCache, LayerDecodeStep, PerHeadDecodeStep, PrefillStep, choose_prefill_form,
+    DecodeStep, LatentCache, LayerDecodeStep, LayerPrefillStep, PerHeadDecodeStep, PrefillStep, choose_prefill_form,
 )

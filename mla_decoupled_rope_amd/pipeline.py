@@ -213,6 +213,36 @@ class PrefillStep:
         return self.out
 
 
+class LayerPrefillStep:
+    """Causal chunked prefill of one layer from hidden states: the chunk's cache rows
+    [c | R k^R] through mla_kv_project, its queries through mla_q_project (+ mla_absorb_q)
+    or mla_q_project_folded, then mla_prefill and mla_out_proj.  Positions before each
+    chunk must already be in the cache."""
+
+    def __init__(self, dims: B.MLADims, cache: LatentCache, cu_q_host: torch.Tensor, q_start_host: torch.Tensor,
+                 d_model: int, d_qlat: int, folded: bool, device="cuda"):
+        self.dims, self.folded = dims, folded
+        self.inner = PrefillStep(dims, cache, cu_q_host, q_start_host, device)
+        n = int(self.inner.cu_q_host[-1])
+        self.q_nope = torch.empty((n, dims.n_heads, dims.d_head), dtype=dims.dtype, device=device)
+        self.front_ws = B.front_workspace(dims, n, d_model, d_qlat, device)
+
+    def run(self, h, w_dkv, w_kr, w_dq, w_up, w_qr, w_uk, w_uv):
+        """h [n, d_model]: the chunk's tokens in (sequence, position) order; w_up is W_UQ, or the
+        folded weight when the step is folded."""
+        s, d = self.inner, self.dims
+        B.kv_project(d, s.cache.data, s.cache.block_table, h, w_dkv, w_kr, s.kv_seq, s.q_pos, self.front_ws)
+        if self.folded:
+            B.q_project_folded(d, h, w_dq, w_up, w_qr, s.q_pos, s.q_lat, self.front_ws)
+        else:
+            B.q_project(d, h, w_dq, w_up, w_qr, s.q_pos, self.q_nope, s.q_lat, self.front_ws)
+            B.absorb_q(d, self.q_nope, w_uk, s.q_lat)
+        B.prefill(d, s.cache.data, s.cache.block_table, s.q_lat, s.cu_q, s.q_start, s.cu_q_host, s.q_start_host,
+                  s.out_latent, s.lse)
+        B.out_proj(d, s.out_latent, w_uv, s.out)
+        return s.out
+
+
 class LayerDecodeStep:
     """One decode step from hidden states h [B, d_model] of each sequence's newest token.
 

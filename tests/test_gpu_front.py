@@ -79,6 +79,12 @@ def _front_case(shape, lens, d_model, d_qlat, seed):
 
 SMALL = [(synth.TINY, 256, 96), (synth.DSV2, 512, 192)]
 FROM_H_TOL = (3e-2, 5e-3)  # the layer output when the cache rows and queries are formed from h
+# Prefill from h: rows of queries near a sequence's start average few keys, so
+# the storage roundings (c, R k^R, c^Q, q^C, R q^R, q~, obar in bf16) weigh
+# more; an exactly rounded float64 emulation of them reaches a row max of
+# 2.77e-2 (RMS 3.4e-3) on the DeepSeek-V2 case below, before the kernels' own
+# float32 sums and bf16 P.
+FROM_H_PREFILL_TOL = (4e-2, 5e-3)
 
 
 @pytest.mark.parametrize("shape,d_model,d_qlat", SMALL, ids=["tiny", "dsv2"])
@@ -244,3 +250,46 @@ def test_front_full_size_decode_batch():
                    2.0 ** -8 * front.content_query(np.abs(cq), np.abs(fc.w_uq)), "q^C")
     _assert_within(G.to64(q_lat)[:, :, 512:], rope.rotate(front.position_query(cq, fc.w_qr), pos[:, None]),
                    2.0 ** -8 * _pair_sum(front.position_query(np.abs(cq), np.abs(fc.w_qr))), "rotated q^R")
+
+
+@pytest.mark.parametrize("shape,d_model,d_qlat", SMALL, ids=["tiny", "dsv2"])
+@pytest.mark.parametrize("folded", [False, True], ids=["unfolded", "folded"])
+def test_layer_prefill_from_hidden_state(shape, d_model, d_qlat, folded):
+    """Prior tokens' rows written from h, then a causal chunk of each sequence (rows and queries
+    from h on the GPU, absorbed prefill, output projection) against the float64 definition."""
+    prior, new = [100, 0, 64], [30, 77, 1]
+    lens = [p_ + n_ for p_, n_ in zip(prior, new)]
+    fc = _front_case(shape, lens, d_model, d_qlat, seed=23)
+    dims = _dims(shape)
+    cache = mla.LatentCache(dims, fc.block_table, fc.num_pages, fill=float("nan"))
+    h = G.dev(fc.h, BF)
+    seqs, pos = fc.kv_seq_pos()
+    is_new = pos >= np.asarray(prior)[seqs]
+    old_rows = np.nonzero(~is_new)[0]
+    new_rows = np.nonzero(is_new)[0]
+    ws = B.front_workspace(dims, len(seqs), d_model, d_qlat)
+    if len(old_rows):
+        idx = torch.from_numpy(old_rows).cuda()
+        B.kv_project(dims, cache.data, cache.block_table, h[idx].contiguous(), G.dev(fc.w_dkv, BF),
+                     G.dev(fc.w_kr, BF), torch.from_numpy(seqs[old_rows]).cuda(),
+                     torch.from_numpy(pos[old_rows]).cuda(), ws)
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum(new)]), dtype=torch.int32)
+    step = mla.LayerPrefillStep(dims, cache, cu_q, torch.tensor(prior, dtype=torch.int32), d_model, d_qlat, folded)
+    w_uk = G.dev(fc.w_uk, BF)
+    w_up = G.dev(fc.w_uq, BF)
+    if folded:
+        w_fold = torch.empty((shape.n_heads, shape.d_latent, d_qlat), dtype=BF, device="cuda")
+        B.fold_q_weights(dims, w_up, w_uk, w_fold)
+        w_up = w_fold
+    out = step.run(h[torch.from_numpy(new_rows).cuda()].contiguous(), G.dev(fc.w_dkv, BF), G.dev(fc.w_kr, BF),
+                   G.dev(fc.w_dq, BF), w_up, G.dev(fc.w_qr, BF), w_uk, G.dev(fc.w_uv, BF))
+    torch.cuda.synchronize()
+    c = front.kv_latent(fc.h, fc.w_dkv)
+    kr = front.position_key(fc.h, fc.w_kr)
+    cq = front.query_latent(fc.h[new_rows], fc.w_dq)
+    qc = front.content_query(cq, fc.w_uq)
+    qr = front.position_query(cq, fc.w_qr)
+    want = attention.prefill_batch(cu_q.numpy(), np.asarray(prior), c, kr, fc.row_offsets, qc, qr, fc.w_uk,
+                                   fc.w_uv, shape.scale)
+    G.assert_close(G.to64(out), want["o"], "bf16", "layer prefill output o", tol=FROM_H_PREFILL_TOL)
+    G.assert_lse_close(G.to64(step.inner.lse), want["lse"], "bf16")
