@@ -38,22 +38,23 @@ def kernel_hash(src: str = KERNEL_SRC) -> str:
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def decode_bytes(seq_lens, n_heads=128, d_latent=512, d_rope=64) -> int:
-    """Algorithmic HBM bytes of one decode call: cache rows read once, the query
-    read once, the latent output written once, the block table read once."""
-    row = (d_latent + d_rope) * 2
+def decode_bytes(seq_lens, n_heads=128, d_latent=512, d_rope=64, elt=2, q_elt=2) -> int:
+    """Algorithmic HBM bytes of one decode call: cache rows (elt bytes an element)
+    read once, the query (q_elt bytes) read once, the float32 latent output
+    written once, the block table read once."""
+    row = (d_latent + d_rope) * elt
     t = np.asarray(seq_lens, np.int64)
-    per_q = n_heads * (d_latent + d_rope) * 2 + n_heads * d_latent * 2
+    per_q = n_heads * (d_latent + d_rope) * q_elt + n_heads * d_latent * 4
     return int(np.sum(row * t + per_q + 4 * ((t + 63) // 64)))
 
 
-def per_head_decode_bytes(seq_lens, n_heads=16, d_latent=256, d_rope=32) -> int:
-    """Algorithmic HBM bytes of one per-head-key decode call: rows of the latent and
-    one position key per head read once, the query read once, the latent output
-    written once, the block table read once."""
+def per_head_decode_bytes(seq_lens, n_heads=16, d_latent=256, d_rope=32, q_elt=2) -> int:
+    """Algorithmic HBM bytes of one per-head-key decode call: bf16 rows of the latent
+    and one position key per head read once, the query read once, the float32
+    latent output written once, the block table read once."""
     row = (d_latent + n_heads * d_rope) * 2
     t = np.asarray(seq_lens, np.int64)
-    per_q = n_heads * (d_latent + d_rope) * 2 + n_heads * d_latent * 2
+    per_q = n_heads * (d_latent + d_rope) * q_elt + n_heads * d_latent * 4
     return int(np.sum(row * t + per_q + 4 * ((t + 63) // 64)))
 
 
@@ -138,25 +139,64 @@ def load_traffic(config_name: str, src: str = KERNEL_SRC):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(case, budget_s: float = 15.0):
-    """The float64 materialised oracle on the host cores, on a bounded sample of sequences."""
+def metric_name(args, case, per_head: bool) -> str:
+    """The metric string of a bench line: the headline metric for the 64 x 4096 decode,
+    and a name of its own for every other workload and mode."""
+    s = case.shape
+    shape = f"n_h={s.n_heads},d_c={s.d_latent},d_r={s.d_rope}"
+    if per_head:
+        return f"MLA decode over per-head position keys tokens/s + % HBM roofline ({shape}, 64 x 4096)"
+    if case.kind == "decode":
+        what = {"c1": "tiny MLA decode (fp32, 1 x 256)", "c3": None, "c4": "absorbed MLA ragged paged decode "
+                "(128 seqs, T ~ U[512, 32768])", "c5a": "absorbed MLA long-context decode (4 x 131072)"}[args.config]
+        if args.front != "none":
+            return f"MLA decode layer step from hidden states ({args.front} front) tokens/s + % HBM roofline " \
+                   f"of mla_decode ({shape})"
+        if args.score == "two":
+            return f"absorbed MLA decode, two-scale score, tokens/s + % HBM roofline ({shape})"
+        return METRIC if what is None else f"{what} tokens/s + % HBM roofline ({shape})"
+    what = {"c2": "tiny MLA causal prefill (4 x 1024 from position 0)",
+            "c5b": "MLA chunked causal prefill (2048 after 16384)"}[args.config]
+    form = "absorbed" if args.prefill_form == "absorbed" else "materialised"
+    score = ", two-scale score" if args.score == "two" else ""
+    return f"{what}, {form} form{score}, tokens/s + % MFMA roofline ({shape})"
+
+
+def cpu_baseline(case, budget_s: float = 12.0, form: str = "materialised"):
+    """The float64 oracle (the materialised definition, or its absorbed twin) on the host
+    cores, on a bounded sample of the same workload: whole decode sequences, or prefill
+    queries in blocks of 8 taken evenly across the chunk, until `budget_s` has passed."""
     from threadpoolctl import threadpool_info
 
     from oracle import attention
 
+    evaluate = attention.materialised if form == "materialised" else attention.absorbed
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     done, t0 = 0, time.perf_counter()
-    order = list(range(case.batch))
-    for b in order:
-        attention.decode_batch(case.seq_lens, case.c_rows, case.kr_rows, case.row_offsets, case.qc, case.qr,
-                               case.w_uk, case.w_uv, case.shape.scale, case.shape.rope_base, seqs=[b])
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    if case.kind == "decode":
+        for b in range(case.batch):
+            attention.decode_batch(case.seq_lens, case.c_rows, case.kr_rows, case.row_offsets, case.qc, case.qr,
+                                   case.w_uk, case.w_uv, case.shape.scale, case.shape.rope_base, seqs=[b],
+                                   evaluate=evaluate)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        what = (f"{form} float64 decode of {done} of {case.batch} sequences "
+                f"({int(np.min(case.seq_lens))}..{int(np.max(case.seq_lens))} cached tokens)")
+    else:
+        n = int(case.cu_q[-1])
+        order = np.concatenate([np.arange(i, n, 64) for i in range(64)])  # evenly across the chunk first
+        for i in range(0, n, 8):
+            attention.prefill_batch(case.cu_q, case.q_start, case.c_rows, case.kr_rows, case.row_offsets, case.qc,
+                                    case.qr, case.w_uk, case.w_uv, case.shape.scale, case.shape.rope_base,
+                                    queries=np.sort(order[i:i + 8]), evaluate=evaluate)
+            done += len(order[i:i + 8])
+            if time.perf_counter() - t0 > budget_s:
+                break
+        what = f"{form} float64 causal prefill of {done} of {n} queries, spread evenly over the chunk"
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"materialised float64 decode of {done} of {case.batch} sequences "
-                      f"({int(case.seq_lens[0])} cached tokens each) in {el:.1f} s"}
+            "sample": f"{what} in {el:.1f} s"}
 
 
 def main():
@@ -208,8 +248,12 @@ def main():
     scale, position_scale = s.scale, None
     if args.score == "two":
         scale, position_scale = 1.0 / np.sqrt(s.d_head), 1.0 / np.sqrt(s.d_rope)
+    # the small shape runs in the float32 working precision (two-term q~ and softmax
+    # weights), the path its parity tests hold to the configured bounds
+    work = torch.float32 if (dt == torch.float32 or s.row <= 288) and args.prefill_form == "absorbed" else dt
     dims = mla.MLADims(s.n_heads, s.d_head, s.d_v, s.d_latent, s.d_rope, dtype=dt, softmax_scale=scale,
-                       position_scale=position_scale)
+                       position_scale=position_scale, work_dtype=work)
+    q_elt = 4 if work == torch.float32 else 2
 
     def dev(x, dtype=dt):
         return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(dtype).contiguous()
@@ -271,7 +315,7 @@ def main():
             B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = case.batch
         kernel_name = "mla_decode_per_head (split attention + merge)"
-        algo = per_head_decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope)
+        algo = per_head_decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope, q_elt)
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
     elif case.kind == "decode" and args.front != "none":
         d_model, d_qlat = s.hidden, QUERY_LATENT
@@ -306,7 +350,7 @@ def main():
             B.out_proj(dims, inner.out_latent, w_uv, inner.out)
         tokens_per_step = case.batch
         kernel_name = "mla_decode (split attention + merge)"
-        algo = decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope)
+        algo = decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope, 4 if dt == torch.float32 else 2, q_elt)
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
     elif case.kind == "decode":
         steps = [mla.DecodeStep(dims, c, torch.from_numpy(case.seq_lens)) for c in caches]
@@ -327,7 +371,7 @@ def main():
             B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = case.batch
         kernel_name = "mla_decode (split attention + merge)"
-        algo = decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope)
+        algo = decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope, 4 if dt == torch.float32 else 2, q_elt)
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
     elif args.prefill_form == "materialised":
         steps = [mla.PrefillStep(dims, c, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
@@ -387,14 +431,7 @@ def main():
     else:
         traffic = load_traffic(args.config + "_mha", MHA_SRC)
     out = {
-        "metric": ("MLA decode over per-head position keys tokens/s + % HBM roofline" if per_head else
-                   METRIC if case.kind == "decode" and args.front == "none" and args.score == "one" else
-                   "absorbed MLA decode, two-scale score, tokens/s + % HBM roofline"
-                   if case.kind == "decode" and args.front == "none" else
-                   "MLA decode layer step from hidden states tokens/s + % HBM roofline of mla_decode"
-                   if case.kind == "decode" else
-                   "absorbed MLA causal prefill tokens/s + % MFMA roofline" if args.prefill_form == "absorbed" else
-                   "MLA causal prefill, materialised form, tokens/s + % MFMA roofline"),
+        "metric": metric_name(args, case, per_head),
         "value": tokens_per_step / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -423,9 +460,9 @@ def main():
         out["front"] = {"form": args.front, "d_model": s.hidden, "d_qlat": QUERY_LATENT, "avg_ms": front_ms,
                         "weight_bytes": front_bytes, "weight_GBps": front_bytes / (front_ms * 1e-3) / 1e9,
                         "calls": "kv_project + q_project" + (" + absorb_q" if args.front == "unfolded" else "")}
-    if case.kind == "decode" and not args.no_cpu_baseline and args.front == "none" and not per_head \
-            and args.score == "one":
+    if not args.no_cpu_baseline and args.front == "none" and not per_head and args.score == "one":
         out["cpu_baseline"] = cpu_baseline(case)
+        out["cpu_baseline_absorbed"] = cpu_baseline(case, form="absorbed")
     print(json.dumps(out), flush=True)
 
 

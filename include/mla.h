@@ -25,10 +25,12 @@
  *   _host.  Tensors are dense and row-major in the shapes given.  The caller
  *   owns every buffer; the library allocates nothing and keeps no pointer
  *   after a call returns.
- * - dtype: the cache, q_rope, q_nope, kv_latent, k_rope, the weights and
- *   out_latent share dims->dtype (MLA_F32 or MLA_BF16).  q_lat has
- *   dims->q_lat_dtype.  The layer output of mla_out_proj and lse are always
- *   float32; indices are int32.  Accumulation is float32 in every kernel.
+ * - dtype: the cache, q_rope, q_nope, kv_latent, k_rope and the weights
+ *   share dims->dtype (MLA_F32 or MLA_BF16).  q_lat has dims->work_dtype.
+ *   The latent output out_latent (obar, the input of mla_out_proj), the
+ *   decode's split partials, the layer output of mla_out_proj and lse are
+ *   always float32, so the path's roundings stop at the softmax weights;
+ *   indices are int32.  Accumulation is float32 in every kernel.
  * - Work is enqueued on `stream` (a hipStream_t, NULL = default stream) and
  *   is asynchronous: no call synchronises.  Keep buffers alive until the
  *   stream has passed the work.
@@ -72,13 +74,19 @@ typedef struct {
   int32_t d_latent;    /* d_c: width of the cached latent c_t            */
   int32_t d_rope;      /* d_r: width of the decoupled RoPE channel, even */
   int32_t page_size;   /* tokens per cache page (must be 64)             */
-  int32_t dtype;       /* mla_dtype of cache, inputs, weights, out_latent */
-  int32_t q_lat_dtype; /* mla_dtype of q_lat.  MLA_F32 with dtype MLA_BF16
-                        * keeps the absorbed query at float32 and scores it
-                        * as a two-term bf16 split (hi + lo): twice the QK
-                        * MFMA work, bf16 rounding of q~ removed.  Supported
-                        * for d_latent + d_rope <= 288.  With dtype MLA_F32
-                        * it must be MLA_F32.                             */
+  int32_t dtype;       /* mla_dtype of cache, inputs and weights          */
+  int32_t work_dtype;  /* the attention's working precision, and the
+                        * mla_dtype of q_lat.  MLA_BF16 (with dtype
+                        * MLA_BF16): q_lat, and the softmax weights fed to
+                        * the weighted sum, are bf16 -- the fast path.
+                        * MLA_F32 with dtype MLA_BF16, the float32 working
+                        * precision: q_lat is float32, the score takes q~
+                        * as a two-term bf16 split (hi = bf16(x), lo =
+                        * bf16(x - hi)) and the weighted sum takes the
+                        * softmax weights the same way, so neither is
+                        * rounded to bf16 once (twice the MFMA work).
+                        * Supported for d_latent + d_rope <= 288.  With
+                        * dtype MLA_F32 it must be MLA_F32.               */
   float softmax_scale; /* scale on the content part of the score          */
   float position_scale; /* scale on the position part of the score.  Equal
                         * to softmax_scale: one scale on the summed score.
@@ -144,8 +152,8 @@ size_t mla_decode_workspace_size(const mla_dims* dims, int32_t batch, const int3
  * "AI decoupled RoPE MLA", decoupled-RoPE score equation).
  *   query b sits at position seq_lens[b] - 1 and sees cached positions
  *   0 .. seq_lens[b] - 1;  q_lat [batch, H, d_latent + d_rope] (from
- *   mla_rope_apply + mla_absorb_q);  out_latent [batch, H, d_latent] gets
- *   obar = sum_t alpha_t c_t;  lse [batch, H] (float32, may be NULL) gets
+ *   mla_rope_apply + mla_absorb_q);  out_latent [batch, H, d_latent]
+ *   (float32) gets obar = sum_t alpha_t c_t;  lse [batch, H] (float32, may be NULL) gets
  *   log sum_t exp(s_t).  A sequence of length 0 yields obar = 0, lse = -inf.
  * seq_lens is the device copy, seq_lens_host the same values on the host
  * (used to plan the split).  workspace: device memory of at least
@@ -163,7 +171,8 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
  *   sits at position q_start_pos[b] + j and sees cached positions t <= that
  *   position (the chunk's own rows must already be in the cache, written by
  *   mla_rope_apply).  q_lat [cu_q[batch], H, d_latent + d_rope];
- *   out_latent [cu_q[batch], H, d_latent]; lse [cu_q[batch], H] or NULL.
+ *   out_latent [cu_q[batch], H, d_latent] (float32); lse [cu_q[batch], H] or
+ *   NULL.
  * cu_q_host / q_start_pos_host are host copies of cu_q / q_start_pos. */
 mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
                        const int32_t* cu_q, const int32_t* q_start_pos, const int32_t* cu_q_host,
@@ -198,7 +207,7 @@ size_t mla_prefill_mha_workspace_size(const mla_dims* dims, int32_t batch, const
  * bytes (otherwise MLA_ERR_WORKSPACE).  The up-projected keys and values,
  * the content query and the softmax weights are rounded to float16 (keys and
  * values must stay below 65504 in magnitude); the rotated part stays bf16.
- * bf16 inputs only, d_head = d_v = 128,
+ * bf16 inputs and work_dtype only, d_head = d_v = 128,
  * (n_heads, d_latent, d_rope) = (128, 512, 64) or (16, 256, 32); other
  * shapes return MLA_ERR_UNSUPPORTED. */
 mla_status mla_prefill_mha(const mla_dims* dims, const mla_paged_cache* cache, const void* q_nope, const void* q_lat,
@@ -233,8 +242,9 @@ mla_status mla_cache_write_per_head(const mla_dims* dims, const mla_paged_cache*
  * softmax_scale * (q~_i . c_t + R_m q^R_i . R_t k^R_{t,i}) over keys
  * 0 .. T_b - 1 and returns obar_i = sum_t alpha_{i,t} c_t and lse, with the
  * arguments, output layout, workspace (mla_decode_workspace_size with the same
- * dims and lengths) and errors of mla_decode.  q_lat may be bf16 or float32
- * (q_lat_dtype; float32 enters as a two-term bf16 split). */
+ * dims and lengths) and errors of mla_decode.  work_dtype may be MLA_BF16 or
+ * MLA_F32 (float32 q_lat; q~ and the softmax weights enter as two-term bf16
+ * splits). */
 mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
                                const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* out_latent,
                                float* lse, void* workspace, size_t ws_bytes, void* stream);
@@ -242,8 +252,9 @@ mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cach
 /* mla_out_proj -- output absorption ("AI decoupled RoPE MLA", recap section:
  * Attn_m = W^UV sum_t alpha_mt c_t).
  *   out[n, h, :] = W_UV[h] out_latent[n, h, :]
- *   out_latent [n, H, d_latent]; w_uv [H, d_v, d_latent]; out [n, H, d_v]
- *   in float32 (the float32 accumulator is kept, not rounded to dtype). */
+ *   out_latent [n, H, d_latent] float32 (with bf16 weights it enters as a
+ *   two-term bf16 split); w_uv [H, d_v, d_latent]; out [n, H, d_v] float32
+ *   (the float32 accumulator is kept, not rounded to dtype). */
 mla_status mla_out_proj(const mla_dims* dims, const void* out_latent, const void* w_uv, int64_t n,
                         void* out, void* stream);
 
@@ -259,7 +270,7 @@ mla_status mla_out_proj(const mla_dims* dims, const void* out_latent, const void
  * Weights are stored [out, in]: W_DKV [d_latent, d_model], W_KR [d_rope,
  * d_model], W_DQ [d_qlat, d_model], W_UQ [H, d_head, d_qlat], W_QR [H, d_rope,
  * d_qlat], the folded W_fold [H, d_latent, d_qlat] = W_UK,i^T W_UQ,i.
- * bf16 only (dims->dtype and q_lat_dtype), d_model and d_qlat multiples of 32,
+ * bf16 only (dims->dtype and work_dtype), d_model and d_qlat multiples of 32,
  * h and the weights 16-byte aligned; otherwise MLA_ERR_UNSUPPORTED or
  * MLA_ERR_INVALID_ARG and nothing is launched.  Accumulation is float32 over
  * K splits summed in a fixed order (bitwise repeatable); RoPE angles are

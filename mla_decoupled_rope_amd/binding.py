@@ -32,7 +32,7 @@ class Dims(ctypes.Structure):
     _fields_ = [
         ("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32), ("d_v", ctypes.c_int32),
         ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("page_size", ctypes.c_int32),
-        ("dtype", ctypes.c_int32), ("q_lat_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32), ("work_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("position_scale", ctypes.c_float), ("rope_base", ctypes.c_double),
     ]
 
@@ -110,21 +110,23 @@ class MLADims:
     position_scale: float | None = None  # None: softmax_scale (one scale on the summed score)
     rope_base: float = 10000.0
     page_size: int = 64
-    q_lat_dtype: torch.dtype | None = None  # None: same as dtype
+    # dtype of q_lat (None: same as dtype).  torch.float32 with a bf16 dtype is
+    # the float32 working precision (two-term q~ and softmax weights).
+    work_dtype: torch.dtype | None = None
 
     @property
     def row(self) -> int:
         return self.d_latent + self.d_rope
 
     @property
-    def qdtype(self) -> torch.dtype:
-        return self.dtype if self.q_lat_dtype is None else self.q_lat_dtype
+    def wdtype(self) -> torch.dtype:
+        return self.dtype if self.work_dtype is None else self.work_dtype
 
     def c(self) -> Dims:
         scale = self.softmax_scale if self.softmax_scale is not None else 1.0 / math.sqrt(self.d_head + self.d_rope)
         code = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}
         return Dims(self.n_heads, self.d_head, self.d_v, self.d_latent, self.d_rope, self.page_size,
-                    code[self.dtype], code[self.qdtype], scale,
+                    code[self.dtype], code[self.wdtype], scale,
                     scale if self.position_scale is None else self.position_scale, self.rope_base)
 
 
@@ -175,7 +177,7 @@ def rope_apply(dims: MLADims, cache: torch.Tensor | None, block_table: torch.Ten
     if n_q:
         _dev(q_rope, "q_rope", dims.dtype, (n_q, dims.n_heads, dims.d_rope))
         _dev(q_pos, "q_pos", torch.int32, (n_q,))
-        _dev(q_lat, "q_lat", dims.qdtype, (n_q, dims.n_heads, dims.row))
+        _dev(q_lat, "q_lat", dims.wdtype, (n_q, dims.n_heads, dims.row))
     cstruct = None
     if n_kv:
         cstruct = _cache(dims, cache, block_table)
@@ -196,7 +198,7 @@ def absorb_q(dims: MLADims, q_nope: torch.Tensor, w_uk: torch.Tensor, q_lat: tor
     n = q_nope.shape[0]
     _dev(q_nope, "q_nope", dims.dtype, (n, dims.n_heads, dims.d_head))
     _dev(w_uk, "w_uk", dims.dtype, (dims.n_heads, dims.d_head, dims.d_latent))
-    _dev(q_lat, "q_lat", dims.qdtype, (n, dims.n_heads, dims.row))
+    _dev(q_lat, "q_lat", dims.wdtype, (n, dims.n_heads, dims.row))
     d = dims.c()
     _check(LIB.mla_absorb_q(ctypes.byref(d), q_nope.data_ptr(), w_uk.data_ptr(), n, q_lat.data_ptr(), _stream()))
 
@@ -227,10 +229,10 @@ def decode(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat:
     """mla_decode: out_latent[b] = sum_t softmax(s)_t c_t over positions 0 .. seq_lens[b]-1."""
     batch = seq_lens_host.numel()
     cstruct = _cache(dims, cache, block_table)
-    _dev(q_lat, "q_lat", dims.qdtype, (batch, dims.n_heads, dims.row))
+    _dev(q_lat, "q_lat", dims.wdtype, (batch, dims.n_heads, dims.row))
     _dev(seq_lens, "seq_lens", torch.int32, (batch,))
     _host_i32(seq_lens_host, "seq_lens_host")
-    _dev(out_latent, "out_latent", dims.dtype, (batch, dims.n_heads, dims.d_latent))
+    _dev(out_latent, "out_latent", torch.float32, (batch, dims.n_heads, dims.d_latent))
     if lse is not None:
         _dev(lse, "lse", torch.float32, (batch, dims.n_heads))
     if workspace is not None:
@@ -266,10 +268,10 @@ def decode_per_head(dims: MLADims, cache: torch.Tensor, block_table: torch.Tenso
     """mla_decode_per_head: decode over a cache with one position key per head."""
     batch = seq_lens_host.numel()
     cstruct = _cache(dims, cache, block_table, per_head_row(dims))
-    _dev(q_lat, "q_lat", dims.qdtype, (batch, dims.n_heads, dims.row))
+    _dev(q_lat, "q_lat", dims.wdtype, (batch, dims.n_heads, dims.row))
     _dev(seq_lens, "seq_lens", torch.int32, (batch,))
     _host_i32(seq_lens_host, "seq_lens_host")
-    _dev(out_latent, "out_latent", dims.dtype, (batch, dims.n_heads, dims.d_latent))
+    _dev(out_latent, "out_latent", torch.float32, (batch, dims.n_heads, dims.d_latent))
     if lse is not None:
         _dev(lse, "lse", torch.float32, (batch, dims.n_heads))
     if workspace is not None:
@@ -291,10 +293,10 @@ def prefill(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat
     if cu_q_host.numel() != batch + 1:
         raise ValueError("cu_q must have batch + 1 entries")
     n = int(cu_q_host[-1])
-    _dev(q_lat, "q_lat", dims.qdtype, (n, dims.n_heads, dims.row))
+    _dev(q_lat, "q_lat", dims.wdtype, (n, dims.n_heads, dims.row))
     _dev(cu_q, "cu_q", torch.int32, (batch + 1,))
     _dev(q_start, "q_start", torch.int32, (batch,))
-    _dev(out_latent, "out_latent", dims.dtype, (n, dims.n_heads, dims.d_latent))
+    _dev(out_latent, "out_latent", torch.float32, (n, dims.n_heads, dims.d_latent))
     if lse is not None:
         _dev(lse, "lse", torch.float32, (n, dims.n_heads))
     d = dims.c()
@@ -333,7 +335,7 @@ def prefill_mha(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q
         raise ValueError("cu_q must have batch + 1 entries")
     n = int(cu_q_host[-1])
     _dev(q_nope, "q_nope", dims.dtype, (n, dims.n_heads, dims.d_head))
-    _dev(q_lat, "q_lat", dims.qdtype, (n, dims.n_heads, dims.row))
+    _dev(q_lat, "q_lat", dims.wdtype, (n, dims.n_heads, dims.row))
     _dev(w_uk, "w_uk", dims.dtype, (dims.n_heads, dims.d_head, dims.d_latent))
     _dev(w_uv, "w_uv", dims.dtype, (dims.n_heads, dims.d_v, dims.d_latent))
     _dev(cu_q, "cu_q", torch.int32, (batch + 1,))
@@ -351,9 +353,9 @@ def prefill_mha(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q
 
 
 def out_proj(dims: MLADims, out_latent: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor) -> None:
-    """mla_out_proj: out[n, h] = W_UV[h] out_latent[n, h] (out is float32)."""
+    """mla_out_proj: out[n, h] = W_UV[h] out_latent[n, h] (out_latent and out are float32)."""
     n = out_latent.shape[0]
-    _dev(out_latent, "out_latent", dims.dtype, (n, dims.n_heads, dims.d_latent))
+    _dev(out_latent, "out_latent", torch.float32, (n, dims.n_heads, dims.d_latent))
     _dev(w_uv, "w_uv", dims.dtype, (dims.n_heads, dims.d_v, dims.d_latent))
     _dev(out, "out", torch.float32, (n, dims.n_heads, dims.d_v))
     d = dims.c()
@@ -400,7 +402,7 @@ def q_project(dims: MLADims, h: torch.Tensor, w_dq: torch.Tensor, w_uq: torch.Te
     _dev(w_qr, "w_qr", dims.dtype, (dims.n_heads, dims.d_rope, d_qlat))
     _dev(q_pos, "q_pos", torch.int32, (n,))
     _dev(q_nope, "q_nope", dims.dtype, (n, dims.n_heads, dims.d_head))
-    _dev(q_lat, "q_lat", dims.qdtype, (n, dims.n_heads, dims.row))
+    _dev(q_lat, "q_lat", dims.wdtype, (n, dims.n_heads, dims.row))
     _dev(workspace, "workspace", torch.uint8)
     d = dims.c()
     _check(LIB.mla_q_project(ctypes.byref(d), h.data_ptr(), n, d_model, d_qlat, w_dq.data_ptr(), w_uq.data_ptr(),
@@ -418,7 +420,7 @@ def q_project_folded(dims: MLADims, h: torch.Tensor, w_dq: torch.Tensor, w_fold:
     _dev(w_fold, "w_fold", dims.dtype, (dims.n_heads, dims.d_latent, d_qlat))
     _dev(w_qr, "w_qr", dims.dtype, (dims.n_heads, dims.d_rope, d_qlat))
     _dev(q_pos, "q_pos", torch.int32, (n,))
-    _dev(q_lat, "q_lat", dims.qdtype, (n, dims.n_heads, dims.row))
+    _dev(q_lat, "q_lat", dims.wdtype, (n, dims.n_heads, dims.row))
     _dev(workspace, "workspace", torch.uint8)
     d = dims.c()
     _check(LIB.mla_q_project_folded(ctypes.byref(d), h.data_ptr(), n, d_model, d_qlat, w_dq.data_ptr(),

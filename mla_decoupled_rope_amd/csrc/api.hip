@@ -58,10 +58,10 @@ mla_status check_dims(const mla_dims* d) {
   if (d->d_rope > 128) return fail(MLA_ERR_UNSUPPORTED, "d_rope > 128 is not supported (got %d)", d->d_rope);
   if (d->page_size != mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size must be 64 (got %d)", d->page_size);
   if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
-  if (d->q_lat_dtype != MLA_F32 && d->q_lat_dtype != MLA_BF16)
-    return fail(MLA_ERR_INVALID_ARG, "unknown q_lat_dtype %d", d->q_lat_dtype);
-  if (d->dtype == MLA_F32 && d->q_lat_dtype != MLA_F32)
-    return fail(MLA_ERR_INVALID_ARG, "float32 inputs need a float32 q_lat");
+  if (d->work_dtype != MLA_F32 && d->work_dtype != MLA_BF16)
+    return fail(MLA_ERR_INVALID_ARG, "unknown work_dtype %d", d->work_dtype);
+  if (d->dtype == MLA_F32 && d->work_dtype != MLA_F32)
+    return fail(MLA_ERR_INVALID_ARG, "float32 inputs need the float32 working precision");
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f))
     return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
   if (!(std::isfinite(d->position_scale) && d->position_scale > 0.f))
@@ -75,8 +75,8 @@ mla_status check_attn_shape(const mla_dims* d) {
   if (d->dtype == MLA_BF16) {
     const bool dsv2 = d->n_heads == 128 && d->d_latent == 512 && d->d_rope == 64;
     const bool tiny = d->n_heads == 16 && d->d_latent == 256 && d->d_rope == 32;
-    if (d->q_lat_dtype == MLA_F32 && d->d_latent + d->d_rope > 288)
-      return fail(MLA_ERR_UNSUPPORTED, "a float32 q_lat (two-term scores) needs d_latent + d_rope <= 288");
+    if (d->work_dtype == MLA_F32 && d->d_latent + d->d_rope > 288)
+      return fail(MLA_ERR_UNSUPPORTED, "the float32 working precision needs d_latent + d_rope <= 288");
     if (!dsv2 && !tiny)
       return fail(MLA_ERR_UNSUPPORTED,
                   "bf16 attention supports (n_heads, d_latent, d_rope) = (128, 512, 64) or (16, 256, 32); got (%d, %d, %d)",
@@ -224,11 +224,16 @@ Plan make_plan(const mla_dims* d, int batch, const int32_t* lens) {
   return last.plan;
 }
 
+// Split partials: normalised obar [n_items, H, d_latent] float32, then lse
+// [n_items, H] float32 at a 256-byte aligned offset.
+size_t partial_bytes(const mla_dims* d, const Plan& p) {
+  const size_t o = static_cast<size_t>(p.n_items) * d->n_heads * d->d_latent * sizeof(float);
+  return (o + kWsAlign - 1) / kWsAlign * kWsAlign;
+}
+
 size_t workspace_bytes(const mla_dims* d, const Plan& p) {
   if (d->dtype != MLA_BF16 || !p.needs_merge || p.n_items == 0) return 0;
-  const size_t o = static_cast<size_t>(p.n_items) * d->n_heads * d->d_latent * sizeof(uint16_t);
-  const size_t o_al = (o + kWsAlign - 1) / kWsAlign * kWsAlign;
-  return o_al + static_cast<size_t>(p.n_items) * d->n_heads * sizeof(float);
+  return partial_bytes(d, p) + static_cast<size_t>(p.n_items) * d->n_heads * sizeof(float);
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -271,7 +276,7 @@ mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache, co
   p.d_latent = dims->d_latent;
   p.d_rope = dims->d_rope;
   p.dtype = dims->dtype;
-  p.q_lat_dtype = dims->q_lat_dtype;
+  p.work_dtype = dims->work_dtype;
   p.q_rope = q_rope; p.q_pos = q_pos; p.n_q = n_q; p.q_lat = q_lat;
   p.kv_latent = kv_latent; p.k_rope = k_rope; p.kv_seq = kv_seq; p.kv_pos = kv_pos; p.n_kv = n_kv;
   if (n_kv > 0) {
@@ -299,7 +304,7 @@ mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_
   if (n_q > 65535LL * 512 || n_q * dims->n_heads * dims->d_latent > (1LL << 40))
     return fail(MLA_ERR_UNSUPPORTED, "n_q too large for one launch");
   mla::GemmParams p{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
-                    dims->q_lat_dtype, q_nope, w_uk, q_lat, n_q};
+                    dims->work_dtype, q_nope, w_uk, q_lat, n_q};
   const hipError_t e = mla::launch_absorb(p, as_stream(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "absorb launch");
 }
@@ -317,7 +322,7 @@ mla_status mla_out_proj(const mla_dims* dims, const void* out_latent, const void
                                      "multiple of 64");
   if (n > (1LL << 31) / dims->n_heads) return fail(MLA_ERR_UNSUPPORTED, "n too large for one launch");
   mla::GemmParams p{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
-                    dims->q_lat_dtype, out_latent, w_uv, out, n};
+                    dims->work_dtype, out_latent, w_uv, out, n};
   const hipError_t e = mla::launch_out_proj(p, as_stream(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "out_proj launch");
 }
@@ -362,7 +367,7 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
   }
   mla::AttnParams p{};
   p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
-  p.q_f32 = dims->q_lat_dtype == MLA_F32;
+  p.f32w = dims->work_dtype == MLA_F32;
   p.scale = dims->softmax_scale;
   p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);
   p.q_lat = q_lat; p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
@@ -383,14 +388,13 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
   p.n_items = plan.n_items;
   p.n_head_chunks = 1;
   if (need > 0) {
-    const size_t o = static_cast<size_t>(plan.n_items) * dims->n_heads * dims->d_latent * sizeof(uint16_t);
-    p.ws_o = static_cast<mla::bf16_t*>(workspace);
-    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (o + kWsAlign - 1) / kWsAlign * kWsAlign);
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + partial_bytes(dims, plan));
   }
   hipError_t e = mla::launch_decode_bf16(p, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (plan.needs_merge) {
-    e = mla::launch_merge(p, dims->dtype, s);
+    e = mla::launch_merge(p, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return MLA_OK;
@@ -424,7 +428,7 @@ mla_status mla_cache_write_per_head(const mla_dims* dims, const mla_paged_cache*
   if (n_kv > (static_cast<int64_t>(UINT32_MAX) - 3) * 4) return fail(MLA_ERR_UNSUPPORTED, "too many rows for one launch");
   mla::RopeParams p{};
   p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
-  p.dtype = dims->dtype; p.q_lat_dtype = dims->q_lat_dtype;
+  p.dtype = dims->dtype; p.work_dtype = dims->work_dtype;
   p.kv_latent = kv_latent; p.k_rope = k_rope; p.kv_seq = kv_seq; p.kv_pos = kv_pos; p.n_kv = n_kv;
   p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
   p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
@@ -462,7 +466,7 @@ mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cach
   if (plan.n_items > (1LL << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
   mla::AttnParams p{};
   p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
-  p.q_f32 = dims->q_lat_dtype == MLA_F32;
+  p.f32w = dims->work_dtype == MLA_F32;
   p.scale = dims->softmax_scale;
   p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);
   p.q_lat = q_lat; p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
@@ -470,15 +474,14 @@ mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cach
   p.seq_lens = seq_lens; p.batch = batch; p.out_latent = out_latent; p.lse = lse;
   p.split_pages = plan.split_pages; p.n_full = plan.n_full; p.n_items = plan.n_items; p.n_head_chunks = 1;
   if (need > 0) {
-    const size_t o = static_cast<size_t>(plan.n_items) * dims->n_heads * dims->d_latent * sizeof(uint16_t);
-    p.ws_o = static_cast<mla::bf16_t*>(workspace);
-    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + (o + kWsAlign - 1) / kWsAlign * kWsAlign);
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + partial_bytes(dims, plan));
   }
   const hipStream_t s = as_stream(stream);
   hipError_t e = mla::launch_perhead_decode(p, s);
   if (e != hipSuccess) return hip_fail(e, "per-head decode launch");
   if (plan.needs_merge) {
-    e = mla::launch_merge(p, dims->dtype, s);
+    e = mla::launch_merge(p, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return MLA_OK;
@@ -520,7 +523,7 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const
   if (n_blocks > (1LL << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, "too many workgroups");
   mla::AttnParams p{};
   p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
-  p.q_f32 = dims->q_lat_dtype == MLA_F32;
+  p.f32w = dims->work_dtype == MLA_F32;
   p.scale = dims->softmax_scale;
   p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);
   p.q_lat = q_lat; p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
@@ -543,7 +546,8 @@ struct MhaPlan {
 mla_status plan_mha(const mla_dims* dims, const mla_paged_cache* cache, int32_t batch, const int32_t* cu_q_host,
                     const int32_t* q_start_pos_host, MhaPlan* plan) {
   MLA_TRY(check_dims(dims));
-  if (dims->dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "the materialised prefill is bf16 only");
+  if (dims->dtype != MLA_BF16 || dims->work_dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "the materialised prefill is bf16 only (dtype and work_dtype)");
   if (dims->d_head != 128 || dims->d_v != 128)
     return fail(MLA_ERR_UNSUPPORTED, "the materialised prefill needs d_head = d_v = 128 (got %d, %d)", dims->d_head,
                 dims->d_v);
@@ -666,7 +670,7 @@ size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 mla_status check_front(const mla_dims* d, int64_t n, int32_t d_model, int32_t d_qlat, bool need_q) {
   MLA_TRY(check_dims(d));
-  if (d->dtype != MLA_BF16 || d->q_lat_dtype != MLA_BF16)
+  if (d->dtype != MLA_BF16 || d->work_dtype != MLA_BF16)
     return fail(MLA_ERR_UNSUPPORTED, "the front projections are bf16 only");
   if (n < 0) return fail(MLA_ERR_INVALID_ARG, "n must be >= 0");
   if (n > 65535LL * 64) return fail(MLA_ERR_UNSUPPORTED, "more than %lld tokens in one call", 65535LL * 64);

@@ -37,6 +37,13 @@
 // Tokens past the end of a sequence are masked; their LDS rows are filled
 // from the last valid row of the tile, so garbage or NaN in unused page
 // slots never reaches the accumulators.
+//
+// Precision.  obar and the split partials are float32 (normalised rows).  By
+// default q_lat and the softmax weights P fed to P.V are bf16.  The float32
+// working precision (F32W, the small shape only) takes a float32 q_lat and
+// feeds both q~ and P to their contractions as two-term bf16 splits
+// (x = hi + lo, hi = bf16(x), lo = bf16(x - hi)), so neither is rounded to
+// bf16 once; the contractions then take twice the MFMAs.
 #include <cfloat>
 #include <type_traits>
 
@@ -223,7 +230,7 @@ __device__ __forceinline__ void mfma_qk_drain(f32x16& s) {
 // MFMA 32x32x16 lane layouts used below (lane l, r = l % 32, h = l / 32):
 //   A[i][k]: row i = r, k = 8h .. 8h+7;   B[k][j]: column j = r, k = 8h .. 8h+7;
 //   D[i][j]: column j = r, rows i = 8g + 4h + e in register 4g + e (g, e < 4).
-template <int DC, int DR, int HG, int TW, bool PREFILL, bool QF32>
+template <int DC, int DR, int HG, int TW, bool PREFILL, bool F32W>
 __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p) {
   constexpr int D = DC + DR;
   constexpr int ROWB = D * 2;       // bytes per cache row
@@ -257,10 +264,11 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   __shared__ __attribute__((aligned(16))) char lds0[TILE];
   __shared__ __attribute__((aligned(16))) char lds1[TILE];
   __shared__ __attribute__((aligned(16))) char lds2[TILE];
-  __shared__ bf16x8 ldsq[(QF32 ? 2 : 1) * ROWS * QCH];
+  __shared__ bf16x8 ldsq[(F32W ? 2 : 1) * ROWS * QCH];
   // P^T of a tile for the column split: entry (kp * 2 + h) * ROWS + row holds
-  // row's P at the 8 tokens that half h of k-step kp covers
-  __shared__ bf16x8 ldsp[DSPLIT ? 4 * ROWS : 1];
+  // row's P at the 8 tokens that half h of k-step kp covers (with F32W, the
+  // lo terms follow at 4 * ROWS)
+  __shared__ bf16x8 ldsp[DSPLIT ? (F32W ? 8 : 4) * ROWS : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -334,7 +342,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
   // lane keeps exactly the fragments it will read back (no sharing, so no
   // barrier), XOR-swizzled like the cache tiles.
   bf16x8 qf[KSQ];
-  bf16x8 qlo[QF32 ? KSQ : 1];
+  bf16x8 qlo[F32W ? KSQ : 1];
   // this lane's LDS home of a fragment of k-step ks; lr, lh are the lane's r32, h2.
   // Rows of a multiple of 8 chunks take the cache tiles' swizzle; other rows
   // (a stride of 16 banks mod 64) XOR with bits 2-3 of the row.  Either way
@@ -348,7 +356,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     bf16x8 hi8, lo8;
-    if constexpr (QF32) {
+    if constexpr (F32W) {
       const float* qlat = static_cast<const float*>(p.q_lat);
       bf16_t hi[8], lo[8];
 #pragma unroll
@@ -366,10 +374,10 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     }
     if (ks < KSQ) {
       qf[ks < KSQ ? ks : 0] = hi8;
-      if constexpr (QF32) qlo[ks < KSQ ? ks : 0] = lo8;
+      if constexpr (F32W) qlo[ks < KSQ ? ks : 0] = lo8;
     } else {
       *q_slot(0, ks, r32, h2) = hi8;
-      if constexpr (QF32) *q_slot(1, ks, r32, h2) = lo8;
+      if constexpr (F32W) *q_slot(1, ks, r32, h2) = lo8;
     }
   }
 
@@ -487,13 +495,13 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
         // K fragments run KPF steps ahead of the MFMAs that consume them.
         constexpr int KPF = 8;
         bf16x8 ka[KS];
-        bf16x8 qr[KS], qrlo[QF32 ? KS : 1];
+        bf16x8 qr[KS], qrlo[F32W ? KS : 1];
         auto load_k = [&](int ks) {
           const char* a = 2 * ks < CHF8 ? buf + k_off[ks & 3] + (ks / 4) * 128 : buf + k_tail[(ks - CHF8 / 2) & 1];
           ka[ks] = *reinterpret_cast<const bf16x8*>(a);
           if (ks >= KSQ) {
             qr[ks] = *q_slot(0, ks, lr, lh);
-            if constexpr (QF32) qrlo[ks] = *q_slot(1, ks, lr, lh);
+            if constexpr (F32W) qrlo[ks] = *q_slot(1, ks, lr, lh);
           }
         };
 #pragma unroll
@@ -509,7 +517,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
             mfma_qk_first(sacc, ka[ks], qb);
           else
             mfma_qk(sacc, ka[ks], qb);
-          if constexpr (QF32) mfma_qk(sacc, ka[ks], ks < KSQ ? qlo[ks < KSQ ? ks : 0] : qrlo[QF32 ? ks : 0]);
+          if constexpr (F32W) mfma_qk(sacc, ka[ks], ks < KSQ ? qlo[ks < KSQ ? ks : 0] : qrlo[F32W ? ks : 0]);
           __builtin_amdgcn_sched_barrier(0);  // keep the K reads of step ks + KPF above the MFMA of step ks
         }
         mfma_qk_drain(sacc);
@@ -549,11 +557,12 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
         if constexpr (MODE == 1) return;
         // ---- P = 2^(scale*log2e*s - m) rounded to bf16 (hardware RNE, two at a
         // time); registers 8kp .. 8kp+7 are the B operand of k-step kp.
-        bf16x8 pb[2];
+        bf16x8 pb[2], pl[F32W ? 2 : 1];
         // a row still without a reference has only masked (-inf) scores here,
         // which give 0 against any finite reference
         const float m_use = __builtin_fmaxf(m_run, -FLT_MAX);
-        // P of k-step kp into pb[kp]; returns its float32 sum
+        // P of k-step kp into pb[kp] (and its lo term into pl[kp]); returns
+        // the float32 sum of the unrounded weights
         auto p_half = [&](int kp) -> float {
           float pf[8];
 #pragma unroll
@@ -563,6 +572,12 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
             const bf16x2 pair = __builtin_convertvector((f32x2){pf[2 * i], pf[2 * i + 1]}, bf16x2);
             pb[kp][2 * i] = pair[0];
             pb[kp][2 * i + 1] = pair[1];
+            if constexpr (F32W) {
+              const f32x2 rest = {pf[2 * i] - static_cast<float>(pair[0]), pf[2 * i + 1] - static_cast<float>(pair[1])};
+              const bf16x2 lo = __builtin_convertvector(rest, bf16x2);
+              pl[F32W ? kp : 0][2 * i] = lo[0];
+              pl[F32W ? kp : 0][2 * i + 1] = lo[1];
+            }
           }
           float sum = 0.f;
 #pragma unroll
@@ -602,23 +617,34 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
           for (int kp = 0; kp < 2; ++kp) {
             l_part += p_half(kp);
             ldsp[(kp * 2 + lh) * ROWS + hg * 32 + lr] = pb[kp];
+            if constexpr (F32W) ldsp[4 * ROWS + (kp * 2 + lh) * ROWS + hg * 32 + lr] = pl[F32W ? kp : 0];
 #pragma unroll
-            for (int cbl = 0; cbl < CBW; ++cbl)
+            for (int cbl = 0; cbl < CBW; ++cbl) {
               oacc[cbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kp * CBW + cbl], pb[kp], oacc[cbl], 0, 0, 0);
+              if constexpr (F32W)
+                oacc[cbl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kp * CBW + cbl], pl[F32W ? kp : 0], oacc[cbl],
+                                                                    0, 0, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
           }
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-          bf16x8 px[2][4];
+          constexpr int NT2 = F32W ? 2 : 1;  // P terms
+          bf16x8 px[NT2][2][4];
 #pragma unroll
-          for (int kp = 0; kp < 2; ++kp)
+          for (int tm = 0; tm < NT2; ++tm)
 #pragma unroll
-            for (int j = 1; j < 4; ++j) px[kp][j] = ldsp[(kp * 2 + lh) * ROWS + ((hg + j) & 3) * 32 + lr];
+            for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+              for (int j = 1; j < 4; ++j)
+                px[tm][kp][j] = ldsp[tm * 4 * ROWS + (kp * 2 + lh) * ROWS + ((hg + j) & 3) * 32 + lr];
 #pragma unroll
           for (int idx = 0; idx < NV; ++idx)
 #pragma unroll
             for (int j = 1; j < 4; ++j)
-              oacc[j * CBW + idx % CBW] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[idx], px[idx / CBW][j], oacc[j * CBW + idx % CBW], 0, 0, 0);
+#pragma unroll
+              for (int tm = 0; tm < NT2; ++tm)
+                oacc[j * CBW + idx % CBW] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[idx], px[tm][idx / CBW][j],
+                                                                                   oacc[j * CBW + idx % CBW], 0, 0, 0);
         } else {
           l_part += p_half(0);
           l_part += p_half(1);
@@ -642,6 +668,8 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
             __builtin_memcpy(&va, &vt[idx][0], 8);
             __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vt[idx][1], 8);
             oacc[idx % CB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[idx / CB], oacc[idx % CB], 0, 0, 0);
+            if constexpr (F32W)
+              oacc[idx % CB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pl[F32W ? idx / CB : 0], oacc[idx % CB], 0, 0, 0);
             // Keep source order: the reads of block idx + VPF stay above the MFMA
             // of block idx (the scheduler would otherwise sink them to their use).
             __builtin_amdgcn_sched_barrier(0);
@@ -717,16 +745,9 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       }
   }
 
-  // ---- normalise and store.  O^T lane layout: lane (row r32, half h2) holds
-  // columns cb*32 + 8g + 4h2 + e at oacc[cb][4g + e].  Each wave stages its 32
-  // rows (bf16), half of the columns at a time, in its own part of an idle
-  // tile buffer, then writes whole half-rows (d_c contiguous bytes) with
-  // 16-byte stores.  Partial results of a split are stored normalised in
-  // bf16, like the final ones.
-  constexpr int SROW = DC + 16;  // staging row stride in bytes (d_c/2 bf16 + padding against bank conflicts)
-  static_assert(2 * 32 * SROW <= TILE && HG <= 4, "staging must fit two waves per idle tile buffer");
-  char* stage = (hg < 2 ? lds1 : lds2) + (hg % 2) * 32 * SROW;
-  bf16_t* const out_base = final_out ? static_cast<bf16_t*>(p.out_latent) : p.ws_o;
+  // ---- normalise and store, in float32: obar (or this split's partial slot)
+  // row by row.  A lane holds four consecutive columns of one row per
+  // (accumulator, group) and writes them as one 16-byte store.
   const float l = pair32_sum(l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (lrow < row_count && h2 == 0) {
@@ -738,101 +759,52 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
       p.ws_lse[static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H)] = lse_v;
     }
   }
+  auto out_row = [&](int lr) -> int64_t {
+    const int64_t row_g = row_base + lr;
+    return final_out ? row_g : static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
+  };
+  float* const outf = final_out ? static_cast<float*>(p.out_latent) : p.ws_o;
   if constexpr (DSPLIT) {
-    // This wave holds columns (hg * CBW + cbl) * 32 + 8g' + 4h2 + e of rows
-    // q * 32 + r32, q = (hg + j) mod 4, at oacc[j * CBW + cbl][4g' + e].
-    // Every row's 1/l goes to LDS (the P buffer is idle now); then the rows
-    // are staged a quarter (32 rows, all d_c columns, bf16) per idle tile
-    // buffer and written as whole rows by all threads with 16-byte stores:
-    // quarters 0-2 first, then quarter 3.
+    // This wave holds columns (hg * CBW + cbl) * 32 + 8g + 4h2 + e of rows
+    // q * 32 + r32, q = (hg + j) mod 4, at oacc[j * CBW + cbl][4g + e]; every
+    // row's 1/l goes through LDS (the P buffer is idle now).
     float* ldsl = reinterpret_cast<float*>(ldsp);
     if (h2 == 0) ldsl[lrow] = inv;
     __syncthreads();
-    float inv_s[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) inv_s[j] = ldsl[((hg + j) & 3) * 32 + r32];
-    constexpr int SROWQ = DC * 2 + 16;  // staging row stride in bytes
-    static_assert(32 * SROWQ <= TILE, "a quarter of the rows must fit one tile buffer");
-    auto stage_slot = [&](int j, char* st) {
-#pragma unroll
-      for (int cbl = 0; cbl < CBW; ++cbl)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x16& o = oacc[j * CBW + cbl];
-          uint2 pk;
-          pk.x = pack_bf16x2(o[4 * g4] * inv_s[j], o[4 * g4 + 1] * inv_s[j]);
-          pk.y = pack_bf16x2(o[4 * g4 + 2] * inv_s[j], o[4 * g4 + 3] * inv_s[j]);
-          *reinterpret_cast<uint2*>(st + r32 * SROWQ + ((hg * CBW + cbl) * 32 + 8 * g4 + 4 * h2) * 2) = pk;
-        }
-    };
-    auto store_quarter = [&](int q, const char* st) {
-      constexpr int PIECES = DC * 2 / 16;  // 16-byte pieces per row
-      static_assert(NT % PIECES == 0, "row pieces must tile the workgroup");
-      constexpr int RPI = NT / PIECES;     // rows per store instruction
-#pragma unroll
-      for (int i0 = 0; i0 < 32; i0 += RPI) {
-        const int i = i0 + tid / PIECES;
-        const int pc = tid % PIECES;
-        const int lr = q * 32 + i;
-        const i32x4 v = *reinterpret_cast<const i32x4*>(st + i * SROWQ + pc * 16);
-        if (lr < row_count) {
-          const int64_t row_g = row_base + lr;
-          const int64_t orow = final_out ? row_g : static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
-          *reinterpret_cast<i32x4*>(out_base + orow * DC + pc * 8) = v;
-        }
-      }
-    };
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int q = (hg + j) & 3;  // wave-uniform
-      if (q < 3) stage_slot(j, q == 0 ? lds0 : (q == 1 ? lds1 : lds2));
-    }
-    __syncthreads();
-    store_quarter(0, lds0);
-    store_quarter(1, lds1);
-    store_quarter(2, lds2);
-    __syncthreads();
+      const int lr = ((hg + j) & 3) * 32 + r32;
+      const float iv = ldsl[lr];
+      if (lr < row_count) {
+        float* orow = outf + out_row(lr) * DC;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (((hg + j) & 3) == 3) stage_slot(j, lds0);
-    __syncthreads();
-    store_quarter(3, lds0);
+        for (int cbl = 0; cbl < CBW; ++cbl)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x16& o = oacc[j * CBW + cbl];
+            *reinterpret_cast<f32x4*>(orow + (hg * CBW + cbl) * 32 + 8 * g4 + 4 * h2) =
+                f32x4{o[4 * g4] * iv, o[4 * g4 + 1] * iv, o[4 * g4 + 2] * iv, o[4 * g4 + 3] * iv};
+          }
+      }
+    }
   } else {
-    constexpr int PIECES = DC / 16;  // 16-byte pieces per half-row
-    static_assert(64 % PIECES == 0, "half-row pieces must tile a wave");
-    constexpr int RPI = 64 / PIECES;  // half-rows per store instruction
-  #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-  #pragma unroll
-      for (int cbl = 0; cbl < CB / 2; ++cbl) {
-        const int cb = half * (CB / 2) + cbl;
-  #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 pk;
-          pk.x = pack_bf16x2(oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv);
-          pk.y = pack_bf16x2(oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
-          *reinterpret_cast<uint2*>(stage + r32 * SROW + (cbl * 32 + 8 * g + 4 * h2) * 2) = pk;
-        }
-      }
-  #pragma unroll
-      for (int i0 = 0; i0 < 32; i0 += RPI) {
-        const int i = i0 + lane / PIECES;
-        const int pc = lane % PIECES;
-        const int lr = hg * 32 + i;
-        const i32x4 v = *reinterpret_cast<const i32x4*>(stage + i * SROW + pc * 16);
-        if (lr < row_count) {
-          const int64_t row_g = row_base + lr;
-          const int64_t orow = final_out ? row_g : static_cast<int64_t>(slot) * H + (row_g - static_cast<int64_t>(b) * H);
-          *reinterpret_cast<i32x4*>(out_base + orow * DC + half * (DC / 2) + pc * 8) = v;
-        }
-      }
+    if (lrow < row_count) {
+      float* orow = outf + out_row(lrow) * DC;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(orow + cb * 32 + 8 * g + 4 * h2) =
+              f32x4{oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv, oacc[cb][4 * g + 2] * inv,
+                    oacc[cb][4 * g + 3] * inv};
     }
   }
 }
 
 // K4: merge the splits of each sequence:  lse = log sum_s e^{lse_s},
 // obar = sum_s e^{lse_s - lse} obar_s, in split order (deterministic).
-// One workgroup per (sequence, 4 heads); 64 lanes per head.
+// One workgroup per (sequence, 4 heads); 64 lanes per head.  Partials and
+// obar are float32.
 template <int DC>
 __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
   constexpr int PER = DC / 64;
@@ -859,13 +831,13 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
   }
   if (head >= H || ns_b == 1 || base + ns_b > p.n_items) return;
   const int64_t row = static_cast<int64_t>(b) * H + head;
-  bf16_t* out = static_cast<bf16_t*>(p.out_latent) + row * DC;
+  float* out = static_cast<float*>(p.out_latent) + row * DC;
   const float* lse_s = p.ws_lse + static_cast<int64_t>(base) * H + head;  // split s at lse_s[s * H]
-  const bf16_t* part = p.ws_o + (static_cast<int64_t>(base) * H + head) * DC + lane * PER;
+  const float* part = p.ws_o + (static_cast<int64_t>(base) * H + head) * DC + lane * PER;
   // Splits go four a round, every load of a round issued before its use; the
   // first round's loads go out before the lse max, so they share its wait.
   constexpr int U = 4;
-  bf16_t v[U][PER];
+  float v[U][PER];
   float w[U];
   auto load_round = [&](int s0) {
 #pragma unroll
@@ -873,7 +845,7 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
       // a sequence with no splits (no tokens; then the workspace may be
       // empty) reads nothing
       if (s0 + u < ns_b) {
-        __builtin_memcpy(v[u], part + static_cast<int64_t>(s0 + u) * H * DC, PER * sizeof(bf16_t));
+        __builtin_memcpy(v[u], part + static_cast<int64_t>(s0 + u) * H * DC, PER * sizeof(float));
         w[u] = lse_s[static_cast<int64_t>(s0 + u) * H];
       } else {
 #pragma unroll
@@ -901,22 +873,22 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
         const float wu = __expf(w[u] - m);
         wsum += wu;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, bf16_to_f32(v[u][i]), acc[i]);
+        for (int i = 0; i < PER; ++i) acc[i] = fmaf(wu, v[u][i], acc[i]);
       }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint32_t o[PER / 2];
+  float o[PER];
 #pragma unroll
-  for (int i = 0; i < PER / 2; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
-  __builtin_memcpy(out + lane * PER, o, PER * sizeof(bf16_t));
+  for (int i = 0; i < PER; ++i) o[i] = acc[i] * inv;
+  __builtin_memcpy(out + lane * PER, o, PER * sizeof(float));
   if (p.lse != nullptr && lane == 0) p.lse[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 
-template <int DC, int DR, int HG, int TW, bool PREFILL, bool QF32>
+template <int DC, int DR, int HG, int TW, bool PREFILL, bool F32W>
 hipError_t launch_attn(const AttnParams& p, int64_t n_wg, hipStream_t s) {
   if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_bf16_kernel<DC, DR, HG, TW, PREFILL, QF32>), dim3(static_cast<unsigned>(n_wg)),
+  hipLaunchKernelGGL((attn_bf16_kernel<DC, DR, HG, TW, PREFILL, F32W>), dim3(static_cast<unsigned>(n_wg)),
                      dim3(64 * HG * TW), 0, s, p);
   return hipGetLastError();
 }
@@ -925,25 +897,24 @@ hipError_t launch_attn(const AttnParams& p, int64_t n_wg, hipStream_t s) {
 
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s) {
   const int64_t n_wg = p.n_items * p.n_head_chunks;
-  if (p.d_latent == 512 && p.d_rope == 64 && !p.q_f32) return launch_attn<512, 64, 4, 1, false, false>(p, n_wg, s);
+  if (p.d_latent == 512 && p.d_rope == 64 && !p.f32w) return launch_attn<512, 64, 4, 1, false, false>(p, n_wg, s);
   if (p.d_latent == 256 && p.d_rope == 32) {
-    if (p.q_f32) return launch_attn<256, 32, 1, 2, false, true>(p, n_wg, s);
+    if (p.f32w) return launch_attn<256, 32, 1, 2, false, true>(p, n_wg, s);
     return launch_attn<256, 32, 1, 2, false, false>(p, n_wg, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t s) {
-  if (p.d_latent == 512 && p.d_rope == 64 && !p.q_f32) return launch_attn<512, 64, 4, 1, true, false>(p, p.n_blocks, s);
+  if (p.d_latent == 512 && p.d_rope == 64 && !p.f32w) return launch_attn<512, 64, 4, 1, true, false>(p, p.n_blocks, s);
   if (p.d_latent == 256 && p.d_rope == 32) {
-    if (p.q_f32) return launch_attn<256, 32, 4, 1, true, true>(p, p.n_blocks, s);
+    if (p.f32w) return launch_attn<256, 32, 4, 1, true, true>(p, p.n_blocks, s);
     return launch_attn<256, 32, 4, 1, true, false>(p, p.n_blocks, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_merge(const AttnParams& p, int dtype, hipStream_t s) {
-  (void)dtype;
+hipError_t launch_merge(const AttnParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   const dim3 grid(p.batch, (p.n_heads + 3) / 4);
   if (p.d_latent == 512)

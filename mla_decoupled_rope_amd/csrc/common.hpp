@@ -72,7 +72,7 @@ __device__ __forceinline__ float pair32_sum(float v) {
 // ---------------------------------------------------------------- params --
 
 struct RopeParams {
-  int n_heads, d_latent, d_rope, dtype, q_lat_dtype;
+  int n_heads, d_latent, d_rope, dtype, work_dtype;
   const void* q_rope; const int32_t* q_pos; int64_t n_q; void* q_lat;
   const void* kv_latent; const void* k_rope; const int32_t* kv_seq; const int32_t* kv_pos; int64_t n_kv;
   void* cache; int64_t num_pages; const int32_t* block_table; int32_t num_seqs; int32_t max_pages;
@@ -82,7 +82,7 @@ struct RopeParams {
 };
 
 struct GemmParams {
-  int n_heads, d_head, d_v, d_latent, d_rope, dtype, q_lat_dtype;
+  int n_heads, d_head, d_v, d_latent, d_rope, dtype, work_dtype;
   const void* a; const void* w; void* out; int64_t n;
 };
 
@@ -125,7 +125,7 @@ hipError_t launch_fold(const FoldParams& p, hipStream_t s);
 struct AttnParams {
   // shape
   int n_heads, d_latent, d_rope;
-  int q_f32;         // q_lat is float32 (two-term bf16 split in QK)
+  int f32w;          // float32 working precision: float32 q_lat; q~ and P enter as two-term bf16
   float scale;       // softmax_scale
   float scale_log2;  // softmax_scale * log2(e)
   // inputs
@@ -138,7 +138,7 @@ struct AttnParams {
   const int32_t* cu_q; const int32_t* q_start; int64_t n_blocks;
   // outputs
   void* out_latent; float* lse;
-  bf16_t* ws_o; float* ws_lse;  // split partials: normalised obar (bf16) [slot, H, d_latent] / lse [slot, H]
+  float* ws_o; float* ws_lse;  // split partials: normalised obar [slot, H, d_latent] / lse [slot, H]
 };
 
 // Materialised-form prefill: per-head keys and values up-projected from the
@@ -167,7 +167,7 @@ hipError_t launch_absorb(const GemmParams& p, hipStream_t s);
 hipError_t launch_out_proj(const GemmParams& p, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t s);
-hipError_t launch_merge(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_merge(const AttnParams& p, hipStream_t s);
 hipError_t launch_decode_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_prefill_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_mha_prefill(const MhaParams& p, hipStream_t s);

@@ -12,8 +12,9 @@
 //    [d_h, d_c], so the MFMA A operand (8 consecutive i for one j) is a
 //    column read: the W tile is staged in LDS and read with ds_read_tr16_b64.
 //  * out_proj: o^T[v, n] = sum_j W_UV[h][v][j] obar[n, h, j].  Both operands
-//    are already contiguous along j and come straight from global memory;
-//    the float32 accumulator is stored as is (the layer output is float32).
+//    are already contiguous along j; obar is float32 and enters as a
+//    two-term bf16 split; the float32 accumulator is stored as is (the
+//    layer output is float32).
 // float32 path: one thread per output element, float32 accumulation.
 #include "common.hpp"
 
@@ -159,12 +160,16 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
 // in registers, loaded once, while the tokens go by in chunks of 64: a chunk
 // of obar[:, h, :] is staged in LDS once and read by all four waves.  So
 // W_UV is read once per call and obar twice (once per 64-row half of d_v).
+// TO is obar's element type; a float32 obar is staged as a two-term bf16
+// split hi + lo and takes two MFMAs per step, so it enters at ~16
+// significant bits.
 constexpr int kOutRows = 64;     // v rows per workgroup
 constexpr int kOutChunk = 64;    // tokens per chunk
-constexpr int kOutMaxK = 512;    // largest d_c this kernel takes
-constexpr int kOutLdsStride = kOutMaxK + 8;  // bf16 elements per staged row (padding against bank conflicts)
+template <typename TO, int KMAX>
 __global__ void __launch_bounds__(256) out_proj_bf16_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) bf16_t ob_lds[kOutChunk * kOutLdsStride];
+  constexpr int NTERM = sizeof(TO) == 4 ? 2 : 1;
+  constexpr int LSTRIDE = KMAX + 8;  // bf16 elements per staged row (padding against bank conflicts)
+  __shared__ __attribute__((aligned(16))) bf16_t ob_lds[NTERM][kOutChunk * LSTRIDE];
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -174,45 +179,63 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(GemmParams p) {
   const int q16 = lane >> 4, r16 = lane & 15;
   const int ks_n = DC / 32;
   const bf16_t* w = static_cast<const bf16_t*>(p.w) + (static_cast<int64_t>(h) * DV + v0 + r16) * DC + q16 * 8;
-  const bf16_t* ob = static_cast<const bf16_t*>(p.a);
+  const TO* ob = static_cast<const TO*>(p.a);
   float* out = static_cast<float*>(p.out);
   // A fragments: W_UV[h][v0 + r16][k*32 + q16*8 .. +7] for every k step
-  bf16x8 wa[kOutMaxK / 32];
+  bf16x8 wa[KMAX / 32];
 #pragma unroll
-  for (int k = 0; k < kOutMaxK / 32; ++k)
+  for (int k = 0; k < KMAX / 32; ++k)
     if (k < ks_n) wa[k] = load8(w + k * 32);
   for (int64_t c0 = 0; c0 < p.n; c0 += kOutChunk) {
     const int rows = static_cast<int>(min<int64_t>(kOutChunk, p.n - c0));
     // stage obar[c0 .. c0 + rows, h, :] (zeros past the end)
     __syncthreads();
     // all of this thread's loads first, then its LDS stores: one round trip
-    const int pieces = DC / 8;  // 16-byte pieces per row
-    constexpr int PPT = kOutChunk * (kOutMaxK / 8) / 256;  // pieces per thread at the largest d_c
-    bf16x8 v[PPT];
+    const int pieces = DC / 8;  // 8-element pieces per row
+    constexpr int PPT = kOutChunk * (KMAX / 8) / 256;  // pieces per thread at the largest d_c
+    bf16x8 v[NTERM][PPT];
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
       const int c = tid + k * 256;
       const int r = c / pieces, pc = c % pieces;
-      v[k] = (c < kOutChunk * pieces && r < rows) ? load8(ob + ((c0 + r) * H + h) * DC + pc * 8) : bf16x8{};
+      const bool ok = c < kOutChunk * pieces && r < rows;
+      const TO* src = ob + ((c0 + r) * H + h) * DC + pc * 8;
+      if constexpr (NTERM == 1) {
+        v[0][k] = ok ? load8(src) : bf16x8{};
+      } else {
+        f32x4 x0 = ok ? *reinterpret_cast<const f32x4*>(src) : f32x4{};
+        f32x4 x1 = ok ? *reinterpret_cast<const f32x4*>(src + 4) : f32x4{};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = e < 4 ? x0[e] : x1[e - 4];
+          const __bf16 hi = static_cast<__bf16>(x);
+          v[0][k][e] = hi;
+          v[NTERM - 1][k][e] = static_cast<__bf16>(x - static_cast<float>(hi));
+        }
+      }
     }
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const int c = tid + k * 256;
-      const int r = c / pieces, pc = c % pieces;
-      if (c < kOutChunk * pieces) *reinterpret_cast<bf16x8*>(&ob_lds[r * kOutLdsStride + pc * 8]) = v[k];
-    }
+    for (int t = 0; t < NTERM; ++t)
+#pragma unroll
+      for (int k = 0; k < PPT; ++k) {
+        const int c = tid + k * 256;
+        const int r = c / pieces, pc = c % pieces;
+        if (c < kOutChunk * pieces) *reinterpret_cast<bf16x8*>(&ob_lds[t][r * LSTRIDE + pc * 8]) = v[t][k];
+      }
     __syncthreads();
     f32x4 acc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < kOutMaxK / 32; ++k) {
+    for (int k = 0; k < KMAX / 32; ++k) {
       if (k < ks_n) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&ob_lds[(nb * 16 + r16) * kOutLdsStride + k * 32 + q16 * 8]);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[k], bv, acc[nb], 0, 0, 0);
-        }
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int t = 0; t < NTERM; ++t) {
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&ob_lds[t][(nb * 16 + r16) * LSTRIDE + k * 32 + q16 * 8]);
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[k], bv, acc[nb], 0, 0, 0);
+          }
       }
     }
     // D^T[v][n]: lane holds n = nb*16 + r16, v = v0 + 4*q16 + e
@@ -262,7 +285,7 @@ hipError_t launch_absorb(const GemmParams& p, hipStream_t s) {
   } else {
     const dim3 grid(p.d_latent / kAbsorbJTile, p.n_heads,
                     static_cast<unsigned>((p.n + kAbsorbNChunk - 1) / kAbsorbNChunk));
-    if (p.q_lat_dtype == 0)
+    if (p.work_dtype == 0)
       hipLaunchKernelGGL((absorb_bf16_kernel<128, float>), grid, dim3(256), 0, s, p);
     else
       hipLaunchKernelGGL((absorb_bf16_kernel<128, bf16_t>), grid, dim3(256), 0, s, p);
@@ -277,7 +300,10 @@ hipError_t launch_out_proj(const GemmParams& p, hipStream_t s) {
     hipLaunchKernelGGL(out_proj_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, p);
   } else {
     const dim3 grid(p.d_v / kOutRows, p.n_heads);
-    hipLaunchKernelGGL(out_proj_bf16_kernel, grid, dim3(256), 0, s, p);
+    if (p.d_latent <= 256)
+      hipLaunchKernelGGL((out_proj_bf16_kernel<float, 256>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((out_proj_bf16_kernel<float, 512>), grid, dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

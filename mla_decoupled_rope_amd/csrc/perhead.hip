@@ -54,10 +54,11 @@ constexpr int kPhBufferWord3 = 0x00020000;
 static_assert(kPage * kPhChunks % 256 == 0, "a page must split evenly over the threads");
 static_assert(kPhDr == 32, "one position block per 32-wide k-step");
 
-template <bool QF32>
+template <bool F32W>
 __global__ void __launch_bounds__(256, 1) perhead_decode_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t tile[kPage * kPhStride];
-  __shared__ __attribute__((aligned(16))) bf16_t pbuf[kPhH * kPhPStride];
+  // softmax weights P^T of the page (with F32W, their lo terms follow)
+  __shared__ __attribute__((aligned(16))) bf16_t pbuf[(F32W ? 2 : 1) * kPhH * kPhPStride];
   __shared__ float red[4][kPhH];
 
   const int tid = threadIdx.x;
@@ -81,12 +82,12 @@ __global__ void __launch_bounds__(256, 1) perhead_decode_kernel(AttnParams p) {
   // 32-wide k-step).  Content: q~ of head r16, 8 k-steps.  Position: head r16's
   // rotated q^R (one k-step), used only in k-step r16 of the position part.
   // A float32 q_lat enters as hi = bf16(q) and lo = bf16(q - hi), two terms.
-  bf16x8 qc_hi[kPhDc / 32], qc_lo[QF32 ? kPhDc / 32 : 1];
+  bf16x8 qc_hi[kPhDc / 32], qc_lo[F32W ? kPhDc / 32 : 1];
   bf16x8 qr_hi, qr_lo;
   {
     const int64_t qrow = static_cast<int64_t>(b) * kPhH + r16;
     auto frag = [&](int k0, bf16x8& hi, bf16x8& lo) {
-      if constexpr (QF32) {
+      if constexpr (F32W) {
         const float* q = static_cast<const float*>(p.q_lat) + qrow * (kPhDc + kPhDr) + k0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -101,7 +102,7 @@ __global__ void __launch_bounds__(256, 1) perhead_decode_kernel(AttnParams p) {
       }
     };
 #pragma unroll
-    for (int ks = 0; ks < kPhDc / 32; ++ks) frag(ks * 32 + 8 * q16, qc_hi[ks], qc_lo[QF32 ? ks : 0]);
+    for (int ks = 0; ks < kPhDc / 32; ++ks) frag(ks * 32 + 8 * q16, qc_hi[ks], qc_lo[F32W ? ks : 0]);
     frag(kPhDc + 8 * q16, qr_hi, qr_lo);
   }
   const bf16x8 zero8 = {};
@@ -170,7 +171,7 @@ __global__ void __launch_bounds__(256, 1) perhead_decode_kernel(AttnParams p) {
     for (int ks = 0; ks < kPhDc / 32; ++ks) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + ks * 32);
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qc_hi[ks], s, 0, 0, 0);
-      if constexpr (QF32) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qc_lo[ks], s, 0, 0, 0);
+      if constexpr (F32W) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qc_lo[ks], s, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < kPhH; ++j) {
@@ -182,7 +183,7 @@ __global__ void __launch_bounds__(256, 1) perhead_decode_kernel(AttnParams p) {
       asm volatile("" : "+s"(jj));
       const bool own = r16 == jj;
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, own ? qr_hi : zero8, s, 0, 0, 0);
-      if constexpr (QF32) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, own ? qr_lo : zero8, s, 0, 0, 0);
+      if constexpr (F32W) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, own ? qr_lo : zero8, s, 0, 0, 0);
     }
 
     // ---- softmax over the page, head r16; tokens past the end are masked
@@ -215,12 +216,27 @@ __global__ void __launch_bounds__(256, 1) perhead_decode_kernel(AttnParams p) {
     pk.x = pack_bf16x2(pv[0], pv[1]);
     pk.y = pack_bf16x2(pv[2], pv[3]);
     *reinterpret_cast<uint2*>(&pbuf[r16 * kPhPStride + d_tok0]) = pk;
+    if constexpr (F32W) {
+      // lo terms: P - bf16(P), exact in float32, then rounded once
+      float rest[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t word = e < 2 ? pk.x : pk.y;
+        rest[e] = pv[e] - bf16_to_f32(static_cast<bf16_t>((e & 1) ? word >> 16 : word & 0xffffu));
+      }
+      uint2 pl;
+      pl.x = pack_bf16x2(rest[0], rest[1]);
+      pl.y = pack_bf16x2(rest[2], rest[3]);
+      *reinterpret_cast<uint2*>(&pbuf[kPhH * kPhPStride + r16 * kPhPStride + d_tok0]) = pl;
+    }
     __syncthreads();
 
     // ---- P.V: O^T[col][head] over the page's two 32-token k-steps
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const bf16x8 pb = *reinterpret_cast<const bf16x8*>(&pbuf[r16 * kPhPStride + 32 * kt + 8 * q16]);
+      bf16x8 pbl;
+      if constexpr (F32W) pbl = *reinterpret_cast<const bf16x8*>(&pbuf[(kPhH + r16) * kPhPStride + 32 * kt + 8 * q16]);
       const int t0 = 32 * kt + 8 * q16 + (r16 >> 2);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
@@ -233,6 +249,7 @@ __global__ void __launch_bounds__(256, 1) perhead_decode_kernel(AttnParams p) {
         __builtin_memcpy(&a, &lo, 8);
         __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
         oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[cb], 0, 0, 0);
+        if constexpr (F32W) oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pbl, oacc[cb], 0, 0, 0);
       }
     }
   }
@@ -245,14 +262,11 @@ __global__ void __launch_bounds__(256, 1) perhead_decode_kernel(AttnParams p) {
   const float l = (red[0][r16] + red[1][r16]) + (red[2][r16] + red[3][r16]);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int64_t hrow = final_out ? static_cast<int64_t>(b) * kPhH + r16 : static_cast<int64_t>(slot) * kPhH + r16;
-  bf16_t* out = (final_out ? static_cast<bf16_t*>(p.out_latent) : p.ws_o) + hrow * kPhDc;
+  float* out = (final_out ? static_cast<float*>(p.out_latent) : p.ws_o) + hrow * kPhDc;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    uint2 pk;
-    pk.x = pack_bf16x2(oacc[cb][0] * inv, oacc[cb][1] * inv);
-    pk.y = pack_bf16x2(oacc[cb][2] * inv, oacc[cb][3] * inv);
-    *reinterpret_cast<uint2*>(out + wave * 64 + cb * 16 + 4 * q16) = pk;
-  }
+  for (int cb = 0; cb < 4; ++cb)
+    *reinterpret_cast<f32x4*>(out + wave * 64 + cb * 16 + 4 * q16) =
+        f32x4{oacc[cb][0] * inv, oacc[cb][1] * inv, oacc[cb][2] * inv, oacc[cb][3] * inv};
   if (wave == 0 && q16 == 0) {
     const float lse_v = l > 0.f ? (m_run + log2f(l)) * kPhLn2 : -INFINITY;
     if (final_out) {
@@ -298,7 +312,7 @@ hipError_t launch_perhead_decode(const AttnParams& p, hipStream_t s) {
   if (p.n_items == 0) return hipSuccess;
   if (p.n_heads != kPhH || p.d_latent != kPhDc || p.d_rope != kPhDr) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.n_items));
-  if (p.q_f32)
+  if (p.f32w)
     hipLaunchKernelGGL(perhead_decode_kernel<true>, grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(perhead_decode_kernel<false>, grid, dim3(256), 0, s, p);

@@ -112,7 +112,7 @@ hipError_t launch_rope(const RopeParams& p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(blocks));
   if (p.dtype == 0)
     hipLaunchKernelGGL((rope_kernel<float, float>), grid, dim3(256), 0, s, p);
-  else if (p.q_lat_dtype == 0)
+  else if (p.work_dtype == 0)
     hipLaunchKernelGGL((rope_kernel<bf16_t, float>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((rope_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, p);

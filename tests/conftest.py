@@ -8,10 +8,16 @@ TESTS = os.path.dirname(os.path.abspath(__file__))
 if TESTS not in sys.path:
     sys.path.insert(0, TESTS)
 
-# The tests load the built library; build it only when nothing is built yet.
-if not os.path.exists(os.path.join(ROOT, "mla_decoupled_rope_amd", "libmla.so")):
-    from mla_decoupled_rope_amd import build as _build
+# The tests load the built library: rebuild it when it is missing or was built
+# from other sources than the ones in the tree (a hash of every HIP source and
+# header, recorded next to the library by the build).
+import importlib.util  # noqa: E402
 
+_spec = importlib.util.spec_from_file_location("_mla_build", os.path.join(ROOT, "mla_decoupled_rope_amd", "build.py"))
+_build = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(_build)
+if not _build.is_current():
+    print("libmla.so is missing or older than its sources: building it", flush=True)
     _build.build()
 
 

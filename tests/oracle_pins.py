@@ -229,6 +229,71 @@ def pin_prefill_is_decode_of_prefix():
             assert _rel(pre[k][i], dec[k][0]) < 1e-13, (k, int(m))
 
 
+def pin_decode_batch():
+    """The batch driver: query b sits at position T_b - 1 and sees that sequence's rows
+    row_offsets[b] .. row_offsets[b] + T_b - 1.
+
+    (1) The tiny fp32 decode workload written out: one query at position 255 over
+    the keys of positions 0 .. 255, through the definition itself.  (2) A ragged
+    batch with non-zero row offsets and an empty sequence, each sequence against
+    the pure-Python brute force on its own rows."""
+    import synth
+
+    case = synth.config1()
+    got = attention.decode_batch(case.seq_lens, case.c_rows, case.kr_rows, case.row_offsets, case.qc, case.qr,
+                                 case.w_uk, case.w_uv, case.shape.scale)
+    want = attention.materialised(case.qc, case.qr, np.array([255]), case.c_rows[:256], case.kr_rows[:256],
+                                  case.w_uk, case.w_uv, case.shape.scale)
+    for k in ("o", "obar", "lse"):
+        assert np.array_equal(got[k], want[k]), k
+    rng = np.random.default_rng(41)
+    lens = np.array([3, 1, 0, 5])
+    offs = np.array([0, 3, 4, 4])
+    n_h, d_h, d_c, d_r, d_v = 2, 2, 3, 4, 2
+    c = rng.standard_normal((9, d_c))
+    kr = rng.standard_normal((9, d_r))
+    qc = rng.standard_normal((4, n_h, d_h))
+    qr = rng.standard_normal((4, n_h, d_r))
+    w_uk = rng.standard_normal((n_h, d_h, d_c))
+    w_uv = rng.standard_normal((n_h, d_v, d_c))
+    got = attention.decode_batch(lens, c, kr, offs, qc, qr, w_uk, w_uv, 0.6)
+    for b in range(4):
+        t, r0 = int(lens[b]), int(offs[b])
+        if t == 0:  # no visible key
+            assert np.all(np.isneginf(got["lse"][b])) and np.all(got["obar"][b] == 0) and np.all(got["o"][b] == 0)
+            continue
+        bf = attention.brute_force(qc[b:b + 1], qr[b:b + 1], [t - 1], c[r0:r0 + t], kr[r0:r0 + t], w_uk, w_uv, 0.6)
+        for k in ("o", "obar", "lse"):
+            assert np.max(np.abs(got[k][b] - bf[k][0])) <= 1e-13 * max(1.0, np.max(np.abs(bf[k]))), (k, b)
+
+
+def pin_prefill_batch():
+    """The chunk driver: query j of sequence b sits at position q_start[b] + j, is causal,
+    and reads that sequence's rows; each query against the brute force on its own rows."""
+    rng = np.random.default_rng(43)
+    prior, new = np.array([2, 0, 3]), np.array([2, 3, 0])
+    lens = prior + new
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    cu_q = np.concatenate([[0], np.cumsum(new)])
+    n_h, d_h, d_c, d_r, d_v = 2, 2, 3, 2, 2
+    c = rng.standard_normal((int(lens.sum()), d_c))
+    kr = rng.standard_normal((int(lens.sum()), d_r))
+    qc = rng.standard_normal((int(new.sum()), n_h, d_h))
+    qr = rng.standard_normal((int(new.sum()), n_h, d_r))
+    w_uk = rng.standard_normal((n_h, d_h, d_c))
+    w_uv = rng.standard_normal((n_h, d_v, d_c))
+    got = attention.prefill_batch(cu_q, prior, c, kr, offs, qc, qr, w_uk, w_uv, 0.8)
+    for b in range(3):
+        for j in range(int(new[b])):
+            g = int(cu_q[b]) + j
+            m = int(prior[b]) + j
+            r0 = int(offs[b])
+            bf = attention.brute_force(qc[g:g + 1], qr[g:g + 1], [m], c[r0:r0 + m + 1], kr[r0:r0 + m + 1], w_uk,
+                                       w_uv, 0.8)
+            for k in ("o", "obar", "lse"):
+                assert np.max(np.abs(got[k][g] - bf[k][0])) <= 1e-13 * max(1.0, np.max(np.abs(bf[k]))), (k, g)
+
+
 # ------------------------------------------------------ paging, figures ----
 
 def pin_paging():
@@ -536,6 +601,7 @@ ALL_PINS = [
     pin_obstruction_decomposition,
     pin_obstruction_span, pin_obstruction_best_single_matrix, pin_two_scale_brute_force,
     pin_two_scale_special_cases, pin_per_head_keys_brute_force, pin_per_head_keys_reduce_to_shared,
+    pin_decode_batch, pin_prefill_batch,
 ]
 
 

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def _dims(**kw):
     base = dict(n_heads=128, d_head=128, d_v=128, d_latent=512, d_rope=64, page_size=64, dtype=B.MLA_BF16,
-                q_lat_dtype=B.MLA_BF16, softmax_scale=0.0722, position_scale=0.0722, rope_base=10000.0)
+                work_dtype=B.MLA_BF16, softmax_scale=0.0722, position_scale=0.0722, rope_base=10000.0)
     base.update(kw)
     return B.Dims(**base)
 
@@ -58,8 +58,8 @@ def status_of_decode(d, batch=1, lens=(10,), ws=None, ws_bytes=0, cache_kw=None)
     (dict(d_rope=63), 1), (dict(n_heads=0), 1), (dict(page_size=32), 2), (dict(dtype=7), 1),
     (dict(softmax_scale=float("nan")), 1), (dict(position_scale=0.0), 1), (dict(position_scale=float("inf")), 1),
     (dict(rope_base=-1.0), 1), (dict(n_heads=64), 2),
-    (dict(d_rope=256), 2), (dict(q_lat_dtype=B.MLA_F32), 2), (dict(dtype=B.MLA_F32), 1),
-    (dict(q_lat_dtype=5), 1),
+    (dict(d_rope=256), 2), (dict(work_dtype=B.MLA_F32), 2), (dict(dtype=B.MLA_F32), 1),
+    (dict(work_dtype=5), 1),
 ])
 def test_decode_rejects_bad_dims(kw, status):
     assert status_of_decode(_dims(**kw)) == status
@@ -127,7 +127,7 @@ def test_materialised_prefill_validates():
     assert call(ws_bytes=need - 1) == 3
     assert call(ws=None) == 3
     assert call(dims=_dims(d_head=64)) == 2
-    assert call(dims=_dims(dtype=0, q_lat_dtype=0)) == 2
+    assert call(dims=_dims(dtype=0, work_dtype=0)) == 2
     assert call(cu=(ctypes.c_int32 * 3)(1, 5, 9)) == 1  # cu_q[0] != 0
     assert call(cu=(ctypes.c_int32 * 3)(0, 5, 2)) == 1  # decreasing
     assert call(st=(ctypes.c_int32 * 2)(0, 300)) == 1   # beyond the block table (4 pages of 64)
@@ -193,7 +193,7 @@ def test_front_projections_validate():
     assert ws_q % 256 == 0
     assert B.LIB.mla_front_workspace_size(ctypes.byref(d), 64, 5000, 1536) == 0      # d_model % 32
     assert B.LIB.mla_front_workspace_size(ctypes.byref(d), 64, 5120, 1500) == 0      # d_qlat % 32
-    assert B.LIB.mla_front_workspace_size(ctypes.byref(_dims(dtype=0, q_lat_dtype=0)), 64, 5120, 1536) == 0
+    assert B.LIB.mla_front_workspace_size(ctypes.byref(_dims(dtype=0, work_dtype=0)), 64, 5120, 1536) == 0
     cache = B.PagedCache(FAKE.value, 4, FAKE.value, 2, 4)
     seq = ctypes.cast(FAKE, i32p)
 
@@ -203,7 +203,7 @@ def test_front_projections_validate():
 
     assert kv(n=0) == 0                      # nothing to do, nothing launched
     assert kv(d_model=100) == 1
-    assert kv(dims=_dims(dtype=0, q_lat_dtype=0)) == 2
+    assert kv(dims=_dims(dtype=0, work_dtype=0)) == 2
     assert kv(h=None) == 1
     assert kv(h=ctypes.c_void_p(FAKE.value + 2)) == 1  # misaligned
     assert kv(ws_bytes=ws_kv - 1) == 3
@@ -236,7 +236,7 @@ def test_per_head_calls_validate():
 
     assert write(n=0) == 0
     assert write(dims=_dims()) == 2                           # the DeepSeek-V2 shape has no per-head kernel
-    assert write(dims=_dims(n_heads=16, d_latent=256, d_rope=32, dtype=0, q_lat_dtype=0)) == 2
+    assert write(dims=_dims(n_heads=16, d_latent=256, d_rope=32, dtype=0, work_dtype=0)) == 2
     assert write(n=-1) == 1
     assert write(lat=None) == 1
     assert B.LIB.mla_last_error().decode()

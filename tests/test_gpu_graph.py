@@ -74,7 +74,7 @@ def test_layer_step_from_hidden_state_graph():
     shape = synth.DSV2
     fc = synth.front_layer(shape, [300, 65, 1], 512, 192, seed=235, shuffle=True)
     dims = mla.MLADims(shape.n_heads, shape.d_head, shape.d_v, shape.d_latent, shape.d_rope, dtype=BF,
-                       softmax_scale=shape.scale, rope_base=shape.rope_base, q_lat_dtype=BF)
+                       softmax_scale=shape.scale, rope_base=shape.rope_base, work_dtype=BF)
     cache = mla.LatentCache(dims, fc.block_table, fc.num_pages, fill=0.0)
     step = mla.LayerDecodeStep(dims, cache, torch.from_numpy(fc.seq_lens), 512, 192, False)
     w = {k: G.dev(getattr(fc, k), BF) for k in ("w_dkv", "w_kr", "w_dq", "w_uq", "w_qr", "w_uk", "w_uv")}

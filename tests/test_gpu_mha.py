@@ -5,13 +5,17 @@ softmax) is the reference at small sizes; at the full 2048-after-16384 chunk
 sampled queries are checked against the oracle's absorbed float64 form
 (pinned to the materialised form to 1e-12 by the oracle's own tests).  This
 path rounds the up-projected keys and values, the content query and the
-softmax weights to float16, and is held to the same bf16 bounds.
+softmax weights to float16; each test is held to the configured bf16 bound,
+widened only where the storage-rounding model predicts more for its inputs
+(tests/tolerances.py).
 """
 
 import numpy as np
 import pytest
 import torch
 
+import bound_recipes
+import cases
 import gpu_util as G
 import mla_decoupled_rope_amd as mla
 import synth
@@ -26,36 +30,38 @@ def oracle_prefill(case, queries=None, evaluate=attention.materialised):
                                    queries=queries, evaluate=evaluate)
 
 
-def check(got, want, rows=None, what=""):
+def check(got, want, rows=None, what="", name=None):
     g = got["o"] if rows is None else got["o"][rows]
-    G.assert_close(g, want["o"], "bf16", f"{what} o")
+    G.assert_close(g, want["o"], "bf16", f"{what} o", name=name)
     g = got["lse"] if rows is None else got["lse"][rows]
-    G.assert_lse_close(g, want["lse"], "bf16", f"{what} lse")
+    G.assert_lse_close(g, want["lse"], "bf16", f"{what} lse", name=name)
 
 
 @pytest.mark.parametrize("shape", [synth.TINY, synth.DSV2], ids=["tiny", "dsv2"])
 def test_mha_prefill_ragged_chunks(shape):
     """Chunks of 5, 130, 1 and 64 queries after 0, 100, 64 and 7 cached tokens (several key and query blocks,
     ragged tails, a chunk that starts a sequence)."""
-    case = synth.direct_prefill(shape, "bf16", [0, 100, 64, 7], [5, 130, 1, 64], seed=67, shuffle=True)
-    check(G.run_prefill_mha(case), oracle_prefill(case), what=f"materialised prefill n_h={shape.n_heads}")
+    case = cases.prefill_ragged(shape)
+    check(G.run_prefill_mha(case), oracle_prefill(case), what=f"materialised prefill n_h={shape.n_heads}",
+          name="mha_ragged_tiny" if shape is synth.TINY else "mha_ragged_dsv2")
 
 
 def test_mha_prefill_long_prefix_and_empty_chunk():
     """A chunk of 300 after 700 cached tokens next to an empty chunk (no queries, keys still up-projected)."""
-    case = synth.direct_prefill(synth.DSV2, "bf16", [700, 50], [300, 0], seed=83, shuffle=True)
+    case = cases.mha_long_prefix()
     got = G.run_prefill_mha(case)
-    check(got, oracle_prefill(case), what="long prefix")
+    check(got, oracle_prefill(case), what="long prefix", name="mha_long_prefix")
     assert np.all(np.isfinite(got["o"]))
 
 
 def test_mha_prefill_matches_absorbed_path():
-    """The two forms of the same chunk agree within the bf16 bounds (each against the other's output)."""
-    case = synth.direct_prefill(synth.DSV2, "bf16", [200], [96], seed=89)
+    """The two forms of the same chunk agree (each against the other's output) within the sum
+    of what the rounding model predicts for each form against the oracle."""
+    case = cases.mha_vs_absorbed()
     cache = G.build_cache(case)
     a = G.run_prefill(case, cache=cache)
     m = G.run_prefill_mha(case, cache=cache)
-    G.assert_close(m["o"], a["o"], "bf16", "materialised vs absorbed o", tol=(4e-2, 1e-2))
+    G.assert_close(m["o"], a["o"], "bf16", "materialised vs absorbed o", name="mha_vs_absorbed")
 
 
 def test_mha_prefill_bitwise_repeatable():
@@ -68,15 +74,15 @@ def test_mha_prefill_bitwise_repeatable():
 
 def test_mha_config2_tiny_prefill():
     case = synth.config2()
-    check(G.run_prefill_mha(case), oracle_prefill(case), what="C2 materialised")
+    check(G.run_prefill_mha(case), oracle_prefill(case), what="C2 materialised", name="mha_c2")
 
 
 def test_mha_config5_full_prefill_sampled():
     case = synth.config5_prefill()
     got = G.run_prefill_mha(case)
-    queries = [0, 1, 127, 128, 1023, 2046, 2047]
+    queries = bound_recipes.c5b_queries()
     want = oracle_prefill(case, queries=queries, evaluate=attention.absorbed)
-    check(got, want, rows=queries, what="C5 materialised")
+    check(got, want, rows=queries, what=f"C5 materialised, {len(queries)} queries", name="c5b_mha")
     assert np.all(np.isfinite(got["o"]))
 
 

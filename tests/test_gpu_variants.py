@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import cases
 import gpu_util as G
 import mla_decoupled_rope_amd as mla
 import synth
@@ -28,29 +29,15 @@ def two_scales(shape):
     return 1.0 / math.sqrt(shape.d_head), 1.0 / math.sqrt(shape.d_rope)
 
 
-# The two-scale score's logits are larger than the one-scale score's (content by
-# sqrt((d_h + d_r) / d_h), position by sqrt((d_h + d_r) / d_r)), so the same
-# storage roundings move them further: an exactly rounded float64 emulation of
-# the bf16 roundings of q~, R q^R, R k^R and obar reaches a row max of 2.1e-2
-# on the DeepSeek-V2 decode case below (1.3e-2 with one scale), and of the
-# tiny shape's R k^R and obar (float32 q~) 1.7e-2 on the tiny prefill case
-# (0.9e-2 with one scale).  The bf16 bound for the two-scale score is 3e-2
-# (4e-2 where the tiny shape also rounds q~, as for its one-scale bf16 query
-# path); RMS stays within 5e-3.
-TWO_SCALE_TOL = (3e-2, 5e-3)
-BF16_Q_TWO_SCALE = {"TINY": (4e-2, 5e-3), "DSV2": TWO_SCALE_TOL}
-
-
-def _check(got, want, dtype, what, tol=None):
+def _check(got, want, dtype, what, name=None):
     for k in ("o", "obar"):
         if k in got:
-            t = (4e-2, 5e-3) if (k == "obar" and dtype == "bf16") else tol
-            G.assert_close(got[k], want[k], dtype, f"{what} {k}", tol=t)
-    G.assert_lse_close(got["lse"], want["lse"], dtype, f"{what} lse")
+            G.assert_close(got[k], want[k], dtype, f"{what} {k}", name=name, output=k)
+    G.assert_lse_close(got["lse"], want["lse"], dtype, f"{what} lse", name=name)
 
 
 def _name(shape):
-    return "TINY" if shape is synth.TINY else "DSV2"
+    return "tiny" if shape is synth.TINY else "dsv2"
 
 
 def _oracle_decode(case, ps):
@@ -68,26 +55,26 @@ def _oracle_prefill(case, ps):
 @pytest.mark.parametrize("shape,dtype", [(synth.TINY, "f32"), (synth.TINY, "bf16"), (synth.DSV2, "bf16")],
                          ids=["tiny-f32", "tiny-bf16", "dsv2-bf16"])
 def test_two_scale_decode(shape, dtype):
-    case = synth.direct_decode(shape, dtype, [1, 64, 65, 700, 129], seed=201, shuffle=True)
+    case = cases.two_scale_decode(shape, dtype)
     ps = two_scales(shape)
-    tol = TWO_SCALE_TOL if dtype == "bf16" else None
-    _check(G.run_decode(case, scales=ps), _oracle_decode(case, ps), dtype, "two-scale decode", tol)
+    name = None if dtype == "f32" else f"two_scale_decode_{_name(shape)}"
+    _check(G.run_decode(case, scales=ps), _oracle_decode(case, ps), dtype, "two-scale decode", name)
 
 
 @pytest.mark.parametrize("shape", [synth.TINY, synth.DSV2], ids=["tiny", "dsv2"])
 def test_two_scale_prefill(shape):
-    case = synth.direct_prefill(shape, "bf16", [0, 100, 7], [5, 130, 64], seed=203, shuffle=True)
+    case = cases.two_scale_prefill(shape)
     ps = two_scales(shape)
-    tol = TWO_SCALE_TOL
-    _check(G.run_prefill(case, scales=ps), _oracle_prefill(case, ps), "bf16", "two-scale prefill", tol)
+    _check(G.run_prefill(case, scales=ps), _oracle_prefill(case, ps), "bf16", "two-scale prefill",
+           f"two_scale_prefill_{_name(shape)}")
 
 
 @pytest.mark.parametrize("shape", [synth.TINY, synth.DSV2], ids=["tiny", "dsv2"])
 def test_two_scale_prefill_materialised(shape):
-    case = synth.direct_prefill(shape, "bf16", [0, 100, 7], [5, 130, 64], seed=205, shuffle=True)
+    case = cases.two_scale_prefill_materialised(shape)
     ps = two_scales(shape)
     _check(G.run_prefill_mha(case, scales=ps), _oracle_prefill(case, ps), "bf16", "two-scale materialised prefill",
-           BF16_Q_TWO_SCALE[_name(shape)])
+           f"two_scale_mha_{_name(shape)}")
 
 
 def test_two_scale_is_one_scale_when_equal():
@@ -105,7 +92,7 @@ def test_two_scale_query_projection():
     fc = synth.front_layer(shape, [9, 40], 512, 192, seed=209, shuffle=True)
     sc, pp = two_scales(shape)
     dims = mla.MLADims(shape.n_heads, shape.d_head, shape.d_v, shape.d_latent, shape.d_rope, dtype=BF,
-                       softmax_scale=sc, position_scale=pp, rope_base=shape.rope_base, q_lat_dtype=BF)
+                       softmax_scale=sc, position_scale=pp, rope_base=shape.rope_base, work_dtype=BF)
     n = fc.h.shape[0]
     q_pos = np.arange(n, dtype=np.int32) * 37 % 5000
     ws = B.front_workspace(dims, n, 512, 192)
@@ -167,25 +154,20 @@ def test_per_head_cache_write():
 def test_per_head_decode(precise, split_pages, monkeypatch):
     if split_pages is not None:
         monkeypatch.setenv("MLA_DECODE_SPLIT_PAGES", str(split_pages))
-    lens = [1, 63, 64, 65, 300, 0, 1000, 129]
-    case = synth.direct_decode(synth.TINY, "bf16", lens, seed=213, shuffle=True, per_head_rope=True)
+    case = cases.per_head_decode()
     got, _ = _run_per_head(case, precise)
     want = attention.decode_batch(case.seq_lens, case.c_rows, case.kr_rows, case.row_offsets, case.qc, case.qr,
                                   case.w_uk, case.w_uv, case.shape.scale, case.shape.rope_base)
-    # a bf16 q~ adds one rounding at this shape (the same bound as the shared-key tiny path)
-    tol = None if precise else (4e-2, 5e-3)
-    G.assert_close(got["o"], want["o"], "bf16", "per-head o", tol=tol)
-    G.assert_close(got["obar"], want["obar"], "bf16", "per-head obar", tol=(4e-2, 5e-3))
-    G.assert_lse_close(got["lse"], want["lse"], "bf16", "per-head lse")
+    _check(got, want, "bf16", "per-head decode", "per_head_f32w" if precise else "per_head_bf16")
 
 
 def test_per_head_decode_two_scale():
-    case = synth.direct_decode(synth.TINY, "bf16", [77, 640, 5], seed=215, shuffle=True, per_head_rope=True)
+    case = cases.per_head_two_scale()
     ps = two_scales(case.shape)
     got, _ = _run_per_head(case, scales=ps)
     want = attention.decode_batch(case.seq_lens, case.c_rows, case.kr_rows, case.row_offsets, case.qc, case.qr,
                                   case.w_uk, case.w_uv, ps[0], case.shape.rope_base, position_scale=ps[1])
-    G.assert_close(got["o"], want["o"], "bf16", "per-head two-scale o", tol=TWO_SCALE_TOL)
+    _check(got, want, "bf16", "per-head two-scale", "per_head_two_scale")
 
 
 def test_per_head_decode_repeatable():
@@ -197,15 +179,13 @@ def test_per_head_decode_repeatable():
 
 
 def test_per_head_full_size_sampled():
-    """64 sequences of 4096 tokens (the bench's per-head workload), sampled sequences against the oracle."""
-    case = synth.direct_decode(synth.TINY, "bf16", [4096] * 64, seed=219, shuffle=True, per_head_rope=True)
+    """64 sequences of 4096 tokens (the bench's per-head workload), every sequence against the oracle."""
+    case = cases.per_head_full()
     got, _ = _run_per_head(case)
-    seqs = [0, 17, 63]
     want = attention.decode_batch(case.seq_lens, case.c_rows, case.kr_rows, case.row_offsets, case.qc, case.qr,
-                                  case.w_uk, case.w_uv, case.shape.scale, case.shape.rope_base, seqs=seqs,
+                                  case.w_uk, case.w_uv, case.shape.scale, case.shape.rope_base,
                                   evaluate=attention.absorbed)
-    G.assert_close(got["o"][seqs], want["o"], "bf16", "per-head full-size o")
-    G.assert_lse_close(got["lse"][seqs], want["lse"], "bf16")
+    _check(got, want, "bf16", "per-head full size", "per_head_full")
 
 
 @pytest.mark.parametrize("per_head", [False, True], ids=["shared", "per-head"])
@@ -216,7 +196,7 @@ def test_decode_all_sequences_empty(per_head):
     lens = torch.from_numpy(case.seq_lens)
     assert mla.decode_workspace_size(dims, lens) == 0
     q_lat = torch.zeros((3, dims.n_heads, dims.row), dtype=BF, device="cuda")
-    out = torch.full((3, dims.n_heads, dims.d_latent), float("nan"), dtype=BF, device="cuda")
+    out = torch.full((3, dims.n_heads, dims.d_latent), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.zeros((3, dims.n_heads), dtype=torch.float32, device="cuda")
     table = torch.from_numpy(case.block_table).cuda()
     if per_head:

@@ -96,6 +96,32 @@ def _materialised_query_unrotated(qc, qr, q_pos, *a, **k):
     return _orig_materialised(qc, qr, np.zeros_like(np.asarray(q_pos)), *a, **k)
 
 
+_orig_decode_batch = attention.decode_batch
+_orig_prefill_batch = attention.prefill_batch
+
+
+def _decode_query_one_late(seq_lens, c_rows, kr_rows, row_offsets, qc, qr, *a, **k):
+    # the query placed at T_b (one past its own token) instead of T_b - 1
+    lens = np.asarray(seq_lens)
+    out = []
+    for b in range(len(lens)):
+        t, r0 = int(lens[b]), int(row_offsets[b])
+        out.append(attention.materialised(qc[b:b + 1], qr[b:b + 1], np.array([t]), c_rows[r0:r0 + t],
+                                          kr_rows[r0:r0 + t], *a[:3]))
+    return {key: np.concatenate([r[key] for r in out]) for key in ("o", "obar", "lse")}
+
+
+def _decode_rows_shifted(seq_lens, c_rows, kr_rows, row_offsets, *a, **k):
+    # every sequence reads its rows one further on (an offset slip)
+    offs = np.minimum(np.asarray(row_offsets) + 1, len(c_rows) - np.asarray(seq_lens))
+    return _orig_decode_batch(seq_lens, c_rows, kr_rows, np.maximum(offs, 0), *a, **k)
+
+
+def _prefill_not_causal(cu_q, q_start, *a, **k):
+    # every chunk query sees its whole chunk (start positions taken as one chunk later)
+    return _orig_prefill_batch(cu_q, np.asarray(q_start) + 1, *a, **k)
+
+
 def _bad_slot(table, seq, pos, ps):
     return int(table[seq, pos // ps]) * ps + pos // ps
 
@@ -169,6 +195,9 @@ MUTATIONS = {
     "two_scale_swapped": [(attention, "materialised", _materialised_scales_swapped)],
     "query_not_rotated": [(attention, "materialised", _materialised_query_unrotated)],
     "paging_offset_slip": [(paging, "slot", _bad_slot)],
+    "decode_query_one_late": [(attention, "decode_batch", _decode_query_one_late)],
+    "decode_rows_shifted": [(attention, "decode_batch", _decode_rows_shifted)],
+    "prefill_positions_shifted": [(attention, "prefill_batch", _prefill_not_causal)],
     "front_latent_weight_transposed": [(front, "kv_latent", _kv_latent_transposed)],
     "front_fold_wrong_index": [(front, "fold_query_weights", _fold_wrong_side)],
     "front_query_heads_swapped": [(front, "content_query", _query_skips_latent)],
