@@ -166,6 +166,21 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
                       void* out_latent, float* lse, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* mla_decode_noalloc -- mla_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The same computation, arguments, results and errors as
+ * mla_decode, with no workspace: the split partials go to a fixed scratch
+ * array of 96 MiB that the library holds on each device it runs on until the
+ * process ends.  A batch whose partials need more than that
+ * (mla_decode_workspace_size) returns MLA_ERR_WORKSPACE and launches nothing.
+ * Every call on a device shares that device's scratch, which keeps the last
+ * call's contents (nothing in it needs clearing): calls that overlap on one
+ * device (two streams, two threads) race and must be ordered by the caller.
+ * Allocates nothing (no hipMalloc or hipFree, no allocating library call). */
+mla_status mla_decode_noalloc(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                              const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch,
+                              void* out_latent, float* lse, void* stream);
+
 /* mla_prefill -- causal chunked prefill in the same absorbed form.
  *   Sequence b contributes queries cu_q[b] .. cu_q[b+1]-1; its j-th query
  *   sits at position q_start_pos[b] + j and sees cached positions t <= that

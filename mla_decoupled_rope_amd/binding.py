@@ -54,6 +54,7 @@ def _load():
         "mla_rope_apply": [pd, pc, vp, vp, i64, vp, vp, vp, vp, vp, i64, vp],
         "mla_absorb_q": [pd, vp, vp, i64, vp, vp],
         "mla_decode": [pd, pc, vp, vp, vp, i32, vp, vp, vp, sz, vp],
+        "mla_decode_noalloc": [pd, pc, vp, vp, vp, i32, vp, vp, vp],
         "mla_prefill": [pd, pc, vp, vp, vp, vp, vp, i32, vp, vp, vp],
         "mla_out_proj": [pd, vp, vp, i64, vp, vp],
         "mla_decode_plan": [pd, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(i64)],
@@ -84,7 +85,8 @@ def _load():
 
 LIB = _load()
 
-EXPORTS = ("mla_rope_apply", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode", "mla_prefill",
+EXPORTS = ("mla_rope_apply", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode", "mla_decode_noalloc",
+           "mla_prefill",
            "mla_out_proj", "mla_status_string", "mla_last_error", "mla_decode_plan",
            "mla_prefill_mha_workspace_size", "mla_prefill_mha", "mla_front_workspace_size", "mla_kv_project",
            "mla_q_project", "mla_q_project_folded", "mla_fold_q_weights", "mla_cache_write_per_head",
@@ -241,6 +243,23 @@ def decode(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat:
     _check(LIB.mla_decode(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), seq_lens.data_ptr(),
                           seq_lens_host.data_ptr(), batch, out_latent.data_ptr(), _ptr(lse), _ptr(workspace),
                           0 if workspace is None else workspace.numel(), _stream()))
+
+
+def decode_noalloc(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat: torch.Tensor,
+                   seq_lens: torch.Tensor, seq_lens_host: torch.Tensor, out_latent: torch.Tensor,
+                   lse: torch.Tensor | None = None) -> None:
+    """mla_decode_noalloc: mla_decode with the split partials in the library's fixed device scratch."""
+    batch = seq_lens_host.numel()
+    cstruct = _cache(dims, cache, block_table)
+    _dev(q_lat, "q_lat", dims.wdtype, (batch, dims.n_heads, dims.row))
+    _dev(seq_lens, "seq_lens", torch.int32, (batch,))
+    _host_i32(seq_lens_host, "seq_lens_host")
+    _dev(out_latent, "out_latent", torch.float32, (batch, dims.n_heads, dims.d_latent))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (batch, dims.n_heads))
+    d = dims.c()
+    _check(LIB.mla_decode_noalloc(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), seq_lens.data_ptr(),
+                                  seq_lens_host.data_ptr(), batch, out_latent.data_ptr(), _ptr(lse), _stream()))
 
 
 def per_head_row(dims: MLADims) -> int:

@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <queue>
 #include <string>
 #include <vector>
@@ -238,6 +239,40 @@ size_t workspace_bytes(const mla_dims* d, const Plan& p) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Fixed device scratch of mla_decode_noalloc: the split partials of a decode
+// call live here instead of in a caller's workspace.  Each device the library
+// runs on holds one copy until the process ends.  Host code never passes the
+// array's name to a kernel (in host code it is only a stand-in for the
+// symbol): its device address is taken once per device with
+// hipGetSymbolAddress and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = 96u << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of this device's scratch (the current device's), looked up
+// on its first use and kept.
+mla_status noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_fail(g_scratch_err[dev], "hipGetSymbolAddress(scratch)");
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat, const int32_t* seq_lens,
+                         const int32_t* seq_lens_host, int32_t batch, void* out_latent, float* lse, void* workspace,
+                         size_t ws_bytes, void* stream, bool fixed_scratch);
+
 }  // namespace
 
 extern "C" {
@@ -348,6 +383,27 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
                       const int32_t* seq_lens_host, int32_t batch, void* out_latent, float* lse, void* workspace,
                       size_t ws_bytes, void* stream) {
   g_err.clear();
+  return decode_common(dims, cache, q_lat, seq_lens, seq_lens_host, batch, out_latent, lse, workspace, ws_bytes,
+                       stream, false);
+}
+
+mla_status mla_decode_noalloc(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                              const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* out_latent,
+                              float* lse, void* stream) {
+  g_err.clear();
+  void* scratch_ptr = nullptr;
+  MLA_TRY(noalloc_scratch(&scratch_ptr));
+  return decode_common(dims, cache, q_lat, seq_lens, seq_lens_host, batch, out_latent, lse, scratch_ptr,
+                       kNoAllocScratchBytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat, const int32_t* seq_lens,
+                         const int32_t* seq_lens_host, int32_t batch, void* out_latent, float* lse, void* workspace,
+                         size_t ws_bytes, void* stream, bool fixed_scratch) {
   MLA_TRY(check_dims(dims));
   MLA_TRY(check_attn_shape(dims));
   MLA_TRY(check_cache(cache));
@@ -380,6 +436,10 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
   }
   const Plan plan = make_plan(dims, batch, seq_lens_host);
   const size_t need = workspace_bytes(dims, plan);
+  if (fixed_scratch && need > ws_bytes)
+    return fail(MLA_ERR_WORKSPACE,
+                "mla_decode_noalloc: this batch needs %zu bytes of split partials, more than its fixed scratch of %zu "
+                "bytes; use mla_decode with a workspace", need, ws_bytes);
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(MLA_ERR_WORKSPACE, "decode needs %zu bytes of workspace, got %zu", need, workspace ? ws_bytes : 0);
   if (plan.n_items > (1LL << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
@@ -399,6 +459,10 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
   }
   return MLA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 // ---- per-head position keys (rows [c | R k^R_0 | ... | R k^R_{H-1}])
 
