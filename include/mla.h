@@ -220,8 +220,12 @@ size_t mla_prefill_mha_workspace_size(const mla_dims* dims, int32_t batch, const
  *   o = sum_t alpha_t W_UV c_t; lse [cu_q[batch], H] float32 or NULL.
  * workspace: device memory of at least mla_prefill_mha_workspace_size()
  * bytes (otherwise MLA_ERR_WORKSPACE).  The up-projected keys and values,
- * the content query and the softmax weights are rounded to float16 (keys and
- * values must stay below 65504 in magnitude); the rotated part stays bf16.
+ * the content query and the softmax weights are rounded to float16; the
+ * rotated part stays bf16.  A key, value or content-query element whose
+ * float16 rounding would overflow (|x| >= 65520) is stored as NaN instead, so
+ * the outputs of that head that it reaches (every query that sees the key,
+ * and possibly other queries of the chunk) come out NaN: an input outside
+ * float16 range is flagged, never turned into finite wrong values.
  * bf16 inputs and work_dtype only, d_head = d_v = 128,
  * (n_heads, d_latent, d_rope) = (128, 512, 64) or (16, 256, 32); other
  * shapes return MLA_ERR_UNSUPPORTED. */

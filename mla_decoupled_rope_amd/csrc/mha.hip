@@ -15,10 +15,11 @@
 // Kernel 1 (upproj_kernel): for every key position t of every sequence,
 //   K^C[h][t][:] = W_UK[h] c_t      (float16, [head][key][128])
 //   V^T[h][:][t] = W_UV[h] c_t      (float16, [head][128][key], transposed)
-// one workgroup per (128 keys, head), one launch for K^C and one for V^T, on
-// v_mfma_f32_32x32x16_bf16,
-// both operands staged through LDS in 64-wide slices of d_c, double
-// buffered.  Each sequence's keys take a range padded to a multiple of 128;
+// one workgroup per (256 keys, head) computes both: waves 0-1 the K^C rows,
+// waves 2-3 the V^T rows, on v_mfma_f32_32x32x16_bf16, with the latent rows
+// and both weight matrices staged through LDS in 32-wide slices of d_c (a
+// ring of four, filled by buffer-load DMA).  Each sequence's keys take a
+// range padded to a multiple of 128;
 // the padding rows repeat the sequence's last latent, so every value in the
 // workspace is finite.  V is stored transposed so that the P.V operand is a
 // plain 16-byte LDS read (a transpose read would make the compiler wait for
@@ -37,7 +38,9 @@
 // (11-bit significands: this form rounds keys and values the absorbed form
 // never forms, and float16 keeps that rounding 8x below bf16's); the position
 // part stays bf16 from the cache and takes the bf16 MFMA into the same
-// accumulator.  Keys and values must stay within float16 range (|x| < 65504).
+// accumulator.  Keys, values and the content query must stay within float16
+// range: an element beyond it is stored as NaN, so the outputs it reaches are
+// NaN rather than silently wrong.
 #include <cfloat>
 
 #include "common.hpp"
@@ -134,6 +137,13 @@ constexpr int kUpKeys = 256;  // keys per up-projection workgroup
 constexpr int kUpSl = 32;     // d_c per slice
 
 __device__ __forceinline__ int up_slot(int r, int ch) { return ch ^ ((r >> 2) & 3); }
+
+// x where its float16 rounding is finite, NaN where it would overflow to
+// infinity (|x| >= 65520, half way past 65504 rounds up): a key, value or
+// content-query element outside the float16 range turns the outputs of its
+// head that it reaches into NaN, never into finite wrong values (an infinite
+// key could drop out of a softmax unnoticed).
+__device__ __forceinline__ float f16_range(float x) { return __builtin_fabsf(x) < 65520.f ? x : __builtin_nanf(""); }
 
 // D += A . B on an accumulator pinned to AGPRs (inline asm): the 256
 // accumulator registers fill the AGPR file and the fragments the VGPRs; with
@@ -282,7 +292,7 @@ __global__ void __launch_bounds__(256, 1) upproj_kernel(MhaParams p) {
   // the stored key order), so the global writes are whole rows: the K^C tile
   // is one contiguous 64 KiB run, each V^T row 512 contiguous bytes.
   auto h2pack = [](float u, float v) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){u, v}, f16x2));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){f16_range(u), f16_range(v)}, f16x2));
   };
   constexpr int KROW = kDh * 2;        // K^C row bytes (256)
   constexpr int VROW = kUpKeys * 2;    // V^T row bytes in the tile (512)
@@ -492,7 +502,8 @@ __global__ void __launch_bounds__(256, 2) mha_prefill_kernel(MhaParams p) {
   const int ntile = (wg_last + kKeyTile) / kKeyTile;
 
   // ---- Q fragments (B operand): row r32, d = ks*16 + 8*h2 .. +7; the content
-  // part converted to float16 (exact for bf16 values in float16 range)
+  // part converted to float16 (exact for bf16 values of magnitude 2^-17 ..
+  // 65504; NaN beyond float16 range)
   f16x8 qc[KSC];
   bf16x8 qr[KS - KSC];
   {
@@ -505,7 +516,7 @@ __global__ void __launch_bounds__(256, 2) mha_prefill_kernel(MhaParams p) {
         const bf16x8 x = qvalid ? *reinterpret_cast<const bf16x8*>(qn + d) : bf16x8{};
         f16x8 y;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = static_cast<_Float16>(static_cast<float>(x[e]));
+        for (int e = 0; e < 8; ++e) y[e] = static_cast<_Float16>(f16_range(static_cast<float>(x[e])));
         qc[ks < KSC ? ks : 0] = y;
       } else {
         qr[ks >= KSC ? ks - KSC : 0] = qvalid ? *reinterpret_cast<const bf16x8*>(ql + (d - kDh)) : bf16x8{};
@@ -714,7 +725,8 @@ __global__ void __launch_bounds__(256, 2) mha_prefill_kernel(MhaParams p) {
                     oacc[cb][4 * g + 3] * inv};
       *reinterpret_cast<f32x4*>(o + cb * 32 + 8 * g + 4 * h2) = v;
     }
-  if (p.lse != nullptr && h2 == 0) p.lse[row] = l > 0.f ? (m_run + log2f(l)) * kLn2f : -INFINITY;
+  // (no visible key: -inf; a NaN sum -- an input out of float16 range -- stays NaN)
+  if (p.lse != nullptr && h2 == 0) p.lse[row] = l == 0.f ? -INFINITY : (m_run + log2f(l)) * kLn2f;
 }
 
 template <int DC, int DR>

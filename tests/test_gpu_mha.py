@@ -98,3 +98,23 @@ def test_mha_workspace_is_checked():
     with pytest.raises(mla.MLAError):
         step.run_materialised(G.dev(case.qc, torch.bfloat16), G.dev(case.qr, torch.bfloat16),
                               G.dev(case.w_uk, torch.bfloat16), G.dev(case.w_uv, torch.bfloat16))
+
+
+def test_mha_prefill_flags_float16_overflow():
+    """A head whose up-projected keys leave float16 range comes out NaN (never finite and wrong);
+    the other heads are untouched, bit for bit."""
+    import dataclasses
+
+    case = synth.direct_prefill(synth.TINY, "bf16", [9], [23], seed=131)
+    cache = G.build_cache(case)
+    base = G.run_prefill_mha(case, cache=cache)
+    h = 2
+    # scale head h's W_UK so that key 0's largest content-key element is twice float16's overflow point
+    k0 = case.w_uk[h] @ case.c_rows[0]
+    w_uk = case.w_uk.copy()
+    w_uk[h] *= 2 * 65520.0 / np.max(np.abs(k0))
+    big = G.run_prefill_mha(dataclasses.replace(case, w_uk=w_uk), cache=cache)
+    assert np.all(np.isnan(big["o"][:, h])) and np.all(np.isnan(big["lse"][:, h]))
+    others = [i for i in range(case.shape.n_heads) if i != h]
+    assert np.array_equal(big["o"][:, others], base["o"][:, others])
+    assert np.array_equal(big["lse"][:, others], base["lse"][:, others])
