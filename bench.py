@@ -292,26 +292,22 @@ def main():
     q_nope, q_rope = dev(case.qc), dev(case.qr)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    events = DeviceEvents(3 * args.steps)
-    ev = []
-
-    front_ev = []
+    events = DeviceEvents(4)
     front_bytes = 0
     if per_head:
         last = case.row_offsets + np.maximum(case.seq_lens - 1, 0)
         new_lat, new_kr = dev(case.c_rows[last]), dev(case.kr_rows[last])
         kv_seq = torch.arange(case.batch, dtype=torch.int32, device="cuda")
 
-        def step(i, timed):
+        def call(i):
+            ph_steps[i % len(ph_steps)].attend()
+
+        def step(i):
             st = ph_steps[i % len(ph_steps)]
             st.write(new_lat, new_kr, kv_seq, st.q_pos)
             B.rope_apply(dims, None, None, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat)
             B.absorb_q(dims, q_nope, w_uk, st.q_lat)
-            if timed:
-                e0 = events.record(sh)
-            st.attend()
-            if timed:
-                ev.append((e0, events.record(sh)))
+            call(i)
             B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = case.batch
         kernel_name = "mla_decode_per_head (split attention + merge)"
@@ -334,19 +330,20 @@ def main():
         front_bytes = 2 * (w_dkv.numel() + w_kr.numel() + w_dq.numel() + w_qr.numel() + w_up.numel()
                            + (0 if folded else w_uk.numel()))
 
-        def step(i, timed):
+        def front(i):
             st = steps[i % len(steps)]
-            f0 = events.record(sh) if timed else None
             st.kv(h_new, w_dkv, w_kr)
             st.query(h_new, w_dq, w_up, w_qr, w_uk)
-            if timed:
-                e0 = events.record(sh)
-                front_ev.append((f0, e0))
-            inner = st.inner
+
+        def call(i):
+            inner = steps[i % len(steps)].inner
             B.decode(dims, inner.cache.data, inner.cache.block_table, inner.q_lat, inner.seq_lens,
                      inner.seq_lens_host, inner.out_latent, inner.lse, inner.workspace)
-            if timed:
-                ev.append((e0, events.record(sh)))
+
+        def step(i):
+            front(i)
+            call(i)
+            inner = steps[i % len(steps)].inner
             B.out_proj(dims, inner.out_latent, w_uv, inner.out)
         tokens_per_step = case.batch
         kernel_name = "mla_decode (split attention + merge)"
@@ -357,17 +354,17 @@ def main():
         last = case.row_offsets + np.maximum(case.seq_lens - 1, 0)
         new_lat, new_kr = dev(case.c_rows[last]), dev(case.kr_rows[last])
 
-        def step(i, timed):
+        def call(i):
+            st = steps[i % len(steps)]
+            B.decode(dims, st.cache.data, st.cache.block_table, st.q_lat, st.seq_lens, st.seq_lens_host,
+                     st.out_latent, st.lse, st.workspace)
+
+        def step(i):
             st = steps[i % len(steps)]
             B.rope_apply(dims, st.cache.data, st.cache.block_table, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat,
                          kv_latent=new_lat, k_rope=new_kr, kv_seq=st.kv_seq, kv_pos=st.q_pos)
             B.absorb_q(dims, q_nope, w_uk, st.q_lat)
-            if timed:
-                e0 = events.record(sh)
-            B.decode(dims, st.cache.data, st.cache.block_table, st.q_lat, st.seq_lens, st.seq_lens_host,
-                     st.out_latent, st.lse, st.workspace)
-            if timed:
-                ev.append((e0, events.record(sh)))
+            call(i)
             B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = case.batch
         kernel_name = "mla_decode (split attention + merge)"
@@ -378,15 +375,15 @@ def main():
                  for c in caches]
         mha_ws = B.prefill_mha_workspace(dims, steps[0].cu_q_host, steps[0].q_start_host)
 
-        def step(i, timed):
+        def call(i):
             st = steps[i % len(steps)]
-            B.rope_apply(dims, None, None, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat)
-            if timed:
-                e0 = events.record(sh)
             B.prefill_mha(dims, st.cache.data, st.cache.block_table, q_nope, st.q_lat, w_uk, w_uv, st.cu_q,
                           st.q_start, st.cu_q_host, st.q_start_host, st.out, st.lse, mha_ws)
-            if timed:
-                ev.append((e0, events.record(sh)))
+
+        def step(i):
+            st = steps[i % len(steps)]
+            B.rope_apply(dims, None, None, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat)
+            call(i)
         tokens_per_step = int(case.cu_q[-1])
         kernel_name = "mla_prefill_mha (key/value up-projection + causal attention)"
         algo = prefill_mha_flops(case)
@@ -395,16 +392,16 @@ def main():
         steps = [mla.PrefillStep(dims, c, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
                  for c in caches]
 
-        def step(i, timed):
+        def call(i):
+            st = steps[i % len(steps)]
+            B.prefill(dims, st.cache.data, st.cache.block_table, st.q_lat, st.cu_q, st.q_start, st.cu_q_host,
+                      st.q_start_host, st.out_latent, st.lse)
+
+        def step(i):
             st = steps[i % len(steps)]
             B.rope_apply(dims, None, None, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat)
             B.absorb_q(dims, q_nope, w_uk, st.q_lat)
-            if timed:
-                e0 = events.record(sh)
-            B.prefill(dims, st.cache.data, st.cache.block_table, st.q_lat, st.cu_q, st.q_start, st.cu_q_host,
-                      st.q_start_host, st.out_latent, st.lse)
-            if timed:
-                ev.append((e0, events.record(sh)))
+            call(i)
             B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = int(case.cu_q[-1])
         kernel_name = "mla_prefill (causal attention)"
@@ -412,16 +409,29 @@ def main():
         bound, unit, peak = "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, True)
+        step(i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_per_step = el / args.steps * 1e3
-    kern_ms = float(np.mean([events.elapsed_ms(a, b) for a, b in ev]))
-    front_ms = float(np.mean([events.elapsed_ms(a, b) for a, b in front_ev])) if front_ev else None
+
+    # The measured call alone, `steps` times back to back on the launch stream
+    # between two HIP events: an event recorded between two kernels idles the
+    # queue for several microseconds (a kernel trace shows the gap exactly where
+    # the event sits), so bracketing each call would time the events too.
+    def timed_loop(fn):
+        e0 = events.record(sh)
+        for i in range(args.steps):
+            fn(i)
+        e1 = events.record(sh)
+        torch.cuda.synchronize()
+        return events.elapsed_ms(e0, e1) / args.steps
+
+    kern_ms = timed_loop(call)
+    front_ms = timed_loop(front) if args.front != "none" and not per_head and case.kind == "decode" else None
     events.close()
     achieved = algo / (kern_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
     if per_head:

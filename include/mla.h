@@ -28,8 +28,11 @@
  * - dtype: the cache, q_rope, q_nope, kv_latent, k_rope and the weights
  *   share dims->dtype (MLA_F32 or MLA_BF16).  q_lat has dims->work_dtype.
  *   The latent output out_latent (obar, the input of mla_out_proj), the
- *   decode's split partials, the layer output of mla_out_proj and lse are
- *   always float32, so the path's roundings stop at the softmax weights;
+ *   layer output of mla_out_proj and lse are always float32, so the path's
+ *   roundings stop at the softmax weights (and, for a decode split over the
+ *   cache at d_latent 512 with bf16 work_dtype, at its split partials, kept
+ *   in the workspace as float16 scaled by a power of two per 128 columns:
+ *   2^-11 relative to each group's largest value; float32 everywhere else);
  *   indices are int32.  Accumulation is float32 in every kernel.
  * - Work is enqueued on `stream` (a hipStream_t, NULL = default stream) and
  *   is asynchronous: no call synchronises.  Keep buffers alive until the

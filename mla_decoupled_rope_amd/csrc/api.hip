@@ -155,6 +155,14 @@ double simulate(const std::vector<int>& pages, int L, int workers, double item_c
   return makespan;
 }
 
+// Split partials of the shared-key decode at d_c = 512 in bf16 working
+// precision are float16 with a power-of-two scale per 128-column quarter of a
+// row (half the bytes of float32 at 2^-11 relative rounding); every other
+// decode keeps float32 partials.
+bool half_partials(const mla_dims* d) {
+  return d->dtype == MLA_BF16 && d->work_dtype == MLA_BF16 && d->d_latent == 512 && d->d_rope == 64;
+}
+
 Plan compute_plan(const mla_dims* d, const std::vector<int>& pages, int env) {
   Plan p;
   const int batch = static_cast<int>(pages.size());
@@ -170,7 +178,8 @@ Plan compute_plan(const mla_dims* d, const std::vector<int>& pages, int env) {
     const int wg_per_cu = row > 288 ? 1 : 2;
     const int workers = kPlanCUs * wg_per_cu;
     const double page_bytes = 64.0 * row * 2.0;
-    const double partial_cost = 2.0 * d->n_heads * (d->d_latent + 1) * 4.0 / page_bytes;  // write + merge read
+    const double elt = half_partials(d) ? 2.0 : 4.0;  // bytes of a stored partial element
+    const double partial_cost = 2.0 * d->n_heads * (d->d_latent * elt + 4.0) / page_bytes;  // write + merge read
     const double item_cost = 1.0;
     double best = -1.0;
     L = max_pages;
@@ -225,11 +234,15 @@ Plan make_plan(const mla_dims* d, int batch, const int32_t* lens) {
   return last.plan;
 }
 
-// Split partials: normalised obar [n_items, H, d_latent] float32, then lse
-// [n_items, H] float32 at a 256-byte aligned offset.
+// Workspace: normalised obar partials [n_items, H, d_latent] (float32, or
+// float16 with int32 quarter exponents [n_items, H, d_latent / 128] after
+// them), then lse [n_items, H] float32, each part at a 256-byte aligned offset.
+size_t align_ws(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
 size_t partial_bytes(const mla_dims* d, const Plan& p) {
-  const size_t o = static_cast<size_t>(p.n_items) * d->n_heads * d->d_latent * sizeof(float);
-  return (o + kWsAlign - 1) / kWsAlign * kWsAlign;
+  const size_t rows = static_cast<size_t>(p.n_items) * d->n_heads;
+  if (half_partials(d)) return align_ws(rows * d->d_latent * 2) + align_ws(rows * (d->d_latent / 128) * 4);
+  return align_ws(rows * d->d_latent * sizeof(float));
 }
 
 size_t workspace_bytes(const mla_dims* d, const Plan& p) {
@@ -450,6 +463,12 @@ mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, con
   if (need > 0) {
     p.ws_o = static_cast<float*>(workspace);
     p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + partial_bytes(dims, plan));
+    if (half_partials(dims)) {
+      p.half_partials = 1;
+      p.ws_exp = reinterpret_cast<int32_t*>(
+          static_cast<char*>(workspace) +
+          align_ws(static_cast<size_t>(plan.n_items) * dims->n_heads * dims->d_latent * 2));
+    }
   }
   hipError_t e = mla::launch_decode_bf16(p, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");

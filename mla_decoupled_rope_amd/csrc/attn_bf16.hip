@@ -771,6 +771,42 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     float* ldsl = reinterpret_cast<float*>(ldsp);
     if (h2 == 0) ldsl[lrow] = inv;
     __syncthreads();
+    // float16 partials (decode at d_c = 512): this wave's 128 columns of a row
+    // are one scaled quarter
+    if constexpr (!PREFILL && CBW * 32 == 128) if (!final_out && p.half_partials) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int lr = ((hg + j) & 3) * 32 + r32;
+        const float iv = ldsl[lr];
+        float mx = 0.f;
+#pragma unroll
+        for (int cbl = 0; cbl < CBW; ++cbl)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, __builtin_fabsf(oacc[j * CBW + cbl][i]));
+        mx = pair32_max(mx) * iv;
+        int ex = 0;
+        if (mx > 0.f && mx <= FLT_MAX) (void)frexpf(mx, &ex);
+        const float sc = ldexpf(iv, -ex);  // 1/l and 2^-e in one (exact) factor
+        if (lr < row_count) {
+          const int64_t orow_i = out_row(lr);
+          _Float16* hrow = reinterpret_cast<_Float16*>(p.ws_o) + orow_i * DC;
+#pragma unroll
+          for (int cbl = 0; cbl < CBW; ++cbl)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const f32x16& o = oacc[j * CBW + cbl];
+              const f16x2 lo = __builtin_convertvector((f32x2){o[4 * g4] * sc, o[4 * g4 + 1] * sc}, f16x2);
+              const f16x2 hi = __builtin_convertvector((f32x2){o[4 * g4 + 2] * sc, o[4 * g4 + 3] * sc}, f16x2);
+              uint2 pk;
+              pk.x = __builtin_bit_cast(uint32_t, lo);
+              pk.y = __builtin_bit_cast(uint32_t, hi);
+              *reinterpret_cast<uint2*>(hrow + (hg * CBW + cbl) * 32 + 8 * g4 + 4 * h2) = pk;
+            }
+          if (h2 == 0) p.ws_exp[orow_i * (DC / 128) + hg] = ex;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int lr = ((hg + j) & 3) * 32 + r32;
@@ -805,7 +841,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
 // obar = sum_s e^{lse_s - lse} obar_s, in split order (deterministic).
 // One workgroup per (sequence, 4 heads); 64 lanes per head.  Partials and
 // obar are float32.
-template <int DC>
+template <int DC, bool HALF>
 __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
   constexpr int PER = DC / 64;
   const int b = blockIdx.x;
@@ -834,6 +870,11 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
   float* out = static_cast<float*>(p.out_latent) + row * DC;
   const float* lse_s = p.ws_lse + static_cast<int64_t>(base) * H + head;  // split s at lse_s[s * H]
   const float* part = p.ws_o + (static_cast<int64_t>(base) * H + head) * DC + lane * PER;
+  // float16 partials: element offsets as above, and the lane's quarter's exponent
+  const _Float16* hpart = reinterpret_cast<const _Float16*>(p.ws_o) + (static_cast<int64_t>(base) * H + head) * DC +
+                          lane * PER;
+  const int32_t* pexp = HALF ? p.ws_exp + (static_cast<int64_t>(base) * H + head) * (DC / 128) + lane * PER / 128
+                             : nullptr;
   // Splits go four a round, every load of a round issued before its use; the
   // first round's loads go out before the lse max, so they share its wait.
   constexpr int U = 4;
@@ -845,7 +886,15 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams p) {
       // a sequence with no splits (no tokens; then the workspace may be
       // empty) reads nothing
       if (s0 + u < ns_b) {
-        __builtin_memcpy(v[u], part + static_cast<int64_t>(s0 + u) * H * DC, PER * sizeof(float));
+        if constexpr (HALF) {
+          _Float16 hv[PER];
+          __builtin_memcpy(hv, hpart + static_cast<int64_t>(s0 + u) * H * DC, PER * sizeof(_Float16));
+          const int ex = pexp[static_cast<int64_t>(s0 + u) * H * (DC / 128)];
+#pragma unroll
+          for (int i = 0; i < PER; ++i) v[u][i] = ldexpf(static_cast<float>(hv[i]), ex);
+        } else {
+          __builtin_memcpy(v[u], part + static_cast<int64_t>(s0 + u) * H * DC, PER * sizeof(float));
+        }
         w[u] = lse_s[static_cast<int64_t>(s0 + u) * H];
       } else {
 #pragma unroll
@@ -917,10 +966,12 @@ hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t s) {
 hipError_t launch_merge(const AttnParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   const dim3 grid(p.batch, (p.n_heads + 3) / 4);
-  if (p.d_latent == 512)
-    hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(256), 0, s, p);
-  else if (p.d_latent == 256)
-    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, s, p);
+  if (p.d_latent == 512 && p.half_partials)
+    hipLaunchKernelGGL((merge_kernel<512, true>), grid, dim3(256), 0, s, p);
+  else if (p.d_latent == 512)
+    hipLaunchKernelGGL((merge_kernel<512, false>), grid, dim3(256), 0, s, p);
+  else if (p.d_latent == 256 && !p.half_partials)
+    hipLaunchKernelGGL((merge_kernel<256, false>), grid, dim3(256), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -138,7 +138,12 @@ struct AttnParams {
   const int32_t* cu_q; const int32_t* q_start; int64_t n_blocks;
   // outputs
   void* out_latent; float* lse;
-  float* ws_o; float* ws_lse;  // split partials: normalised obar [slot, H, d_latent] / lse [slot, H]
+  // split partials: normalised obar [slot, H, d_latent] / lse [slot, H].  With
+  // half_partials the obar partials are float16 scaled by 2^-e per 128-column
+  // quarter of a row (e = the quarter's largest magnitude's frexp exponent, so
+  // every stored value is below 1 in magnitude), e in ws_exp [slot, H, d_latent / 128].
+  float* ws_o; float* ws_lse;
+  int half_partials; int32_t* ws_exp;
 };
 
 // Materialised-form prefill: per-head keys and values up-projected from the

@@ -33,6 +33,13 @@ from oracle import attention, front  # noqa: E402
 # small shape.
 BF16 = dict(q_lat="bf16", p="bf16", obar="f32", partial="f32")
 F32W = dict(q_lat="f32", p="two_term", obar="f32", partial="f32")
+# The shared-key decode at d_c = 512 in bf16 keeps its split partials as float16
+# scaled per 128 columns (the other shapes and working precisions keep float32).
+BF16_DC512_DECODE = dict(BF16, partial="f16q")
+
+
+def _decode_prec(prec, shape):
+    return BF16_DC512_DECODE if (prec is BF16 and shape.d_latent == 512) else prec
 # Decode splits follow the library's plan, which the model does not know: it
 # takes the worst over one range per sequence and splits of 1, 2, 3, 4, 8 and 16
 # pages (each split rounds against its own reference maximum).
@@ -59,6 +66,7 @@ def _worst(results, want, key):
 
 
 def _decode_figures(case, prec, want=None, seqs=None, scales=None):
+    prec = _decode_prec(prec, case.shape)
     kw = dict(prec)
     if scales is not None:
         kw["position_scale"] = scales[1]
@@ -160,7 +168,8 @@ def _front_decode_figures(name, folded):
             t, r0 = int(lens[b]), int(fc.row_offsets[b])
             outs.append(R.absorbed(None if folded else qc[b:b + 1], qr[b:b + 1], np.array([t - 1]),
                                    c[r0:r0 + t], kr[r0:r0 + t], fc.w_uk, fc.w_uv, s.scale, s.rope_base,
-                                   split_keys=split, q_tilde=None if not folded else q_t[b:b + 1], **BF16))
+                                   split_keys=split, q_tilde=None if not folded else q_t[b:b + 1],
+                                   **_decode_prec(BF16, s)))
         got.append({k: np.concatenate([r[k] for r in outs], axis=0) for k in ("o", "obar", "lse")})
     return {"o": _worst(got, want, "o"), "lse": _worst(got, want, "lse")}
 
@@ -198,8 +207,8 @@ def _prefix_rows():
     want = _oracle_prefill(pre, queries=rows)
     gp = R.prefill_batch(pre, queries=rows, **BF16)
     decs = [cases.prefix_decode(pre, j) for j in rows]
-    gd = [{k: np.concatenate([R.decode_batch(d, split_keys=sp, **BF16)[k] for d in decs]) for k in ("o", "obar")}
-          for sp in SPLITS]
+    gd = [{k: np.concatenate([R.decode_batch(d, split_keys=sp, **_decode_prec(BF16, d.shape))[k] for d in decs])
+           for k in ("o", "obar")} for sp in SPLITS]
     out = {}
     for k in ("o", "obar"):
         ep = R.errors(gp[k], want[k])
@@ -229,7 +238,7 @@ def _full(case_fn, kind, queries=None, seqs=None):
     if kind == "decode":
         seqs = seqs(case) if callable(seqs) else seqs
         want = _oracle_decode(case, evaluate=attention.absorbed, seqs=seqs)
-        got = [R.decode_batch(case, seqs=seqs, split_keys=sp, **BF16) for sp in FULL_SPLITS]
+        got = [R.decode_batch(case, seqs=seqs, split_keys=sp, **_decode_prec(BF16, case.shape)) for sp in FULL_SPLITS]
         return {k: _worst(got, want, k) for k in ("o", "obar", "lse")}
     return _prefill_figures(case, BF16, queries=queries,
                             want=_oracle_prefill(case, evaluate=attention.absorbed, queries=queries))

@@ -30,8 +30,10 @@ Rounding points (each a keyword below):
   the kernel's.  The row sum l is always the sum of the unrounded weights
   (float32 in the kernels).
 * ``obar``   -- the latent output: "bf16" or "f32".  Decode partials of a
-  split sequence are stored in bf16 (or float32 with ``partial="f32"``) and
-  merged with float32 weights.
+  split sequence are stored as ``partial``: "f32", "bf16", or "f16q" (float16
+  with a power-of-two scale per 128 consecutive columns, chosen so that the
+  group's largest magnitude lies in [0.5, 1)), and merged with float32
+  weights.
 * materialised form: K^C = W_UK c and V = W_UV c rounded to ``kv`` ("f16" or
   "bf16"), the content query converted to the same type, the position part
   bf16, the weights P rounded to ``p``.
@@ -72,7 +74,19 @@ def two_term(x):
     return hi + bf16(x - hi)
 
 
-_CAST = {"bf16": bf16, "f16": f16, "f32": f32, "two_term": two_term, "exact": lambda x: np.asarray(x, np.float64)}
+def f16_scaled(x, group=128):
+    """A float32 value stored as float16 after scaling by 2^-e, e the exponent
+    (frexp) of the largest magnitude in its group of ``group`` consecutive
+    elements of the last axis; scaled back exactly."""
+    x = f32(x)
+    g = x.reshape(x.shape[:-1] + (x.shape[-1] // group, group))
+    mx = np.max(np.abs(g), axis=-1, keepdims=True)
+    e = np.where(mx > 0, np.frexp(mx)[1], 0)
+    return np.ldexp(f16(np.ldexp(g, -e)), e).reshape(x.shape)
+
+
+_CAST = {"bf16": bf16, "f16": f16, "f32": f32, "two_term": two_term, "f16q": f16_scaled,
+         "exact": lambda x: np.asarray(x, np.float64)}
 
 
 def _q_cast(kind):

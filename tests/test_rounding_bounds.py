@@ -43,6 +43,26 @@ def test_casts_against_library_roundings():
     assert np.all(np.abs(R.two_term(y) - y) <= (2.0 ** -16 + 2.0 ** -24) * np.abs(y))
 
 
+def test_scaled_float16_partials():
+    """f16q: each group of 128 columns is scaled by 2^-e (e the frexp exponent of its largest
+    magnitude), rounded to float16 and scaled back -- checked against numpy's float16 on each
+    group one by one, and against float16's error bound relative to the group's largest value."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((3, 5, 256)) * np.exp(rng.uniform(-30, 30, (3, 5, 1)))
+    x[0, 0, :128] = 0.0  # an all-zero group stays zero
+    got = R.f16_scaled(x)
+    for i in range(3):
+        for j in range(5):
+            for g in range(2):
+                v = x[i, j, 128 * g:128 * (g + 1)].astype(np.float32).astype(np.float64)
+                mx = np.max(np.abs(v))
+                e = math.frexp(mx)[1] if mx > 0 else 0
+                want = (v / 2.0 ** e).astype(np.float16).astype(np.float64) * 2.0 ** e
+                assert np.array_equal(got[i, j, 128 * g:128 * (g + 1)], want)
+                assert np.all(np.abs(want - v) <= 2.0 ** -11 * mx)
+    assert np.all(got[0, 0, :128] == 0)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_model_without_casts_is_the_oracle(causal):
     case = synth.direct_prefill(synth.TINY, "bf16", [9], [23], seed=3) if causal else \

@@ -45,12 +45,13 @@ def test_noalloc_matches_decode_twice_smaller_second(shape):
         assert np.all(np.isfinite(got["obar"]))
 
 
-def test_noalloc_rejects_a_batch_beyond_its_scratch():
-    """384 sequences of 4160 tokens split into 768 items whose partials need 192 MiB, more than the
-    96 MiB scratch: an error before any launch."""
+def test_noalloc_rejects_a_batch_beyond_its_scratch(monkeypatch):
+    """64 sequences of 4160 tokens forced into 4-page splits: 1088 items whose partials need
+    over 130 MiB, more than the 96 MiB scratch -- an error before any launch."""
+    monkeypatch.setenv("MLA_DECODE_SPLIT_PAGES", "4")
     case = synth.direct_decode(synth.DSV2, "bf16", [64] * 4, seed=307)
     dims = G.dims_of(case)
-    n = 384
+    n = 64
     lens_host = torch.full((n,), 4160, dtype=torch.int32)
     assert mla.decode_workspace_size(dims, lens_host) > 96 << 20
     cache = torch.zeros((1, 64, dims.row), dtype=torch.bfloat16, device="cuda")
