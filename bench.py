@@ -1,9 +1,9 @@
 """Benchmark: absorbed MLA decode with decoupled RoPE on one MI355X.
 
 One step = one pass of the decode hot path over a batch: RoPE on the new
-query's q^R and the new token's cache row (mla_rope_apply), query absorption
-(mla_absorb_q), split attention over the paged latent cache plus the split
-merge (mla_decode), output absorption (mla_out_proj).  Default workload:
+query's q^R and the new token's cache row with query absorption in one launch
+(mla_rope_absorb_q), split attention over the paged latent cache plus the
+split merge (mla_decode), output absorption (mla_out_proj).  Default workload:
 64 sequences x 4096 cached tokens, n_h = 128, d_c = 512, d_r = 64, bf16, in
 64-token pages.  Three identical cache copies are used in rotation so that
 the 256 MB Infinity Cache cannot serve a step from the previous one.
@@ -305,8 +305,7 @@ def main():
         def step(i):
             st = ph_steps[i % len(ph_steps)]
             st.write(new_lat, new_kr, kv_seq, st.q_pos)
-            B.rope_apply(dims, None, None, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat)
-            B.absorb_q(dims, q_nope, w_uk, st.q_lat)
+            B.rope_absorb_q(dims, None, None, q_nope, w_uk, q_rope, st.q_pos, st.q_lat)
             call(i)
             B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = case.batch
@@ -361,9 +360,8 @@ def main():
 
         def step(i):
             st = steps[i % len(steps)]
-            B.rope_apply(dims, st.cache.data, st.cache.block_table, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat,
-                         kv_latent=new_lat, k_rope=new_kr, kv_seq=st.kv_seq, kv_pos=st.q_pos)
-            B.absorb_q(dims, q_nope, w_uk, st.q_lat)
+            B.rope_absorb_q(dims, st.cache.data, st.cache.block_table, q_nope, w_uk, q_rope, st.q_pos, st.q_lat,
+                            new_lat, new_kr, st.kv_seq, st.q_pos)
             call(i)
             B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = case.batch
@@ -399,8 +397,7 @@ def main():
 
         def step(i):
             st = steps[i % len(steps)]
-            B.rope_apply(dims, None, None, q_rope=q_rope, q_pos=st.q_pos, q_lat=st.q_lat)
-            B.absorb_q(dims, q_nope, w_uk, st.q_lat)
+            B.rope_absorb_q(dims, None, None, q_nope, w_uk, q_rope, st.q_pos, st.q_lat)
             call(i)
             B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = int(case.cu_q[-1])
@@ -458,10 +455,10 @@ def main():
                    "n_heads": s.n_heads, "d_latent": s.d_latent, "d_rope": s.d_rope, "page_size": s.page_size,
                    "cache_copies": len(caches), "score": "two-scale" if args.score == "two" else "one scale",
                    "cache_layout": args.cache_layout,
-                   "step": ("cache_write_per_head + rope_apply + absorb_q + decode_per_head + out_proj" if per_head
+                   "step": ("cache_write_per_head + rope_absorb_q + decode_per_head + out_proj" if per_head
                             else "rope_apply + prefill_mha" if case.kind != "decode" and args.prefill_form == "materialised"
                             else f"kv_project + q_project ({args.front}) + decode + out_proj" if args.front != "none"
-                            else "rope_apply + absorb_q + decode/prefill + out_proj")},
+                            else "rope_absorb_q + decode/prefill + out_proj")},
         "roofline": {"kernel": kernel_name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic, "algorithmic_per_launch": algo,
                      "avg_launch_ms": kern_ms},

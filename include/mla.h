@@ -48,7 +48,8 @@
  *   for MLA_BF16 attention: (16, 256, 32) and (128, 512, 64); MLA_F32
  *   accepts any n_heads <= 1024, d_latent <= 1024, d_rope <= 128.
  * - Outputs never alias inputs, except that mla_rope_apply and mla_absorb_q
- *   write disjoint column ranges of the same q_lat buffer.
+ *   (or mla_rope_absorb_q, both at once) write disjoint column ranges of the
+ *   same q_lat buffer.
  */
 #ifndef MLA_H
 #define MLA_H
@@ -143,6 +144,20 @@ mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache,
  *   so k^C = W_UK[h] c); q_lat [n_q, H, d_latent + d_rope]. */
 mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int64_t n_q,
                         void* q_lat, void* stream);
+
+/* mla_rope_absorb_q -- mla_rope_apply and mla_absorb_q in one launch: both
+ * sides of the query ("AI decoupled RoPE MLA", recap section: q~ = W^UK^T q
+ * ahead of the cache; the position part rotated by its own R_m, the
+ * decoupled-RoPE section), and the new tokens' cache rows.  Arguments as in
+ * the two calls (q_lat gets q~ in [0, d_latent) and R_m q^R in
+ * [d_latent, d_latent + d_rope)); the results are bit-identical to calling
+ * mla_rope_apply then mla_absorb_q.  With MLA_F32 dims, or n_q = 0, it
+ * enqueues the two launches instead.  Every check of both calls runs before
+ * anything is launched. */
+mla_status mla_rope_absorb_q(const mla_dims* dims, const mla_paged_cache* cache, const void* q_nope,
+                             const void* w_uk, const void* q_rope, const int32_t* q_pos, int64_t n_q, void* q_lat,
+                             const void* kv_latent, const void* k_rope, const int32_t* kv_seq,
+                             const int32_t* kv_pos, int64_t n_kv, void* stream);
 
 /* Bytes of workspace mla_decode needs for this batch (0 when no sequence is
  * split).  seq_lens_host [batch] must hold the same lengths later passed to

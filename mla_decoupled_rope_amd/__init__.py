@@ -11,7 +11,8 @@ from .binding import (  # noqa: F401
     decode_plan,
     decode_workspace, per_head_row,
     decode_workspace_size, fold_q_weights, front_workspace, front_workspace_size, kv_project, out_proj, prefill,
-    prefill_mha, prefill_mha_workspace, prefill_mha_workspace_size, q_project, q_project_folded, rope_apply,
+    prefill_mha, prefill_mha_workspace, prefill_mha_workspace_size, q_project, q_project_folded, rope_absorb_q,
+    rope_apply,
 )
 from .pipeline import (  # noqa: F401
     DecodeStep, LatentCache, LayerDecodeStep, LayerPrefillStep, PerHeadDecodeStep, PrefillStep, choose_prefill_form,

@@ -53,6 +53,7 @@ def _load():
     sig = {
         "mla_rope_apply": [pd, pc, vp, vp, i64, vp, vp, vp, vp, vp, i64, vp],
         "mla_absorb_q": [pd, vp, vp, i64, vp, vp],
+        "mla_rope_absorb_q": [pd, pc, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, i64, vp],
         "mla_decode": [pd, pc, vp, vp, vp, i32, vp, vp, vp, sz, vp],
         "mla_decode_noalloc": [pd, pc, vp, vp, vp, i32, vp, vp, vp],
         "mla_prefill": [pd, pc, vp, vp, vp, vp, vp, i32, vp, vp, vp],
@@ -85,7 +86,7 @@ def _load():
 
 LIB = _load()
 
-EXPORTS = ("mla_rope_apply", "mla_absorb_q", "mla_decode_workspace_size", "mla_decode", "mla_decode_noalloc",
+EXPORTS = ("mla_rope_apply", "mla_absorb_q", "mla_rope_absorb_q", "mla_decode_workspace_size", "mla_decode", "mla_decode_noalloc",
            "mla_prefill",
            "mla_out_proj", "mla_status_string", "mla_last_error", "mla_decode_plan",
            "mla_prefill_mha_workspace_size", "mla_prefill_mha", "mla_front_workspace_size", "mla_kv_project",
@@ -203,6 +204,32 @@ def absorb_q(dims: MLADims, q_nope: torch.Tensor, w_uk: torch.Tensor, q_lat: tor
     _dev(q_lat, "q_lat", dims.wdtype, (n, dims.n_heads, dims.row))
     d = dims.c()
     _check(LIB.mla_absorb_q(ctypes.byref(d), q_nope.data_ptr(), w_uk.data_ptr(), n, q_lat.data_ptr(), _stream()))
+
+
+def rope_absorb_q(dims: MLADims, cache: torch.Tensor | None, block_table: torch.Tensor | None,
+                  q_nope: torch.Tensor, w_uk: torch.Tensor, q_rope: torch.Tensor, q_pos: torch.Tensor,
+                  q_lat: torch.Tensor, kv_latent: torch.Tensor | None = None, k_rope: torch.Tensor | None = None,
+                  kv_seq: torch.Tensor | None = None, kv_pos: torch.Tensor | None = None) -> None:
+    """mla_rope_absorb_q: rope_apply and absorb_q in one launch (bit-identical results)."""
+    n_q = q_nope.shape[0]
+    n_kv = 0 if kv_latent is None else kv_latent.shape[0]
+    _dev(q_nope, "q_nope", dims.dtype, (n_q, dims.n_heads, dims.d_head))
+    _dev(w_uk, "w_uk", dims.dtype, (dims.n_heads, dims.d_head, dims.d_latent))
+    _dev(q_rope, "q_rope", dims.dtype, (n_q, dims.n_heads, dims.d_rope))
+    _dev(q_pos, "q_pos", torch.int32, (n_q,))
+    _dev(q_lat, "q_lat", dims.wdtype, (n_q, dims.n_heads, dims.row))
+    cstruct = None
+    if n_kv:
+        cstruct = _cache(dims, cache, block_table)
+        _dev(kv_latent, "kv_latent", dims.dtype, (n_kv, dims.d_latent))
+        _dev(k_rope, "k_rope", dims.dtype, (n_kv, dims.d_rope))
+        _dev(kv_seq, "kv_seq", torch.int32, (n_kv,))
+        _dev(kv_pos, "kv_pos", torch.int32, (n_kv,))
+    d = dims.c()
+    _check(LIB.mla_rope_absorb_q(ctypes.byref(d), ctypes.byref(cstruct) if cstruct else None, _ptr(q_nope),
+                                 _ptr(w_uk), _ptr(q_rope), _ptr(q_pos), n_q, _ptr(q_lat),
+                                 _ptr(kv_latent) if n_kv else None, _ptr(k_rope) if n_kv else None,
+                                 _ptr(kv_seq) if n_kv else None, _ptr(kv_pos) if n_kv else None, n_kv, _stream()))
 
 
 def decode_plan(dims: MLADims, seq_lens_host: torch.Tensor):

@@ -303,12 +303,15 @@ const char* mla_status_string(mla_status s) {
 
 const char* mla_last_error(void) { return g_err.c_str(); }
 
-mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache, const void* q_rope,
-                          const int32_t* q_pos, int64_t n_q, void* q_lat, const void* kv_latent,
-                          const void* k_rope, const int32_t* kv_seq, const int32_t* kv_pos, int64_t n_kv,
-                          void* stream) {
-  g_err.clear();
-  MLA_TRY(check_dims(dims));
+}  // extern "C"
+
+namespace {
+
+// Checks and kernel parameters of the RoPE channel (mla_rope_apply and the
+// rotation half of mla_rope_absorb_q).
+mla_status rope_params(const mla_dims* dims, const mla_paged_cache* cache, const void* q_rope, const int32_t* q_pos,
+                       int64_t n_q, void* q_lat, const void* kv_latent, const void* k_rope, const int32_t* kv_seq,
+                       const int32_t* kv_pos, int64_t n_kv, mla::RopeParams* out) {
   if (n_q < 0 || n_kv < 0) return fail(MLA_ERR_INVALID_ARG, "n_q and n_kv must be >= 0");
   if (n_q > 0 && (q_rope == nullptr || q_pos == nullptr || q_lat == nullptr))
     return fail(MLA_ERR_INVALID_ARG, "q_rope, q_pos and q_lat are required when n_q > 0");
@@ -335,24 +338,63 @@ mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache, co
             reinterpret_cast<uintptr_t>(q_lat) % 16 == 0;
   for (int j = 0; j < dims->d_rope / 2; ++j) p.theta[j] = std::pow(dims->rope_base, -2.0 * j / dims->d_rope);
   p.q_scale = position_ratio(dims);
+  *out = p;
+  return MLA_OK;
+}
+
+// Checks and kernel parameters of the query absorption.
+mla_status absorb_params(const mla_dims* dims, const void* q_nope, const void* w_uk, int64_t n_q, void* q_lat,
+                         mla::GemmParams* out) {
+  if (n_q < 0) return fail(MLA_ERR_INVALID_ARG, "n_q must be >= 0");
+  if (n_q > 0 && (q_nope == nullptr || w_uk == nullptr || q_lat == nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "q_nope, w_uk and q_lat must be non-NULL");
+  if (dims->dtype == MLA_BF16 && (dims->d_head != 128 || dims->d_latent % 128 != 0))
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 absorption needs d_head = 128 and d_latent a multiple of 128");
+  if (n_q > 65535LL * 512 || n_q * dims->n_heads * dims->d_latent > (1LL << 40))
+    return fail(MLA_ERR_UNSUPPORTED, "n_q too large for one launch");
+  *out = mla::GemmParams{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
+                         dims->work_dtype, q_nope, w_uk, q_lat, n_q};
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache, const void* q_rope,
+                          const int32_t* q_pos, int64_t n_q, void* q_lat, const void* kv_latent,
+                          const void* k_rope, const int32_t* kv_seq, const int32_t* kv_pos, int64_t n_kv,
+                          void* stream) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  mla::RopeParams p{};
+  MLA_TRY(rope_params(dims, cache, q_rope, q_pos, n_q, q_lat, kv_latent, k_rope, kv_seq, kv_pos, n_kv, &p));
   const hipError_t e = mla::launch_rope(p, as_stream(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "rope launch");
+}
+
+mla_status mla_rope_absorb_q(const mla_dims* dims, const mla_paged_cache* cache, const void* q_nope,
+                             const void* w_uk, const void* q_rope, const int32_t* q_pos, int64_t n_q, void* q_lat,
+                             const void* kv_latent, const void* k_rope, const int32_t* kv_seq,
+                             const int32_t* kv_pos, int64_t n_kv, void* stream) {
+  g_err.clear();
+  MLA_TRY(check_dims(dims));
+  mla::RopeParams r{};
+  MLA_TRY(rope_params(dims, cache, q_rope, q_pos, n_q, q_lat, kv_latent, k_rope, kv_seq, kv_pos, n_kv, &r));
+  mla::GemmParams g{};
+  MLA_TRY(absorb_params(dims, q_nope, w_uk, n_q, q_lat, &g));
+  if (n_q == 0 && n_kv == 0) return MLA_OK;
+  const hipError_t e = mla::launch_rope_absorb(g, r, as_stream(stream));
+  return e == hipSuccess ? MLA_OK : hip_fail(e, "rope + absorb launch");
 }
 
 mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, int64_t n_q, void* q_lat,
                         void* stream) {
   g_err.clear();
   MLA_TRY(check_dims(dims));
-  if (n_q < 0) return fail(MLA_ERR_INVALID_ARG, "n_q must be >= 0");
+  mla::GemmParams p{};
+  MLA_TRY(absorb_params(dims, q_nope, w_uk, n_q, q_lat, &p));
   if (n_q == 0) return MLA_OK;
-  if (q_nope == nullptr || w_uk == nullptr || q_lat == nullptr)
-    return fail(MLA_ERR_INVALID_ARG, "q_nope, w_uk and q_lat must be non-NULL");
-  if (dims->dtype == MLA_BF16 && (dims->d_head != 128 || dims->d_latent % 128 != 0))
-    return fail(MLA_ERR_UNSUPPORTED, "bf16 absorption needs d_head = 128 and d_latent a multiple of 128");
-  if (n_q > 65535LL * 512 || n_q * dims->n_heads * dims->d_latent > (1LL << 40))
-    return fail(MLA_ERR_UNSUPPORTED, "n_q too large for one launch");
-  mla::GemmParams p{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
-                    dims->work_dtype, q_nope, w_uk, q_lat, n_q};
   const hipError_t e = mla::launch_absorb(p, as_stream(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "absorb launch");
 }

@@ -169,6 +169,7 @@ hipError_t launch_rope(const RopeParams& p, hipStream_t s);
 hipError_t launch_perhead_decode(const AttnParams& p, hipStream_t s);
 hipError_t launch_perhead_cache_write(const RopeParams& p, hipStream_t s);
 hipError_t launch_absorb(const GemmParams& p, hipStream_t s);
+hipError_t launch_rope_absorb(const GemmParams& g, const RopeParams& r, hipStream_t s);
 hipError_t launch_out_proj(const GemmParams& p, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t s);

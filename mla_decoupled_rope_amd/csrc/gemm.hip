@@ -17,6 +17,8 @@
 //    layer output is float32).
 // float32 path: one thread per output element, float32 accumulation.
 #include "common.hpp"
+#include "decode_items.hpp"
+#include "rope_block.hpp"
 
 namespace mla {
 
@@ -34,13 +36,14 @@ __device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
 // W_UK tile [d_head rows (i), 128 cols (j)] in LDS; each wave owns 32 j x 64 n.
 // A 64-token chunk of q^C goes through LDS once per workgroup (rows padded to
 // 288 bytes: conflict-free fragment reads) instead of once per wave.
+// One workgroup (256 threads) of the absorption: feature tile jt, head h,
+// token chunk nz.
 template <int DH, typename TQ>
-__global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
+__device__ __forceinline__ void absorb_block(const GemmParams& p, int jt, int h, int nz) {
   __shared__ __attribute__((aligned(16))) bf16_t w_lds[DH * kAbsorbLdsStride];
   constexpr int QS = DH + 16;  // q^C row stride in LDS (elements)
   __shared__ __attribute__((aligned(16))) bf16_t q_lds[64 * QS];
-  const int h = blockIdx.y;
-  const int j0 = blockIdx.x * kAbsorbJTile;
+  const int j0 = jt * kAbsorbJTile;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -50,7 +53,7 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
   const bf16_t* w = static_cast<const bf16_t*>(p.w) + static_cast<int64_t>(h) * DH * DC;
   const bf16_t* q = static_cast<const bf16_t*>(p.a);
   TQ* out = static_cast<TQ*>(p.out);
-  const int64_t n_begin = static_cast<int64_t>(blockIdx.z) * kAbsorbNChunk;
+  const int64_t n_begin = static_cast<int64_t>(nz) * kAbsorbNChunk;
   const int64_t n_end = min(p.n, n_begin + kAbsorbNChunk);
   const int q16 = lane >> 4, r16 = lane & 15;
   const int jw = wave * 32;  // this wave's j offset inside the tile
@@ -155,11 +158,45 @@ __global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
   }
 }
 
+// Work index w of the absorption: feature tile fastest, then head, then token
+// chunk.  Through xcd_local the four feature tiles of a head (which read the
+// same q^C chunk) share an XCD, so that chunk comes from HBM once.
+template <int DH, typename TQ>
+__device__ __forceinline__ void absorb_work(const GemmParams& g, int64_t a, int64_t n_abs) {
+  const int64_t w = xcd_local(a, n_abs);
+  const int jt_n = g.d_latent / kAbsorbJTile;
+  const int64_t hn = w / jt_n;
+  absorb_block<DH, TQ>(g, static_cast<int>(w % jt_n), static_cast<int>(hn % g.n_heads),
+                       static_cast<int>(hn / g.n_heads));
+}
+
+template <int DH, typename TQ>
+__global__ void __launch_bounds__(256) absorb_bf16_kernel(GemmParams p) {
+  absorb_work<DH, TQ>(p, blockIdx.x, gridDim.x);
+}
+
+// The query prologue in one launch: blocks [0, n_rope) run K1 (query rotation
+// and cache rows), blocks [r_pad, r_pad + n_abs) absorb (r_pad = n_rope rounded
+// up to 32, so the absorption's XCD grouping holds; blocks in between exit).
+// The two write disjoint columns of q_lat and share nothing else, so their
+// blocks run side by side; the rotation's blocks come first so that its
+// float64 angle chains start at once and end under the absorption.
+template <int DH, typename T, typename TQ>
+__global__ void __launch_bounds__(256) rope_absorb_kernel(GemmParams g, RopeParams r, int64_t n_rope, int64_t r_pad,
+                                                          int64_t n_abs) {
+  const int64_t blk = blockIdx.x;
+  if (blk < n_rope)
+    rope_block<T, TQ>(r, blk);
+  else if (blk >= r_pad)
+    absorb_work<DH, TQ>(g, blk - r_pad, n_abs);
+}
+
 // o^T[v, n] = W_UV[h][v, :] . obar[n, h, :].  A workgroup takes one head and
 // 64 rows v; each of its four waves keeps its 16 rows of W_UV[h] (all of d_c)
 // in registers, loaded once, while the tokens go by in chunks of 64: a chunk
 // of obar[:, h, :] is staged in LDS once and read by all four waves.  So
-// W_UV is read once per call and obar twice (once per 64-row half of d_v).
+// W_UV is read once per call and obar once from HBM (its second reader, the
+// other 64-row half of d_v, runs on the same XCD and finds it in L2).
 // TO is obar's element type; a float32 obar is staged as a two-term bf16
 // split hi + lo and takes two MFMAs per step, so it enters at ~16
 // significant bits.
@@ -170,12 +207,16 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(GemmParams p) {
   constexpr int NTERM = sizeof(TO) == 4 ? 2 : 1;
   constexpr int LSTRIDE = KMAX + 8;  // bf16 elements per staged row (padding against bank conflicts)
   __shared__ __attribute__((aligned(16))) bf16_t ob_lds[NTERM][kOutChunk * LSTRIDE];
-  const int h = blockIdx.y;
+  // work index w = head * (d_v / 64) + row block; through xcd_local the row
+  // blocks of a head (which read the same obar rows) share an XCD, so obar
+  // comes from HBM once
+  const int H = p.n_heads, DC = p.d_latent, DV = p.d_v;
+  const int64_t wk = xcd_local(blockIdx.x, gridDim.x);
+  const int h = static_cast<int>(wk / (DV / kOutRows));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int v0 = blockIdx.x * kOutRows + wave * 16;
-  const int H = p.n_heads, DC = p.d_latent, DV = p.d_v;
+  const int v0 = static_cast<int>(wk % (DV / kOutRows)) * kOutRows + wave * 16;
   const int q16 = lane >> 4, r16 = lane & 15;
   const int ks_n = DC / 32;
   const bf16_t* w = static_cast<const bf16_t*>(p.w) + (static_cast<int64_t>(h) * DV + v0 + r16) * DC + q16 * 8;
@@ -283,13 +324,33 @@ hipError_t launch_absorb(const GemmParams& p, hipStream_t s) {
     const int64_t total = p.n * p.n_heads * p.d_latent;
     hipLaunchKernelGGL(absorb_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, p);
   } else {
-    const dim3 grid(p.d_latent / kAbsorbJTile, p.n_heads,
-                    static_cast<unsigned>((p.n + kAbsorbNChunk - 1) / kAbsorbNChunk));
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.d_latent / kAbsorbJTile) * p.n_heads *
+                                          ((p.n + kAbsorbNChunk - 1) / kAbsorbNChunk)));
     if (p.work_dtype == 0)
       hipLaunchKernelGGL((absorb_bf16_kernel<128, float>), grid, dim3(256), 0, s, p);
     else
       hipLaunchKernelGGL((absorb_bf16_kernel<128, bf16_t>), grid, dim3(256), 0, s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_absorb(const GemmParams& g, const RopeParams& r, hipStream_t s) {
+  // the fused launch covers the bf16 absorption; other types take the two launches
+  if (g.dtype == 0 || g.n == 0) {
+    hipError_t e = launch_rope(r, s);
+    if (e != hipSuccess) return e;
+    return launch_absorb(g, s);
+  }
+  const int64_t n_abs = static_cast<int64_t>(g.d_latent / kAbsorbJTile) * g.n_heads *
+                        ((g.n + kAbsorbNChunk - 1) / kAbsorbNChunk);
+  const int64_t n_rope = rope_blocks(r);
+  const int64_t r_pad = (n_rope + 31) / 32 * 32;
+  const dim3 grid(static_cast<unsigned>(r_pad + n_abs));
+  if (g.work_dtype == 0)
+    hipLaunchKernelGGL((rope_absorb_kernel<128, bf16_t, float>), grid, dim3(256), 0, s, g, r, n_rope, r_pad, n_abs);
+  else
+    hipLaunchKernelGGL((rope_absorb_kernel<128, bf16_t, bf16_t>), grid, dim3(256), 0, s, g, r, n_rope, r_pad,
+                       n_abs);
   return hipGetLastError();
 }
 
@@ -299,7 +360,7 @@ hipError_t launch_out_proj(const GemmParams& p, hipStream_t s) {
     const int64_t total = p.n * p.n_heads * p.d_v;
     hipLaunchKernelGGL(out_proj_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, p);
   } else {
-    const dim3 grid(p.d_v / kOutRows, p.n_heads);
+    const dim3 grid(static_cast<unsigned>(p.d_v / kOutRows * p.n_heads));
     if (p.d_latent <= 256)
       hipLaunchKernelGGL((out_proj_bf16_kernel<float, 256>), grid, dim3(256), 0, s, p);
     else

@@ -1,13 +1,13 @@
 """Device-side state and the two hot-path pipelines built from the five C-ABI calls.
 
 * ``LatentCache``  -- the paged [c | R k^R] cache and its block table.
-* ``DecodeStep``   -- rope_apply (new token + q^R) -> absorb_q -> decode
+* ``DecodeStep``   -- rope_absorb_q (new token + q^R + q~, one launch) -> decode
                       (split + merge) -> out_proj, with every buffer
                       preallocated so a step launches kernels only.
 * ``LayerDecodeStep`` -- the same step from hidden states: kv_project (the new
                       token's cache row) -> q_project -> absorb_q (or
                       q_project_folded) -> decode -> out_proj.
-* ``PrefillStep``  -- rope_apply (chunk rows + q^R) -> absorb_q -> prefill ->
+* ``PrefillStep``  -- rope_absorb_q (chunk rows + q^R + q~) -> prefill ->
                       out_proj, or rope_apply -> prefill_mha (the materialised
                       form); ``choose_prefill_form`` picks between them.
 """
@@ -101,13 +101,9 @@ class DecodeStep:
     def run(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
         """q_nope [B,H,d_h], q_rope [B,H,d_r] (un-rotated); optional new token rows at position T_b - 1."""
         d = self.dims
-        if new_latent is not None:
-            B.rope_apply(d, self.cache.data, self.cache.block_table, q_rope=q_rope, q_pos=self.q_pos,
-                         q_lat=self.q_lat, kv_latent=new_latent, k_rope=new_k_rope, kv_seq=self.kv_seq,
-                         kv_pos=self.q_pos)
-        else:
-            B.rope_apply(d, None, None, q_rope=q_rope, q_pos=self.q_pos, q_lat=self.q_lat)
-        B.absorb_q(d, q_nope, w_uk, self.q_lat)
+        B.rope_absorb_q(d, self.cache.data, self.cache.block_table, q_nope, w_uk, q_rope, self.q_pos, self.q_lat,
+                        new_latent, new_k_rope, self.kv_seq if new_latent is not None else None,
+                        self.q_pos if new_latent is not None else None)
         B.decode(d, self.cache.data, self.cache.block_table, self.q_lat, self.seq_lens, self.seq_lens_host,
                  self.out_latent, self.lse, self.workspace)
         B.out_proj(d, self.out_latent, w_uv, self.out)
@@ -145,8 +141,7 @@ class PerHeadDecodeStep:
 
     def run(self, q_nope, q_rope, w_uk, w_uv):
         d = self.dims
-        B.rope_apply(d, None, None, q_rope=q_rope, q_pos=self.q_pos, q_lat=self.q_lat)
-        B.absorb_q(d, q_nope, w_uk, self.q_lat)
+        B.rope_absorb_q(d, None, None, q_nope, w_uk, q_rope, self.q_pos, self.q_lat)
         self.attend()
         B.out_proj(d, self.out_latent, w_uv, self.out)
         return self.out
@@ -176,13 +171,9 @@ class PrefillStep:
     def run(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
         """Queries of the chunk at positions q_start[b] + j; optional chunk rows written to the cache first."""
         d = self.dims
-        if new_latent is not None:
-            B.rope_apply(d, self.cache.data, self.cache.block_table, q_rope=q_rope, q_pos=self.q_pos,
-                         q_lat=self.q_lat, kv_latent=new_latent, k_rope=new_k_rope, kv_seq=self.kv_seq,
-                         kv_pos=self.q_pos)
-        else:
-            B.rope_apply(d, None, None, q_rope=q_rope, q_pos=self.q_pos, q_lat=self.q_lat)
-        B.absorb_q(d, q_nope, w_uk, self.q_lat)
+        B.rope_absorb_q(d, self.cache.data, self.cache.block_table, q_nope, w_uk, q_rope, self.q_pos, self.q_lat,
+                        new_latent, new_k_rope, self.kv_seq if new_latent is not None else None,
+                        self.q_pos if new_latent is not None else None)
         B.prefill(d, self.cache.data, self.cache.block_table, self.q_lat, self.cu_q, self.q_start, self.cu_q_host,
                   self.q_start_host, self.out_latent, self.lse)
         B.out_proj(d, self.out_latent, w_uv, self.out)

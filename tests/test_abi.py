@@ -98,6 +98,15 @@ def test_other_calls_validate():
     assert B.LIB.mla_out_proj(ctypes.byref(_dims(d_v=100)), FAKE, FAKE, 2, FAKE, None) == 2
     assert B.LIB.mla_rope_apply(ctypes.byref(d), None, None, None, 2, None, None, None, None, None, 0, None) == 1
     assert B.LIB.mla_rope_apply(ctypes.byref(d), None, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == 1
+    # the fused prologue runs the checks of both calls before any launch
+    rab = B.LIB.mla_rope_absorb_q
+    assert rab(ctypes.byref(d), None, None, FAKE, FAKE, FAKE, 2, FAKE, None, None, None, None, 0, None) == 1  # q_nope
+    assert rab(ctypes.byref(d), None, FAKE, FAKE, None, FAKE, 2, FAKE, None, None, None, None, 0, None) == 1  # q_rope
+    assert rab(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == 1  # cache
+    assert rab(ctypes.byref(_dims(d_head=64)), None, FAKE, FAKE, FAKE, FAKE, 2, FAKE, None, None, None, None, 0,
+               None) == 2
+    assert rab(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, -1, FAKE, None, None, None, None, 0, None) == 1
+    assert rab(ctypes.byref(d), None, None, None, None, None, 0, None, None, None, None, None, 0, None) == 0
     cache = B.PagedCache(FAKE.value, 4, FAKE.value, 2, 4)
     cu = (ctypes.c_int32 * 3)(1, 2, 3)
     st = (ctypes.c_int32 * 2)(0, 0)

@@ -120,3 +120,40 @@ def test_out_proj(dtype, n):
     # float32 accumulation, float32 output; with bf16 weights the float32 obar enters as a
     # two-term bf16 split (within 2^-16 of each value): float32-level error on both paths
     G.assert_close(got, want, "f32", "o")
+
+
+@pytest.mark.parametrize("dtype,qdtype,with_rows", [("bf16", "bf16", True), ("bf16", "f32", True),
+                                                      ("bf16", "bf16", False), ("f32", "f32", True)])
+@pytest.mark.parametrize("shape", [synth.TINY, synth.DSV2], ids=["tiny", "dsv2"])
+def test_rope_absorb_q_is_the_two_calls(dtype, qdtype, with_rows, shape):
+    """mla_rope_absorb_q (one launch for bf16) leaves q_lat and the cache bit-identical to
+    mla_rope_apply followed by mla_absorb_q, for 300 queries (several token chunks of the
+    absorption) and 70 new cache rows."""
+    rng = np.random.default_rng(17)
+    n, lens = 300, [70, 1, 200]
+    case = synth.direct_decode(shape, dtype, lens, seed=19, shuffle=True)
+    case_dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q_dt = torch.float32 if qdtype == "f32" else torch.bfloat16
+    dims = mla.MLADims(shape.n_heads, shape.d_head, shape.d_v, shape.d_latent, shape.d_rope, dtype=case_dt,
+                       work_dtype=q_dt)
+    q_nope = G.dev(synth.to_storage(rng.standard_normal((n, shape.n_heads, shape.d_head)), dtype), case_dt)
+    q_rope = G.dev(synth.to_storage(rng.standard_normal((n, shape.n_heads, shape.d_rope)), dtype), case_dt)
+    w_uk = G.dev(case.w_uk, case_dt)
+    q_pos = torch.from_numpy(rng.integers(0, 131072, n).astype(np.int32)).cuda()
+    seqs, pos = case.kv_seq_pos()
+    rows = dict(kv_latent=G.dev(case.c_rows, case_dt), k_rope=G.dev(case.kr_rows, case_dt),
+                kv_seq=torch.from_numpy(seqs).cuda(), kv_pos=torch.from_numpy(pos).cuda()) if with_rows else {}
+    outs = []
+    for fused in (False, True):
+        cache = mla.LatentCache(dims, case.block_table, case.num_pages, fill=float("nan"))
+        q_lat = torch.full((n, shape.n_heads, shape.row), float("nan"), dtype=q_dt, device="cuda")
+        if fused:
+            mla.rope_absorb_q(dims, cache.data, cache.block_table, q_nope, w_uk, q_rope, q_pos, q_lat, **rows)
+        else:
+            mla.rope_apply(dims, cache.data, cache.block_table, q_rope=q_rope, q_pos=q_pos, q_lat=q_lat, **rows)
+            mla.absorb_q(dims, q_nope, w_uk, q_lat)
+        torch.cuda.synchronize()
+        outs.append((q_lat.view(torch.int16 if q_dt == torch.bfloat16 else torch.int32).cpu(),
+                     cache.data.view(torch.int16 if case_dt == torch.bfloat16 else torch.int32).cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]), "q_lat differs"
+    assert torch.equal(outs[0][1], outs[1][1]), "cache differs"
