@@ -84,6 +84,7 @@ struct RopeParams {
 struct GemmParams {
   int n_heads, d_head, d_v, d_latent, d_rope, dtype, work_dtype;
   const void* a; const void* w; void* out; int64_t n;
+  int64_t n_chunk;  // tokens per workgroup (a multiple of 64; set by the launcher)
 };
 
 // Front of the layer: Y = X W^T in split-K partials, then a reduce that

@@ -16,6 +16,8 @@
 //    two-term bf16 split; the float32 accumulator is stored as is (the
 //    layer output is float32).
 // float32 path: one thread per output element, float32 accumulation.
+#include <algorithm>
+
 #include "common.hpp"
 #include "decode_items.hpp"
 #include "rope_block.hpp"
@@ -26,7 +28,17 @@ namespace {
 
 constexpr int kAbsorbJTile = 128;  // output features per workgroup
 constexpr int kAbsorbLdsStride = kAbsorbJTile + 16;  // padded row (elements): 288 B
-constexpr int kAbsorbNChunk = 512;  // tokens per workgroup (looped in 64s)
+constexpr int kAbsorbNChunk = 512;  // most tokens per workgroup (looped in 64s)
+
+// Tokens per workgroup for a grid of `per_chunk` workgroups per token chunk:
+// the smallest multiple of 64 (at least 64, at most max_chunk) that keeps
+// the grid within about `target` workgroups.  Small batches get one chunk
+// (one load of each weight tile); long ones enough chunks to fill the chip.
+inline int64_t token_chunk(int64_t n, int64_t per_chunk, int64_t target, int64_t max_chunk) {
+  int64_t c = (n * per_chunk + target - 1) / target;
+  c = (c + 63) / 64 * 64;
+  return std::max<int64_t>(64, std::min<int64_t>(c, max_chunk));
+}
 static_assert((128 * (kAbsorbJTile / 8)) % 256 == 0, "W tile pieces must split evenly over the threads");
 
 __device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
@@ -53,8 +65,8 @@ __device__ __forceinline__ void absorb_block(const GemmParams& p, int jt, int h,
   const bf16_t* w = static_cast<const bf16_t*>(p.w) + static_cast<int64_t>(h) * DH * DC;
   const bf16_t* q = static_cast<const bf16_t*>(p.a);
   TQ* out = static_cast<TQ*>(p.out);
-  const int64_t n_begin = static_cast<int64_t>(nz) * kAbsorbNChunk;
-  const int64_t n_end = min(p.n, n_begin + kAbsorbNChunk);
+  const int64_t n_begin = static_cast<int64_t>(nz) * p.n_chunk;
+  const int64_t n_end = min(p.n, n_begin + p.n_chunk);
   const int q16 = lane >> 4, r16 = lane & 15;
   const int jw = wave * 32;  // this wave's j offset inside the tile
   // A chunk of q^C (64 tokens x DH): this thread's 16-byte pieces, loaded
@@ -191,11 +203,12 @@ __global__ void __launch_bounds__(256) rope_absorb_kernel(GemmParams g, RopePara
     absorb_work<DH, TQ>(g, blk - r_pad, n_abs);
 }
 
-// o^T[v, n] = W_UV[h][v, :] . obar[n, h, :].  A workgroup takes one head and
-// 64 rows v; each of its four waves keeps its 16 rows of W_UV[h] (all of d_c)
-// in registers, loaded once, while the tokens go by in chunks of 64: a chunk
-// of obar[:, h, :] is staged in LDS once and read by all four waves.  So
-// W_UV is read once per call and obar once from HBM (its second reader, the
+// o^T[v, n] = W_UV[h][v, :] . obar[n, h, :].  A workgroup takes one head, 64
+// rows v and a group of tokens (n_chunk, sized by the launcher to fill the
+// chip); each of its four waves keeps its 16 rows of W_UV[h] (all of d_c) in
+// registers, loaded once, while its tokens go by in chunks of 64: a chunk of
+// obar[:, h, :] is staged in LDS once and read by all four waves.  So W_UV is
+// read once per token group and obar once from HBM (its second reader, the
 // other 64-row half of d_v, runs on the same XCD and finds it in L2).
 // TO is obar's element type; a float32 obar is staged as a two-term bf16
 // split hi + lo and takes two MFMAs per step, so it enters at ~16
@@ -212,7 +225,9 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(GemmParams p) {
   // comes from HBM once
   const int H = p.n_heads, DC = p.d_latent, DV = p.d_v;
   const int64_t wk = xcd_local(blockIdx.x, gridDim.x);
-  const int h = static_cast<int>(wk / (DV / kOutRows));
+  const int64_t hw = wk / (DV / kOutRows);  // token group * H + head
+  const int h = static_cast<int>(hw % H);
+  const int64_t t_begin = (hw / H) * p.n_chunk, t_end = min(p.n, t_begin + p.n_chunk);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -227,8 +242,8 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(GemmParams p) {
 #pragma unroll
   for (int k = 0; k < KMAX / 32; ++k)
     if (k < ks_n) wa[k] = load8(w + k * 32);
-  for (int64_t c0 = 0; c0 < p.n; c0 += kOutChunk) {
-    const int rows = static_cast<int>(min<int64_t>(kOutChunk, p.n - c0));
+  for (int64_t c0 = t_begin; c0 < t_end; c0 += kOutChunk) {
+    const int rows = static_cast<int>(min<int64_t>(kOutChunk, t_end - c0));
     // stage obar[c0 .. c0 + rows, h, :] (zeros past the end)
     __syncthreads();
     // all of this thread's loads first, then its LDS stores: one round trip
@@ -318,14 +333,23 @@ __global__ void __launch_bounds__(256) out_proj_f32_kernel(GemmParams p) {
 
 }  // namespace
 
-hipError_t launch_absorb(const GemmParams& p, hipStream_t s) {
+namespace {
+// workgroups of the bf16 absorption, with p.n_chunk set
+int64_t absorb_grid(GemmParams& p) {
+  const int64_t per_chunk = static_cast<int64_t>(p.d_latent / kAbsorbJTile) * p.n_heads;
+  p.n_chunk = token_chunk(p.n, per_chunk, 1024, kAbsorbNChunk);
+  return per_chunk * ((p.n + p.n_chunk - 1) / p.n_chunk);
+}
+}  // namespace
+
+hipError_t launch_absorb(const GemmParams& p_in, hipStream_t s) {
+  GemmParams p = p_in;
   if (p.n == 0) return hipSuccess;
   if (p.dtype == 0) {
     const int64_t total = p.n * p.n_heads * p.d_latent;
     hipLaunchKernelGGL(absorb_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, p);
   } else {
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.d_latent / kAbsorbJTile) * p.n_heads *
-                                          ((p.n + kAbsorbNChunk - 1) / kAbsorbNChunk)));
+    const dim3 grid(static_cast<unsigned>(absorb_grid(p)));
     if (p.work_dtype == 0)
       hipLaunchKernelGGL((absorb_bf16_kernel<128, float>), grid, dim3(256), 0, s, p);
     else
@@ -334,15 +358,15 @@ hipError_t launch_absorb(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rope_absorb(const GemmParams& g, const RopeParams& r, hipStream_t s) {
+hipError_t launch_rope_absorb(const GemmParams& g_in, const RopeParams& r, hipStream_t s) {
   // the fused launch covers the bf16 absorption; other types take the two launches
-  if (g.dtype == 0 || g.n == 0) {
+  if (g_in.dtype == 0 || g_in.n == 0) {
     hipError_t e = launch_rope(r, s);
     if (e != hipSuccess) return e;
-    return launch_absorb(g, s);
+    return launch_absorb(g_in, s);
   }
-  const int64_t n_abs = static_cast<int64_t>(g.d_latent / kAbsorbJTile) * g.n_heads *
-                        ((g.n + kAbsorbNChunk - 1) / kAbsorbNChunk);
+  GemmParams g = g_in;
+  const int64_t n_abs = absorb_grid(g);
   const int64_t n_rope = rope_blocks(r);
   const int64_t r_pad = (n_rope + 31) / 32 * 32;
   const dim3 grid(static_cast<unsigned>(r_pad + n_abs));
@@ -354,13 +378,17 @@ hipError_t launch_rope_absorb(const GemmParams& g, const RopeParams& r, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_out_proj(const GemmParams& p, hipStream_t s) {
+hipError_t launch_out_proj(const GemmParams& p_in, hipStream_t s) {
+  GemmParams p = p_in;
   if (p.n == 0) return hipSuccess;
   if (p.dtype == 0) {
     const int64_t total = p.n * p.n_heads * p.d_v;
     hipLaunchKernelGGL(out_proj_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, p);
   } else {
-    const dim3 grid(static_cast<unsigned>(p.d_v / kOutRows * p.n_heads));
+    // token groups: enough workgroups to fill the chip (each loads its head's W_UV rows once)
+    const int64_t per_group = static_cast<int64_t>(p.d_v / kOutRows) * p.n_heads;
+    p.n_chunk = token_chunk(p.n, per_group, 512, (p.n + 63) / 64 * 64);
+    const dim3 grid(static_cast<unsigned>(per_group * ((p.n + p.n_chunk - 1) / p.n_chunk)));
     if (p.d_latent <= 256)
       hipLaunchKernelGGL((out_proj_bf16_kernel<float, 256>), grid, dim3(256), 0, s, p);
     else
