@@ -34,8 +34,13 @@ KERNEL_SRC = os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "attn_bf16.hip
 MHA_SRC = os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "mha.hip")
 
 
-def kernel_hash(src: str = KERNEL_SRC) -> str:
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+GEMM_SRC = os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "gemm.hip")
+
+
+def kernel_hash(src=KERNEL_SRC) -> str:
+    """sha256[:16] of a kernel source, or of several sources concatenated in order."""
+    srcs = [src] if isinstance(src, str) else list(src)
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()[:16]
 
 
 def decode_bytes(seq_lens, n_heads=128, d_latent=512, d_rope=64, elt=2, q_elt=2) -> int:
@@ -46,6 +51,16 @@ def decode_bytes(seq_lens, n_heads=128, d_latent=512, d_rope=64, elt=2, q_elt=2)
     t = np.asarray(seq_lens, np.int64)
     per_q = n_heads * (d_latent + d_rope) * q_elt + n_heads * d_latent * 4
     return int(np.sum(row * t + per_q + 4 * ((t + 63) // 64)))
+
+
+def decode_proj_bytes(seq_lens, n_heads=128, d_latent=512, d_rope=64, d_v=128, elt=2, q_elt=2) -> int:
+    """Algorithmic HBM bytes of one mla_decode_proj call: cache rows (elt bytes an
+    element) read once, the query read once, W_UV (elt bytes) read once, the float32
+    layer output written once, the block table read once (obar is not an output)."""
+    row = (d_latent + d_rope) * elt
+    t = np.asarray(seq_lens, np.int64)
+    per_q = n_heads * (d_latent + d_rope) * q_elt + n_heads * d_v * 4
+    return int(np.sum(row * t + per_q + 4 * ((t + 63) // 64))) + n_heads * d_v * d_latent * elt
 
 
 def per_head_decode_bytes(seq_lens, n_heads=16, d_latent=256, d_rope=32, q_elt=2) -> int:
@@ -218,6 +233,9 @@ def main():
     ap.add_argument("--cache-layout", default="shared", choices=["shared", "per-head"],
                     help="per-head: decode over a cache with one position key per head (16 heads, d_c 256, "
                          "d_r 32, 768-element rows; 64 sequences x 4096 tokens)")
+    ap.add_argument("--out-proj", default="fused", choices=["fused", "separate"],
+                    help="decode: attention then the split merge and output absorption in one launch "
+                         "(mla_decode_proj), or mla_decode + mla_out_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="run one plain 256 MiB copy kernel before timing (HBM counter calibration under rocprofv3)")
@@ -294,6 +312,16 @@ def main():
     sh = stream.cuda_stream
     events = DeviceEvents(4)
     front_bytes = 0
+    fused = args.out_proj == "fused"
+
+    def decode_roofline():
+        """(name, algorithmic bytes) of the measured decode call."""
+        if fused:
+            return ("mla_decode_proj (split attention + merge with output absorption)",
+                    decode_proj_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope, s.d_v,
+                                      4 if dt == torch.float32 else 2, q_elt))
+        return ("mla_decode (split attention + merge)",
+                decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope, 4 if dt == torch.float32 else 2, q_elt))
     if per_head:
         last = case.row_offsets + np.maximum(case.seq_lens - 1, 0)
         new_lat, new_kr = dev(case.c_rows[last]), dev(case.kr_rows[last])
@@ -334,19 +362,26 @@ def main():
             st.kv(h_new, w_dkv, w_kr)
             st.query(h_new, w_dq, w_up, w_qr, w_uk)
 
-        def call(i):
-            inner = steps[i % len(steps)].inner
-            B.decode(dims, inner.cache.data, inner.cache.block_table, inner.q_lat, inner.seq_lens,
-                     inner.seq_lens_host, inner.out_latent, inner.lse, inner.workspace)
+        if fused:
+            def call(i):
+                steps[i % len(steps)].inner.attend_proj(w_uv)
 
-        def step(i):
-            front(i)
-            call(i)
-            inner = steps[i % len(steps)].inner
-            B.out_proj(dims, inner.out_latent, w_uv, inner.out)
+            def step(i):
+                front(i)
+                call(i)
+        else:
+            def call(i):
+                inner = steps[i % len(steps)].inner
+                B.decode(dims, inner.cache.data, inner.cache.block_table, inner.q_lat, inner.seq_lens,
+                         inner.seq_lens_host, inner.out_latent, inner.lse, inner.workspace)
+
+            def step(i):
+                front(i)
+                call(i)
+                inner = steps[i % len(steps)].inner
+                B.out_proj(dims, inner.out_latent, w_uv, inner.out)
         tokens_per_step = case.batch
-        kernel_name = "mla_decode (split attention + merge)"
-        algo = decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope, 4 if dt == torch.float32 else 2, q_elt)
+        kernel_name, algo = decode_roofline()
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
     elif case.kind == "decode":
         steps = [mla.DecodeStep(dims, c, torch.from_numpy(case.seq_lens)) for c in caches]
@@ -355,18 +390,21 @@ def main():
 
         def call(i):
             st = steps[i % len(steps)]
-            B.decode(dims, st.cache.data, st.cache.block_table, st.q_lat, st.seq_lens, st.seq_lens_host,
-                     st.out_latent, st.lse, st.workspace)
+            if fused:
+                st.attend_proj(w_uv)
+            else:
+                B.decode(dims, st.cache.data, st.cache.block_table, st.q_lat, st.seq_lens, st.seq_lens_host,
+                         st.out_latent, st.lse, st.workspace)
 
         def step(i):
             st = steps[i % len(steps)]
             B.rope_absorb_q(dims, st.cache.data, st.cache.block_table, q_nope, w_uk, q_rope, st.q_pos, st.q_lat,
                             new_lat, new_kr, st.kv_seq, st.q_pos)
             call(i)
-            B.out_proj(dims, st.out_latent, w_uv, st.out)
+            if not fused:
+                B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = case.batch
-        kernel_name = "mla_decode (split attention + merge)"
-        algo = decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope, 4 if dt == torch.float32 else 2, q_elt)
+        kernel_name, algo = decode_roofline()
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
     elif args.prefill_form == "materialised":
         steps = [mla.PrefillStep(dims, c, torch.from_numpy(case.cu_q), torch.from_numpy(case.q_start))
@@ -433,6 +471,8 @@ def main():
     achieved = algo / (kern_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
     if per_head:
         traffic = load_traffic("per_head", os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "perhead.hip"))
+    elif case.kind == "decode" and fused:
+        traffic = load_traffic(args.config + "_proj", [KERNEL_SRC, GEMM_SRC])
     elif case.kind == "decode" or args.prefill_form == "absorbed":
         traffic = load_traffic(args.config)
     else:
@@ -457,7 +497,9 @@ def main():
                    "cache_layout": args.cache_layout,
                    "step": ("cache_write_per_head + rope_absorb_q + decode_per_head + out_proj" if per_head
                             else "rope_apply + prefill_mha" if case.kind != "decode" and args.prefill_form == "materialised"
-                            else f"kv_project + q_project ({args.front}) + decode + out_proj" if args.front != "none"
+                            else (f"kv_project + q_project ({args.front}) + "
+                                  + ("decode_proj" if fused else "decode + out_proj")) if args.front != "none"
+                            else "rope_absorb_q + decode_proj" if case.kind == "decode" and fused
                             else "rope_absorb_q + decode/prefill + out_proj")},
         "roofline": {"kernel": kernel_name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic, "algorithmic_per_launch": algo,

@@ -184,6 +184,40 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
                       void* out_latent, float* lse, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Bytes of workspace mla_decode_proj needs for this batch: on bf16 caches a
+ * partial slot (and its lse) for every work item of the split plan, split or
+ * not; on float32 caches the float32 obar [batch, H, d_latent].  0 when batch
+ * is 0, when no sequence has a token (bf16), or when the arguments are
+ * rejected.  seq_lens_host as for mla_decode_workspace_size. */
+size_t mla_decode_proj_workspace_size(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host);
+
+/* mla_decode_proj -- mla_decode followed by mla_out_proj in one call, the
+ * layer's decode output ("AI decoupled RoPE MLA", recap section: the output
+ * is W^UV applied to sum_t alpha_t c_t; "Multi-Head Latent Attention", "Why
+ * this matters on a GPU").  The split merge and the output absorption run as
+ * one launch: obar goes from the merged partials to the projection through
+ * on-chip memory and is not written.
+ *   q_lat, seq_lens, seq_lens_host, batch, cache as for mla_decode;  w_uv
+ *   [H, d_v, d_latent] in the cache dtype;  out [batch, H, d_v] float32 gets
+ *   W_UV[h] obar[b, h, :];  lse [batch, H] (float32, may be NULL) as for
+ *   mla_decode.  d_v must be 128 (MLA_ERR_UNSUPPORTED otherwise).  A sequence
+ *   of length 0 yields out = 0, lse = -inf.
+ * workspace: device memory of at least mla_decode_proj_workspace_size()
+ * bytes (may be NULL when that is 0); its contents on entry do not matter.
+ * On bf16 caches every work item leaves a partial, so a sequence of one item
+ * also takes the merge; for a sequence of several items the merge and the
+ * projection are mla_decode's and mla_out_proj's arithmetic in the same
+ * order, so out and lse equal those two calls' bit for bit; for a sequence of
+ * one item obar carries its partial's rounding (float16 scaled per 128
+ * columns at d_latent = 512, float32 otherwise).  Bitwise reproducible and
+ * independent of which physical pages hold which positions, as mla_decode.
+ * Errors: those of mla_decode and mla_out_proj; nothing is launched on a
+ * failed check. */
+mla_status mla_decode_proj(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                           const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch,
+                           const void* w_uv, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* mla_decode_noalloc -- mla_decode for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation.  The same computation, arguments, results and errors as

@@ -250,6 +250,15 @@ size_t workspace_bytes(const mla_dims* d, const Plan& p) {
   return partial_bytes(d, p) + static_cast<size_t>(p.n_items) * d->n_heads * sizeof(float);
 }
 
+// Workspace of mla_decode_proj: a partial slot for every work item, split or
+// not (the fused merge reads only partials), laid out as workspace_bytes';
+// on float32 caches the float32 obar [batch, H, d_latent] instead.
+size_t proj_workspace_bytes(const mla_dims* d, const Plan& p, int32_t batch) {
+  if (d->dtype == MLA_F32) return align_ws(static_cast<size_t>(batch) * d->n_heads * d->d_latent * sizeof(float));
+  if (p.n_items == 0) return 0;
+  return partial_bytes(d, p) + static_cast<size_t>(p.n_items) * d->n_heads * sizeof(float);
+}
+
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // Fixed device scratch of mla_decode_noalloc: the split partials of a decode
@@ -284,7 +293,8 @@ mla_status noalloc_scratch(void** ptr) {
 
 mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat, const int32_t* seq_lens,
                          const int32_t* seq_lens_host, int32_t batch, void* out_latent, float* lse, void* workspace,
-                         size_t ws_bytes, void* stream, bool fixed_scratch);
+                         size_t ws_bytes, void* stream, bool fixed_scratch, const void* w_uv = nullptr,
+                         float* out = nullptr);
 
 }  // namespace
 
@@ -442,6 +452,20 @@ mla_status mla_decode(const mla_dims* dims, const mla_paged_cache* cache, const 
                        stream, false);
 }
 
+size_t mla_decode_proj_workspace_size(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host) {
+  if (check_dims(dims) != MLA_OK || batch <= 0 || seq_lens_host == nullptr) return 0;
+  return proj_workspace_bytes(dims, make_plan(dims, batch, seq_lens_host), batch);
+}
+
+mla_status mla_decode_proj(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                           const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, const void* w_uv,
+                           void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (w_uv == nullptr || out == nullptr) return fail(MLA_ERR_INVALID_ARG, "w_uv and out must be non-NULL");
+  return decode_common(dims, cache, q_lat, seq_lens, seq_lens_host, batch, nullptr, lse, workspace, ws_bytes,
+                       stream, false, w_uv, static_cast<float*>(out));
+}
+
 mla_status mla_decode_noalloc(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
                               const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* out_latent,
                               float* lse, void* stream) {
@@ -458,7 +482,7 @@ namespace {
 
 mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat, const int32_t* seq_lens,
                          const int32_t* seq_lens_host, int32_t batch, void* out_latent, float* lse, void* workspace,
-                         size_t ws_bytes, void* stream, bool fixed_scratch) {
+                         size_t ws_bytes, void* stream, bool fixed_scratch, const void* w_uv, float* out) {
   MLA_TRY(check_dims(dims));
   MLA_TRY(check_attn_shape(dims));
   MLA_TRY(check_cache(cache));
@@ -466,8 +490,12 @@ mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, con
   if (batch == 0) return MLA_OK;
   if (batch > cache->num_seqs)
     return fail(MLA_ERR_INVALID_ARG, "batch (%d) exceeds the block table's rows (%d)", batch, cache->num_seqs);
-  if (q_lat == nullptr || seq_lens == nullptr || seq_lens_host == nullptr || out_latent == nullptr)
-    return fail(MLA_ERR_INVALID_ARG, "q_lat, seq_lens, seq_lens_host and out_latent must be non-NULL");
+  const bool fused = w_uv != nullptr || out != nullptr;  // mla_decode_proj
+  if (q_lat == nullptr || seq_lens == nullptr || seq_lens_host == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "q_lat, seq_lens and seq_lens_host must be non-NULL");
+  if (!fused && out_latent == nullptr) return fail(MLA_ERR_INVALID_ARG, "out_latent must be non-NULL");
+  if (fused && (w_uv == nullptr || out == nullptr)) return fail(MLA_ERR_INVALID_ARG, "w_uv and out must be non-NULL");
+  if (fused && dims->d_v != 128) return fail(MLA_ERR_UNSUPPORTED, "mla_decode_proj needs d_v = 128");
   for (int b = 0; b < batch; ++b) {
     if (seq_lens_host[b] < 0 ||
         static_cast<int64_t>(seq_lens_host[b]) > static_cast<int64_t>(cache->max_pages_per_seq) * mla::kPage)
@@ -485,12 +513,21 @@ mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, con
   p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
   p.seq_lens = seq_lens; p.batch = batch; p.out_latent = out_latent; p.lse = lse;
   hipStream_t s = as_stream(stream);
-  if (dims->dtype == MLA_F32) {
-    const hipError_t e = mla::launch_decode_f32(p, s);
-    return e == hipSuccess ? MLA_OK : hip_fail(e, "decode launch");
-  }
   const Plan plan = make_plan(dims, batch, seq_lens_host);
-  const size_t need = workspace_bytes(dims, plan);
+  const size_t need = fused ? proj_workspace_bytes(dims, plan, batch) : workspace_bytes(dims, plan);
+  if (fused && need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "decode_proj needs %zu bytes of workspace, got %zu", need,
+                workspace ? ws_bytes : 0);
+  if (dims->dtype == MLA_F32) {
+    // float32 path: obar goes through the workspace to the output absorption
+    if (fused) p.out_latent = workspace;
+    hipError_t e = mla::launch_decode_f32(p, s);
+    if (e != hipSuccess || !fused) return e == hipSuccess ? MLA_OK : hip_fail(e, "decode launch");
+    const mla::GemmParams g{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
+                            dims->work_dtype, workspace, w_uv, out, batch};
+    e = mla::launch_out_proj(g, s);
+    return e == hipSuccess ? MLA_OK : hip_fail(e, "out_proj launch");
+  }
   if (fixed_scratch && need > ws_bytes)
     return fail(MLA_ERR_WORKSPACE,
                 "mla_decode_noalloc: this batch needs %zu bytes of split partials, more than its fixed scratch of %zu "
@@ -502,6 +539,7 @@ mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, con
   p.n_full = plan.n_full;
   p.n_items = plan.n_items;
   p.n_head_chunks = 1;
+  p.all_partials = fused ? 1 : 0;
   if (need > 0) {
     p.ws_o = static_cast<float*>(workspace);
     p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + partial_bytes(dims, plan));
@@ -514,6 +552,12 @@ mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, con
   }
   hipError_t e = mla::launch_decode_bf16(p, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (fused) {
+    const mla::GemmParams g{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
+                            dims->work_dtype, nullptr, w_uv, out, batch};
+    e = mla::launch_merge_proj(g, p, s);
+    return e == hipSuccess ? MLA_OK : hip_fail(e, "merge + output absorption launch");
+  }
   if (plan.needs_merge) {
     e = mla::launch_merge(p, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");

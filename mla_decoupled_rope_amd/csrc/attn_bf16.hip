@@ -316,7 +316,7 @@ __global__ void __launch_bounds__(64 * HG * TW, 1) attn_bf16_kernel(AttnParams p
     const int pages = (key_end + kPage - 1) / kPage;
     page_begin = __builtin_amdgcn_readfirstlane(it.s) * p.split_pages;
     page_end = min(pages, page_begin + p.split_pages);
-    final_out = __builtin_amdgcn_readfirstlane(it.n_s) == 1;
+    final_out = !p.all_partials && __builtin_amdgcn_readfirstlane(it.n_s) == 1;
     slot = __builtin_amdgcn_readfirstlane(it.slot);
     row_base = static_cast<int64_t>(b) * H + hc * ROWS;
     row_count = H - hc * ROWS;

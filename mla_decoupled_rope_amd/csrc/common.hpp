@@ -145,6 +145,9 @@ struct AttnParams {
   // every stored value is below 1 in magnitude), e in ws_exp [slot, H, d_latent / 128].
   float* ws_o; float* ws_lse;
   int half_partials; int32_t* ws_exp;
+  // every decode work item writes a partial, a sequence of one item included
+  // (for the fused merge and output absorption, which reads only partials)
+  int all_partials;
 };
 
 // Materialised-form prefill: per-head keys and values up-projected from the
@@ -175,6 +178,7 @@ hipError_t launch_out_proj(const GemmParams& p, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnParams& p, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t s);
 hipError_t launch_merge(const AttnParams& p, hipStream_t s);
+hipError_t launch_merge_proj(const GemmParams& g, const AttnParams& a, hipStream_t s);
 hipError_t launch_decode_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_prefill_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_mha_prefill(const MhaParams& p, hipStream_t s);

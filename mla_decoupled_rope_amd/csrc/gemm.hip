@@ -17,6 +17,7 @@
 //    layer output is float32).
 // float32 path: one thread per output element, float32 accumulation.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "decode_items.hpp"
@@ -303,6 +304,160 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(GemmParams p) {
   }
 }
 
+// K4 + K6 in one launch: the split merge of a decode call and the output
+// absorption, o[b, h, :] = W_UV[h] obar[b, h, :], where obar[b, h, :] is the
+// lse-weighted sum of the sequence's split partials (every work item of the
+// call left one, a sequence of one item included).  A workgroup of 8 waves
+// takes one head and 16 sequences:
+//  * 32 threads per sequence merge its row, DC/32 columns each, split by
+//    split in index order with the arithmetic of merge_kernel, so obar has
+//    the bits mla_decode's merge gives it;
+//  * the merged rows go to LDS as a two-term bf16 split (as out_proj stages
+//    a float32 obar) and never to HBM;
+//  * wave w multiplies rows 16w .. 16w+15 of W_UV[h] with them: the MFMA
+//    sequence of out_proj_bf16_kernel, so o has the bits mla_out_proj gives
+//    it.  Two workgroups fit a CU (128 registers a lane).
+// Work index = head * (sequence groups) + group; through xcd_local the groups
+// of a head share an XCD and so W_UV[h] comes from HBM once per run of four.
+constexpr int kMpSeqs = 16;   // sequences per workgroup
+constexpr int kMpRows = 128;  // d_v rows per workgroup: 8 waves x 16
+template <int DC, bool HALF>
+__global__ void __launch_bounds__(512, 4) merge_proj_kernel(GemmParams g, AttnParams a) {
+  constexpr int LSTRIDE = DC + 8;  // bf16 elements per staged row
+  constexpr int CPT = DC / 32;     // merged columns per thread
+  constexpr int U = 4;             // splits per load round
+  __shared__ __attribute__((aligned(16))) bf16_t ob_lds[2][kMpSeqs * LSTRIDE];
+  const int H = g.n_heads, DV = g.d_v;
+  const int64_t n_grp = (g.n + kMpSeqs - 1) / kMpSeqs;
+  const int64_t wk = xcd_local(blockIdx.x, gridDim.x);
+  const int h = static_cast<int>(wk / n_grp);
+  const int64_t s_begin = (wk % n_grp) * kMpSeqs;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q16 = lane >> 4, r16 = lane & 15;
+  // this thread's sequence and columns; its split count and first slot
+  const int sq = tid >> 5, l32 = tid & 31;
+  const int col = l32 * CPT;
+  const int64_t b = s_begin + sq;
+  const int64_t s_end = min(g.n, s_begin + kMpSeqs);
+  const int L = a.split_pages;
+  int ns = 0;
+  int64_t base = 0;
+  for (int64_t b0 = 0; b0 < s_end; b0 += 64) {
+    const int64_t bb = b0 + lane;
+    int t = bb < g.n ? a.seq_lens[bb] : 0;
+    t = t < 0 ? 0 : t;
+    const int pages = (t + kPage - 1) / kPage;
+    const int nsl = pages / L + ((pages % L) != 0 ? 1 : 0);
+    const int incl = wave_incl_scan(nsl);
+    const int64_t rel = b - b0;
+    const int src = static_cast<int>(rel < 0 ? 0 : rel > 63 ? 63 : rel);
+    const int ns_src = __shfl(nsl, src, 64), incl_src = __shfl(incl, src, 64), total = __shfl(incl, 63, 64);
+    if (rel >= 64) {
+      base += total;
+    } else if (rel >= 0) {
+      ns = ns_src;
+      base += incl_src - ns_src;
+    }
+  }
+  if (b >= g.n || base + ns > a.n_items) ns = 0;
+  const int64_t row0 = base * H + h;  // split s at partial row row0 + s * H
+  const float* lse_s = a.ws_lse + row0;
+  const float* part = a.ws_o + row0 * DC + col;
+  const _Float16* hpart = reinterpret_cast<const _Float16*>(a.ws_o) + row0 * DC + col;
+  const int32_t* pexp = HALF ? a.ws_exp + row0 * (DC / 128) + col / 128 : nullptr;
+  // a round's partials stay in their stored type until used (float16 ones
+  // take half the registers of their float32 values)
+  using PT = typename std::conditional<HALF, _Float16, float>::type;
+  PT v[U][CPT];
+  int vex[U];
+  float wl[U];
+  auto load_round = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < ns) {
+        const int64_t so = static_cast<int64_t>(s0 + u) * H;
+        if constexpr (HALF) {
+          __builtin_memcpy(v[u], hpart + so * DC, CPT * sizeof(_Float16));
+          vex[u] = pexp[so * (DC / 128)];
+        } else {
+          __builtin_memcpy(v[u], part + so * DC, CPT * sizeof(float));
+        }
+        wl[u] = lse_s[so];
+      } else {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) v[u][i] = 0;
+        vex[u] = 0;
+        wl[u] = -INFINITY;
+      }
+    }
+  };
+  load_round(0);
+  // max of the splits' lse: the sequence's 32 threads take splits side by side
+  float m = -INFINITY;
+  for (int s0 = 0; s0 < ns; s0 += 32)
+    if (s0 + l32 < ns) m = fmaxf(m, lse_s[static_cast<int64_t>(s0 + l32) * H]);
+#pragma unroll
+  for (int k = 1; k < 32; k <<= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
+  float acc[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) acc[i] = 0.f;
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int s0 = 0; s0 < ns; s0 += U) {
+      if (s0 > 0) load_round(s0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wu = __expf(wl[u] - m);
+        wsum += wu;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          const float x = HALF ? ldexpf(static_cast<float>(v[u][i]), vex[u]) : static_cast<float>(v[u][i]);
+          acc[i] = fmaf(wu, x, acc[i]);
+        }
+      }
+    }
+  }
+  // W_UV[h] rows v0 + r16, all of d_c, as MFMA A fragments: loaded after the
+  // merge (so the two sets of registers are not live together), their
+  // latency under the staging below and the other workgroup on the CU
+  const int v0 = wave * 16;
+  const bf16_t* w = static_cast<const bf16_t*>(g.w) + (static_cast<int64_t>(h) * DV + v0 + r16) * DC + q16 * 8;
+  bf16x8 wa[DC / 32];
+#pragma unroll
+  for (int k = 0; k < DC / 32; ++k) wa[k] = load8(w + k * 32);
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if (a.lse != nullptr && l32 == 0 && b < g.n) a.lse[b * H + h] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+  // stage obar (zeros for rows past the batch) as hi + lo.  No contraction
+  // here: x must be rounded to float32 before lo = x - hi, as when out_proj
+  // reads a stored obar (an fma would take lo from the unrounded product)
+#pragma unroll
+  for (int c8 = 0; c8 < CPT / 8; ++c8) {
+#pragma clang fp contract(off)
+    bf16x8 hi8, lo8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = acc[c8 * 8 + e] * inv;
+      const __bf16 hi = static_cast<__bf16>(x);
+      hi8[e] = hi;
+      lo8[e] = static_cast<__bf16>(x - static_cast<float>(hi));
+    }
+    *reinterpret_cast<bf16x8*>(&ob_lds[0][sq * LSTRIDE + col + c8 * 8]) = hi8;
+    *reinterpret_cast<bf16x8*>(&ob_lds[1][sq * LSTRIDE + col + c8 * 8]) = lo8;
+  }
+  __syncthreads();
+  f32x4 acc_o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < DC / 32; ++k)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&ob_lds[t][r16 * LSTRIDE + k * 32 + q16 * 8]);
+      acc_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[k], bv, acc_o, 0, 0, 0);
+    }
+  // D^T[v][n]: lane holds sequence s_begin + r16, rows v0 + 4 q16 .. + 3
+  if (s_begin + r16 < s_end)
+    *reinterpret_cast<f32x4*>(static_cast<float*>(g.out) + ((s_begin + r16) * H + h) * DV + v0 + 4 * q16) = acc_o;
+}
+
 __global__ void __launch_bounds__(256) absorb_f32_kernel(GemmParams p) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int DC = p.d_latent, DH = p.d_head, H = p.n_heads;
@@ -375,6 +530,21 @@ hipError_t launch_rope_absorb(const GemmParams& g_in, const RopeParams& r, hipSt
   else
     hipLaunchKernelGGL((rope_absorb_kernel<128, bf16_t, bf16_t>), grid, dim3(256), 0, s, g, r, n_rope, r_pad,
                        n_abs);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_proj(const GemmParams& g, const AttnParams& a, hipStream_t s) {
+  if (g.n == 0) return hipSuccess;
+  if (g.d_v != kMpRows) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(g.n_heads * ((g.n + kMpSeqs - 1) / kMpSeqs)));
+  if (g.d_latent == 512 && a.half_partials)
+    hipLaunchKernelGGL((merge_proj_kernel<512, true>), grid, dim3(512), 0, s, g, a);
+  else if (g.d_latent == 512)
+    hipLaunchKernelGGL((merge_proj_kernel<512, false>), grid, dim3(512), 0, s, g, a);
+  else if (g.d_latent == 256 && !a.half_partials)
+    hipLaunchKernelGGL((merge_proj_kernel<256, false>), grid, dim3(512), 0, s, g, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -96,6 +96,8 @@ class DecodeStep:
         self.lse = torch.empty((n, dims.n_heads), dtype=torch.float32, device=device)
         self.out = torch.empty((n, dims.n_heads, dims.d_v), dtype=torch.float32, device=device)
         self.workspace = B.decode_workspace(dims, self.seq_lens_host, device)
+        self.proj_ws_bytes = B.decode_proj_workspace_size(dims, self.seq_lens_host)
+        self.proj_workspace = None  # allocated on the first fused call
         self.kv_seq = torch.arange(n, dtype=torch.int32, device=device)
 
     def run(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
@@ -107,6 +109,23 @@ class DecodeStep:
         B.decode(d, self.cache.data, self.cache.block_table, self.q_lat, self.seq_lens, self.seq_lens_host,
                  self.out_latent, self.lse, self.workspace)
         B.out_proj(d, self.out_latent, w_uv, self.out)
+        return self.out
+
+    def attend_proj(self, w_uv):
+        """mla_decode_proj over q_lat: the layer output in self.out, lse in self.lse (obar is not formed)."""
+        if self.proj_workspace is None and self.proj_ws_bytes:
+            self.proj_workspace = torch.empty(self.proj_ws_bytes, dtype=torch.uint8, device=self.q_lat.device)
+        B.decode_proj(self.dims, self.cache.data, self.cache.block_table, self.q_lat, self.seq_lens,
+                      self.seq_lens_host, w_uv, self.out, self.lse, self.proj_workspace)
+
+    def run_fused(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
+        """As run(), with attention, the split merge and the output absorption through
+        mla_decode_proj: two launches after the query prologue instead of three."""
+        d = self.dims
+        B.rope_absorb_q(d, self.cache.data, self.cache.block_table, q_nope, w_uk, q_rope, self.q_pos, self.q_lat,
+                        new_latent, new_k_rope, self.kv_seq if new_latent is not None else None,
+                        self.q_pos if new_latent is not None else None)
+        self.attend_proj(w_uv)
         return self.out
 
 

@@ -65,9 +65,12 @@ def _worst(results, want, key):
     return max(f[0] for f in figs), max(f[1] for f in figs)
 
 
-def _decode_figures(case, prec, want=None, seqs=None, scales=None):
+def _decode_figures(case, prec, want=None, seqs=None, scales=None, fused=False):
+    """Worst over the split lengths of the model against the oracle; ``fused``: the
+    decode with the merge and output absorption in one launch (every range stored
+    as a partial)."""
     prec = _decode_prec(prec, case.shape)
-    kw = dict(prec)
+    kw = dict(prec, all_partials=True) if fused else dict(prec)
     if scales is not None:
         kw["position_scale"] = scales[1]
     want = want if want is not None else _oracle_decode(
@@ -262,6 +265,8 @@ RECIPES = {
     "tiny_decode_ragged": lambda: _decode_figures(cases.tiny_decode_ragged(), F32W),
     "dsv2_decode_ragged": lambda: _decode_figures(cases.dsv2_decode_ragged(), BF16),
     "decode_empty": lambda: _decode_figures(cases.decode_empty(), BF16),
+    "decode_proj_many": lambda: _decode_figures(cases.decode_proj_many(), BF16, seqs=cases.DECODE_PROJ_MANY_ROWS,
+                                                fused=True),
     "decode_overflow": lambda: _decode_figures(cases.decode_overflow(), BF16),
     "tiny_bf16_prefill": lambda: _prefill_figures(cases.tiny_prefill_short(), BF16),
     "tiny_bf16_decode": lambda: _decode_figures(cases.tiny_decode_short(), BF16),

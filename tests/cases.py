@@ -26,6 +26,16 @@ def decode_empty():
     return synth.direct_decode(synth.DSV2, "bf16", [0, 5, 0, 70], seed=47)
 
 
+def decode_proj_many():
+    """150 sequences of 0 .. 901 keys (several 64-sequence blocks, a ragged last group
+    of 16), shuffled pages: the fused decode and output absorption."""
+    lens = [(37 * i) % 900 + (i % 3) for i in range(150)]
+    return synth.direct_decode(synth.DSV2, "bf16", lens, seed=313, shuffle=True)
+
+
+DECODE_PROJ_MANY_ROWS = list(range(0, 150, 7))
+
+
 def decode_overflow():
     """Scores that climb by far more than 2^64 within one split (DeepSeek-V2 shape, 600 tokens).
 

@@ -97,7 +97,7 @@ def _q_cast(kind):
 
 def absorbed(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False, key_offset=0,
              q_lat="bf16", p="bf16", obar="bf16", split_keys=None, partial="bf16", key_cast="bf16",
-             position_scale=None, q_tilde=None):
+             position_scale=None, q_tilde=None, all_partials=False):
     """Absorbed attention (q~ . c_t + R_m q^R . R_t k^R_t) with the library's storage roundings.
 
     Arguments as ``oracle.attention.absorbed`` (kr [T, d_r] shared, or
@@ -106,7 +106,9 @@ def absorbed(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False
     as ``partial`` with its lse and merged in order, as the split decode does;
     None keeps one range.  ``q_tilde`` [N, H, d_c] replaces W_UK^T q^C (a
     query formed elsewhere, e.g. through a folded weight); it is cast like
-    q_lat.  Returns dict(o, obar, lse).
+    q_lat.  ``all_partials`` (the fused decode and output absorption) stores a
+    single range as ``partial`` too before obar is formed from it.  Returns
+    dict(o, obar, lse).
     """
     qc = np.asarray(qc, np.float64)
     c = np.asarray(c, np.float64)
@@ -166,6 +168,8 @@ def absorbed(qc, qr, q_pos, c, kr, w_uk, w_uv, scale, base=10000.0, causal=False
         lses.append(lse)
     if len(ranges) == 1:
         ob, lse = parts[0], lses[0]
+        if all_partials:
+            ob = _CAST[partial](ob)
     else:
         pc = _CAST[partial]
         lse_all = np.stack(lses)                                           # [S, N, H]

@@ -88,6 +88,56 @@ def test_decode_workspace_is_checked(monkeypatch):
     assert "workspace" in B.LIB.mla_last_error().decode()
 
 
+def status_of_decode_proj(d, batch=1, lens=(10,), w_uv=FAKE, out=FAKE, ws=None, ws_bytes=0):
+    cache = B.PagedCache(data=FAKE.value, num_pages=4, block_table=FAKE.value, num_seqs=4, max_pages_per_seq=4)
+    lens_host = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    return B.LIB.mla_decode_proj(ctypes.byref(d), ctypes.byref(cache), FAKE, FAKE, lens_host, batch, w_uv, out,
+                                 None, ws, ws_bytes, None)
+
+
+def test_decode_proj_validates():
+    """The fused decode + output absorption runs the checks of both calls before any launch."""
+    d = _dims()
+    assert status_of_decode_proj(d, w_uv=None) == 1
+    assert status_of_decode_proj(d, out=None) == 1
+    assert status_of_decode_proj(_dims(d_v=64)) == 2           # the fused kernel covers d_v = 128
+    assert status_of_decode_proj(_dims(n_heads=64)) == 2       # shapes decode does not take
+    assert status_of_decode_proj(d, batch=5, lens=(1, 1, 1, 1, 1)) == 1
+    assert status_of_decode_proj(d, lens=(300,)) == 1
+    assert status_of_decode_proj(d, batch=0) == 0
+    lens = (200,)
+    lens_host = (ctypes.c_int32 * 1)(*lens)
+    # a partial slot for every item, so even an unsplit sequence needs workspace
+    need = B.LIB.mla_decode_proj_workspace_size(ctypes.byref(d), 1, lens_host)
+    assert need > 0 and B.LIB.mla_decode_workspace_size(ctypes.byref(d), 1, lens_host) == 0
+    assert status_of_decode_proj(d, lens=lens) == 3
+    assert status_of_decode_proj(d, lens=lens, ws=FAKE, ws_bytes=need - 1) == 3
+    assert "workspace" in B.LIB.mla_last_error().decode()
+    # no tokens anywhere: no items, no workspace
+    assert B.LIB.mla_decode_proj_workspace_size(ctypes.byref(d), 2, (ctypes.c_int32 * 2)(0, 0)) == 0
+    # float32 caches: obar [batch, H, d_latent] float32 goes through the workspace
+    f = _dims(n_heads=16, d_latent=256, d_rope=32, dtype=B.MLA_F32, work_dtype=B.MLA_F32)
+    assert B.LIB.mla_decode_proj_workspace_size(ctypes.byref(f), 3, (ctypes.c_int32 * 3)(5, 0, 9)) == 3 * 16 * 256 * 4
+
+
+def test_every_export_has_a_ctypes_signature():
+    """Without argtypes ctypes passes a Python int as a C int, truncating 64-bit host
+    pointers: every exported function must declare its arguments."""
+    for name in B.EXPORTS:
+        assert getattr(B.LIB, name).argtypes is not None, f"{name} has no ctypes argtypes"
+
+
+def test_size_queries_take_host_tensors():
+    """The binding's size queries with real (64-bit address) host tensors."""
+    dims = mla.MLADims(128, 128, 128, 512, 64, dtype=torch.bfloat16, softmax_scale=0.0722,
+                       work_dtype=torch.bfloat16)
+    lens = torch.tensor([4096] * 64, dtype=torch.int32)
+    plain, fused = B.decode_workspace_size(dims, lens), B.decode_proj_workspace_size(dims, lens)
+    assert plain > 0 and fused == plain  # every sequence splits here: the same slots
+    short = torch.tensor([10, 20], dtype=torch.int32)  # one item each: no merge
+    assert B.decode_workspace_size(dims, short) == 0 < B.decode_proj_workspace_size(dims, short)
+
+
 def test_other_calls_validate():
     d = _dims()
     assert B.LIB.mla_absorb_q(ctypes.byref(d), None, FAKE, 3, FAKE, None) == 1

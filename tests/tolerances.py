@@ -39,6 +39,7 @@ MARGIN = 1.25
 MODEL = {
     "tiny_decode_ragged": {"o": (2.442e-03, 2.550e-04), "obar": (2.426e-03, 2.591e-04), "lse": (4.902e-04, 1.044e-04)},
     "dsv2_decode_ragged": {"o": (8.224e-03, 6.792e-04), "obar": (7.925e-03, 6.856e-04), "lse": (3.997e-03, 6.345e-04)},
+    "decode_proj_many": {"o": (2.960e-02, 2.149e-03), "obar": (3.823e-02, 2.146e-03), "lse": (1.854e-03, 2.952e-04)},
     "decode_empty": {"o": (2.074e-02, 1.650e-03), "obar": (2.642e-02, 1.664e-03), "lse": (2.936e-03, 7.642e-04)},
     "decode_overflow": {"o": (8.885e-03, 6.323e-04), "obar": (9.830e-03, 6.401e-04), "lse": (8.881e-02, 3.187e-02)},
     "tiny_bf16_prefill": {"o": (2.546e-02, 1.906e-03), "obar": (2.161e-02, 1.917e-03), "lse": (4.161e-03, 4.352e-04)},
