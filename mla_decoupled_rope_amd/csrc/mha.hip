@@ -50,6 +50,7 @@ namespace mla {
 namespace {
 
 constexpr int kDh = 128;   // d_head = d_v of the materialised heads
+constexpr int kUpPassHeads = 8;  // heads an XCD up-projects per pass over the keys
 constexpr int kBlk = 128;  // keys per up-projection tile, queries per attention block
 constexpr int kKeyTile = 32;
 constexpr int kBufWord3 = 0x00020000;  // raw buffer resource, 32-bit format (gfx9 family)
@@ -167,15 +168,22 @@ __global__ void __launch_bounds__(256, 1) upproj_kernel(MhaParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, kh = lane >> 5;
   // Placement: consecutive workgroups go to the 8 XCDs in turn; XCD x takes
-  // heads x, x + 8, ... so its heads' weights stay in its L2, and walks the
-  // key tiles with those heads innermost, so a latent tile is read by
-  // consecutive workgroups.
+  // heads x, x + 8, ... in passes of kUpPassHeads heads (their 2 MB of W_UK
+  // and W_UV stay in the XCD's 4 MB L2 beside the latent tiles in flight; all
+  // of its 16 heads' weights at once did not, and came back from memory for
+  // every key tile).  A pass walks the key tiles with its heads innermost, so
+  // a latent tile is read by consecutive workgroups, once per pass.
   const int H = p.n_heads;
   const int hpx = H / 8;
+  int hpp = hpx < kUpPassHeads ? hpx : kUpPassHeads;  // heads per pass on one XCD: a divisor of hpx
+  while (hpx % hpp != 0) --hpp;
   const int x = blockIdx.x;
   const int j8 = x >> 3;
-  const int h = (j8 % hpx) * 8 + (x & 7);
-  const SeqUnit su = find_unit<0>(p, j8 / hpx);
+  const int64_t per_pass = p.n_key_tiles * hpp;
+  const int pass = static_cast<int>(j8 / per_pass);
+  const int64_t rem = j8 % per_pass;
+  const int h = (pass * hpp + static_cast<int>(rem % hpp)) * 8 + (x & 7);
+  const SeqUnit su = find_unit<0>(p, rem / hpp);
   if (!su.ok) return;
   const int b = __builtin_amdgcn_readfirstlane(su.b);
   const int t0 = __builtin_amdgcn_readfirstlane(static_cast<int>(su.u)) * kUpKeys;
