@@ -63,14 +63,18 @@ def decode_proj_bytes(seq_lens, n_heads=128, d_latent=512, d_rope=64, d_v=128, e
     return int(np.sum(row * t + per_q + 4 * ((t + 63) // 64))) + n_heads * d_v * d_latent * elt
 
 
-def per_head_decode_bytes(seq_lens, n_heads=16, d_latent=256, d_rope=32, q_elt=2) -> int:
+def per_head_decode_bytes(seq_lens, n_heads=16, d_latent=256, d_rope=32, q_elt=2, d_v=None) -> int:
     """Algorithmic HBM bytes of one per-head-key decode call: bf16 rows of the latent
     and one position key per head read once, the query read once, the float32
-    latent output written once, the block table read once."""
+    latent output written once, the block table read once.  With d_v (the fused
+    mla_decode_per_head_proj): the float32 layer output in place of the latent
+    output, and W_UV (bf16) read once."""
     row = (d_latent + n_heads * d_rope) * 2
     t = np.asarray(seq_lens, np.int64)
-    per_q = n_heads * (d_latent + d_rope) * q_elt + n_heads * d_latent * 4
-    return int(np.sum(row * t + per_q + 4 * ((t + 63) // 64)))
+    out_w = d_latent if d_v is None else d_v
+    per_q = n_heads * (d_latent + d_rope) * q_elt + n_heads * out_w * 4
+    w = 0 if d_v is None else n_heads * d_v * d_latent * 2
+    return int(np.sum(row * t + per_q + 4 * ((t + 63) // 64))) + w
 
 
 def prefill_flops(case) -> float:
@@ -328,17 +332,25 @@ def main():
         kv_seq = torch.arange(case.batch, dtype=torch.int32, device="cuda")
 
         def call(i):
-            ph_steps[i % len(ph_steps)].attend()
+            if fused:
+                ph_steps[i % len(ph_steps)].attend_proj(w_uv)
+            else:
+                ph_steps[i % len(ph_steps)].attend()
 
         def step(i):
             st = ph_steps[i % len(ph_steps)]
             st.write(new_lat, new_kr, kv_seq, st.q_pos)
             B.rope_absorb_q(dims, None, None, q_nope, w_uk, q_rope, st.q_pos, st.q_lat)
             call(i)
-            B.out_proj(dims, st.out_latent, w_uv, st.out)
+            if not fused:
+                B.out_proj(dims, st.out_latent, w_uv, st.out)
         tokens_per_step = case.batch
-        kernel_name = "mla_decode_per_head (split attention + merge)"
-        algo = per_head_decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope, q_elt)
+        if fused:
+            kernel_name = "mla_decode_per_head_proj (split attention + merge with output absorption)"
+            algo = per_head_decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope, q_elt, d_v=s.d_v)
+        else:
+            kernel_name = "mla_decode_per_head (split attention + merge)"
+            algo = per_head_decode_bytes(case.seq_lens, s.n_heads, s.d_latent, s.d_rope, q_elt)
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
     elif case.kind == "decode" and args.front != "none":
         d_model, d_qlat = s.hidden, QUERY_LATENT
@@ -470,7 +482,9 @@ def main():
     events.close()
     achieved = algo / (kern_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
     if per_head:
-        traffic = load_traffic("per_head", os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "perhead.hip"))
+        ph_src = os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "perhead.hip")
+        traffic = (load_traffic("per_head_proj", [ph_src, GEMM_SRC]) if fused
+                   else load_traffic("per_head", ph_src))
     elif case.kind == "decode" and fused:
         traffic = load_traffic(args.config + "_proj", [KERNEL_SRC, GEMM_SRC])
     elif case.kind == "decode" or args.prefill_form == "absorbed":
@@ -495,7 +509,8 @@ def main():
                    "n_heads": s.n_heads, "d_latent": s.d_latent, "d_rope": s.d_rope, "page_size": s.page_size,
                    "cache_copies": len(caches), "score": "two-scale" if args.score == "two" else "one scale",
                    "cache_layout": args.cache_layout,
-                   "step": ("cache_write_per_head + rope_absorb_q + decode_per_head + out_proj" if per_head
+                   "step": (("cache_write_per_head + rope_absorb_q + decode_per_head_proj" if fused else
+                             "cache_write_per_head + rope_absorb_q + decode_per_head + out_proj") if per_head
                             else "rope_apply + prefill_mha" if case.kind != "decode" and args.prefill_form == "materialised"
                             else (f"kv_project + q_project ({args.front}) + "
                                   + ("decode_proj" if fused else "decode + out_proj")) if args.front != "none"

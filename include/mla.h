@@ -320,6 +320,17 @@ mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cach
                                const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* out_latent,
                                float* lse, void* workspace, size_t ws_bytes, void* stream);
 
+/* mla_decode_per_head_proj -- mla_decode_per_head followed by mla_out_proj,
+ * with the split merge and the output absorption in one launch, as
+ * mla_decode_proj is for the shared-key cache: out [batch, H, d_v] float32,
+ * lse [batch, H] or NULL; workspace of mla_decode_proj_workspace_size() bytes
+ * with the same dims and lengths.  Partials are float32 on this layout, so
+ * out and lse equal the two separate calls' bit for bit.  d_v must be 128. */
+mla_status mla_decode_per_head_proj(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                                    const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch,
+                                    const void* w_uv, void* out, float* lse, void* workspace, size_t ws_bytes,
+                                    void* stream);
+
 /* mla_out_proj -- output absorption ("AI decoupled RoPE MLA", recap section:
  * Attn_m = W^UV sum_t alpha_mt c_t).
  *   out[n, h, :] = W_UV[h] out_latent[n, h, :]

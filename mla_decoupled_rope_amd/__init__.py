@@ -8,7 +8,7 @@ Importing it without the built library raises ImportError.
 
 from .binding import (  # noqa: F401
     LIB, LIB_PATH, MLADims, MLAError, absorb_q, cache_write_per_head, decode, decode_noalloc, decode_per_head,
-    decode_plan, decode_proj, decode_proj_workspace, decode_proj_workspace_size,
+    decode_per_head_proj, decode_plan, decode_proj, decode_proj_workspace, decode_proj_workspace_size,
     decode_workspace, per_head_row,
     decode_workspace_size, fold_q_weights, front_workspace, front_workspace_size, kv_project, out_proj, prefill,
     prefill_mha, prefill_mha_workspace, prefill_mha_workspace_size, q_project, q_project_folded, rope_absorb_q,

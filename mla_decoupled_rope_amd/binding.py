@@ -67,6 +67,7 @@ def _load():
         "mla_fold_q_weights": [pd, i32, vp, vp, vp, vp],
         "mla_cache_write_per_head": [pd, pc, vp, vp, vp, vp, i64, vp],
         "mla_decode_per_head": [pd, pc, vp, vp, vp, i32, vp, vp, vp, sz, vp],
+        "mla_decode_per_head_proj": [pd, pc, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -95,7 +96,7 @@ EXPORTS = ("mla_rope_apply", "mla_absorb_q", "mla_rope_absorb_q", "mla_decode_wo
            "mla_out_proj", "mla_status_string", "mla_last_error", "mla_decode_plan",
            "mla_prefill_mha_workspace_size", "mla_prefill_mha", "mla_front_workspace_size", "mla_kv_project",
            "mla_q_project", "mla_q_project_folded", "mla_fold_q_weights", "mla_cache_write_per_head",
-           "mla_decode_per_head")
+           "mla_decode_per_head", "mla_decode_per_head_proj")
 
 
 def _check(status: int):
@@ -363,6 +364,28 @@ def decode_per_head(dims: MLADims, cache: torch.Tensor, block_table: torch.Tenso
     _check(LIB.mla_decode_per_head(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), seq_lens.data_ptr(),
                                    seq_lens_host.data_ptr(), batch, out_latent.data_ptr(), _ptr(lse),
                                    _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
+
+
+def decode_per_head_proj(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat: torch.Tensor,
+                         seq_lens: torch.Tensor, seq_lens_host: torch.Tensor, w_uv: torch.Tensor, out: torch.Tensor,
+                         lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> None:
+    """mla_decode_per_head_proj: decode over per-head position keys, then the split merge
+    and the output absorption in one launch (workspace of decode_proj_workspace_size)."""
+    batch = seq_lens_host.numel()
+    cstruct = _cache(dims, cache, block_table, per_head_row(dims))
+    _dev(q_lat, "q_lat", dims.wdtype, (batch, dims.n_heads, dims.row))
+    _dev(seq_lens, "seq_lens", torch.int32, (batch,))
+    _host_i32(seq_lens_host, "seq_lens_host")
+    _dev(w_uv, "w_uv", dims.dtype, (dims.n_heads, dims.d_v, dims.d_latent))
+    _dev(out, "out", torch.float32, (batch, dims.n_heads, dims.d_v))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (batch, dims.n_heads))
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+    d = dims.c()
+    _check(LIB.mla_decode_per_head_proj(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), seq_lens.data_ptr(),
+                                        seq_lens_host.data_ptr(), batch, w_uv.data_ptr(), out.data_ptr(), _ptr(lse),
+                                        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
 
 
 def prefill(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat: torch.Tensor,

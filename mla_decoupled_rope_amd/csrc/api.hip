@@ -607,10 +607,14 @@ mla_status mla_cache_write_per_head(const mla_dims* dims, const mla_paged_cache*
   return e == hipSuccess ? MLA_OK : hip_fail(e, "per-head cache write launch");
 }
 
-mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
-                               const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* out_latent,
-                               float* lse, void* workspace, size_t ws_bytes, void* stream) {
-  g_err.clear();
+namespace {
+
+// mla_decode_per_head, or with w_uv and out (mla_decode_per_head_proj) the
+// fused merge and output absorption in place of the merge
+mla_status per_head_common(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                           const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* out_latent,
+                           float* lse, void* workspace, size_t ws_bytes, void* stream, const void* w_uv, float* out) {
+  const bool fused = w_uv != nullptr || out != nullptr;
   MLA_TRY(check_dims(dims));
   MLA_TRY(check_per_head_shape(dims));
   MLA_TRY(check_cache(cache));
@@ -618,8 +622,11 @@ mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cach
   if (batch == 0) return MLA_OK;
   if (batch > cache->num_seqs)
     return fail(MLA_ERR_INVALID_ARG, "batch (%d) exceeds the block table's rows (%d)", batch, cache->num_seqs);
-  if (q_lat == nullptr || seq_lens == nullptr || seq_lens_host == nullptr || out_latent == nullptr)
-    return fail(MLA_ERR_INVALID_ARG, "q_lat, seq_lens, seq_lens_host and out_latent must be non-NULL");
+  if (q_lat == nullptr || seq_lens == nullptr || seq_lens_host == nullptr)
+    return fail(MLA_ERR_INVALID_ARG, "q_lat, seq_lens and seq_lens_host must be non-NULL");
+  if (!fused && out_latent == nullptr) return fail(MLA_ERR_INVALID_ARG, "out_latent must be non-NULL");
+  if (fused && (w_uv == nullptr || out == nullptr)) return fail(MLA_ERR_INVALID_ARG, "w_uv and out must be non-NULL");
+  if (fused && dims->d_v != 128) return fail(MLA_ERR_UNSUPPORTED, "the fused output absorption needs d_v = 128");
   for (int b = 0; b < batch; ++b) {
     if (seq_lens_host[b] < 0 ||
         static_cast<int64_t>(seq_lens_host[b]) > static_cast<int64_t>(cache->max_pages_per_seq) * mla::kPage)
@@ -629,7 +636,7 @@ mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cach
       return fail(MLA_ERR_INVALID_ARG, "sequence %d has tokens but the cache has no pages", b);
   }
   const Plan plan = make_plan(dims, batch, seq_lens_host);
-  const size_t need = workspace_bytes(dims, plan);
+  const size_t need = fused ? proj_workspace_bytes(dims, plan, batch) : workspace_bytes(dims, plan);
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(MLA_ERR_WORKSPACE, "decode needs %zu bytes of workspace, got %zu", need, workspace ? ws_bytes : 0);
   if (plan.n_items > (1LL << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
@@ -642,6 +649,7 @@ mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cach
   p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
   p.seq_lens = seq_lens; p.batch = batch; p.out_latent = out_latent; p.lse = lse;
   p.split_pages = plan.split_pages; p.n_full = plan.n_full; p.n_items = plan.n_items; p.n_head_chunks = 1;
+  p.all_partials = fused ? 1 : 0;
   if (need > 0) {
     p.ws_o = static_cast<float*>(workspace);
     p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + partial_bytes(dims, plan));
@@ -649,11 +657,37 @@ mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cach
   const hipStream_t s = as_stream(stream);
   hipError_t e = mla::launch_perhead_decode(p, s);
   if (e != hipSuccess) return hip_fail(e, "per-head decode launch");
+  if (fused) {
+    const mla::GemmParams g{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
+                            dims->work_dtype, nullptr, w_uv, out, batch};
+    e = mla::launch_merge_proj(g, p, s);
+    return e == hipSuccess ? MLA_OK : hip_fail(e, "merge + output absorption launch");
+  }
   if (plan.needs_merge) {
     e = mla::launch_merge(p, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return MLA_OK;
+}
+
+}  // namespace
+
+mla_status mla_decode_per_head(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                               const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* out_latent,
+                               float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  return per_head_common(dims, cache, q_lat, seq_lens, seq_lens_host, batch, out_latent, lse, workspace, ws_bytes,
+                         stream, nullptr, nullptr);
+}
+
+mla_status mla_decode_per_head_proj(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                                    const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch,
+                                    const void* w_uv, void* out, float* lse, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  g_err.clear();
+  if (w_uv == nullptr || out == nullptr) return fail(MLA_ERR_INVALID_ARG, "w_uv and out must be non-NULL");
+  return per_head_common(dims, cache, q_lat, seq_lens, seq_lens_host, batch, nullptr, lse, workspace, ws_bytes,
+                         stream, w_uv, static_cast<float*>(out));
 }
 
 mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat, const int32_t* cu_q,

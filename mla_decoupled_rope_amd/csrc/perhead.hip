@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(256, 1) perhead_decode_kernel(AttnParams p) {
   const int pages = (key_end + kPage - 1) / kPage;
   const int page_begin = __builtin_amdgcn_readfirstlane(it.s) * p.split_pages;
   const int page_end = min(pages, page_begin + p.split_pages);
-  const bool final_out = __builtin_amdgcn_readfirstlane(it.n_s) == 1;
+  const bool final_out = !p.all_partials && __builtin_amdgcn_readfirstlane(it.n_s) == 1;
   const int slot = __builtin_amdgcn_readfirstlane(it.slot);
 
   // ---- query fragments (MFMA B operand: head r16, k = 8 q16 .. 8 q16 + 7 of a

@@ -149,6 +149,8 @@ class PerHeadDecodeStep:
         self.lse = torch.empty((n, dims.n_heads), dtype=torch.float32, device=device)
         self.out = torch.empty((n, dims.n_heads, dims.d_v), dtype=torch.float32, device=device)
         self.workspace = B.decode_workspace(dims, self.seq_lens_host, device)
+        self.proj_ws_bytes = B.decode_proj_workspace_size(dims, self.seq_lens_host)
+        self.proj_workspace = None  # allocated on the first fused call
 
     def write(self, kv_latent, k_rope, kv_seq, kv_pos):
         """Cache rows [c | R_t k^R_{t,0} | ... ] for tokens (kv_seq, kv_pos); k_rope [n, H, d_r]."""
@@ -157,6 +159,20 @@ class PerHeadDecodeStep:
     def attend(self):
         B.decode_per_head(self.dims, self.cache, self.block_table, self.q_lat, self.seq_lens, self.seq_lens_host,
                           self.out_latent, self.lse, self.workspace)
+
+    def attend_proj(self, w_uv):
+        """mla_decode_per_head_proj over q_lat: the layer output in self.out, lse in self.lse."""
+        if self.proj_workspace is None and self.proj_ws_bytes:
+            self.proj_workspace = torch.empty(self.proj_ws_bytes, dtype=torch.uint8, device=self.q_lat.device)
+        B.decode_per_head_proj(self.dims, self.cache, self.block_table, self.q_lat, self.seq_lens,
+                               self.seq_lens_host, w_uv, self.out, self.lse, self.proj_workspace)
+
+    def run_fused(self, q_nope, q_rope, w_uk, w_uv):
+        """As run(), with attention, the split merge and the output absorption through
+        mla_decode_per_head_proj."""
+        B.rope_absorb_q(self.dims, None, None, q_nope, w_uk, q_rope, self.q_pos, self.q_lat)
+        self.attend_proj(w_uv)
+        return self.out
 
     def run(self, q_nope, q_rope, w_uk, w_uv):
         d = self.dims

@@ -315,6 +315,19 @@ def test_per_head_calls_validate():
     if need:                                                   # a plan that splits needs the workspace
         assert decode(ws=FAKE, ws_bytes=need - 1) == 3
 
+    def decode_proj(dims=tiny, lens=(100, 3), ws=None, ws_bytes=0, w_uv=FAKE, out=FAKE):
+        lens_host = (ctypes.c_int32 * len(lens))(*lens)
+        return B.LIB.mla_decode_per_head_proj(ctypes.byref(dims), ctypes.byref(cache), FAKE, seq, lens_host,
+                                              len(lens), w_uv, out, None, ws, ws_bytes, None)
+
+    assert decode_proj(w_uv=None) == 1
+    assert decode_proj(out=None) == 1
+    assert decode_proj(dims=_dims()) == 2
+    assert decode_proj(dims=_dims(n_heads=16, d_head=128, d_v=64, d_latent=256, d_rope=32)) == 2
+    need = B.LIB.mla_decode_proj_workspace_size(ctypes.byref(tiny), 2, lens)
+    assert need > 0                                            # a partial slot per item, split or not
+    assert decode_proj() == 3 and decode_proj(ws=FAKE, ws_bytes=need - 1) == 3
+
 
 def test_header_compiles_as_c_and_cpp(tmp_path):
     """include/mla.h is a plain C header: it compiles as strict C99 and as C++17, warning-free."""

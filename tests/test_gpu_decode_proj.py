@@ -184,3 +184,39 @@ def test_config5_full_decode_proj():
     fused, sep, dims = both_paths(case)
     check_against(fused, sep, oracle_decode(case, evaluate=attention.absorbed), dims, case.seq_lens, "bf16", "c5a",
                   "C5 decode_proj")
+
+
+# ------------------------------------------------------ per-head position keys ----
+
+def per_head_both(case, precise):
+    """(fused, separate) over a per-head-key cache: mla_decode_per_head_proj against
+    mla_decode_per_head + mla_out_proj on the same q_lat."""
+    dims = G.dims_of(case, precise)
+    bf = torch.bfloat16
+    step = mla.PerHeadDecodeStep(dims, case.block_table, case.num_pages, torch.from_numpy(case.seq_lens),
+                                 fill=float("nan"))
+    seqs, pos = case.kv_seq_pos()
+    step.write(G.dev(case.c_rows, bf), G.dev(case.kr_rows, bf), torch.from_numpy(seqs).cuda(),
+               torch.from_numpy(pos).cuda())
+    w_uv = G.dev(case.w_uv, bf)
+    step.run(G.dev(case.qc, bf), G.dev(case.qr, bf), G.dev(case.w_uk, bf), w_uv)
+    torch.cuda.synchronize()
+    sep = {"o": G.to64(step.out), "lse": G.to64(step.lse)}
+    step.out.fill_(float("nan"))
+    step.lse.fill_(float("nan"))
+    step.attend_proj(w_uv)
+    torch.cuda.synchronize()
+    return {"o": G.to64(step.out), "lse": G.to64(step.lse)}, sep, dims
+
+
+@pytest.mark.parametrize("precise", [True, False], ids=["f32-q", "bf16-q"])
+@pytest.mark.parametrize("split_pages", [None, 1, 3])
+def test_decode_per_head_proj(precise, split_pages, monkeypatch):
+    """float32 partials on this layout: every sequence equals the two calls bit for bit."""
+    if split_pages is not None:
+        monkeypatch.setenv("MLA_DECODE_SPLIT_PAGES", str(split_pages))
+    case = cases.per_head_decode()
+    fused, sep, dims = per_head_both(case, precise)
+    check_against(fused, sep, oracle_decode(case), dims, case.seq_lens, "bf16",
+                  "per_head_f32w" if precise else "per_head_bf16", f"per-head decode_proj split={split_pages}",
+                  bitwise_all=True)
