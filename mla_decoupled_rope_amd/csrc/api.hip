@@ -421,6 +421,8 @@ mla_status mla_out_proj(const mla_dims* dims, const void* out_latent, const void
     return fail(MLA_ERR_UNSUPPORTED, "bf16 output projection needs d_latent a multiple of 32 up to 512 and d_v a "
                                      "multiple of 64");
   if (n > (1LL << 31) / dims->n_heads) return fail(MLA_ERR_UNSUPPORTED, "n too large for one launch");
+  if (dims->dtype == MLA_F32 && n * dims->n_heads * static_cast<int64_t>(dims->d_v) / 4 >= (1LL << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "n too large for one float32 launch");
   mla::GemmParams p{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
                     dims->work_dtype, out_latent, w_uv, out, n};
   const hipError_t e = mla::launch_out_proj(p, as_stream(stream));

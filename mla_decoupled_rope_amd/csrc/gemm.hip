@@ -472,8 +472,11 @@ __global__ void __launch_bounds__(256) absorb_f32_kernel(GemmParams p) {
   static_cast<float*>(p.out)[nh * (DC + p.d_rope) + j] = acc;
 }
 
+// One wave per output o[n, h, v]: the lanes walk the W_UV row and the obar row
+// side by side (coalesced), then sum across the wave in a fixed order.
 __global__ void __launch_bounds__(256) out_proj_f32_kernel(GemmParams p) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int DC = p.d_latent, DV = p.d_v, H = p.n_heads;
   if (idx >= p.n * H * DV) return;
   const int v = idx % DV;
@@ -482,8 +485,10 @@ __global__ void __launch_bounds__(256) out_proj_f32_kernel(GemmParams p) {
   const float* ob = static_cast<const float*>(p.a) + nh * DC;
   const float* w = static_cast<const float*>(p.w) + (static_cast<int64_t>(h) * DV + v) * DC;
   float acc = 0.f;
-  for (int j = 0; j < DC; ++j) acc = fmaf(w[j], ob[j], acc);
-  static_cast<float*>(p.out)[idx] = acc;
+  for (int j = lane; j < DC; j += 64) acc = fmaf(w[j], ob[j], acc);
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) acc += __shfl_xor(acc, k, 64);
+  if (lane == 0) static_cast<float*>(p.out)[idx] = acc;
 }
 
 }  // namespace
@@ -553,7 +558,8 @@ hipError_t launch_out_proj(const GemmParams& p_in, hipStream_t s) {
   if (p.n == 0) return hipSuccess;
   if (p.dtype == 0) {
     const int64_t total = p.n * p.n_heads * p.d_v;
-    hipLaunchKernelGGL(out_proj_f32_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, p);
+    if ((total + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;  // one wave per output: grid limit
+    hipLaunchKernelGGL(out_proj_f32_kernel, dim3(static_cast<unsigned>((total + 3) / 4)), dim3(256), 0, s, p);
   } else {
     // token groups: enough workgroups to fill the chip (each loads its head's W_UV rows once)
     const int64_t per_group = static_cast<int64_t>(p.d_v / kOutRows) * p.n_heads;
