@@ -44,6 +44,14 @@
  *   out-of-range page id or sequence index makes the kernels skip (for
  *   writes) or clamp (for reads) that access, so memory stays safe but the
  *   affected outputs are unspecified.
+ * - Debug mode: with MLA_DEBUG_VALIDATE=1 in the environment, every call that
+ *   reads or writes the paged cache first checks on the device the
+ *   block-table entries (every page of every sequence it will read) and the
+ *   cache rows (kv_seq, kv_pos) it will write, and that the device lengths
+ *   (seq_lens, or cu_q and q_start_pos) equal their host copies.  It waits for
+ *   that check (synchronising `stream`, so not under graph capture) and on a
+ *   bad entry returns MLA_ERR_INVALID_ARG, naming the entry, having launched
+ *   nothing else.  The check allocates nothing.
  * - Page size must be 64 tokens.  Supported (n_heads, d_latent, d_rope)
  *   for MLA_BF16 attention: (16, 256, 32) and (128, 512, 64); MLA_F32
  *   accepts any n_heads <= 1024, d_latent <= 1024, d_rope <= 128.

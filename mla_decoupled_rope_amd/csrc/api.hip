@@ -261,6 +261,49 @@ size_t proj_workspace_bytes(const mla_dims* d, const Plan& p, int32_t batch) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Debug mode: with MLA_DEBUG_VALIDATE=1 in the environment, every call that
+// reads or writes the paged cache first checks on the device the block-table
+// entries and cache rows it will use, and that the device lengths are the host
+// copies it planned with; it synchronises the stream for that, and launches
+// nothing if the check fails.
+bool debug_validate() {
+  const char* e = std::getenv("MLA_DEBUG_VALIDATE");
+  return e != nullptr && e[0] == '1' && e[1] == '\0';
+}
+
+mla_status device_check(const mla_paged_cache* cache, int32_t batch, const int32_t* seq_lens,
+                        const int32_t* seq_lens_host, const int32_t* cu_q, const int32_t* q_start,
+                        const int32_t* cu_q_host, const int32_t* q_start_host, const int32_t* kv_seq,
+                        const int32_t* kv_pos, int64_t n_kv, void* stream) {
+  const mla::CheckParams c{cache->block_table, cache->num_seqs, cache->max_pages_per_seq, cache->num_pages, batch,
+                           seq_lens, cu_q, q_start, kv_seq, kv_pos, n_kv};
+  int32_t rec[6] = {};
+  const hipError_t e = mla::run_check(c, rec, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "MLA_DEBUG_VALIDATE check");
+  switch (rec[0]) {
+    case mla::kCheckPage:
+      return fail(MLA_ERR_INVALID_ARG, "MLA_DEBUG_VALIDATE: block_table[%d][%d] = %d is not a page of the cache "
+                  "(0 .. %lld)", rec[1], rec[2], rec[3], static_cast<long long>(cache->num_pages) - 1);
+    case mla::kCheckLength:
+      return fail(MLA_ERR_INVALID_ARG, "MLA_DEBUG_VALIDATE: sequence %d reaches %d tokens on the device, beyond its "
+                  "block table", rec[1], rec[2]);
+    case mla::kCheckRow:
+      return fail(MLA_ERR_INVALID_ARG, "MLA_DEBUG_VALIDATE: cache row %d (sequence %d, position %d) has no page in "
+                  "the block table", rec[1], rec[2], rec[3]);
+    default:
+      break;
+  }
+  unsigned sum = 0, hash = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int t = cu_q_host != nullptr ? q_start_host[b] + (cu_q_host[b + 1] - cu_q_host[b]) : seq_lens_host[b];
+    sum += static_cast<unsigned>(t);
+    hash ^= (static_cast<unsigned>(t) * 2654435761u) ^ static_cast<unsigned>(b);
+  }
+  if (static_cast<int32_t>(sum) != rec[4] || static_cast<int32_t>(hash) != rec[5])
+    return fail(MLA_ERR_INVALID_ARG, "MLA_DEBUG_VALIDATE: the device lengths differ from their host copies");
+  return MLA_OK;
+}
+
 // Fixed device scratch of mla_decode_noalloc: the split partials of a decode
 // call live here instead of in a caller's workspace.  Each device the library
 // runs on holds one copy until the process ends.  Host code never passes the
@@ -379,6 +422,8 @@ mla_status mla_rope_apply(const mla_dims* dims, const mla_paged_cache* cache, co
   MLA_TRY(check_dims(dims));
   mla::RopeParams p{};
   MLA_TRY(rope_params(dims, cache, q_rope, q_pos, n_q, q_lat, kv_latent, k_rope, kv_seq, kv_pos, n_kv, &p));
+  if (n_kv > 0 && debug_validate())
+    MLA_TRY(device_check(cache, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, kv_seq, kv_pos, n_kv, stream));
   const hipError_t e = mla::launch_rope(p, as_stream(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "rope launch");
 }
@@ -394,6 +439,8 @@ mla_status mla_rope_absorb_q(const mla_dims* dims, const mla_paged_cache* cache,
   mla::GemmParams g{};
   MLA_TRY(absorb_params(dims, q_nope, w_uk, n_q, q_lat, &g));
   if (n_q == 0 && n_kv == 0) return MLA_OK;
+  if (n_kv > 0 && debug_validate())
+    MLA_TRY(device_check(cache, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, kv_seq, kv_pos, n_kv, stream));
   const hipError_t e = mla::launch_rope_absorb(g, r, as_stream(stream));
   return e == hipSuccess ? MLA_OK : hip_fail(e, "rope + absorb launch");
 }
@@ -506,6 +553,9 @@ mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, con
     if (seq_lens_host[b] > 0 && cache->num_pages == 0)
       return fail(MLA_ERR_INVALID_ARG, "sequence %d has tokens but the cache has no pages", b);
   }
+  if (debug_validate())
+    MLA_TRY(device_check(cache, batch, seq_lens, seq_lens_host, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                         stream));
   mla::AttnParams p{};
   p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
   p.f32w = dims->work_dtype == MLA_F32;
@@ -597,6 +647,8 @@ mla_status mla_cache_write_per_head(const mla_dims* dims, const mla_paged_cache*
   if (kv_latent == nullptr || k_rope == nullptr || kv_seq == nullptr || kv_pos == nullptr)
     return fail(MLA_ERR_INVALID_ARG, "kv_latent, k_rope, kv_seq and kv_pos must be non-NULL");
   if (n_kv > (static_cast<int64_t>(UINT32_MAX) - 3) * 4) return fail(MLA_ERR_UNSUPPORTED, "too many rows for one launch");
+  if (debug_validate())
+    MLA_TRY(device_check(cache, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, kv_seq, kv_pos, n_kv, stream));
   mla::RopeParams p{};
   p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
   p.dtype = dims->dtype; p.work_dtype = dims->work_dtype;
@@ -637,6 +689,9 @@ mla_status per_head_common(const mla_dims* dims, const mla_paged_cache* cache, c
     if (seq_lens_host[b] > 0 && cache->num_pages == 0)
       return fail(MLA_ERR_INVALID_ARG, "sequence %d has tokens but the cache has no pages", b);
   }
+  if (debug_validate())
+    MLA_TRY(device_check(cache, batch, seq_lens, seq_lens_host, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                         stream));
   const Plan plan = make_plan(dims, batch, seq_lens_host);
   const size_t need = fused ? proj_workspace_bytes(dims, plan, batch) : workspace_bytes(dims, plan);
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
@@ -726,6 +781,9 @@ mla_status mla_prefill(const mla_dims* dims, const mla_paged_cache* cache, const
   }
   if (n_blocks == 0) return MLA_OK;
   if (n_blocks > (1LL << 31) - 1) return fail(MLA_ERR_UNSUPPORTED, "too many workgroups");
+  if (debug_validate())
+    MLA_TRY(device_check(cache, batch, nullptr, nullptr, cu_q, q_start_pos, cu_q_host, q_start_pos_host, nullptr,
+                         nullptr, 0, stream));
   mla::AttnParams p{};
   p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
   p.f32w = dims->work_dtype == MLA_F32;
@@ -824,6 +882,9 @@ mla_status mla_prefill_mha(const mla_dims* dims, const mla_paged_cache* cache, c
   const size_t half = mha_ws_half(dims, pl.n_keys);
   if (workspace == nullptr || workspace_bytes < 2 * half)
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, 2 * half);
+  if (debug_validate())
+    MLA_TRY(device_check(cache, batch, nullptr, nullptr, cu_q, q_start_pos, cu_q_host, q_start_pos_host, nullptr,
+                         nullptr, 0, stream));
   mla::MhaParams p{};
   p.n_heads = dims->n_heads; p.d_latent = dims->d_latent; p.d_rope = dims->d_rope;
   p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);

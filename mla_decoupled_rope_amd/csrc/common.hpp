@@ -168,6 +168,20 @@ struct MhaParams {
   float* out; float* lse;              // [n_q, H, 128] float32 / [n_q, H]
 };
 
+// The debug-mode check of the paging data (MLA_DEBUG_VALIDATE=1): the
+// lengths are seq_lens (decode) or q_start + (cu_q[b+1] - cu_q[b]) (prefill,
+// when cu_q is set); kv_seq / kv_pos are the cache rows a call writes.
+struct CheckParams {
+  const int32_t* block_table; int32_t num_seqs; int32_t max_pages; int64_t num_pages;
+  int32_t batch;
+  const int32_t* seq_lens; const int32_t* cu_q; const int32_t* q_start;
+  const int32_t* kv_seq; const int32_t* kv_pos; int64_t n_kv;
+};
+enum CheckKind { kCheckOk = 0, kCheckPage = 1, kCheckLength = 2, kCheckRow = 3 };
+// Runs the check on stream s and waits for it: record = {kind, a, b, c,
+// sum of the lengths, xor-hash of (length * 2654435761) ^ index}.
+hipError_t run_check(const CheckParams& p, int32_t* record, hipStream_t s);
+
 // Launchers (each returns hipGetLastError() after the launch).
 hipError_t launch_rope(const RopeParams& p, hipStream_t s);
 hipError_t launch_perhead_decode(const AttnParams& p, hipStream_t s);
