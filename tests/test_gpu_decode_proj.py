@@ -82,8 +82,10 @@ def test_decode_proj_tiny_ragged(dtype):
                   bitwise_all=True)
 
 
-@pytest.mark.parametrize("split_pages", [None, 1, 3])
+@pytest.mark.parametrize("split_pages", [None, 1, 3, 1000])
 def test_decode_proj_dsv2_ragged(split_pages, monkeypatch):
+    """Planned splits, forced 1- and 3-page splits, and 1000-page splits (every sequence
+    one item: every row passes through its float16 partial)."""
     if split_pages is not None:
         monkeypatch.setenv("MLA_DECODE_SPLIT_PAGES", str(split_pages))
     case = cases.dsv2_decode_ragged()
