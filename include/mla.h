@@ -226,6 +226,36 @@ mla_status mla_decode_proj(const mla_dims* dims, const mla_paged_cache* cache, c
                            const void* w_uv, void* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* mla_decode_split_kv, mla_merge_out_proj -- mla_decode_proj's two launches
+ * as two calls, for callers that enqueue them apart or time each step alone.
+ * The first is the split-KV attention over the cache ("Multi-Head Latent
+ * Attention", "Why this matters on a GPU"; "AI decoupled RoPE MLA",
+ * decoupled-RoPE score equation): every work item of the split plan leaves
+ * its normalised partial obar_s and lse_s in the workspace.  The second
+ * merges each sequence's partials in split order (lse = log sum_s e^{lse_s},
+ * obar = sum_s e^{lse_s - lse} obar_s) and applies the output absorption
+ * ("AI decoupled RoPE MLA", recap section: W^UV on the output side).
+ *   mla_decode_split_kv: dims, cache, q_lat, seq_lens, seq_lens_host, batch
+ *   as for mla_decode_proj; it writes only the workspace.
+ *   mla_merge_out_proj: the same dims, seq_lens, seq_lens_host and batch;
+ *   w_uv, out, lse as for mla_decode_proj; it reads the workspace the first
+ *   call filled.
+ * workspace: at least mla_decode_proj_workspace_size() bytes, the same buffer
+ * in both calls; its contents between them are private to the library (the
+ * partials' format is not part of the interface).  Enqueued in that order on
+ * one stream with nothing writing the workspace between them, the pair gives
+ * mla_decode_proj's out and lse bit for bit.  bf16 caches only
+ * (MLA_ERR_UNSUPPORTED otherwise).  Errors as mla_decode_proj; nothing is
+ * launched on a failed check.  mla_merge_out_proj with lengths other than
+ * those the workspace was filled with leaves out unspecified (it reads no
+ * memory outside the workspace's work items). */
+mla_status mla_decode_split_kv(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                               const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch,
+                               void* workspace, size_t workspace_bytes, void* stream);
+mla_status mla_merge_out_proj(const mla_dims* dims, const int32_t* seq_lens, const int32_t* seq_lens_host,
+                              int32_t batch, const void* w_uv, void* out, float* lse, const void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* mla_decode_noalloc -- mla_decode for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation.  The same computation, arguments, results and errors as

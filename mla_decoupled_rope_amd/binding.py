@@ -57,6 +57,8 @@ def _load():
         "mla_decode": [pd, pc, vp, vp, vp, i32, vp, vp, vp, sz, vp],
         "mla_decode_noalloc": [pd, pc, vp, vp, vp, i32, vp, vp, vp],
         "mla_decode_proj": [pd, pc, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp],
+        "mla_decode_split_kv": [pd, pc, vp, vp, vp, i32, vp, sz, vp],
+        "mla_merge_out_proj": [pd, vp, vp, i32, vp, vp, vp, vp, sz, vp],
         "mla_prefill": [pd, pc, vp, vp, vp, vp, vp, i32, vp, vp, vp],
         "mla_out_proj": [pd, vp, vp, i64, vp, vp],
         "mla_decode_plan": [pd, i32, vp, ctypes.POINTER(i32), ctypes.POINTER(i64)],
@@ -91,7 +93,7 @@ def _load():
 LIB = _load()
 
 EXPORTS = ("mla_rope_apply", "mla_absorb_q", "mla_rope_absorb_q", "mla_decode_workspace_size", "mla_decode", "mla_decode_noalloc",
-           "mla_decode_proj_workspace_size", "mla_decode_proj",
+           "mla_decode_proj_workspace_size", "mla_decode_proj", "mla_decode_split_kv", "mla_merge_out_proj",
            "mla_prefill",
            "mla_out_proj", "mla_status_string", "mla_last_error", "mla_decode_plan",
            "mla_prefill_mha_workspace_size", "mla_prefill_mha", "mla_front_workspace_size", "mla_kv_project",
@@ -288,6 +290,42 @@ def decode_proj(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q
     _check(LIB.mla_decode_proj(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), seq_lens.data_ptr(),
                                seq_lens_host.data_ptr(), batch, w_uv.data_ptr(), out.data_ptr(), _ptr(lse),
                                _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
+
+
+def decode_split_kv(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat: torch.Tensor,
+                    seq_lens: torch.Tensor, seq_lens_host: torch.Tensor, workspace: torch.Tensor | None) -> None:
+    """mla_decode_split_kv: mla_decode_proj's split attention alone; every work item's partial
+    goes to the workspace (mla_decode_proj_workspace_size bytes) for merge_out_proj."""
+    batch = seq_lens_host.numel()
+    cstruct = _cache(dims, cache, block_table)
+    _dev(q_lat, "q_lat", dims.wdtype, (batch, dims.n_heads, dims.row))
+    _dev(seq_lens, "seq_lens", torch.int32, (batch,))
+    _host_i32(seq_lens_host, "seq_lens_host")
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+    d = dims.c()
+    _check(LIB.mla_decode_split_kv(ctypes.byref(d), ctypes.byref(cstruct), q_lat.data_ptr(), seq_lens.data_ptr(),
+                                   seq_lens_host.data_ptr(), batch, _ptr(workspace),
+                                   0 if workspace is None else workspace.numel(), _stream()))
+
+
+def merge_out_proj(dims: MLADims, seq_lens: torch.Tensor, seq_lens_host: torch.Tensor, w_uv: torch.Tensor,
+                   out: torch.Tensor, lse: torch.Tensor | None, workspace: torch.Tensor | None) -> None:
+    """mla_merge_out_proj: mla_decode_proj's split merge and output absorption alone, from the
+    workspace decode_split_kv filled."""
+    batch = seq_lens_host.numel()
+    _dev(seq_lens, "seq_lens", torch.int32, (batch,))
+    _host_i32(seq_lens_host, "seq_lens_host")
+    _dev(w_uv, "w_uv", dims.dtype, (dims.n_heads, dims.d_v, dims.d_latent))
+    _dev(out, "out", torch.float32, (batch, dims.n_heads, dims.d_v))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (batch, dims.n_heads))
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+    d = dims.c()
+    _check(LIB.mla_merge_out_proj(ctypes.byref(d), seq_lens.data_ptr(), seq_lens_host.data_ptr(), batch,
+                                  w_uv.data_ptr(), out.data_ptr(), _ptr(lse), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel(), _stream()))
 
 
 def decode(dims: MLADims, cache: torch.Tensor, block_table: torch.Tensor, q_lat: torch.Tensor,

@@ -337,7 +337,12 @@ mla_status noalloc_scratch(void** ptr) {
 mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat, const int32_t* seq_lens,
                          const int32_t* seq_lens_host, int32_t batch, void* out_latent, float* lse, void* workspace,
                          size_t ws_bytes, void* stream, bool fixed_scratch, const void* w_uv = nullptr,
-                         float* out = nullptr);
+                         float* out = nullptr, int phase = 0);
+
+// Which launches of mla_decode_proj a call enqueues: both, the split attention
+// alone (mla_decode_split_kv), or the merge with the output absorption alone
+// (mla_merge_out_proj).
+constexpr int kPhaseBoth = 0, kPhaseAttention = 1, kPhaseMerge = 2;
 
 }  // namespace
 
@@ -515,6 +520,24 @@ mla_status mla_decode_proj(const mla_dims* dims, const mla_paged_cache* cache, c
                        stream, false, w_uv, static_cast<float*>(out));
 }
 
+mla_status mla_decode_split_kv(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
+                               const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  g_err.clear();
+  return decode_common(dims, cache, q_lat, seq_lens, seq_lens_host, batch, nullptr, nullptr, workspace, ws_bytes,
+                       stream, false, nullptr, nullptr, kPhaseAttention);
+}
+
+mla_status mla_merge_out_proj(const mla_dims* dims, const int32_t* seq_lens, const int32_t* seq_lens_host,
+                              int32_t batch, const void* w_uv, void* out, float* lse, const void* workspace,
+                              size_t ws_bytes, void* stream) {
+  g_err.clear();
+  if (w_uv == nullptr || out == nullptr) return fail(MLA_ERR_INVALID_ARG, "w_uv and out must be non-NULL");
+  return decode_common(dims, nullptr, nullptr, seq_lens, seq_lens_host, batch, nullptr, lse,
+                       const_cast<void*>(workspace), ws_bytes, stream, false, w_uv, static_cast<float*>(out),
+                       kPhaseMerge);
+}
+
 mla_status mla_decode_noalloc(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat,
                               const int32_t* seq_lens, const int32_t* seq_lens_host, int32_t batch, void* out_latent,
                               float* lse, void* stream) {
@@ -531,29 +554,36 @@ namespace {
 
 mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, const void* q_lat, const int32_t* seq_lens,
                          const int32_t* seq_lens_host, int32_t batch, void* out_latent, float* lse, void* workspace,
-                         size_t ws_bytes, void* stream, bool fixed_scratch, const void* w_uv, float* out) {
+                         size_t ws_bytes, void* stream, bool fixed_scratch, const void* w_uv, float* out,
+                         int phase) {
+  const bool attend = phase != kPhaseMerge;  // this call launches the attention
   MLA_TRY(check_dims(dims));
   MLA_TRY(check_attn_shape(dims));
-  MLA_TRY(check_cache(cache));
+  if (attend) MLA_TRY(check_cache(cache));
   if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 0");
   if (batch == 0) return MLA_OK;
-  if (batch > cache->num_seqs)
+  if (attend && batch > cache->num_seqs)
     return fail(MLA_ERR_INVALID_ARG, "batch (%d) exceeds the block table's rows (%d)", batch, cache->num_seqs);
-  const bool fused = w_uv != nullptr || out != nullptr;  // mla_decode_proj
-  if (q_lat == nullptr || seq_lens == nullptr || seq_lens_host == nullptr)
+  // mla_decode_proj, or one of its two launches: every work item leaves a partial
+  const bool fused = w_uv != nullptr || out != nullptr || phase != kPhaseBoth;
+  if ((attend && q_lat == nullptr) || seq_lens == nullptr || seq_lens_host == nullptr)
     return fail(MLA_ERR_INVALID_ARG, "q_lat, seq_lens and seq_lens_host must be non-NULL");
   if (!fused && out_latent == nullptr) return fail(MLA_ERR_INVALID_ARG, "out_latent must be non-NULL");
-  if (fused && (w_uv == nullptr || out == nullptr)) return fail(MLA_ERR_INVALID_ARG, "w_uv and out must be non-NULL");
+  if (fused && phase != kPhaseAttention && (w_uv == nullptr || out == nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "w_uv and out must be non-NULL");
   if (fused && dims->d_v != 128) return fail(MLA_ERR_UNSUPPORTED, "mla_decode_proj needs d_v = 128");
+  if (phase != kPhaseBoth && dims->dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_split_kv and mla_merge_out_proj take bf16 caches only");
   for (int b = 0; b < batch; ++b) {
     if (seq_lens_host[b] < 0 ||
-        static_cast<int64_t>(seq_lens_host[b]) > static_cast<int64_t>(cache->max_pages_per_seq) * mla::kPage)
+        (attend &&
+         static_cast<int64_t>(seq_lens_host[b]) > static_cast<int64_t>(cache->max_pages_per_seq) * mla::kPage))
       return fail(MLA_ERR_INVALID_ARG, "seq_lens_host[%d] = %d is negative or beyond the block table", b,
                   seq_lens_host[b]);
-    if (seq_lens_host[b] > 0 && cache->num_pages == 0)
+    if (attend && seq_lens_host[b] > 0 && cache->num_pages == 0)
       return fail(MLA_ERR_INVALID_ARG, "sequence %d has tokens but the cache has no pages", b);
   }
-  if (debug_validate())
+  if (attend && debug_validate())
     MLA_TRY(device_check(cache, batch, seq_lens, seq_lens_host, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
                          stream));
   mla::AttnParams p{};
@@ -561,8 +591,10 @@ mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, con
   p.f32w = dims->work_dtype == MLA_F32;
   p.scale = dims->softmax_scale;
   p.scale_log2 = static_cast<float>(dims->softmax_scale * 1.4426950408889634);
-  p.q_lat = q_lat; p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
-  p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
+  if (attend) {
+    p.q_lat = q_lat; p.cache = cache->data; p.num_pages = cache->num_pages; p.block_table = cache->block_table;
+    p.num_seqs = cache->num_seqs; p.max_pages = cache->max_pages_per_seq;
+  }
   p.seq_lens = seq_lens; p.batch = batch; p.out_latent = out_latent; p.lse = lse;
   hipStream_t s = as_stream(stream);
   const Plan plan = make_plan(dims, batch, seq_lens_host);
@@ -602,8 +634,12 @@ mla_status decode_common(const mla_dims* dims, const mla_paged_cache* cache, con
           align_ws(static_cast<size_t>(plan.n_items) * dims->n_heads * dims->d_latent * 2));
     }
   }
-  hipError_t e = mla::launch_decode_bf16(p, s);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  hipError_t e = hipSuccess;
+  if (attend) {
+    e = mla::launch_decode_bf16(p, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  if (phase == kPhaseAttention) return MLA_OK;
   if (fused) {
     const mla::GemmParams g{dims->n_heads, dims->d_head, dims->d_v, dims->d_latent, dims->d_rope, dims->dtype,
                             dims->work_dtype, nullptr, w_uv, out, batch};

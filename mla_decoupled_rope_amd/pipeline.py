@@ -118,6 +118,19 @@ class DecodeStep:
         B.decode_proj(self.dims, self.cache.data, self.cache.block_table, self.q_lat, self.seq_lens,
                       self.seq_lens_host, w_uv, self.out, self.lse, self.proj_workspace)
 
+    def attend_split_kv(self):
+        """mla_decode_split_kv over q_lat: the first of mla_decode_proj's two launches (the split
+        partials go to the fused workspace; merge_out_proj finishes the step)."""
+        if self.proj_workspace is None and self.proj_ws_bytes:
+            self.proj_workspace = torch.empty(self.proj_ws_bytes, dtype=torch.uint8, device=self.q_lat.device)
+        B.decode_split_kv(self.dims, self.cache.data, self.cache.block_table, self.q_lat, self.seq_lens,
+                          self.seq_lens_host, self.proj_workspace)
+
+    def merge_out_proj(self, w_uv):
+        """mla_merge_out_proj: the second launch, from the workspace attend_split_kv filled."""
+        B.merge_out_proj(self.dims, self.seq_lens, self.seq_lens_host, w_uv, self.out, self.lse,
+                         self.proj_workspace)
+
     def run_fused(self, q_nope, q_rope, w_uk, w_uv, new_latent=None, new_k_rope=None):
         """As run(), with attention, the split merge and the output absorption through
         mla_decode_proj: two launches after the query prologue instead of three."""

@@ -120,6 +120,42 @@ def test_decode_proj_validates():
     assert B.LIB.mla_decode_proj_workspace_size(ctypes.byref(f), 3, (ctypes.c_int32 * 3)(5, 0, 9)) == 3 * 16 * 256 * 4
 
 
+def test_split_kv_and_merge_validate():
+    """mla_decode_proj's two launches as two calls: each checks its own arguments (and the
+    workspace of the fused call) before any launch; float32 caches are refused."""
+    d = _dims()
+    cache = B.PagedCache(data=FAKE.value, num_pages=4, block_table=FAKE.value, num_seqs=4, max_pages_per_seq=4)
+
+    def split(dd=d, batch=1, lens=(10,), q=FAKE, ws=None, ws_bytes=0):
+        lh = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+        return B.LIB.mla_decode_split_kv(ctypes.byref(dd), ctypes.byref(cache), q, FAKE, lh, batch, ws, ws_bytes,
+                                         None)
+
+    def merge(dd=d, batch=1, lens=(10,), w_uv=FAKE, out=FAKE, ws=None, ws_bytes=0):
+        lh = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+        return B.LIB.mla_merge_out_proj(ctypes.byref(dd), FAKE, lh, batch, w_uv, out, None, ws, ws_bytes, None)
+
+    assert split(q=None) == 1
+    assert split(batch=5, lens=(1, 1, 1, 1, 1)) == 1          # more rows than the block table
+    assert split(lens=(300,)) == 1                            # beyond 4 pages of 64
+    assert split(_dims(d_v=64)) == 2
+    assert split(batch=0) == 0
+    assert merge(w_uv=None) == 1 and merge(out=None) == 1
+    assert merge(lens=(-1,)) == 1
+    assert merge(_dims(n_heads=64)) == 2
+    assert merge(batch=0) == 0
+    f = _dims(n_heads=16, d_latent=256, d_rope=32, dtype=B.MLA_F32, work_dtype=B.MLA_F32)
+    assert split(f) == 2 and merge(f) == 2
+    assert "bf16" in B.LIB.mla_last_error().decode()
+    lens = (200,)
+    need = B.LIB.mla_decode_proj_workspace_size(ctypes.byref(d), 1, (ctypes.c_int32 * 1)(*lens))
+    assert need > 0
+    for call in (split, merge):
+        assert call(lens=lens) == 3
+        assert call(lens=lens, ws=FAKE, ws_bytes=need - 1) == 3
+        assert "workspace" in B.LIB.mla_last_error().decode()
+
+
 def test_every_export_has_a_ctypes_signature():
     """Without argtypes ctypes passes a Python int as a C int, truncating 64-bit host
     pointers: every exported function must declare its arguments."""

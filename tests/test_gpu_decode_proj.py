@@ -94,6 +94,44 @@ def test_decode_proj_dsv2_ragged(split_pages, monkeypatch):
                   f"dsv2 decode_proj split={split_pages}")
 
 
+def fused_in_two_calls(case):
+    """(one call, two calls): mla_decode_proj, then mla_decode_split_kv + mla_merge_out_proj on the
+    same q_lat, each into freshly poisoned outputs."""
+    dims = G.dims_of(case)
+    step = mla.DecodeStep(dims, G.build_cache(case), torch.from_numpy(case.seq_lens))
+    bf = torch.bfloat16
+    w_uv = G.dev(case.w_uv, bf)
+    step.run(G.dev(case.qc, bf), G.dev(case.qr, bf), G.dev(case.w_uk, bf), w_uv)
+    res = []
+    for two in (False, True):
+        step.out.fill_(float("nan"))
+        step.lse.fill_(float("nan"))
+        if step.proj_workspace is not None:
+            step.proj_workspace.fill_(0xFF)  # partials as NaN: a slot left unwritten would show
+        if two:
+            step.attend_split_kv()
+            step.merge_out_proj(w_uv)
+        else:
+            step.attend_proj(w_uv)
+        torch.cuda.synchronize()
+        res.append((step.out.clone(), step.lse.clone()))
+    return res
+
+
+@pytest.mark.parametrize("which", ["tiny", "dsv2", "dsv2_split1", "dsv2_one_item", "empty"])
+def test_split_kv_then_merge_equals_decode_proj(which, monkeypatch):
+    """mla_decode_proj's two launches called one by one give its output and lse bit for bit."""
+    forced = {"dsv2_split1": "1", "dsv2_one_item": "1000"}.get(which)
+    if forced is not None:
+        monkeypatch.setenv("MLA_DECODE_SPLIT_PAGES", forced)
+    case = {"tiny": lambda: cases.tiny_decode_ragged("bf16"), "empty": cases.decode_empty}.get(
+        which, cases.dsv2_decode_ragged)()
+    (o1, l1), (o2, l2) = fused_in_two_calls(case)
+    print(f"{which}: {case.batch} sequences, lengths {case.seq_lens.min()}..{case.seq_lens.max()}", flush=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert not torch.isnan(o1).any()
+
+
 def test_decode_proj_empty_sequences():
     case = cases.decode_empty()
     fused, sep, dims = both_paths(case)
@@ -170,6 +208,13 @@ def test_config3_full_decode_proj():
     assert np.all(items_per_sequence(dims, case.seq_lens) > 1)
     check_against(fused, sep, oracle_decode(case, evaluate=attention.absorbed), dims, case.seq_lens, "bf16", "c3",
                   "C3 decode_proj")
+
+
+def test_config3_split_kv_then_merge():
+    """The launch bench.py times as the dominant kernel (the split attention alone), followed by
+    the merge with the output absorption, equals mla_decode_proj bit for bit at 64 x 4096."""
+    (o1, l1), (o2, l2) = fused_in_two_calls(synth.config3())
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_config4_full_decode_proj():
