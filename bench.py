@@ -470,11 +470,15 @@ def main():
     el = time.perf_counter() - t0
     ms_per_step = el / args.steps * 1e3
 
-    # The measured call alone, `steps` times back to back on the launch stream
-    # between two HIP events: an event recorded between two kernels idles the
+    # The measured call alone, `warmup` untimed then `steps` times back to back
+    # on the launch stream between two HIP events: an event recorded between two kernels idles the
     # queue for several microseconds (a kernel trace shows the gap exactly where
     # the event sits), so bracketing each call would time the events too.
     def timed_loop(fn):
+        # the same W untimed launches first, as for the steps
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
         e0 = events.record(sh)
         for i in range(args.steps):
             fn(i)
