@@ -8,6 +8,9 @@
 namespace mla {
 
 constexpr int kPage = 64;  // tokens per cache page (one attention tile)
+// Cache-policy operand of the buffer intrinsics (gfx950): the nt bit marks a
+// load's lines for early eviction (data read once, as a decode streams the cache).
+constexpr int kCpolNt = 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

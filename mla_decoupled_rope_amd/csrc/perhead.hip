@@ -122,7 +122,8 @@ __global__ void __launch_bounds__(256, 1) perhead_decode_kernel(AttnParams p) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), 0, valid * kPhRow * 2, kPhBufferWord3);
 #pragma unroll
-    for (int i = 0; i < kPhLoads; ++i) ld[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, i * 4096, 0);
+    // nt: each page is read once, by one workgroup (2-3% faster at 64 x 4096)
+    for (int i = 0; i < kPhLoads; ++i) ld[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, i * 4096, kCpolNt);
   };
   auto store_page = [&]() {
 #pragma unroll
