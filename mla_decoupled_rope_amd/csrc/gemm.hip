@@ -365,10 +365,11 @@ __global__ void __launch_bounds__(512, 4) merge_proj_kernel(GemmParams g, AttnPa
   const float* part = a.ws_o + row0 * DC + col;
   const _Float16* hpart = reinterpret_cast<const _Float16*>(a.ws_o) + row0 * DC + col;
   const int32_t* pexp = HALF ? a.ws_exp + row0 * (DC / 128) + col / 128 : nullptr;
-  // a round's partials stay in their stored type until used (float16 ones
-  // take half the registers of their float32 values)
+  // a round's partials stay in their stored type until used, as 32-bit words
+  // (float16 ones two to a register: half the registers of their values)
   using PT = typename std::conditional<HALF, _Float16, float>::type;
-  PT v[U][CPT];
+  constexpr int VW = CPT * static_cast<int>(sizeof(PT)) / 4;
+  uint32_t v[U][VW];
   int vex[U];
   float wl[U];
   auto load_round = [&](int s0) {
@@ -377,21 +378,32 @@ __global__ void __launch_bounds__(512, 4) merge_proj_kernel(GemmParams g, AttnPa
       if (s0 + u < ns) {
         const int64_t so = static_cast<int64_t>(s0 + u) * H;
         if constexpr (HALF) {
-          __builtin_memcpy(v[u], hpart + so * DC, CPT * sizeof(_Float16));
+          __builtin_memcpy(v[u], hpart + so * DC, VW * 4);
           vex[u] = pexp[so * (DC / 128)];
         } else {
-          __builtin_memcpy(v[u], part + so * DC, CPT * sizeof(float));
+          __builtin_memcpy(v[u], part + so * DC, VW * 4);
         }
         wl[u] = lse_s[so];
       } else {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) v[u][i] = 0;
+        for (int i = 0; i < VW; ++i) v[u][i] = 0;
         vex[u] = 0;
         wl[u] = -INFINITY;
       }
     }
   };
   load_round(0);
+  // W_UV[h] rows v0 + r16, all of d_c, as MFMA A fragments.  With float16
+  // partials the first half goes out now, under the partial loads; the rest
+  // after the merge, when the partials' registers are free (all of it at once
+  // would not fit two workgroups a CU).  Float32 partials take twice the
+  // registers, so there all of it waits for the merge.
+  constexpr int KW0 = HALF ? DC / 64 : 0;
+  const int v0 = wave * 16;
+  const bf16_t* w = static_cast<const bf16_t*>(g.w) + (static_cast<int64_t>(h) * DV + v0 + r16) * DC + q16 * 8;
+  bf16x8 wa[DC / 32];
+#pragma unroll
+  for (int k = 0; k < KW0; ++k) wa[k] = load8(w + k * 32);
   // max of the splits' lse: the sequence's 32 threads take splits side by side
   float m = -INFINITY;
   for (int s0 = 0; s0 < ns; s0 += 32)
@@ -411,20 +423,19 @@ __global__ void __launch_bounds__(512, 4) merge_proj_kernel(GemmParams g, AttnPa
         wsum += wu;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-          const float x = HALF ? ldexpf(static_cast<float>(v[u][i]), vex[u]) : static_cast<float>(v[u][i]);
+          float x;
+          if constexpr (HALF)
+            x = ldexpf(static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v[u][i / 2] >> (16 * (i % 2))))),
+                       vex[u]);
+          else
+            x = __builtin_bit_cast(float, v[u][i]);
           acc[i] = fmaf(wu, x, acc[i]);
         }
       }
     }
   }
-  // W_UV[h] rows v0 + r16, all of d_c, as MFMA A fragments: loaded after the
-  // merge (so the two sets of registers are not live together), their
-  // latency under the staging below and the other workgroup on the CU
-  const int v0 = wave * 16;
-  const bf16_t* w = static_cast<const bf16_t*>(g.w) + (static_cast<int64_t>(h) * DV + v0 + r16) * DC + q16 * 8;
-  bf16x8 wa[DC / 32];
 #pragma unroll
-  for (int k = 0; k < DC / 32; ++k) wa[k] = load8(w + k * 32);
+  for (int k = KW0; k < DC / 32; ++k) wa[k] = load8(w + k * 32);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   if (a.lse != nullptr && l32 == 0 && b < g.n) a.lse[b * H + h] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
   // stage obar (zeros for rows past the batch) as hi + lo.  No contraction
