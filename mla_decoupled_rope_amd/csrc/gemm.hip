@@ -339,6 +339,18 @@ __global__ void __launch_bounds__(512, 4) merge_proj_kernel(GemmParams g, AttnPa
   const int col = l32 * CPT;
   const int64_t b = s_begin + sq;
   const int64_t s_end = min(g.n, s_begin + kMpSeqs);
+  // W_UV[h] rows v0 + r16, all of d_c, as MFMA A fragments.  With float16
+  // partials the first half goes out first, under the loads of the lengths
+  // and the partials (its addresses need neither); the rest after the merge,
+  // when the partials' registers are free (all of it at once would not fit
+  // two workgroups a CU).  Float32 partials take twice the registers, so
+  // there all of it waits for the merge.
+  constexpr int KW0 = HALF ? DC / 64 : 0;
+  const int v0 = wave * 16;
+  const bf16_t* w = static_cast<const bf16_t*>(g.w) + (static_cast<int64_t>(h) * DV + v0 + r16) * DC + q16 * 8;
+  bf16x8 wa[DC / 32];
+#pragma unroll
+  for (int k = 0; k < KW0; ++k) wa[k] = load8(w + k * 32);
   const int L = a.split_pages;
   int ns = 0;
   int64_t base = 0;
@@ -393,17 +405,6 @@ __global__ void __launch_bounds__(512, 4) merge_proj_kernel(GemmParams g, AttnPa
     }
   };
   load_round(0);
-  // W_UV[h] rows v0 + r16, all of d_c, as MFMA A fragments.  With float16
-  // partials the first half goes out now, under the partial loads; the rest
-  // after the merge, when the partials' registers are free (all of it at once
-  // would not fit two workgroups a CU).  Float32 partials take twice the
-  // registers, so there all of it waits for the merge.
-  constexpr int KW0 = HALF ? DC / 64 : 0;
-  const int v0 = wave * 16;
-  const bf16_t* w = static_cast<const bf16_t*>(g.w) + (static_cast<int64_t>(h) * DV + v0 + r16) * DC + q16 * 8;
-  bf16x8 wa[DC / 32];
-#pragma unroll
-  for (int k = 0; k < KW0; ++k) wa[k] = load8(w + k * 32);
   // max of the splits' lse: the sequence's 32 threads take splits side by side
   float m = -INFINITY;
   for (int s0 = 0; s0 < ns; s0 += 32)
