@@ -29,6 +29,7 @@ METRIC = "absorbed MLA decode tokens/s + % HBM roofline (n_h=128,d_c=512,d_r=64)
 HBM_PEAK_GBS = 8000.0
 QUERY_LATENT = 1536  # the query latent width of the DeepSeek-V2-like layer
 BF16_PEAK_TFLOPS = 2500.0
+KERNEL_WARMUP_S = 0.05  # untimed lead-in of the kernel-timing loops (not of the steps)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "attn_bf16.hip")
 MHA_SRC = os.path.join(ROOT, "mla_decoupled_rope_amd", "csrc", "mha.hip")
@@ -470,14 +471,22 @@ def main():
     el = time.perf_counter() - t0
     ms_per_step = el / args.steps * 1e3
 
-    # The measured call alone, `warmup` untimed then `steps` times back to back
-    # on the launch stream between two HIP events: an event recorded between two kernels idles the
+    # The measured call alone, after an untimed lead-in, `steps` times back to
+    # back on the launch stream between two HIP events: an event recorded between two kernels idles the
     # queue for several microseconds (a kernel trace shows the gap exactly where
     # the event sits), so bracketing each call would time the events too.
     def timed_loop(fn):
-        # the same W untimed launches first, as for the steps
-        for i in range(args.warmup):
+        # Untimed first: at least W launches and at least KERNEL_WARMUP_S of them
+        # (synchronising every 16 so the host clock follows the GPU), so the
+        # kernel is timed at the clock a sustained decode runs at: after an idle
+        # host phase the GPU takes tens of milliseconds of load to reach it, and
+        # a loop of 20 launches would fall inside that ramp.
+        t_w, i = time.perf_counter(), 0
+        while i < args.warmup or time.perf_counter() - t_w < KERNEL_WARMUP_S:
             fn(i)
+            i += 1
+            if i % 16 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         e0 = events.record(sh)
         for i in range(args.steps):
