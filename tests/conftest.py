@@ -21,15 +21,5 @@ if not _build.is_current():
     _build.build()
 
 
-# Under pytest-xdist every worker would start one BLAS thread per core for the
-# float64 oracle; share the cores among the workers instead.
-_blas_limit = None
-if os.environ.get("PYTEST_XDIST_WORKER"):
-    from threadpoolctl import threadpool_limits
-
-    _workers = max(1, int(os.environ.get("PYTEST_XDIST_WORKER_COUNT", "1")))
-    _blas_limit = threadpool_limits(limits=max(1, (os.cpu_count() or 1) // _workers))
-
-
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
